@@ -1,0 +1,207 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) MoE-layer hot path: top-k routing, permute into
+ * expert-contiguous rows, grouped SwiGLU expert FFN over stacked weights, and the
+ * weighted combine back to token order, all on one GPU.
+ *
+ * The operations follow these pages:
+ *  - "Mixture of Kittens" (MoE megakernel article), Step 1 "The Math": a router picks the
+ *    top-k experts of each token, each expert is Down(SwiGLU(Up x, Gate x)), and the
+ *    routed outputs are summed with their router weights.
+ *  - "Distributed expert parallelism" (open-llm-engineering), "The dispatch-compute-combine
+ *    lifecycle", "Token permutation and metadata" and "Grouped expert computation": copy each
+ *    token k times, group the copies by expert, run one grouped GEMM over the groups, restore
+ *    token order, scale by route weights and add.
+ *  - MoonEP README, "Integration" / "Weight buffer" and "API walkthrough": stacked contiguous
+ *    expert weights addressed purely by expert index, cu_seqlens selecting each expert's rows,
+ *    dispatch/combine taking [S,H] activations, [S,K] fp32 weights and [S,K] int32 expert ids.
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers, row-major and densely packed, unless stated otherwise.
+ *    The caller owns every buffer and keeps it alive until the stream has passed the call.
+ *    The library never allocates, frees or retains caller memory.
+ *  - Calls only enqueue work on `stream` and return; there is no host synchronisation, except
+ *    when the environment variable MOE_VALIDATE=1 asks for the data checks described below.
+ *    All shapes are static (M = T*K rows), cu_seqlens stays on the device.
+ *  - Errors are returned as moe_status_t; nothing is thrown. Argument checks happen on the
+ *    host before anything is enqueued: MOE_EINVAL (bad sizes, NULL where a buffer is needed,
+ *    K > E), MOE_EUNSUPPORTED (a dtype combination or a dimension multiple this build does not
+ *    implement), MOE_EWORKSPACE (workspace too small). A failed launch gives MOE_EHIP.
+ *  - T = 0 and experts that receive no rows are legal and produce valid (empty) groups.
+ *  - Expert ids outside [0, E) in a caller-given top-k are memory-safe: that copy is dropped
+ *    (pos = -1, no row, no contribution). With MOE_VALIDATE=1 the library also checks for
+ *    such ids and for an expert repeated within one token, synchronises the stream and
+ *    returns MOE_EINVAL if any is found.
+ *  - MOE_DEBUG_POISON=1 fills the whole workspace with 0xFF bytes (NaN in every float
+ *    format) before use, so a read of an unwritten workspace byte shows up as NaN.
+ *
+ * Notation: T tokens, H hidden size, Hp expert intermediate size (H'), E experts (or expert
+ * slots), K experts per token, M = T*K routed rows.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#define MOE_API __attribute__((visibility("default")))
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,
+  MOE_EUNSUPPORTED = 2,
+  MOE_EWORKSPACE = 3,
+  MOE_EHIP = 4
+} moe_status_t;
+
+/* Storage formats.
+ *  MOE_F32       IEEE binary32.
+ *  MOE_BF16      bfloat16 (top half of binary32), results rounded to nearest even.
+ *  MOE_FP8_E4M3  OCP e4m3fn bytes (bias 7, max 448, no infinities). Activations in this
+ *                format come with fp32 scales, one per 1x128 block along the row, each an
+ *                exact power of two: value = decode(code) * scale[row][col / 128].
+ *  MOE_MXFP4     OCP MX e2m1 codes, two per byte, with one e8m0 scale byte per 32 elements
+ *                along the reduction dimension: value = e2m1(code) * 2^(scale - 127).
+ *                Stored reduction-contiguous: byte j of output column n holds reduction
+ *                index 2j in its low nibble and 2j+1 in its high nibble. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_dtype_t;
+
+/* How the K expert results of a token are summed.
+ *  MOE_COMBINE_GATHER  deterministic gather-reduce in fixed k order (bitwise reproducible),
+ *                      following "Mixture of Kittens", Step 8 "Full Determinism".
+ *  MOE_COMBINE_SCATTER_ATOMIC  weighted scatter-add fused into the down-projection epilogue
+ *                      (fp32 atomics; the sum order, hence the last bit, may vary). */
+typedef enum { MOE_COMBINE_GATHER = 0, MOE_COMBINE_SCATTER_ATOMIC = 1 } moe_combine_t;
+
+/* Whole-layer description. Supported (act, wgt, out) combinations:
+ *  (F32, F32, F32), (BF16, BF16, BF16), (FP8_E4M3, MXFP4, BF16). */
+typedef struct {
+  int32_t T, H, Hp, E, K;
+  moe_dtype_t act, wgt, out;
+  moe_combine_t combine;
+} moe_layer_desc_t;
+
+/* Top-k routing ("Mixture of Kittens", Step 1; "Distributed expert parallelism", lifecycle
+ * item 1).
+ *  logits    [T, E] fp32.
+ *  topk_idx  [T, K] int32 out: the K experts with the largest logits, largest first; equal
+ *            logits are ordered by ascending expert id.
+ *  topk_w    [T, K] fp32 out: softmax over the K selected logits (= the full softmax
+ *            renormalised over the top K): w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0).
+ * Limits: 1 <= K <= min(E, 32), E <= 4096. */
+MOE_API moe_status_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t K,
+                            int32_t* topk_idx, float* topk_w, hipStream_t stream);
+
+/* Scratch bytes moe_permute needs for (T, E, K). */
+MOE_API size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t K);
+
+/* Permute token copies into expert-contiguous rows ("Distributed expert parallelism",
+ * "Token permutation and metadata"; MoonEP "dispatch fwd" without the remote writes).
+ *  x          [T, H] activations of format `act` (F32, BF16 or FP8_E4M3).
+ *  x_sf       [T, H/128] fp32 block scales when act = FP8_E4M3, else ignored (may be NULL).
+ *  topk_idx   [T, K] int32 expert ids; topk_w [T, K] fp32 (may be NULL when row_w is NULL).
+ *  counts     [E] int32 out: copies routed to each expert.
+ *  cu_seqlens [E+1] int32 out: cu_seqlens[0] = 0, cu_seqlens[e+1] = cu_seqlens[e] + counts[e].
+ *  pos        [T, K] int32 out: row of copy (t, k); -1 for a dropped (invalid-id) copy.
+ *  row_src    [T*K] int32 out: flat index t*K + k of the copy stored in each row.
+ *  row_w      [T*K] fp32 out (or NULL): topk_w of the copy stored in each row.
+ *  x_perm     [T*K, H] out, format `act`: x_perm[pos[t,k]] = x[t], bit for bit.
+ *  x_perm_sf  [T*K, H/128] fp32 out when act = FP8_E4M3.
+ * Row order is a stable counting sort: the rows of expert e hold its copies in ascending
+ * t*K + k. The result is deterministic. Limits: E <= 1024, K <= 32. */
+MOE_API moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t act,
+                         const int32_t* topk_idx, const float* topk_w, int32_t T, int32_t H,
+                         int32_t E, int32_t K, int32_t* counts, int32_t* cu_seqlens,
+                         int32_t* pos, int32_t* row_src, float* row_w, void* x_perm,
+                         float* x_perm_sf, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* First half of the grouped expert FFN ("Mixture of Kittens", Step 1; "Distributed expert
+ * parallelism", "Grouped expert computation"): for every expert e and its rows
+ * r in [cu_seqlens[e], cu_seqlens[e+1]):
+ *     g = x_perm[r] . Wg[e],  u = x_perm[r] . Wu[e],  h[r] = silu(g) * u,
+ * silu(z) = z / (1 + exp(-z)), accumulated in fp32.
+ *  Formats: act F32 + wgt F32 -> h F32; act BF16 + wgt BF16 -> h BF16;
+ *           act FP8_E4M3 + wgt MXFP4 -> h FP8_E4M3 with h_sf [M, Hp/128] fp32 power-of-two
+ *           scales (s = smallest power of two with 448*s >= block amax; code = e4m3fn
+ *           round-to-nearest-even of h/s).
+ *  F32/BF16 weights: w_gate, w_up [E, H, Hp] (g = x . W). MXFP4 weights: bytes [E, Hp, H/2]
+ *  with sf_gate, sf_up [E, Hp, H/32].
+ * One kernel launch; the tile schedule over the variable-size groups is derived on the device
+ * from cu_seqlens. Needs H % 64 == 0 and Hp % 128 == 0 (BF16), H % 128 == 0 and
+ * Hp % 128 == 0 (FP8/MXFP4); F32 has no multiple requirement. */
+MOE_API moe_status_t moe_ffn_gate_up(const void* x_perm, const float* x_perm_sf, moe_dtype_t act,
+                             const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
+                             int32_t Hp, const void* w_gate, const void* w_up,
+                             const uint8_t* sf_gate, const uint8_t* sf_up, moe_dtype_t wgt,
+                             void* h, float* h_sf, hipStream_t stream);
+
+/* Second half of the grouped expert FFN: y_rows[r] = h[r] . Wd[e] for the rows of expert e.
+ *  h_dtype F32 (wgt F32, out F32), BF16 (wgt BF16, out BF16) or FP8_E4M3 with h_sf
+ *  (wgt MXFP4, out BF16). F32/BF16 w_down [E, Hp, H]; MXFP4 bytes [E, H, Hp/2] with
+ *  sf_down [E, H, Hp/32]. Needs H % 256 == 0 and Hp % 64 == 0 (BF16), H % 128 == 0 and
+ *  Hp % 128 == 0 (FP8/MXFP4). One kernel launch. */
+MOE_API moe_status_t moe_ffn_down(const void* h, const float* h_sf, moe_dtype_t h_dtype,
+                          const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
+                          int32_t Hp, const void* w_down, const uint8_t* sf_down,
+                          moe_dtype_t wgt, void* y_rows, moe_dtype_t out, hipStream_t stream);
+
+/* Scratch bytes moe_grouped_ffn needs (the intermediate h and its scales). */
+MOE_API size_t moe_grouped_ffn_workspace_bytes(int32_t M, int32_t Hp, moe_dtype_t act, moe_dtype_t wgt);
+
+/* moe_ffn_gate_up followed by moe_ffn_down, with h kept in `ws`. y_rows [M, H] of format
+ * `out`. MoonEP "Integration": the group GEMM consumes one stacked weight tensor per
+ * projection and cu_seqlens selects the rows of each expert. */
+MOE_API moe_status_t moe_grouped_ffn(const void* x_perm, const float* x_perm_sf, moe_dtype_t act,
+                             const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
+                             int32_t Hp, const void* w_gate, const void* w_up,
+                             const void* w_down, const uint8_t* sf_gate, const uint8_t* sf_up,
+                             const uint8_t* sf_down, moe_dtype_t wgt, void* y_rows,
+                             moe_dtype_t out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Combine ("Distributed expert parallelism", lifecycle item 8 and "A four-rank example";
+ * MoonEP "combine fwd"): out[t] = sum_{k=0..K-1} topk_w[t,k] * y_rows[pos[t,k]], summed in
+ * fp32 in increasing k and rounded once to `out_dtype`; rows with pos < 0 are skipped.
+ *  y_rows [T*K, H] of y_dtype (F32 or BF16); out [T, H] of out_dtype (F32 or BF16).
+ * Deterministic: the same inputs give bitwise the same output. */
+MOE_API moe_status_t moe_combine(const void* y_rows, moe_dtype_t y_dtype, const int32_t* pos,
+                         const float* topk_w, int32_t T, int32_t H, int32_t K, void* out,
+                         moe_dtype_t out_dtype, hipStream_t stream);
+
+/* Workspace bytes of moe_layer_forward for `d` (0 if `d` is invalid). */
+MOE_API size_t moe_layer_workspace_bytes(const moe_layer_desc_t* d);
+
+/* The whole layer on one stream, no host synchronisation ("Distributed expert parallelism",
+ * "The dispatch-compute-combine lifecycle", without the exchanges):
+ *   route (skipped when logits == NULL: topk_idx_in / topk_w_in are used instead)
+ *   -> permute -> gate/up + SwiGLU -> down -> combine.
+ *  x [T, H] (format d->act, with x_sf for FP8_E4M3); logits [T, E] fp32 or NULL;
+ *  topk_idx_in / topk_w_in [T, K] when logits == NULL; weights as for moe_grouped_ffn;
+ *  out [T, H] of d->out. `ws` must hold moe_layer_workspace_bytes(d) bytes; all
+ *  intermediates (routing, counts, cu_seqlens, pos, row_src, x_perm, h, y_rows) live there,
+ *  at offsets reported by moe_layer_workspace_layout. */
+MOE_API moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const void* x, const float* x_sf,
+                               const float* logits, const int32_t* topk_idx_in,
+                               const float* topk_w_in, const void* w_gate, const void* w_up,
+                               const void* w_down, const uint8_t* sf_gate, const uint8_t* sf_up,
+                               const uint8_t* sf_down, void* out, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/* Byte offsets of the intermediates inside the moe_layer_forward workspace, for inspection.
+ * offsets[i] (i in order): 0 topk_idx, 1 topk_w, 2 counts, 3 cu_seqlens, 4 pos, 5 row_src,
+ * 6 row_w, 7 x_perm, 8 x_perm_sf, 9 h, 10 h_sf, 11 y_rows, 12 permute scratch,
+ * 13 fp32 accumulator (scatter combine). Unused entries are set to SIZE_MAX. Writes
+ * n <= 14 entries; returns MOE_EINVAL for an invalid `d`. Host-only. */
+MOE_API moe_status_t moe_layer_workspace_layout(const moe_layer_desc_t* d, size_t* offsets, int32_t n);
+
+/* Static text for a status code. */
+MOE_API const char* moe_status_str(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

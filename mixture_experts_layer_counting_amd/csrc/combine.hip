@@ -1,0 +1,131 @@
+// Combine: deterministic weighted gather-reduce back to token order.
+//
+// "Distributed expert parallelism", lifecycle item 8 and "A four-rank example": restore
+// the original token index, multiply by the route weights and add the k results (the
+// results are added, not overwritten -- "Duplicate route accumulation"). "Mixture of
+// Kittens", Step 8 "Full Determinism": the sum runs in a fixed order (k = 0..K-1, fp32
+// FMA) and is rounded once, so the output is bitwise reproducible.
+//
+// One block per token; each thread owns 16-byte column chunks and keeps the K row loads
+// of a chunk in flight together. HBM-bound: M*H*b read + T*H*b written.
+#include "moe_common.h"
+
+namespace moe {
+
+__device__ __forceinline__ void load8(const uint16_t* p, float* f) {
+  const int4 v = *reinterpret_cast<const int4*>(p);
+  const uint32_t w[4] = {(uint32_t)v.x, (uint32_t)v.y, (uint32_t)v.z, (uint32_t)v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float(w[i] << 16);
+    f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float* f) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+  f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float* f) {
+  int4 v;
+  v.x = (int)pack_bf16x2(f[0], f[1]);
+  v.y = (int)pack_bf16x2(f[2], f[3]);
+  v.z = (int)pack_bf16x2(f[4], f[5]);
+  v.w = (int)pack_bf16x2(f[6], f[7]);
+  *reinterpret_cast<int4*>(p) = v;
+}
+__device__ __forceinline__ void store8(float* p, const float* f) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(f[0], f[1], f[2], f[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
+}
+
+template <typename YT, typename OT, int KMAX>
+__global__ __launch_bounds__(128) void combine_kernel(const YT* __restrict__ y_rows,
+                                                      const int* __restrict__ pos,
+                                                      const float* __restrict__ topk_w, int T,
+                                                      int H, int K, OT* __restrict__ out) {
+  const int t = blockIdx.x;
+  int p[KMAX];
+  float w[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    p[k] = k < K ? pos[(size_t)t * K + k] : -1;
+    w[k] = k < K ? topk_w[(size_t)t * K + k] : 0.f;
+  }
+  const int nchunk = H / 8;
+  for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      if (p[k] >= 0) {
+        float v[8];
+        load8(y_rows + (size_t)p[k] * H + c * 8, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[k], v[i], acc[i]);
+      }
+    }
+    store8(out + (size_t)t * H + c * 8, acc);
+  }
+}
+
+// Scalar fallback for H not a multiple of 8.
+template <typename YT, typename OT>
+__global__ __launch_bounds__(128) void combine_scalar_kernel(const YT* __restrict__ y_rows,
+                                                             const int* __restrict__ pos,
+                                                             const float* __restrict__ topk_w,
+                                                             int T, int H, int K,
+                                                             OT* __restrict__ out) {
+  const int t = blockIdx.x;
+  for (int c = threadIdx.x; c < H; c += blockDim.x) {
+    float acc = 0.f;
+    for (int k = 0; k < K; ++k) {
+      const int p = pos[(size_t)t * K + k];
+      if (p < 0) continue;
+      float v;
+      if constexpr (sizeof(YT) == 2)
+        v = bf16_bits_to_f32(y_rows[(size_t)p * H + c]);
+      else
+        v = y_rows[(size_t)p * H + c];
+      acc = fmaf(topk_w[(size_t)t * K + k], v, acc);
+    }
+    if constexpr (sizeof(OT) == 2)
+      out[(size_t)t * H + c] = f32_to_bf16_bits(acc);
+    else
+      out[(size_t)t * H + c] = acc;
+  }
+}
+
+template <typename YT, typename OT>
+static moe_status_t dispatch_combine(const void* y, const int* pos, const float* w, int T, int H,
+                                     int K, void* out, hipStream_t s) {
+  const YT* yr = static_cast<const YT*>(y);
+  OT* o = static_cast<OT*>(out);
+  const bool vec = (H % 8 == 0) && ((uintptr_t)y % 16 == 0) && ((uintptr_t)out % 16 == 0);
+  if (!vec) {
+    combine_scalar_kernel<YT, OT><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, o);
+  } else if (K <= 2) {
+    combine_kernel<YT, OT, 2><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, o);
+  } else if (K <= 4) {
+    combine_kernel<YT, OT, 4><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, o);
+  } else if (K <= 8) {
+    combine_kernel<YT, OT, 8><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, o);
+  } else if (K <= 16) {
+    combine_kernel<YT, OT, 16><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, o);
+  } else {
+    combine_kernel<YT, OT, 32><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, o);
+  }
+  return launch_status();
+}
+
+moe_status_t launch_combine(const void* y, moe_dtype_t yt, const int* pos, const float* w, int T,
+                            int H, int K, void* out, moe_dtype_t ot, hipStream_t s) {
+  if (T == 0 || H == 0) return MOE_OK;
+  if (yt == MOE_BF16 && ot == MOE_BF16) return dispatch_combine<uint16_t, uint16_t>(y, pos, w, T, H, K, out, s);
+  if (yt == MOE_BF16 && ot == MOE_F32) return dispatch_combine<uint16_t, float>(y, pos, w, T, H, K, out, s);
+  if (yt == MOE_F32 && ot == MOE_F32) return dispatch_combine<float, float>(y, pos, w, T, H, K, out, s);
+  if (yt == MOE_F32 && ot == MOE_BF16) return dispatch_combine<float, uint16_t>(y, pos, w, T, H, K, out, s);
+  return MOE_EUNSUPPORTED;
+}
+
+}  // namespace moe

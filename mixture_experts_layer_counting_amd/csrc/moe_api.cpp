@@ -1,0 +1,352 @@
+// Host side of the C ABI declared in include/moe.h: argument checks, workspace layout and
+// the launch sequence of each entry point. No device code here; every launch goes through
+// the kernel files.
+#include <hip/hip_runtime.h>
+
+#include <cstdlib>
+#include <cstring>
+#include <limits>
+
+#include "moe_common.h"
+
+namespace moe {
+
+moe_status_t launch_route_topk(const float*, int, int, int, int*, float*, hipStream_t);
+size_t permute_ws_bytes(int T, int E, int K);
+moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes, const int* topk_idx,
+                            const float* topk_w, int T, int H, int E, int K, int* counts,
+                            int* cu_seqlens, int* pos, int* row_src, float* row_w, void* x_perm,
+                            float* x_perm_sf, void* ws, bool validate, int** err_out,
+                            hipStream_t s);
+moe_status_t launch_combine(const void*, moe_dtype_t, const int*, const float*, int, int, int,
+                            void*, moe_dtype_t, hipStream_t);
+moe_status_t launch_ffn_gate_up_bf16(const void*, const int*, int, int, int, int, const void*,
+                                     const void*, void*, hipStream_t);
+moe_status_t launch_ffn_down_bf16(const void*, const int*, int, int, int, int, const void*, void*,
+                                  hipStream_t);
+moe_status_t launch_ffn_gate_up_f32(const void*, const int*, int, int, int, int, const void*,
+                                    const void*, void*, hipStream_t);
+moe_status_t launch_ffn_down_f32(const void*, const int*, int, int, int, int, const void*, void*,
+                                 hipStream_t);
+
+int device_cu_count() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+bool env_flag(const char* name) {
+  const char* v = std::getenv(name);
+  return v && v[0] && std::strcmp(v, "0") != 0;
+}
+
+static int act_bytes(moe_dtype_t d) {
+  switch (d) {
+    case MOE_F32: return 4;
+    case MOE_BF16: return 2;
+    case MOE_FP8_E4M3: return 1;
+    default: return 0;
+  }
+}
+
+enum Path { PATH_NONE, PATH_F32, PATH_BF16, PATH_FP8_MXFP4 };
+
+static Path ffn_path(moe_dtype_t act, moe_dtype_t wgt) {
+  if (act == MOE_F32 && wgt == MOE_F32) return PATH_F32;
+  if (act == MOE_BF16 && wgt == MOE_BF16) return PATH_BF16;
+  if (act == MOE_FP8_E4M3 && wgt == MOE_MXFP4) return PATH_FP8_MXFP4;
+  return PATH_NONE;
+}
+
+// h / y formats of a path
+static moe_dtype_t h_dtype_of(Path p) {
+  return p == PATH_F32 ? MOE_F32 : p == PATH_BF16 ? MOE_BF16 : MOE_FP8_E4M3;
+}
+static moe_dtype_t y_dtype_of(Path p) { return p == PATH_F32 ? MOE_F32 : MOE_BF16; }
+
+static moe_status_t check_ffn_dims(Path p, int64_t M, int E, int H, int Hp, bool gate_up) {
+  if (M < 0 || E < 1 || H < 1 || Hp < 1) return MOE_EINVAL;
+  if (M > std::numeric_limits<int32_t>::max() / 2) return MOE_EUNSUPPORTED;
+  switch (p) {
+    case PATH_F32:
+      if (E > 512) return MOE_EUNSUPPORTED;
+      return MOE_OK;
+    case PATH_BF16:
+      if (E > 1024) return MOE_EUNSUPPORTED;
+      // 32-bit buffer offsets: one expert matrix and 256 activation rows must stay < 2 GiB
+      if ((int64_t)H * Hp * 2 >= (1ll << 31) || 256ll * (H > Hp ? H : Hp) * 2 >= (1ll << 31))
+        return MOE_EUNSUPPORTED;
+      if (gate_up) return (H % 64 == 0 && Hp % 128 == 0) ? MOE_OK : MOE_EUNSUPPORTED;
+      return (H % 256 == 0 && Hp % 64 == 0) ? MOE_OK : MOE_EUNSUPPORTED;
+    case PATH_FP8_MXFP4:
+      return MOE_EUNSUPPORTED;
+    default:
+      return MOE_EUNSUPPORTED;
+  }
+}
+
+static void poison(void* ws, size_t bytes, hipStream_t s) {
+  if (ws && bytes && env_flag("MOE_DEBUG_POISON")) (void)hipMemsetAsync(ws, 0xFF, bytes, s);
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_str(moe_status_t st) {
+  switch (st) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_EINVAL: return "MOE_EINVAL: invalid argument";
+    case MOE_EUNSUPPORTED: return "MOE_EUNSUPPORTED: unsupported dtype combination or size";
+    case MOE_EWORKSPACE: return "MOE_EWORKSPACE: workspace too small";
+    case MOE_EHIP: return "MOE_EHIP: HIP launch or runtime error";
+    default: return "MOE_UNKNOWN";
+  }
+}
+
+moe_status_t moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t K,
+                            int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+  if (T < 0 || E < 1 || K < 1 || K > E) return MOE_EINVAL;
+  if (K > 32 || E > 4096) return MOE_EUNSUPPORTED;
+  if (T > 0 && (!logits || !topk_idx || !topk_w)) return MOE_EINVAL;
+  return launch_route_topk(logits, T, E, K, topk_idx, topk_w, stream);
+}
+
+size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t K) {
+  if (T < 0 || E < 1 || K < 1) return 0;
+  return permute_ws_bytes(T, E, K);
+}
+
+moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t act,
+                         const int32_t* topk_idx, const float* topk_w, int32_t T, int32_t H,
+                         int32_t E, int32_t K, int32_t* counts, int32_t* cu_seqlens,
+                         int32_t* pos, int32_t* row_src, float* row_w, void* x_perm,
+                         float* x_perm_sf, void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (T < 0 || H < 1 || E < 1 || K < 1) return MOE_EINVAL;
+  if (E > 1024 || K > 32) return MOE_EUNSUPPORTED;
+  const int eb = act_bytes(act);
+  if (eb == 0) return MOE_EUNSUPPORTED;
+  if (!counts || !cu_seqlens) return MOE_EINVAL;
+  if (T > 0 && (!x || !topk_idx || !pos || !row_src || !x_perm)) return MOE_EINVAL;
+  if (row_w && T > 0 && !topk_w) return MOE_EINVAL;
+  if (act == MOE_FP8_E4M3) {
+    if (H % 128) return MOE_EUNSUPPORTED;
+    if (T > 0 && (!x_sf || !x_perm_sf)) return MOE_EINVAL;
+  }
+  if ((int64_t)T * K > std::numeric_limits<int32_t>::max() / 2) return MOE_EUNSUPPORTED;
+  const size_t need = permute_ws_bytes(T, E, K);
+  if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+  poison(ws, ws_bytes, stream);
+  const bool validate = env_flag("MOE_VALIDATE");
+  int* err = nullptr;
+  moe_status_t st = launch_permute(x, act == MOE_FP8_E4M3 ? x_sf : nullptr, eb, topk_idx, topk_w,
+                                   T, H, E, K, counts, cu_seqlens, pos, row_src, row_w, x_perm,
+                                   act == MOE_FP8_E4M3 ? x_perm_sf : nullptr, ws, validate, &err,
+                                   stream);
+  if (st != MOE_OK || !validate) return st;
+  int h_err = 0;
+  if (hipMemcpyAsync(&h_err, err, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return MOE_EHIP;
+  return h_err ? MOE_EINVAL : MOE_OK;
+}
+
+moe_status_t moe_ffn_gate_up(const void* x_perm, const float* x_perm_sf, moe_dtype_t act,
+                             const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
+                             int32_t Hp, const void* w_gate, const void* w_up,
+                             const uint8_t* sf_gate, const uint8_t* sf_up, moe_dtype_t wgt,
+                             void* h, float* h_sf, hipStream_t stream) {
+  const Path p = ffn_path(act, wgt);
+  if (p == PATH_NONE) return MOE_EUNSUPPORTED;
+  moe_status_t st = check_ffn_dims(p, M, E, H, Hp, true);
+  if (st != MOE_OK) return st;
+  if (!cu_seqlens) return MOE_EINVAL;
+  if (M > 0 && (!x_perm || !w_gate || !w_up || !h)) return MOE_EINVAL;
+  (void)x_perm_sf;
+  (void)sf_gate;
+  (void)sf_up;
+  (void)h_sf;
+  if (p == PATH_F32) return launch_ffn_gate_up_f32(x_perm, cu_seqlens, M, E, H, Hp, w_gate, w_up, h, stream);
+  return launch_ffn_gate_up_bf16(x_perm, cu_seqlens, M, E, H, Hp, w_gate, w_up, h, stream);
+}
+
+moe_status_t moe_ffn_down(const void* h, const float* h_sf, moe_dtype_t h_dtype,
+                          const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
+                          int32_t Hp, const void* w_down, const uint8_t* sf_down,
+                          moe_dtype_t wgt, void* y_rows, moe_dtype_t out, hipStream_t stream) {
+  const Path p = ffn_path(h_dtype, wgt);
+  if (p == PATH_NONE || out != y_dtype_of(p)) return MOE_EUNSUPPORTED;
+  moe_status_t st = check_ffn_dims(p, M, E, H, Hp, false);
+  if (st != MOE_OK) return st;
+  if (!cu_seqlens) return MOE_EINVAL;
+  if (M > 0 && (!h || !w_down || !y_rows)) return MOE_EINVAL;
+  (void)h_sf;
+  (void)sf_down;
+  if (p == PATH_F32) return launch_ffn_down_f32(h, cu_seqlens, M, E, H, Hp, w_down, y_rows, stream);
+  return launch_ffn_down_bf16(h, cu_seqlens, M, E, H, Hp, w_down, y_rows, stream);
+}
+
+size_t moe_grouped_ffn_workspace_bytes(int32_t M, int32_t Hp, moe_dtype_t act, moe_dtype_t wgt) {
+  const Path p = ffn_path(act, wgt);
+  if (p == PATH_NONE || M < 0 || Hp < 1) return 0;
+  const size_t hb = (size_t)act_bytes(h_dtype_of(p));
+  size_t n = align_up((size_t)M * Hp * hb, 256);
+  if (p == PATH_FP8_MXFP4) n += align_up((size_t)M * (Hp / 128) * 4, 256);
+  return n + 256;
+}
+
+moe_status_t moe_grouped_ffn(const void* x_perm, const float* x_perm_sf, moe_dtype_t act,
+                             const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
+                             int32_t Hp, const void* w_gate, const void* w_up,
+                             const void* w_down, const uint8_t* sf_gate, const uint8_t* sf_up,
+                             const uint8_t* sf_down, moe_dtype_t wgt, void* y_rows,
+                             moe_dtype_t out, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const Path p = ffn_path(act, wgt);
+  if (p == PATH_NONE) return MOE_EUNSUPPORTED;
+  const size_t need = moe_grouped_ffn_workspace_bytes(M, Hp, act, wgt);
+  if (need == 0) return MOE_EINVAL;
+  if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+  moe_status_t st = check_ffn_dims(p, M, E, H, Hp, true);
+  if (st == MOE_OK) st = check_ffn_dims(p, M, E, H, Hp, false);
+  if (st != MOE_OK) return st;
+  if (out != y_dtype_of(p)) return MOE_EUNSUPPORTED;
+  poison(ws, ws_bytes, stream);
+  void* h = ws;
+  float* h_sf = p == PATH_FP8_MXFP4
+                    ? reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                               align_up((size_t)M * Hp * act_bytes(h_dtype_of(p)), 256))
+                    : nullptr;
+  st = moe_ffn_gate_up(x_perm, x_perm_sf, act, cu_seqlens, M, E, H, Hp, w_gate, w_up, sf_gate,
+                       sf_up, wgt, h, h_sf, stream);
+  if (st != MOE_OK) return st;
+  return moe_ffn_down(h, h_sf, h_dtype_of(p), cu_seqlens, M, E, H, Hp, w_down, sf_down, wgt,
+                      y_rows, out, stream);
+}
+
+moe_status_t moe_combine(const void* y_rows, moe_dtype_t y_dtype, const int32_t* pos,
+                         const float* topk_w, int32_t T, int32_t H, int32_t K, void* out,
+                         moe_dtype_t out_dtype, hipStream_t stream) {
+  if (T < 0 || H < 1 || K < 1) return MOE_EINVAL;
+  if (K > 32) return MOE_EUNSUPPORTED;
+  if ((y_dtype != MOE_F32 && y_dtype != MOE_BF16) || (out_dtype != MOE_F32 && out_dtype != MOE_BF16))
+    return MOE_EUNSUPPORTED;
+  if (T > 0 && (!y_rows || !pos || !topk_w || !out)) return MOE_EINVAL;
+  return launch_combine(y_rows, y_dtype, pos, topk_w, T, H, K, out, out_dtype, stream);
+}
+
+enum {
+  WS_TOPK_IDX, WS_TOPK_W, WS_COUNTS, WS_CU, WS_POS, WS_ROW_SRC, WS_ROW_W, WS_X_PERM,
+  WS_X_PERM_SF, WS_H, WS_H_SF, WS_Y, WS_PERM_SCRATCH, WS_ACC, WS_N
+};
+
+static moe_status_t layer_layout(const moe_layer_desc_t* d, size_t* off, size_t* total) {
+  if (!d) return MOE_EINVAL;
+  if (d->T < 0 || d->H < 1 || d->Hp < 1 || d->E < 1 || d->K < 1 || d->K > d->E) return MOE_EINVAL;
+  const Path p = ffn_path(d->act, d->wgt);
+  if (p == PATH_NONE || d->out != y_dtype_of(p)) return MOE_EUNSUPPORTED;
+  if (d->combine != MOE_COMBINE_GATHER && d->combine != MOE_COMBINE_SCATTER_ATOMIC) return MOE_EINVAL;
+  const size_t T = d->T, H = d->H, Hp = d->Hp, E = d->E, K = d->K, M = T * K;
+  const size_t ab = act_bytes(d->act), hb = act_bytes(h_dtype_of(p)), yb = act_bytes(y_dtype_of(p));
+  size_t sz[WS_N] = {0};
+  sz[WS_TOPK_IDX] = M * 4;
+  sz[WS_TOPK_W] = M * 4;
+  sz[WS_COUNTS] = E * 4;
+  sz[WS_CU] = (E + 1) * 4;
+  sz[WS_POS] = M * 4;
+  sz[WS_ROW_SRC] = M * 4;
+  sz[WS_ROW_W] = M * 4;
+  sz[WS_X_PERM] = M * H * ab;
+  sz[WS_X_PERM_SF] = p == PATH_FP8_MXFP4 ? M * (H / 128) * 4 : 0;
+  sz[WS_H] = M * Hp * hb;
+  sz[WS_H_SF] = p == PATH_FP8_MXFP4 ? M * (Hp / 128) * 4 : 0;
+  sz[WS_Y] = M * H * yb;
+  sz[WS_PERM_SCRATCH] = permute_ws_bytes(d->T, d->E, d->K);
+  sz[WS_ACC] = d->combine == MOE_COMBINE_SCATTER_ATOMIC ? T * H * 4 : 0;
+  size_t o = 0;
+  for (int i = 0; i < WS_N; ++i) {
+    const bool used = sz[i] > 0 || i == WS_TOPK_IDX || i == WS_TOPK_W || i == WS_POS ||
+                      i == WS_ROW_SRC || i == WS_ROW_W || i == WS_X_PERM || i == WS_H || i == WS_Y;
+    if (!used) {
+      off[i] = SIZE_MAX;
+      continue;
+    }
+    off[i] = o;
+    o = align_up(o + sz[i], 256);
+  }
+  *total = o + 256;
+  return MOE_OK;
+}
+
+size_t moe_layer_workspace_bytes(const moe_layer_desc_t* d) {
+  size_t off[WS_N], total = 0;
+  return layer_layout(d, off, &total) == MOE_OK ? total : 0;
+}
+
+moe_status_t moe_layer_workspace_layout(const moe_layer_desc_t* d, size_t* offsets, int32_t n) {
+  size_t off[WS_N], total = 0;
+  const moe_status_t st = layer_layout(d, off, &total);
+  if (st != MOE_OK) return st;
+  if (!offsets || n < 0) return MOE_EINVAL;
+  for (int i = 0; i < n && i < WS_N; ++i) offsets[i] = off[i];
+  return MOE_OK;
+}
+
+moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const void* x, const float* x_sf,
+                               const float* logits, const int32_t* topk_idx_in,
+                               const float* topk_w_in, const void* w_gate, const void* w_up,
+                               const void* w_down, const uint8_t* sf_gate, const uint8_t* sf_up,
+                               const uint8_t* sf_down, void* out, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  size_t off[WS_N], total = 0;
+  moe_status_t st = layer_layout(d, off, &total);
+  if (st != MOE_OK) return st;
+  if (!ws || ws_bytes < total) return MOE_EWORKSPACE;
+  const Path p = ffn_path(d->act, d->wgt);
+  st = check_ffn_dims(p, (int64_t)d->T * d->K, d->E, d->H, d->Hp, true);
+  if (st == MOE_OK) st = check_ffn_dims(p, (int64_t)d->T * d->K, d->E, d->H, d->Hp, false);
+  if (st != MOE_OK) return st;
+  if (d->combine != MOE_COMBINE_GATHER) return MOE_EUNSUPPORTED;
+  if (d->T > 0 && (!x || !out || !w_gate || !w_up || !w_down)) return MOE_EINVAL;
+  if (d->T > 0 && !logits && (!topk_idx_in || !topk_w_in)) return MOE_EINVAL;
+  poison(ws, ws_bytes, stream);
+  char* base = static_cast<char*>(ws);
+  auto at = [&](int i) -> void* { return off[i] == SIZE_MAX ? nullptr : base + off[i]; };
+  const int T = d->T, E = d->E, K = d->K, H = d->H, Hp = d->Hp, M = T * K;
+  int32_t* topk_idx = static_cast<int32_t*>(at(WS_TOPK_IDX));
+  float* topk_w = static_cast<float*>(at(WS_TOPK_W));
+  if (logits) {
+    st = moe_route_topk(logits, T, E, K, topk_idx, topk_w, stream);
+    if (st != MOE_OK) return st;
+  } else {
+    topk_idx = const_cast<int32_t*>(topk_idx_in);
+    topk_w = const_cast<float*>(topk_w_in);
+  }
+  int32_t* counts = static_cast<int32_t*>(at(WS_COUNTS));
+  int32_t* cu = static_cast<int32_t*>(at(WS_CU));
+  int32_t* pos = static_cast<int32_t*>(at(WS_POS));
+  int32_t* row_src = static_cast<int32_t*>(at(WS_ROW_SRC));
+  const size_t perm_ws = permute_ws_bytes(T, E, K);
+  st = moe_permute(x, x_sf, d->act, topk_idx, topk_w, T, H, E, K, counts, cu, pos, row_src, nullptr,
+                   at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)), at(WS_PERM_SCRATCH), perm_ws,
+                   stream);
+  if (st != MOE_OK) return st;
+  st = moe_ffn_gate_up(at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)), d->act, cu, M, E, H, Hp,
+                       w_gate, w_up, sf_gate, sf_up, d->wgt, at(WS_H), static_cast<float*>(at(WS_H_SF)),
+                       stream);
+  if (st != MOE_OK) return st;
+  st = moe_ffn_down(at(WS_H), static_cast<float*>(at(WS_H_SF)), h_dtype_of(p), cu, M, E, H, Hp, w_down,
+                    sf_down, d->wgt, at(WS_Y), y_dtype_of(p), stream);
+  if (st != MOE_OK) return st;
+  return moe_combine(at(WS_Y), y_dtype_of(p), pos, topk_w, T, H, K, out, d->out, stream);
+}
+
+}  // extern "C"

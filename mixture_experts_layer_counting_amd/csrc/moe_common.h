@@ -1,0 +1,77 @@
+// Internal helpers shared by the MoE kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/moe.h"
+
+#define MOE_WAVE 64
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+#define MOE_LDS __attribute__((address_space(3)))
+
+namespace moe {
+
+// ---- host-side launch helpers -------------------------------------------------------
+
+// Number of compute units of the current device (cached per device id).
+int device_cu_count();
+
+inline moe_status_t launch_status() {
+  return hipGetLastError() == hipSuccess ? MOE_OK : MOE_EHIP;
+}
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+bool env_flag(const char* name);
+
+// ---- device helpers -----------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16_bits(lo) | ((uint32_t)f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+// Wave-uniform broadcast from lane `src`.
+__device__ __forceinline__ int wave_bcast(int v, int src) { return __shfl(v, src, MOE_WAVE); }
+
+// Set of lanes in the wave whose `key` equals this lane's key (keys < 2^bits).
+__device__ __forceinline__ uint64_t match_any(int key, int bits) {
+  uint64_t m = __ballot(1);
+  for (int b = 0; b < bits; ++b) {
+    uint64_t ones = __ballot((key >> b) & 1);
+    m &= ((key >> b) & 1) ? ones : ~ones;
+  }
+  return m;
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Number of set bits of `m` below this lane.
+__device__ __forceinline__ int popc_below(uint64_t m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+}
+
+}  // namespace moe

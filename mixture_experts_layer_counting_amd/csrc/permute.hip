@@ -1,0 +1,297 @@
+// Permute token copies into expert-contiguous rows: a deterministic counting sort.
+//
+// "Distributed expert parallelism", lifecycle items 2-3 and "Token permutation and
+// metadata": each token is copied k times and the copies are grouped by expert; the
+// metadata kept (row of each copy, source of each row, per-expert counts) is what the
+// combine needs to restore token order. MoonEP "dispatch fwd" returns the same things for
+// one rank (tokens_per_expert, cu_seqlens, expert-grouped hidden rows and their weights).
+//
+// Row order inside an expert is ascending flat index t*K + k, i.e. a stable sort. Three
+// launches, none of them with atomics on global memory:
+//  1. hist:    one block per chunk of PERM_CHUNK tokens counts its copies per expert in
+//              LDS and writes them expert-major: hist[e][chunk].
+//  2. scan:    one wave per expert turns hist[e][*] into exclusive chunk offsets and the
+//              expert total (counts[e]).
+//  3. scatter: one block per PERM_TB tokens. It rebuilds cu_seqlens from counts in LDS,
+//              counts the copies of earlier tokens of its chunk, ranks its own copies
+//              with wave ballots (match by key bits + mbcnt) in flat order, writes pos /
+//              row_src / row_w, then copies each token row once from x to its K rows of
+//              x_perm with 16-byte loads and stores (HBM-bound part).
+#include "moe_common.h"
+
+namespace moe {
+
+constexpr int PERM_CHUNK = 128;  // tokens per histogram chunk
+constexpr int PERM_TB = 16;      // tokens per scatter block (divides PERM_CHUNK)
+constexpr int PERM_THREADS = 256;
+constexpr int PERM_WAVES = PERM_THREADS / MOE_WAVE;
+constexpr int PERM_MAX_E = 1024;
+
+__global__ __launch_bounds__(PERM_THREADS) void permute_hist_kernel(
+    const int* __restrict__ topk_idx, int T, int E, int K, int nch, int* __restrict__ hist,
+    int* __restrict__ err) {
+  __shared__ int h[PERM_MAX_E];
+  for (int e = threadIdx.x; e < E; e += PERM_THREADS) h[e] = 0;
+  __syncthreads();
+  const int c = blockIdx.x;
+  const int t0 = c * PERM_CHUNK;
+  const int t1 = min(T, t0 + PERM_CHUNK);
+  const int n = (t1 - t0) * K;
+  const int* idx = topk_idx + (size_t)t0 * K;
+  int bad = 0;
+  for (int i = threadIdx.x; i < n; i += PERM_THREADS) {
+    const int e = idx[i];
+    if ((unsigned)e < (unsigned)E)
+      atomicAdd(&h[e], 1);
+    else
+      bad = 1;
+  }
+  if (bad) atomicOr(err, 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += PERM_THREADS) hist[(size_t)e * nch + c] = h[e];
+}
+
+// Wave-inclusive scan of v across the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(256) void permute_scan_kernel(int* __restrict__ hist, int nch, int E,
+                                                           int* __restrict__ counts) {
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (e >= E) return;
+  int running = 0;
+  int* row = hist + (size_t)e * nch;
+  for (int base = 0; base < nch; base += 64) {
+    const int i = base + lane;
+    const int v = i < nch ? row[i] : 0;
+    const int incl = wave_incl_scan(v);
+    if (i < nch) row[i] = running + incl - v;
+    running += __shfl(incl, 63, 64);
+  }
+  if (lane == 0) counts[e] = running;
+}
+
+// Duplicate expert ids within one token (validation mode only).
+__global__ void permute_dup_check_kernel(const int* __restrict__ topk_idx, int T, int K,
+                                         int* __restrict__ err) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  const int* r = topk_idx + (size_t)t * K;
+  for (int a = 0; a < K; ++a)
+    for (int b = a + 1; b < K; ++b)
+      if (r[a] == r[b]) atomicOr(err, 2);
+}
+
+template <int VB>  // bytes per vector access: 16, 4 or 1
+struct VecT;
+template <>
+struct VecT<16> {
+  typedef int4 type;
+};
+template <>
+struct VecT<4> {
+  typedef int type;
+};
+template <>
+struct VecT<1> {
+  typedef unsigned char type;
+};
+
+template <int VB>
+__global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
+    const unsigned char* __restrict__ x, const float* __restrict__ x_sf,
+    const int* __restrict__ topk_idx, const float* __restrict__ topk_w, int T, int E, int K,
+    int nch, const int* __restrict__ counts, const int* __restrict__ choff,
+    int* __restrict__ cu_seqlens, int* __restrict__ pos, int* __restrict__ row_src,
+    float* __restrict__ row_w, unsigned char* __restrict__ x_perm, float* __restrict__ x_perm_sf,
+    int row_bytes, int sf_per_row, int key_bits, int* __restrict__ err) {
+  typedef typename VecT<VB>::type V;
+  __shared__ int cu[PERM_MAX_E + 1];
+  __shared__ int pre[PERM_MAX_E];
+  __shared__ int wh[PERM_WAVES][PERM_MAX_E];
+  __shared__ int wsum[PERM_WAVES];
+  __shared__ int lpos[PERM_TB * 32];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+
+  // 1. cu_seqlens from counts (block-wide exclusive scan, E <= 1024: 4 per thread)
+  {
+    int loc[4];
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = tid * 4 + j;
+      loc[j] = e < E ? counts[e] : 0;
+      sum += loc[j];
+    }
+    const int incl = wave_incl_scan(sum);
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += wsum[w];
+    int run = base + incl - sum;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = tid * 4 + j;
+      if (e < E) cu[e] = run;
+      run += loc[j];
+    }
+    if (tid == 0) {
+      int total = 0;
+      for (int w = 0; w < PERM_WAVES; ++w) total += wsum[w];
+      cu[E] = total;
+    }
+  }
+  for (int e = tid; e < E; e += PERM_THREADS) pre[e] = 0;
+  for (int i = tid; i < PERM_WAVES * PERM_MAX_E; i += PERM_THREADS) (&wh[0][0])[i] = 0;
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int e = tid; e <= E; e += PERM_THREADS) cu_seqlens[e] = cu[e];
+  if (T == 0) return;
+
+  const int tb0 = blockIdx.x * PERM_TB;
+  const int tb1 = min(T, tb0 + PERM_TB);
+  const int chunk = tb0 / PERM_CHUNK;
+  const int tc0 = chunk * PERM_CHUNK;
+
+  // 2. copies of earlier tokens in the same chunk
+  {
+    const int n = (tb0 - tc0) * K;
+    const int* idx = topk_idx + (size_t)tc0 * K;
+    for (int i = tid; i < n; i += PERM_THREADS) {
+      const int e = idx[i];
+      if ((unsigned)e < (unsigned)E) atomicAdd(&pre[e], 1);
+    }
+  }
+  __syncthreads();
+
+  // 3. stable ranks of this block's copies, 256 at a time in flat order
+  const int nb = (tb1 - tb0) * K;
+  const int* idx = topk_idx + (size_t)tb0 * K;
+  for (int g = 0; g < nb; g += PERM_THREADS) {
+    const int i = g + tid;
+    const bool in = i < nb;
+    const int e = in ? idx[i] : -1;
+    const bool valid = in && (unsigned)e < (unsigned)E;
+    const int key = valid ? e : (1 << key_bits) - 1;
+    const uint64_t m = match_any(key, key_bits);
+    const int r = popc_below(m);
+    if (valid && r == 0) wh[wave][e] = __popcll(m);
+    __syncthreads();
+    if (in) {
+      int p = -1;
+      if (valid) {
+        p = cu[e] + choff[(size_t)e * nch + chunk] + pre[e] + r;
+        for (int w = 0; w < wave; ++w) p += wh[w][e];
+        if (p < cu[e] || p >= cu[e + 1]) {  // cannot happen; keeps every store in bounds
+          atomicOr(err, 4);
+          p = -1;
+        } else {
+          const int flat = tb0 * K + i;
+          row_src[p] = flat;
+          if (row_w) row_w[p] = topk_w[flat];
+        }
+      }
+      pos[(size_t)tb0 * K + i] = p;
+      lpos[i] = p;
+    }
+    __syncthreads();
+    // fold this group's counts into pre[] and clear wh for the next group
+    if (g + PERM_THREADS < nb) {
+      for (int j = tid; j < E; j += PERM_THREADS) {
+        int tot = 0;
+        for (int w = 0; w < PERM_WAVES; ++w) {
+          tot += wh[w][j];
+          wh[w][j] = 0;
+        }
+        pre[j] += tot;
+      }
+      __syncthreads();
+    }
+  }
+
+  // 4. copy each token row once to its K rows
+  const int nv = row_bytes / VB;
+  const int ntok = tb1 - tb0;
+  for (int q = tid; q < ntok * nv; q += PERM_THREADS) {
+    const int j = q / nv;
+    const int c = q - j * nv;
+    const V v = reinterpret_cast<const V*>(x + (size_t)(tb0 + j) * row_bytes)[c];
+    for (int k = 0; k < K; ++k) {
+      const int p = lpos[j * K + k];
+      if (p >= 0) reinterpret_cast<V*>(x_perm + (size_t)p * row_bytes)[c] = v;
+    }
+  }
+  if (x_sf) {
+    for (int q = tid; q < ntok * sf_per_row; q += PERM_THREADS) {
+      const int j = q / sf_per_row;
+      const int c = q - j * sf_per_row;
+      const float v = x_sf[(size_t)(tb0 + j) * sf_per_row + c];
+      for (int k = 0; k < K; ++k) {
+        const int p = lpos[j * K + k];
+        if (p >= 0) x_perm_sf[(size_t)p * sf_per_row + c] = v;
+      }
+    }
+  }
+}
+
+size_t permute_ws_bytes(int T, int E, int K) {
+  (void)K;
+  const size_t nch = (size_t)(T + PERM_CHUNK - 1) / PERM_CHUNK;
+  return align_up(sizeof(int) * (nch * (size_t)E), 256) + 256;  // hist/offsets + error word
+}
+
+moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes,
+                            const int* topk_idx, const float* topk_w, int T, int H, int E, int K,
+                            int* counts, int* cu_seqlens, int* pos, int* row_src, float* row_w,
+                            void* x_perm, float* x_perm_sf, void* ws, bool validate,
+                            int** err_out, hipStream_t s) {
+  const int nch = (T + PERM_CHUNK - 1) / PERM_CHUNK;
+  int* hist = static_cast<int*>(ws);
+  int* err = reinterpret_cast<int*>(static_cast<char*>(ws) +
+                                    align_up(sizeof(int) * ((size_t)nch * E), 256));
+  *err_out = err;
+  if (validate) {
+    if (hipMemsetAsync(err, 0, sizeof(int), s) != hipSuccess) return MOE_EHIP;
+  }
+  if (nch > 0) {
+    permute_hist_kernel<<<nch, PERM_THREADS, 0, s>>>(topk_idx, T, E, K, nch, hist, err);
+    if (validate && K > 1)
+      permute_dup_check_kernel<<<(T + 255) / 256, 256, 0, s>>>(topk_idx, T, K, err);
+  }
+  permute_scan_kernel<<<(E + 3) / 4, 256, 0, s>>>(hist, nch, E, counts);
+  int key_bits = 1;
+  while ((1 << key_bits) <= E) ++key_bits;  // E itself (invalid) must be representable
+  const int row_bytes = H * elem_bytes;
+  const int sf_per_row = x_sf ? H / 128 : 0;
+  const int nblk = T > 0 ? (T + PERM_TB - 1) / PERM_TB : 1;
+  const unsigned char* xb = static_cast<const unsigned char*>(x);
+  unsigned char* xp = static_cast<unsigned char*>(x_perm);
+  const bool a16 = (row_bytes % 16 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)x_perm % 16 == 0);
+  const bool a4 = (row_bytes % 4 == 0) && ((uintptr_t)x % 4 == 0) && ((uintptr_t)x_perm % 4 == 0);
+  if (a16)
+    permute_scatter_kernel<16><<<nblk, PERM_THREADS, 0, s>>>(
+        xb, x_sf, topk_idx, topk_w, T, E, K, nch, counts, hist, cu_seqlens, pos, row_src, row_w,
+        xp, x_perm_sf, row_bytes, sf_per_row, key_bits, err);
+  else if (a4)
+    permute_scatter_kernel<4><<<nblk, PERM_THREADS, 0, s>>>(
+        xb, x_sf, topk_idx, topk_w, T, E, K, nch, counts, hist, cu_seqlens, pos, row_src, row_w,
+        xp, x_perm_sf, row_bytes, sf_per_row, key_bits, err);
+  else
+    permute_scatter_kernel<1><<<nblk, PERM_THREADS, 0, s>>>(
+        xb, x_sf, topk_idx, topk_w, T, E, K, nch, counts, hist, cu_seqlens, pos, row_src, row_w,
+        xp, x_perm_sf, row_bytes, sf_per_row, key_bits, err);
+  return launch_status();
+}
+
+}  // namespace moe

@@ -1,0 +1,267 @@
+"""Parity of the HIP path (called through the C ABI) with the CPU oracle on the same seeded
+inputs. Integers (routing, counts, cu_seqlens, pos, row_src) and copied rows must be
+bit-exact; floating point within the stated tolerance: max|err| / max|ref| <= 1e-5 for the
+fp32 layer, <= 2e-2 for bf16; route weights within 1e-6 absolute."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from workloads import gen, to_numpy_bits
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+from _gpu_run import run_layer, run_steps  # noqa: E402
+from _oracle_run import oracle_layer, oracle_routing, oracle_tokens, rel_err  # noqa: E402
+
+import mixture_experts_layer_counting_amd as moe  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def host(t):
+    return to_numpy_bits(t)
+
+
+def check_integers(r, ref, K):
+    assert np.array_equal(host(r["topk_idx"]), ref["topk_idx"])
+    assert np.abs(host(r["topk_w"]).astype(np.float64) - ref["topk_w"]).max() <= 1e-6
+    assert np.array_equal(host(r["counts"]), ref["counts"])
+    assert np.array_equal(host(r["cu_seqlens"]), ref["cu_seqlens"])
+    assert np.array_equal(host(r["pos"]), ref["pos"])
+    assert np.array_equal(host(r["row_src"]), ref["row_src"])
+    if r.get("row_w") is not None:
+        tw = host(r["topk_w"]).ravel()
+        assert np.array_equal(host(r["row_w"]), tw[ref["row_src"]])
+
+
+def check_x_perm(w, r, ref):
+    xb = host(w.x)
+    assert np.array_equal(host(r["x_perm"]), xb[ref["row_src"] // w.K])
+    if w.x_sf is not None:
+        assert np.array_equal(host(r["x_perm_sf"]), host(w.x_sf)[ref["row_src"] // w.K])
+
+
+def full_check(w, tol=None):
+    tol = tol or TOL[w.act]
+    r = run_steps(w)
+    torch.cuda.synchronize()
+    ref = oracle_layer(w)
+    check_integers(r, ref, w.K)
+    check_x_perm(w, r, ref)
+    e_y = rel_err(host(r["y_rows"]).astype(np.float64) if w.act == "f32" else O.decode_bf16(host(r["y_rows"])),
+                  ref["y_rows"])
+    out = host(r["out"])
+    out = out.astype(np.float64) if w.out == "f32" else O.decode_bf16(out)
+    e_out = rel_err(out, ref["out"])
+    print(f"  y_rows rel err {e_y:.3e}  out rel err {e_out:.3e}  maxvio {ref['maxvio']:.3f}", flush=True)
+    assert e_y <= tol and e_out <= tol
+    return r, ref
+
+
+# ----------------------------------------------------------------------------- whole layer, small
+
+def test_c1_fp32_full():
+    say("c1 fp32 T=64 H=128 Hp=64 E=8 K=2")
+    full_check(gen.config("c1", device=DEV))
+
+
+SMALL = [
+    dict(T=300, H=512, Hp=256, E=12, K=3, routing="normal"),
+    dict(T=1000, H=256, Hp=384, E=40, K=4, routing="skew", beta=0.8),
+    dict(T=700, H=768, Hp=128, E=10, K=4, routing="balanced"),
+    dict(T=257, H=256, Hp=128, E=1, K=1, routing="normal"),
+    dict(T=64, H=256, Hp=128, E=4, K=4, routing="normal"),
+    dict(T=600, H=512, Hp=256, E=32, K=6, routing="skew", beta=3.0),   # many empty experts
+]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: "T{T}_H{H}_Hp{Hp}_E{E}_K{K}_{routing}".format(**s))
+def test_small_bf16_layer(spec):
+    say(f"bf16 small {spec}")
+    w = gen.make(**spec, act="bf16", wgt="bf16", out="bf16", cid=50, device=DEV)
+    full_check(w)
+
+
+def test_small_fp32_layer_ragged():
+    spec = dict(T=333, H=200, Hp=72, E=9, K=3, routing="skew", beta=0.5)
+    say(f"fp32 ragged {spec}")
+    full_check(gen.make(**spec, act="f32", wgt="f32", out="f32", cid=51, device=DEV))
+
+
+def test_c2_bf16_full():
+    say("c2 bf16 T=4096 H=2048 Hp=1024 E=64 K=6 (full oracle)")
+    full_check(gen.config("c2", device=DEV))
+
+
+# ----------------------------------------------------------------------------- single steps, limits
+
+@pytest.mark.parametrize("T,E,K", [(97, 4096, 32), (130, 1, 1), (1024, 384, 8), (65, 64, 64 // 2)])
+def test_route_topk_limits_with_ties(T, E, K):
+    say(f"route T={T} E={E} K={K}")
+    rng = np.random.default_rng(E + K)
+    lg = (np.round(rng.standard_normal((T, E)) * 3) / 3).astype(np.float32)   # many ties
+    logits = torch.from_numpy(lg).to(DEV)
+    idx = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, K), dtype=torch.float32, device=DEV)
+    moe.moe_route_topk(logits, T, E, K, idx, w)
+    ri, rw = O.route_topk(lg, K)
+    assert np.array_equal(host(idx), ri)
+    assert np.abs(host(w).astype(np.float64) - rw).max() <= 1e-6
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16", "fp8"])
+def test_permute_max_experts(act):
+    T, E, K, H = 3000, 1024, 8, 256
+    say(f"permute E={E} K={K} T={T} act={act}")
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    w = gen.make(T=T, H=H, Hp=128, E=8, K=1, act=act, wgt="bf16", routing="normal", cid=52, device=DEV)
+    x, x_sf = w.x, w.x_sf
+    M = T * K
+    ti = torch.from_numpy(idx).to(DEV)
+    tw = torch.rand((T, K), device=DEV)
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    cu = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    pos = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    row_src = torch.empty(M, dtype=torch.int32, device=DEV)
+    row_w = torch.empty(M, dtype=torch.float32, device=DEV)
+    xp = torch.empty((M, H), dtype=x.dtype, device=DEV)
+    xsf = torch.empty((M, H // 128), dtype=torch.float32, device=DEV) if act == "fp8" else None
+    n = moe.moe_permute_workspace_bytes(T, E, K)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    dt = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "fp8": moe.MOE_FP8_E4M3}[act]
+    moe.moe_permute(x, x_sf, dt, ti, tw, T, H, E, K, counts, cu, pos, row_src, row_w, xp, xsf, ws, n)
+    c_ref, cu_ref = O.count_offsets(idx, E)
+    p_ref, rs_ref = O.permute(idx, E)
+    assert np.array_equal(host(counts), c_ref) and np.array_equal(host(cu), cu_ref)
+    assert np.array_equal(host(pos), p_ref) and np.array_equal(host(row_src), rs_ref)
+    assert np.array_equal(host(row_w), host(tw).ravel()[rs_ref])
+    assert np.array_equal(host(xp), host(x)[rs_ref // K])
+    if act == "fp8":
+        assert np.array_equal(host(xsf), host(x_sf)[rs_ref // K])
+
+
+def test_empty_batch():
+    say("T=0")
+    E, K, H = 16, 2, 256
+    counts = torch.full((E,), 7, dtype=torch.int32, device=DEV)
+    cu = torch.full((E + 1,), 7, dtype=torch.int32, device=DEV)
+    n = moe.moe_permute_workspace_bytes(0, E, K)
+    ws = torch.empty(max(n, 1), dtype=torch.uint8, device=DEV)
+    moe.moe_permute(None, None, moe.MOE_BF16, None, None, 0, H, E, K, counts, cu, None, None, None,
+                    None, None, ws, n)
+    assert host(counts).tolist() == [0] * E and host(cu).tolist() == [0] * (E + 1)
+    w = gen.make(T=0, H=H, Hp=128, E=E, K=K, routing="normal", cid=53, device=DEV)
+    out, _, _ = run_layer(w)
+    torch.cuda.synchronize()
+    assert out.shape == (0, H)
+
+
+def test_invalid_ids_are_dropped_and_validated():
+    say("invalid expert ids")
+    w = gen.make(T=128, H=256, Hp=128, E=8, K=2, routing="balanced", cid=54, device=DEV)
+    bad = w.topk_idx.clone()
+    bad[5, 1] = 11
+    bad[9, 0] = -3
+    w.topk_idx = bad
+    r = run_steps(w)
+    torch.cuda.synchronize()
+    pos = host(r["pos"])
+    assert pos[5, 1] == -1 and pos[9, 0] == -1
+    assert int(host(r["cu_seqlens"])[-1]) == 128 * 2 - 2
+    # the dropped copies contribute nothing: compare with weights zeroed in the oracle
+    idx = host(bad).copy()
+    tw = host(w.topk_w).astype(np.float64)
+    tw[5, 1] = 0.0
+    tw[9, 0] = 0.0
+    idx[5, 1] = 0
+    idx[9, 0] = 0
+    x = O.decode_bf16(host(w.x))
+    from _oracle_run import weight_fn
+    ref = O.layer_token_loop(x, idx, tw, weight_fn(w))
+    assert rel_err(O.decode_bf16(host(r["out"])), ref) <= 2e-2
+    os.environ["MOE_VALIDATE"] = "1"
+    try:
+        with pytest.raises(moe.MoeError):
+            run_steps(w)
+        dup = w.topk_idx.clone()
+        dup[:, :] = torch.from_numpy(((np.arange(128)[:, None] * 2 + np.arange(2)) % 8).astype(np.int32)).to(DEV)
+        dup[3, 1] = dup[3, 0]
+        w.topk_idx = dup
+        with pytest.raises(moe.MoeError):
+            run_steps(w)
+    finally:
+        del os.environ["MOE_VALIDATE"]
+
+
+def test_layer_forward_matches_steps_and_is_deterministic():
+    say("layer_forward == steps, bitwise, twice")
+    w = gen.make(T=512, H=512, Hp=256, E=16, K=4, routing="skew", beta=0.5, cid=55, device=DEV)
+    r = run_steps(w)
+    out1, ws, lay = run_layer(w)
+    out2, _, _ = run_layer(w)
+    torch.cuda.synchronize()
+    assert torch.equal(out1.view(torch.int16), r["out"].view(torch.int16))
+    assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+    cu = ws[lay["cu_seqlens"]:lay["cu_seqlens"] + 4 * 17].view(torch.int32)
+    assert torch.equal(cu, r["cu_seqlens"])
+
+
+def test_debug_poison_leaves_no_nan():
+    say("MOE_DEBUG_POISON")
+    w = gen.make(T=200, H=256, Hp=128, E=8, K=2, routing="normal", cid=56, device=DEV)
+    os.environ["MOE_DEBUG_POISON"] = "1"
+    try:
+        out, _, _ = run_layer(w)
+        torch.cuda.synchronize()
+    finally:
+        del os.environ["MOE_DEBUG_POISON"]
+    assert not torch.isnan(out.float()).any()
+    ref = oracle_layer(w)
+    assert rel_err(O.decode_bf16(host(out)), ref["out"]) <= 2e-2
+
+
+# ----------------------------------------------------------------------------- full size, sampled
+
+def sampled_check(w, n_tokens=4):
+    """Full-size run: integers and x_perm in full, out[t] for a few tokens (one of them on
+    the busiest expert) from the oracle's direct expert loop."""
+    r = run_steps(w, with_row_w=False)
+    torch.cuda.synchronize()
+    ref = oracle_routing(w)
+    check_integers(r, ref, w.K)
+    check_x_perm(w, r, ref)
+    counts = ref["counts"]
+    hot = int(np.argmax(counts))
+    hot_rows = ref["row_src"][ref["cu_seqlens"][hot]:ref["cu_seqlens"][hot + 1]] // w.K
+    tokens = sorted({0, w.T - 1, int(hot_rows[0]), int(hot_rows[-1])})[:n_tokens]
+    want = oracle_tokens(w, tokens, ref)
+    out = O.decode_bf16(host(r["out"]))
+    errs = [rel_err(out[t], want[t]) for t in tokens]
+    mv = O.maxvio(counts, w.T, w.K, w.E)
+    print(f"  tokens {tokens} rel errs {[f'{e:.2e}' for e in errs]} maxvio {mv:.3f} "
+          f"rows/expert min {counts.min()} max {counts.max()}", flush=True)
+    assert max(errs) <= TOL[w.act]
+
+
+@pytest.mark.slow
+def test_c3_full_size_sampled():
+    say("c3 bf16 52 slots, full size")
+    sampled_check(gen.config("c3", device=DEV))
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("maxvio", [1.0, 20.0])
+def test_c4_full_size_sampled(maxvio):
+    say(f"c4 bf16 E=384 maxvio={maxvio}, full size")
+    sampled_check(gen.config("c4", device=DEV, maxvio=maxvio))
