@@ -1,0 +1,297 @@
+"""Benchmark of the MoE-layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2|c3|c4|c5] [--maxvio V]
+
+One step = one pass of the whole path over one batch of synthetic input, through the C ABI:
+route -> permute -> gate/up + SwiGLU -> down -> combine (c3 passes its given routing and
+skips route). Inputs and weights are resident in HBM before the timed region starts.
+Prints ONE JSON line. ``value`` is tokens/s of the whole layer. ``roofline`` describes the
+dominant kernel (the gate/up grouped GEMM): its algorithmic flops or bytes per launch over
+its average duration measured with HIP events on the launch stream during the timed steps.
+``cpu_baseline`` is the float64 oracle timed on the host on a bounded sample of the same
+workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s + grouped-FFN TFLOP/s as % of MFMA peak, 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # dense fp8 MFMA
+PEAK_FP32_TFLOPS = 157.3      # fp32 vector
+PEAK_HBM_GBS = 8000.0         # HBM3E
+
+DESCR = {
+    "c1": "tiny fp32 MoE layer T=64 H=128 H'=64 E=8 K=2, logits = x.Wr",
+    "c2": "bf16 MoE layer T=4096 H=2048 H'=1024 E=64 K=6, uniform routing",
+    "c3": "bf16 expert-parallel rank share: 65536 rows (T=8192 K=8) over 52 expert slots "
+          "(1260/1261 rows each), H=7168 H'=2048, routing given",
+    "c4": "bf16 MoE layer T=8192 H=7168 H'=2048 E=384 K=8, skewed routing",
+    "c5": "fp8 x MXFP4 MoE layer T=8192 H=7168 H'=2048 E=384 K=8, maxvio 1",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--maxvio", type=float, default=1.0, help="skew target for c4")
+    ap.add_argument("--cpu-sample-experts", type=int, default=0,
+                    help="experts in the oracle timing sample (0: whole layer when it is small)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "mixture_experts_layer_counting_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload, khash):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were taken on
+    the kernel as it is now (same source hash); otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            table = json.load(f)
+        ent = table[f"{kernel}@{workload}"]
+        if ent.get("source_hash") != khash:
+            return None
+        return float(ent["hbm_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the MoE hot path on exactly one GPU; multi-GPU "
+              "expert parallelism is designed but not built (see the sharding notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import mixture_experts_layer_counting_amd as moe
+    from workloads import gen
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    moe.lib()   # fail loudly if the HIP library is missing
+    w = gen.config(args.config, device=dev, maxvio=args.maxvio if args.config == "c4" else None)
+    T, H, Hp, E, K = w.T, w.H, w.Hp, w.E, w.K
+    M = T * K
+    DT = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "fp8": moe.MOE_FP8_E4M3, "mxfp4": moe.MOE_MXFP4}
+    TD = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+    hf = "fp8" if w.act == "fp8" else w.act
+    yf = "f32" if w.act == "f32" else "bf16"
+    i32 = dict(dtype=torch.int32, device=dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    topk_idx = torch.empty((T, K), **i32) if w.logits is not None else w.topk_idx
+    topk_w = torch.empty((T, K), **f32) if w.logits is not None else w.topk_w
+    counts = torch.empty(E, **i32)
+    cu = torch.empty(E + 1, **i32)
+    pos = torch.empty((T, K), **i32)
+    row_src = torch.empty(M, **i32)
+    x_perm = torch.empty((M, H), dtype=TD[w.act], device=dev)
+    x_perm_sf = torch.empty((M, H // 128), **f32) if w.act == "fp8" else None
+    h = torch.empty((M, Hp), dtype=TD[hf], device=dev)
+    h_sf = torch.empty((M, Hp // 128), **f32) if w.act == "fp8" else None
+    y = torch.empty((M, H), dtype=TD[yf], device=dev)
+    out = torch.empty((T, H), dtype=TD[w.out], device=dev)
+    nws = moe.moe_permute_workspace_bytes(T, E, K)
+    ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+
+    stages = ["route", "permute", "gate_up", "down", "combine"]
+    ev = {s: [] for s in stages}
+
+    def step(record):
+        def mark(name, fn):
+            if record:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                ev[name].append((a, b))
+            else:
+                fn()
+        if w.logits is not None:
+            mark("route", lambda: moe.moe_route_topk(w.logits, T, E, K, topk_idx, topk_w, sh))
+        mark("permute", lambda: moe.moe_permute(w.x, w.x_sf, DT[w.act], topk_idx, topk_w, T, H, E, K,
+                                                counts, cu, pos, row_src, None, x_perm, x_perm_sf,
+                                                ws, nws, sh))
+        mark("gate_up", lambda: moe.moe_ffn_gate_up(x_perm, x_perm_sf, DT[w.act], cu, M, E, H, Hp,
+                                                    w.w_gate, w.w_up, w.sf_gate, w.sf_up, DT[w.wgt],
+                                                    h, h_sf, sh))
+        mark("down", lambda: moe.moe_ffn_down(h, h_sf, DT[hf], cu, M, E, H, Hp, w.w_down, w.sf_down,
+                                              DT[w.wgt], y, DT[yf], sh))
+        mark("combine", lambda: moe.moe_combine(y, DT[yf], pos, topk_w, T, H, K, out, DT[w.out], sh))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    stage_ms = {s: (sum(a.elapsed_time(b) for a, b in ev[s]) / len(ev[s]) if ev[s] else 0.0)
+                for s in stages}
+
+    # ---------------------------------------------------------------- algorithmic units
+    cnt = counts.cpu().numpy()
+    active = int((cnt > 0).sum())
+    ab = {"f32": 4, "bf16": 2, "fp8": 1}[w.act]
+    hb = {"f32": 4, "bf16": 2, "fp8": 1}[hf]
+    yb = 4 if yf == "f32" else 2
+    ob = 4 if w.out == "f32" else 2
+    if w.wgt == "mxfp4":
+        wmat = H * Hp // 2 + H * Hp // 32          # packed e2m1 + e8m0 scales
+    else:
+        wmat = H * Hp * {"f32": 4, "bf16": 2}[w.wgt]
+    xsf_b = M * (H // 128) * 4 if w.act == "fp8" else 0
+    hsf_b = M * (Hp // 128) * 4 if w.act == "fp8" else 0
+    gu_flops = 4.0 * M * H * Hp
+    dn_flops = 2.0 * M * H * Hp
+    gu_bytes = M * H * ab + xsf_b + 2 * active * wmat + M * Hp * hb + hsf_b
+    dn_bytes = M * Hp * hb + hsf_b + active * wmat + M * H * yb
+    perm_bytes = T * H * ab + M * H * ab + (T * (H // 128) * 4 + xsf_b if w.act == "fp8" else 0)
+    comb_bytes = M * H * yb + T * H * ob
+    peak_flops = {"f32": PEAK_FP32_TFLOPS, "bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS}[w.act]
+    gu_s = stage_ms["gate_up"] / 1e3
+    t_mfma = gu_flops / (peak_flops * 1e12)
+    t_hbm = gu_bytes / (PEAK_HBM_GBS * 1e9)
+    khash = source_hash("ffn_bf16.hip", "tile_sched.h", "moe_common.h")
+    traffic = load_traffic("gate_up", args.config, khash)
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": gu_flops / gu_s / 1e12, "peak": peak_flops, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": gu_bytes / gu_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic
+    roof["kernel"] = "ffn_gate_up (grouped GEMM gate+up, SwiGLU epilogue)"
+    roof["per_launch"] = {"flops": gu_flops, "bytes": gu_bytes, "avg_ms": stage_ms["gate_up"]}
+
+    ffn_ms = stage_ms["gate_up"] + stage_ms["down"]
+    ffn_tflops = (gu_flops + dn_flops) / (ffn_ms / 1e3) / 1e12
+    line = {
+        "metric": METRIC,
+        "value": T * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8xmxfp4"}[w.act],
+        "data": "synthetic (seeded; random-init weights of the stated shape)",
+        "config": {"workload": f"{args.config}: {DESCR[args.config]}", "T": T, "H": H, "Hp": Hp,
+                   "E": E, "K": K, "act": w.act, "wgt": w.wgt},
+        "grouped_ffn_tflops": ffn_tflops,
+        "grouped_ffn_frac_of_mfma_peak": ffn_tflops / peak_flops,
+        "stage_ms": stage_ms,
+        "stage_rates": {
+            "gate_up_tflops": gu_flops / gu_s / 1e12,
+            "down_tflops": dn_flops / (stage_ms["down"] / 1e3) / 1e12,
+            "permute_gbs": perm_bytes / (stage_ms["permute"] / 1e3) / 1e9,
+            "combine_gbs": comb_bytes / (stage_ms["combine"] / 1e3) / 1e9,
+        },
+        "routing": {"maxvio": float(cnt.max() / (T * K / E) - 1.0), "active_experts": active,
+                    "rows_min": int(cnt.min()), "rows_max": int(cnt.max()),
+                    "maxvio_target": w.meta.get("maxvio_target")},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args, out)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(w, args, gpu_out):
+    """The oracle, as it stands, on the host: whole layer when small, else routing + permute +
+    combine for all tokens and the FFN for a sample of experts, scaled to all experts."""
+    import numpy as np
+    import torch
+
+    from oracle import moe_oracle as O
+    from workloads import to_numpy_bits
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    xb = to_numpy_bits(w.x)
+    x = O.decode_activations(xb, w.act, to_numpy_bits(w.x_sf))
+    fp8 = w.act == "fp8"
+
+    def wfn(e):
+        if w.wgt == "mxfp4":
+            return (O.decode_mxfp4(to_numpy_bits(w.w_gate[e]), to_numpy_bits(w.sf_gate[e])),
+                    O.decode_mxfp4(to_numpy_bits(w.w_up[e]), to_numpy_bits(w.sf_up[e])),
+                    O.decode_mxfp4(to_numpy_bits(w.w_down[e]), to_numpy_bits(w.sf_down[e])))
+        dec = (lambda a: np.asarray(a, np.float64)) if w.wgt == "f32" else O.decode_bf16
+        return dec(to_numpy_bits(w.w_gate[e])), dec(to_numpy_bits(w.w_up[e])), dec(to_numpy_bits(w.w_down[e]))
+
+    n_sample = args.cpu_sample_experts or (w.E if w.T * w.H <= 4096 * 2048 else 8)
+    n_sample = min(n_sample, w.E)
+    t0 = time.perf_counter()
+    if w.logits is not None:
+        idx, wts = O.route_topk(to_numpy_bits(w.logits), w.K)
+    else:
+        idx, wts = to_numpy_bits(w.topk_idx), to_numpy_bits(w.topk_w).astype(np.float64)
+    counts, cu = O.count_offsets(idx, w.E)
+    pos, row_src = O.permute(idx, w.E)
+    tok = row_src // w.K
+    t1 = time.perf_counter()
+    experts = list(range(w.E)) if n_sample == w.E else \
+        [int(e) for e in np.linspace(0, w.E - 1, n_sample).round().astype(int)]
+    y_rows = np.zeros((w.T * w.K, w.H))
+    t_ffn = 0.0
+    for e in experts:
+        lo, hi = int(cu[e]), int(cu[e + 1])
+        if hi == lo:
+            continue
+        s = time.perf_counter()
+        wg, wu, wd = wfn(e)
+        _, y_rows[lo:hi] = O.expert_ffn(x[tok[lo:hi]], wg, wu, wd, fp8)
+        t_ffn += time.perf_counter() - s
+    t2 = time.perf_counter()
+    ref = O.combine(y_rows, pos, wts)
+    t3 = time.perf_counter()
+    scale = w.E / len(experts)
+    total = (t1 - t0) + t_ffn * scale + (t3 - t2)
+    res = {"value": w.T / total, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "host_cpus": os.cpu_count(), "measured_s": (t1 - t0) + t_ffn + (t3 - t2),
+           "sample": (f"whole layer ({w.T} tokens, all {w.E} experts)" if n_sample == w.E else
+                      f"routing + permute + combine for all {w.T} tokens; expert FFN for "
+                      f"{len(experts)} of {w.E} experts (all their rows), FFN time scaled by "
+                      f"{scale:.1f}")}
+    if n_sample == w.E:
+        got = gpu_out.detach().cpu()
+        got = got.double().numpy() if got.dtype == torch.float32 else got.to(torch.float64).numpy()
+        res["gpu_vs_oracle_rel_err"] = float(np.abs(got - ref).max() / np.abs(ref).max())
+    return res
+
+
+if __name__ == "__main__":
+    main()
