@@ -49,7 +49,22 @@ def parse():
     ap.add_argument("--cpu-sample-experts", type=int, default=0,
                     help="experts in the oracle timing sample (0: whole layer when it is small)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (known bytes) a few times, "
+                         "to scale the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def copy_calibration(steps):
+    import torch
+    n = 1 << 30
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
+                      "launches": steps}), flush=True)
 
 
 def source_hash(*names):
@@ -83,6 +98,9 @@ def main():
               "expert parallelism is designed but not built (see the sharding notes).",
               file=sys.stderr)
         sys.exit(2)
+    if args.copy_calibration:
+        copy_calibration(max(args.steps, 1))
+        return
 
     import torch
 

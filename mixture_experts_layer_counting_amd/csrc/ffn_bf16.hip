@@ -29,37 +29,99 @@
 #include "moe_common.h"
 #include "tile_sched.h"
 
+#include <cstdlib>
+#include <cstring>
+
 namespace moe {
 
 constexpr int FB_BM = 256;
-constexpr int FB_BK = 64;
 constexpr int FB_THREADS = 512;
 constexpr int FB_MAX_E = 1024;
 
-template <bool GATED, int BN>
+template <bool GATED, int BN, int BK, int NS>
 struct FbCfg {
   static constexpr int NB = GATED ? 2 : 1;
   static constexpr int WN = BN / 2;
   static constexpr int NT = WN / 32;
   static constexpr int MT = 2;
-  static constexpr int A_BYTES = FB_BM * FB_BK * 2;
-  static constexpr int B_BYTES = FB_BK * BN * 2;
+  static constexpr int KK = BK / 16;                   // MFMA k-steps per stage
+  static constexpr int CPR = BK / 8;                   // 16-byte chunks per staged A row
+  static constexpr int A_ROW = BK * 2;
+  static constexpr int A_BYTES = FB_BM * A_ROW;
+  static constexpr int A_RPL = 1024 / A_ROW;           // A rows one wave load fills
+  static constexpr int A_LD = A_BYTES / (1024 * 8);    // A loads per wave per stage
+  static constexpr int A_SWZ_DIV = 16 / CPR;           // rows sharing one swizzle value
+  static constexpr int B_ROW = BN * 2;                 // bytes per staged weight row
+  static constexpr int B_BYTES = BK * B_ROW;           // per matrix
+  static constexpr int B_RPL = 1024 / B_ROW;           // weight rows one wave load fills
+  static constexpr int B_LD = NB * B_BYTES / (1024 * 8);
   static constexpr int STAGE = A_BYTES + NB * B_BYTES;
-  static constexpr int A_LD = FB_BM * (FB_BK / 8) / FB_THREADS;  // 16-byte chunks per thread
-  static constexpr int B_LD = FB_BK * (BN / 8) / FB_THREADS;      // per matrix
+  static constexpr int VM_PER_STAGE = A_LD + B_LD;     // vector-memory ops per lane per stage
   static constexpr int SCHED_BYTES = (FB_MAX_E + 1 + 16) * 4;
-  static constexpr int LDS_BYTES = 2 * STAGE + SCHED_BYTES;
+  static constexpr int LDS_BYTES = NS * STAGE + SCHED_BYTES;
+  static_assert(A_LD >= 1 && B_LD >= 1, "tile too small for one load per wave");
+  static_assert(VM_PER_STAGE * (NS - 2) < 16, "vmcnt wait count out of range");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
-template <bool GATED, int BN>
+// Buffer descriptor (base, range in bytes; raw, stride 0) in scalar registers.
+__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff);
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Direct global->LDS load of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane l's bytes
+// land at lds_base + 16*l, offsets past the descriptor's range write zeros. Written as asm so
+// the compiler does not add a full vmcnt(0) wait before every later LDS read; completion is
+// tracked explicitly with wait_barrier<N>() below. No output registers.
+__device__ __forceinline__ void lds_dma16(i32x4_t rsrc_in, uint32_t lds_base, int voff, int soff) {
+  i32x4_t rsrc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc_in[i]);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane((int)lds_base)), "v"(voff), "s"(rsrc),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory operations are outstanding, then
+// barrier the workgroup. The memory clobber keeps LDS reads on their side of the barrier.
+template <int N>
+__device__ __forceinline__ void wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const MOE_LDS void*)p;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_barrier_dyn(int n) {
+  // n in [0, N]: dispatch to the compile-time immediates
+  if constexpr (N > 0) {
+    if (n >= N) {
+      wait_barrier<N>();
+      return;
+    }
+    wait_barrier_dyn<N - 1>(n);
+  } else {
+    wait_barrier<0>();
+  }
+}
+
+template <bool GATED, int BN, int BK, int NS>
 __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
     const uint16_t* __restrict__ A, const int* __restrict__ cu, int M, int E, int Kd, int N,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C) {
-  using CF = FbCfg<GATED, BN>;
-  constexpr int BCH = BN / 8;                    // 16-byte chunks per B row
-  constexpr int B_ROWS_PER_LD = FB_THREADS / BCH;  // B rows covered by one load round
+  using CF = FbCfg<GATED, BN, BK, NS>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  int* tstart = reinterpret_cast<int*>(smem + 2 * CF::STAGE);
+  int* tstart = reinterpret_cast<int*>(smem + NS * CF::STAGE);
   int* wsum = tstart + FB_MAX_E + 1;
 
   const int tid = threadIdx.x;
@@ -69,35 +131,52 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
   const int wn = wave & 1;   // 0..1: BN/2-column half
   const int ntn = N / BN;
   const int total = build_tile_prefix<FB_BM, FB_THREADS>(cu, E, ntn, tstart, wsum);
-  const int nk = Kd / FB_BK;
+  const int nk = Kd / BK;
   const int G = gridDim.x;
   const int slot = xcd_slot(blockIdx.x, G);
 
-  // global -> LDS: thread owns A chunks (row tid/8 + 64 i, chunk tid%8) and B chunks
-  // (row tid/BCH + B_ROWS_PER_LD i, chunk tid%BCH); the swizzle only depends on tid.
-  const int a_voff = (tid >> 3) * Kd * 2 + (tid & 7) * 16;
-  const int a_lds0 = (tid >> 3) * 128 + (((tid & 7) ^ ((tid >> 4) & 7)) << 4);
-  const int b_row = tid / BCH, b_ch = tid % BCH;
-  const int b_voff = b_row * N * 2 + b_ch * 16;
-  const int b_lds0 = b_row * (BN * 2) + ((((b_ch >> 1) ^ ((b_row & 3) << 1))) << 5) + ((b_ch & 1) << 4);
-
-  // LDS -> MFMA fragments. A: row wm*64 + mt*32 + lane%32, 16-byte chunk 2*kk + lane/32,
-  // stored at chunk ^ ((row/2) % 8). B (transpose read): lane group g = lane/16 reads rows
-  // kk*16 + 8*(g/2) + (lane%16)/4 (+4 for the second half) at columns
-  // wn*WN + nt*32 + 16*(g%2) + 4*(lane%4); its 32-byte segment is stored at
-  // segment ^ 2*(row % 4). Both reduce to a per-lane base XOR a compile-time constant.
-  const int a_fbase = (wm * 64 + (lane & 31)) * 128;
-  const int a_t0 = (((lane >> 5) ^ ((lane >> 1) & 7))) << 4;
-  int a_fk[4];
+  // ---- global -> LDS (direct). A stage: [256 rows][BK] bf16; 16-byte slot p of row r holds
+  // chunk p ^ ((r / A_SWZ_DIV) % CPR), so 16 consecutive rows of one chunk hit 16 distinct
+  // bank groups. Wave load j (j = wave + 8 i) fills rows [j*A_RPL, (j+1)*A_RPL), lane l ->
+  // row j*A_RPL + l / CPR, slot l % CPR.
+  int a_voff[CF::A_LD], a_ldo[CF::A_LD];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) a_fk[kk] = a_fbase + ((kk << 5) ^ a_t0);
+  for (int i = 0; i < CF::A_LD; ++i) {
+    const int j = wave + 8 * i;
+    const int r = j * CF::A_RPL + lane / CF::CPR;
+    const int p = lane % CF::CPR;
+    a_voff[i] = r * Kd * 2 + ((p ^ ((r / CF::A_SWZ_DIV) % CF::CPR)) << 4);
+    a_ldo[i] = j * 1024;
+  }
+  // B stage per matrix: [BK rows][BN] bf16; 32-byte segment s of row k stored at
+  // s ^ 2*(k % 4). Wave load j covers B_RPL rows of matrix j / (B_BYTES / 1024).
+  int b_voff[CF::B_LD], b_ldo[CF::B_LD], b_mat[CF::B_LD];
+#pragma unroll
+  for (int i = 0; i < CF::B_LD; ++i) {
+    const int j = wave + 8 * i;
+    const int per_mat = CF::B_BYTES / 1024;
+    const int nb = j / per_mat;
+    const int r = (j % per_mat) * CF::B_RPL + lane / (64 / CF::B_RPL);
+    const int q = lane % (64 / CF::B_RPL);  // 16-byte slot within the row
+    const int sgm = (q >> 1) ^ ((r & 3) << 1);
+    b_voff[i] = r * N * 2 + ((sgm << 1) + (q & 1)) * 16;
+    b_ldo[i] = CF::A_BYTES + j * 1024;
+    b_mat[i] = nb;
+  }
+
+  // ---- LDS -> MFMA fragments
+  const int a_fbase = (wm * 64 + (lane & 31)) * CF::A_ROW;
+  const int a_sw = ((lane & 31) / CF::A_SWZ_DIV) % CF::CPR;
+  int a_fk[CF::KK];
+#pragma unroll
+  for (int kk = 0; kk < CF::KK; ++kk) a_fk[kk] = a_fbase + ((((kk << 1) | (lane >> 5)) ^ a_sw) << 4);
   const int g = lane >> 4, jj = lane & 15;
   const int bP = (wn * CF::WN) / 16 + (g & 1);
-  const int b_fbase = (8 * (g >> 1) + (jj >> 2)) * (BN * 2) + 8 * (jj & 3) +
-                      ((bP ^ ((jj >> 2) << 1)) << 5);
+  const int b_fbase = (8 * (g >> 1) + (jj >> 2)) * CF::B_ROW + 8 * (jj & 3) + ((bP ^ ((jj >> 2) << 1)) << 5);
   int b_fn[CF::NT];
 #pragma unroll
   for (int nt = 0; nt < CF::NT; ++nt) b_fn[nt] = b_fbase ^ (nt << 6);
+  const uint32_t smem_lds = lds_addr(smem);
 
   for (int t = slot; t < total; t += G) {
     const int e = find_expert(tstart, E, t);
@@ -111,41 +190,20 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
     const int rows_valid = min(FB_BM, rows_e - mtile * FB_BM);
     const int n0 = ntile * BN;
 
-    // buffer descriptors: rows past M read as zero (hardware range check)
     const size_t a_rem = (size_t)(M - row0) * Kd * 2;
-    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(A + (size_t)row0 * Kd), 0, (int)(a_rem > 0x7fffffffu ? 0x7fffffffu : a_rem), 0x00020000);
+    const i32x4_t rA = make_rsrc(A + (size_t)row0 * Kd, (uint32_t)(a_rem > 0x7fffffffu ? 0x7fffffffu : a_rem));
     const size_t woff = (size_t)e * Kd * N + n0;
-    const int b_rem = (int)(((size_t)Kd * N - n0) * 2);
-    const __amdgpu_buffer_rsrc_t rB0 = __builtin_amdgcn_make_buffer_rsrc((void*)(B0 + woff), 0, b_rem, 0x00020000);
-    __amdgpu_buffer_rsrc_t rB1 = rB0;
-    if constexpr (GATED) rB1 = __builtin_amdgcn_make_buffer_rsrc((void*)(B1 + woff), 0, b_rem, 0x00020000);
+    const uint32_t b_rem = (uint32_t)(((size_t)Kd * N - n0) * 2);
+    const i32x4_t rB0 = make_rsrc(B0 + woff, b_rem);
+    const i32x4_t rB1 = GATED ? make_rsrc(B1 + woff, b_rem) : rB0;
 
-    i32x4_t ra[CF::A_LD];
-    i32x4_t rb[CF::NB][CF::B_LD];
-    auto gload = [&](int kt) {
+    auto issue = [&](int kt) {  // A_LD + B_LD direct loads per lane for stage kt
+      const uint32_t so = smem_lds + (uint32_t)((kt % NS) * CF::STAGE);
 #pragma unroll
-      for (int i = 0; i < CF::A_LD; ++i)
-        ra[i] = __builtin_bit_cast(i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rA, a_voff, i * 64 * Kd * 2 + kt * FB_BK * 2, 0));
+      for (int i = 0; i < CF::A_LD; ++i) lds_dma16(rA, so + a_ldo[i], a_voff[i], kt * BK * 2);
 #pragma unroll
-      for (int i = 0; i < CF::B_LD; ++i) {
-        const int so = (kt * FB_BK + i * B_ROWS_PER_LD) * N * 2;
-        rb[0][i] = __builtin_bit_cast(i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB0, b_voff, so, 0));
-        if constexpr (GATED)
-          rb[1][i] = __builtin_bit_cast(i32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rB1, b_voff, so, 0));
-      }
-    };
-    auto sstore = [&](int st) {
-      unsigned char* base = smem + st * CF::STAGE;
-#pragma unroll
-      for (int i = 0; i < CF::A_LD; ++i) *reinterpret_cast<i32x4_t*>(base + a_lds0 + i * 64 * 128) = ra[i];
-#pragma unroll
-      for (int nb = 0; nb < CF::NB; ++nb)
-#pragma unroll
-        for (int i = 0; i < CF::B_LD; ++i)
-          *reinterpret_cast<i32x4_t*>(base + CF::A_BYTES + nb * CF::B_BYTES + b_lds0 +
-                                      i * B_ROWS_PER_LD * BN * 2) = rb[nb][i];
+      for (int i = 0; i < CF::B_LD; ++i)
+        lds_dma16(b_mat[i] ? rB1 : rB0, so + b_ldo[i], b_voff[i], kt * BK * N * 2);
     };
 
     f32x16_t acc[CF::NB][CF::MT][CF::NT];
@@ -158,27 +216,29 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[nb][mt][nt][i] = 0.f;
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
+    __syncthreads();  // previous tile's readers are done with every stage
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+      if (s < nk) issue(s);
     for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) gload(kt + 1);
-      const unsigned char* sa = smem + cur * CF::STAGE;
+      // stage kt has landed once at most (stages issued after it) * VM_PER_STAGE remain
+      wait_barrier_dyn<CF::VM_PER_STAGE*(NS - 2)>(min(NS - 2, nk - 1 - kt) * CF::VM_PER_STAGE);
+      if (kt + NS - 1 < nk) issue(kt + NS - 1);
+      const unsigned char* sa = smem + (kt % NS) * CF::STAGE;
       const unsigned char* sb = sa + CF::A_BYTES;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
+      for (int kk = 0; kk < CF::KK; ++kk) {
         bf16x8_t af[CF::MT];
 #pragma unroll
         for (int mt = 0; mt < CF::MT; ++mt)
-          af[mt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const i32x4_t*>(sa + a_fk[kk] + mt * 32 * 128));
+          af[mt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const i32x4_t*>(sa + a_fk[kk] + mt * 32 * CF::A_ROW));
 #pragma unroll
         for (int nb = 0; nb < CF::NB; ++nb) {
 #pragma unroll
           for (int nt = 0; nt < CF::NT; ++nt) {
-            const unsigned char* p = sb + nb * CF::B_BYTES + b_fn[nt] + kk * 16 * BN * 2;
+            const unsigned char* p = sb + nb * CF::B_BYTES + b_fn[nt] + kk * 16 * CF::B_ROW;
             const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(p));
-            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(p + 4 * BN * 2));
+            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(p + 4 * CF::B_ROW));
             const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
             for (int mt = 0; mt < CF::MT; ++mt)
@@ -186,8 +246,6 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
           }
         }
       }
-      if (kt + 1 < nk) sstore(cur ^ 1);
-      __syncthreads();
     }
 
     // epilogue: lane holds column lane%32 of rows 8*(i/4) + 4*(lane/32) + i%4
@@ -212,26 +270,43 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
   }
 }
 
-template <bool GATED, int BN>
+template <bool GATED, int BN, int BK, int NS>
 static moe_status_t launch_fb(const uint16_t* A, const int* cu, int M, int E, int Kd, int N,
                               const uint16_t* B0, const uint16_t* B1, uint16_t* C, hipStream_t s) {
-  using CF = FbCfg<GATED, BN>;
+  using CF = FbCfg<GATED, BN, BK, NS>;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_kernel<GATED, BN>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_kernel<GATED, BN, BK, NS>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS_BYTES) != hipSuccess)
       return MOE_EHIP;
     attr_set = true;
   }
   const int grid = device_cu_count();
-  ffn_bf16_kernel<GATED, BN><<<grid, FB_THREADS, CF::LDS_BYTES, s>>>(A, cu, M, E, Kd, N, B0, B1, C);
+  ffn_bf16_kernel<GATED, BN, BK, NS><<<grid, FB_THREADS, CF::LDS_BYTES, s>>>(A, cu, M, E, Kd, N, B0, B1, C);
   return launch_status();
+}
+
+// K-step / LDS-stage pipeline variant: MOE_FFN_PIPE = "64x2" (default) or "32x4".
+static int pipe_variant() {
+  static int v = -1;
+  if (v < 0) {
+    const char* p = std::getenv("MOE_FFN_PIPE");
+    v = (p && !std::strcmp(p, "32x4")) ? 1 : 0;
+  }
+  return v;
+}
+
+template <bool GATED, int BN>
+static moe_status_t launch_fb_any(const uint16_t* A, const int* cu, int M, int E, int Kd, int N,
+                                  const uint16_t* B0, const uint16_t* B1, uint16_t* C, hipStream_t s) {
+  if (pipe_variant() == 1) return launch_fb<GATED, BN, 32, 4>(A, cu, M, E, Kd, N, B0, B1, C, s);
+  return launch_fb<GATED, BN, 64, 2>(A, cu, M, E, Kd, N, B0, B1, C, s);
 }
 
 moe_status_t launch_ffn_gate_up_bf16(const void* x_perm, const int* cu, int M, int E, int H, int Hp,
                                      const void* wg, const void* wu, void* h, hipStream_t s) {
   if (M == 0) return MOE_OK;
-  return launch_fb<true, 128>(static_cast<const uint16_t*>(x_perm), cu, M, E, H, Hp,
+  return launch_fb_any<true, 128>(static_cast<const uint16_t*>(x_perm), cu, M, E, H, Hp,
                               static_cast<const uint16_t*>(wg), static_cast<const uint16_t*>(wu),
                               static_cast<uint16_t*>(h), s);
 }
@@ -239,7 +314,7 @@ moe_status_t launch_ffn_gate_up_bf16(const void* x_perm, const int* cu, int M, i
 moe_status_t launch_ffn_down_bf16(const void* h, const int* cu, int M, int E, int H, int Hp,
                                   const void* wd, void* y, hipStream_t s) {
   if (M == 0) return MOE_OK;
-  return launch_fb<false, 256>(static_cast<const uint16_t*>(h), cu, M, E, Hp, H,
+  return launch_fb_any<false, 256>(static_cast<const uint16_t*>(h), cu, M, E, Hp, H,
                                static_cast<const uint16_t*>(wd), nullptr, static_cast<uint16_t*>(y), s);
 }
 
