@@ -1,0 +1,390 @@
+// Grouped expert FFN with fp8 (e4m3fn, 1x128 power-of-two block scales) activations and
+// MXFP4 (e2m1 + e8m0 per 32 along the reduction) weights, on gfx950 scaled matrix cores.
+//
+// "Mixture of Kittens", Step 1 (expert = Down(SwiGLU(Up x, Gate x))) and Step 8 (low
+// precision with activation quantisation fused into the GEMMs and SwiGLU); DeepGEMM's
+// Mega-MoE how-to names the same dual FP8 x FP4 GEMMs with per-block scale factors for the
+// inputs and for the activations between the two GEMMs. Here:
+//   gate/up:  h = silu(x.Wg) * (x.Wu) in fp32, requantised in the epilogue to e4m3fn with one
+//             power-of-two scale per 1x128 block of each row (s = smallest 2^e with
+//             448 s >= block amax; code = round-to-nearest-even(h / s)),
+//   down:     y = h.Wd, bf16 output.
+//
+// MFMA v_mfma_scale_f32_32x32x64_f8f6f4 (A fp8, B fp4). Operand layouts (verified on the
+// device): an fp8 operand lane in group G = lane/32 holds two 16-byte runs of consecutive k,
+// at k = 16G and k = 32 + 16G; an fp4 operand lane holds the 32 consecutive k = 32G.. in 16
+// bytes, low nibble first; the scale register of lane (row or column, G) applies to k-block
+// [32G, 32G+32). Activation scales are per 128 k, so one exponent covers a whole K step.
+//
+// Same persistent, XCD-contiguous tile schedule and direct global->LDS double buffering as the
+// bf16 kernels. Block tile 256 rows x BN columns per weight matrix, K step 128. Activations are
+// staged [256][128 B] (16-byte chunk ^ (row/2 mod 8)); weights, stored reduction-contiguous
+// [N][K/2], are staged [BN][64 B] (chunk ^ (col/4 mod 4)). Both fragment reads are
+// ds_read_b128 without transposes. Per-stage scales are loaded straight into registers one
+// stage ahead.
+#include "moe_common.h"
+#include "tile_sched.h"
+
+namespace moe {
+
+constexpr int F8_BM = 256;
+constexpr int F8_BK = 128;  // reduction elements per stage
+constexpr int F8_NS = 2;
+constexpr int F8_THREADS = 512;
+constexpr int F8_MAX_E = 1024;
+
+template <bool GATED, int BN>
+struct F8Cfg {
+  static constexpr int NB = GATED ? 2 : 1;
+  static constexpr int WN = BN / 2;
+  static constexpr int NT = WN / 32;
+  static constexpr int MT = 2;
+  static constexpr int NF = NB * NT;
+  static constexpr int KK = F8_BK / 64;                   // MFMA k-steps per stage
+  static constexpr int A_BYTES = F8_BM * F8_BK;            // 32 KiB, 128 B per row
+  static constexpr int A_LD = A_BYTES / (1024 * 8);        // wave loads per stage (8 rows each)
+  static constexpr int B_ROW = F8_BK / 2;                  // 64 B per weight column
+  static constexpr int B_BYTES = BN * B_ROW;               // per matrix
+  static constexpr int B_LD = NB * B_BYTES / (1024 * 8);   // wave loads per stage (16 cols each)
+  static constexpr int STAGE = A_BYTES + NB * B_BYTES;
+  static constexpr int VM_PER_STAGE = A_LD + B_LD;
+  static constexpr int SCHED_BYTES = (F8_MAX_E + 1 + 16) * 4;
+  static constexpr int LDS_BYTES = F8_NS * STAGE + SCHED_BYTES;
+  static_assert(A_LD >= 1 && B_LD >= 1, "tile too small");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
+
+__device__ __forceinline__ i32x4_t f8_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4_t r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff);
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+
+// Direct global->LDS 16-byte load (see ffn_bf16.hip): asm so the compiler does not wait for
+// it before unrelated LDS reads; completion is tracked with f8_wait_barrier.
+__device__ __forceinline__ void f8_dma16(i32x4_t rsrc_in, uint32_t lds_base, int voff, int soff) {
+  i32x4_t rsrc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc_in[i]);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane((int)lds_base)), "v"(voff), "s"(rsrc),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ void f8_wait_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
+}
+
+// e8m0 byte of an fp32 power of two
+__device__ __forceinline__ int pow2_to_e8m0(float s) { return (__float_as_uint(s) >> 23) & 0xff; }
+
+// fp32 -> OCP e4m3fn code, round to nearest even; |v| <= 448 by construction of the scale.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sgn = (u >> 24) & 0x80u;
+  const float a = __builtin_fabsf(v);
+  uint32_t code;
+  if (a < 0.015625f) {  // below 2^-6: subnormal grid of step 2^-9 (code 8 is 2^-6 itself)
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    const uint32_t m = u & 0x7fffffffu;
+    const uint32_t r = (m + 0x7ffffu + ((m >> 20) & 1u)) >> 20;  // keep 3 mantissa bits, RNE
+    code = r - ((127u - 7u) << 3);
+    if (code > 0x7eu) code = 0x7eu;                               // saturate at 448
+  }
+  return sgn | code;
+}
+
+template <bool GATED, int BN>
+__global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
+    const uint8_t* __restrict__ A, const float* __restrict__ A_sf, const int* __restrict__ cu,
+    int M, int E, int Kd, int N, const uint8_t* __restrict__ B0, const uint8_t* __restrict__ B0_sf,
+    const uint8_t* __restrict__ B1, const uint8_t* __restrict__ B1_sf, uint8_t* __restrict__ C8,
+    float* __restrict__ C8_sf, uint16_t* __restrict__ C16) {
+  using CF = F8Cfg<GATED, BN>;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int* tstart = reinterpret_cast<int*>(smem + F8_NS * CF::STAGE);
+  int* wsum = tstart + F8_MAX_E + 1;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const int ntn = N / BN;
+  const int total = build_tile_prefix<F8_BM, F8_THREADS>(cu, E, ntn, tstart, wsum);
+  const int nk = Kd / F8_BK;
+  const int kbytes = Kd / 2;     // bytes per weight column
+  const int ksf_b = Kd / 32;     // weight scale bytes per column
+  const int ksf_a = Kd / 128;    // activation scales per row
+  const int G = gridDim.x;
+  const int slot = xcd_slot(blockIdx.x, G);
+  const uint32_t smem_lds = (uint32_t)(uintptr_t)(const MOE_LDS void*)smem;
+
+  // global -> LDS coordinates. A wave load j (= wave + 8 i) covers rows 8j..8j+7 (128 B each):
+  // lane -> row 8j + lane/8, slot lane%8 holds chunk slot ^ ((row/2) % 8).
+  int a_voff[CF::A_LD];
+#pragma unroll
+  for (int i = 0; i < CF::A_LD; ++i) {
+    const int r = (wave + 8 * i) * 8 + (lane >> 3);
+    a_voff[i] = r * Kd + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
+  }
+  // B wave load j covers columns 16j'..16j'+15 (64 B each) of matrix j / (B_BYTES/1024):
+  // lane -> column lane/4, slot lane%4 holds chunk slot ^ ((col/4) % 4).
+  int b_voff[CF::B_LD];
+#pragma unroll
+  for (int i = 0; i < CF::B_LD; ++i) {
+    const int j = wave + 8 * i;
+    const int c = (j % (CF::B_BYTES / 1024)) * 16 + (lane >> 2);
+    b_voff[i] = c * kbytes + (((lane & 3) ^ ((c >> 2) & 3)) << 4);
+  }
+
+  // fragment offsets. A (fp8, 32x64 per MFMA): row wm*64 + mt*32 + lane%32, chunks 4kk + G
+  // and 4kk + 2 + G. B (fp4): column wn*WN + nt*32 + lane%32, chunk 2kk + G.
+  const int g2 = lane >> 5;
+  const int ar = wm * 64 + (lane & 31);
+  const int a_sw = (ar >> 1) & 7;  // (mt*32)/2 is a multiple of 8: same swizzle for both mt
+  int a_off[CF::KK][2];
+#pragma unroll
+  for (int kk = 0; kk < CF::KK; ++kk)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) a_off[kk][h] = ar * F8_BK + (((4 * kk + 2 * h + g2) ^ a_sw) << 4);
+  int b_off[CF::NT][CF::KK];
+#pragma unroll
+  for (int nt = 0; nt < CF::NT; ++nt) {
+    const int c = wn * CF::WN + nt * 32 + (lane & 31);
+#pragma unroll
+    for (int kk = 0; kk < CF::KK; ++kk) b_off[nt][kk] = c * CF::B_ROW + (((2 * kk + g2) ^ ((c >> 2) & 3)) << 4);
+  }
+
+  for (int t = slot; t < total; t += G) {
+    const int e = find_expert(tstart, E, t);
+    const int lt = t - tstart[e];
+    const int gbeg = cu[e];
+    const int rows_e = cu[e + 1] - gbeg;
+    const int mte = (rows_e + F8_BM - 1) / F8_BM;
+    const int ntile = lt / mte;
+    const int mtile = lt - ntile * mte;
+    const int row0 = gbeg + mtile * F8_BM;
+    const int rows_valid = min(F8_BM, rows_e - mtile * F8_BM);
+    const int n0 = ntile * BN;
+
+    const size_t a_rem = (size_t)(M - row0) * Kd;
+    const i32x4_t rA = f8_rsrc(A + (size_t)row0 * Kd, (uint32_t)(a_rem > 0x7fffffffu ? 0x7fffffffu : a_rem));
+    const size_t wbase = ((size_t)e * N + n0) * kbytes;
+    const uint32_t b_rem = (uint32_t)((size_t)(N - n0) * kbytes);
+    const i32x4_t rB0 = f8_rsrc(B0 + wbase, b_rem);
+    const i32x4_t rB1 = GATED ? f8_rsrc(B1 + wbase, b_rem) : rB0;
+    // scale rows of this lane: activations (per mt) and weight columns (per fragment)
+    const float* asf_row[CF::MT];
+#pragma unroll
+    for (int mt = 0; mt < CF::MT; ++mt) {
+      const int r = min(row0 + ar + mt * 32, M - 1);
+      asf_row[mt] = A_sf + (size_t)r * ksf_a;
+    }
+    const uint8_t* bsf_col[CF::NF];
+#pragma unroll
+    for (int f = 0; f < CF::NF; ++f) {
+      const int nb = f / CF::NT, nt = f % CF::NT;
+      const uint8_t* base = (GATED && nb) ? B1_sf : B0_sf;
+      bsf_col[f] = base + ((size_t)e * N + n0 + wn * CF::WN + nt * 32 + (lane & 31)) * ksf_b;
+    }
+
+    auto issue = [&](int kt) {
+      const uint32_t so = smem_lds + (uint32_t)((kt % F8_NS) * CF::STAGE);
+#pragma unroll
+      for (int i = 0; i < CF::A_LD; ++i) f8_dma16(rA, so + (wave + 8 * i) * 1024, a_voff[i], kt * F8_BK);
+#pragma unroll
+      for (int i = 0; i < CF::B_LD; ++i) {
+        const int j = wave + 8 * i;
+        const bool second = GATED && (j / (CF::B_BYTES / 1024)) != 0;
+        f8_dma16(second ? rB1 : rB0, so + CF::A_BYTES + j * 1024, b_voff[i], kt * (F8_BK / 2));
+      }
+    };
+    // per-stage scales: one activation exponent per mt (its 1x128 block), one dword of four
+    // weight exponents per fragment (k-blocks 4kt..4kt+3 of the lane's column)
+    int sa_next[CF::MT], sb_next[CF::NF];
+    auto load_scales = [&](int kt) {
+#pragma unroll
+      for (int mt = 0; mt < CF::MT; ++mt) sa_next[mt] = pow2_to_e8m0(asf_row[mt][kt]);
+#pragma unroll
+      for (int f = 0; f < CF::NF; ++f) sb_next[f] = *reinterpret_cast<const int*>(bsf_col[f] + 4 * kt);
+    };
+
+    f32x16_t acc[CF::NB][CF::MT][CF::NT];
+#pragma unroll
+    for (int nb = 0; nb < CF::NB; ++nb)
+#pragma unroll
+      for (int mt = 0; mt < CF::MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < CF::NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[nb][mt][nt][i] = 0.f;
+
+    __syncthreads();
+    issue(0);
+    load_scales(0);
+    for (int kt = 0; kt < nk; ++kt) {
+      f8_wait_barrier();
+      // Take this stage's scales now: their loads are complete (the barrier waited for every
+      // outstanding vector-memory op), and consuming them here keeps the compiler's own wait
+      // for them from landing after the next stage's loads are issued.
+      int sa[CF::MT], sb[CF::NF];
+#pragma unroll
+      for (int mt = 0; mt < CF::MT; ++mt) {
+        sa[mt] = sa_next[mt];
+        asm volatile("" : : "v"(sa[mt]));
+      }
+#pragma unroll
+      for (int f = 0; f < CF::NF; ++f) {
+        sb[f] = sb_next[f];
+        asm volatile("" : : "v"(sb[f]));
+      }
+      if (kt + 1 < nk) {
+        issue(kt + 1);
+        load_scales(kt + 1);
+      }
+      const unsigned char* sa_l = smem + (kt % F8_NS) * CF::STAGE;
+      const unsigned char* sb_l = sa_l + CF::A_BYTES;
+#pragma unroll
+      for (int kk = 0; kk < CF::KK; ++kk) {
+        i32x8_t af[CF::MT];
+#pragma unroll
+        for (int mt = 0; mt < CF::MT; ++mt) {
+          const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(sa_l + a_off[kk][0] + mt * 32 * F8_BK);
+          const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(sa_l + a_off[kk][1] + mt * 32 * F8_BK);
+          af[mt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+#pragma unroll
+        for (int nb = 0; nb < CF::NB; ++nb) {
+#pragma unroll
+          for (int nt = 0; nt < CF::NT; ++nt) {
+            const i32x4_t bq = *reinterpret_cast<const i32x4_t*>(sb_l + nb * CF::B_BYTES + b_off[nt][kk]);
+            const i32x4_t z = {0, 0, 0, 0};
+            const i32x8_t bfr = __builtin_shufflevector(bq, z, 0, 1, 2, 3, 4, 5, 6, 7);
+            // weight scale byte for k-block 4kt + 2kk + G of this column
+            const int sbw = (sb[nb * CF::NT + nt] >> (8 * (2 * kk + g2))) & 0xff;
+#pragma unroll
+            for (int mt = 0; mt < CF::MT; ++mt)
+              acc[nb][mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  af[mt], bfr, acc[nb][mt][nt], 0, 4, 0, sa[mt], 0, sbw);
+          }
+        }
+      }
+    }
+
+    if constexpr (GATED) {
+      // SwiGLU, then per-row amax over this wave's 64 columns of the 128-column block; the two
+      // column halves (wn = 0, 1) meet in LDS.
+      float* part = reinterpret_cast<float*>(smem);  // [2][256]
+      float hv[CF::MT][CF::NT][16];
+      float rmax[CF::MT][16];
+#pragma unroll
+      for (int mt = 0; mt < CF::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float m = 0.f;
+#pragma unroll
+          for (int nt = 0; nt < CF::NT; ++nt) {
+            const float v = silu_f32(acc[0][mt][nt][i]) * acc[1][mt][nt][i];
+            hv[mt][nt][i] = v;
+            m = fmaxf(m, __builtin_fabsf(v));
+          }
+#pragma unroll
+          for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+          rmax[mt][i] = m;
+        }
+      __syncthreads();  // every wave is done with the stage buffers
+      if ((lane & 31) == 0) {
+#pragma unroll
+        for (int mt = 0; mt < CF::MT; ++mt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            part[wn * 256 + wm * 64 + mt * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3)] = rmax[mt][i];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int mt = 0; mt < CF::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = wm * 64 + mt * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3);
+          const float amax = fmaxf(part[r], part[256 + r]);
+          // smallest power of two s with 448 s >= amax (amax = 0 -> 1)
+          float s = 1.0f;
+          if (amax > 0.f) {
+            int ex;
+            const float mant = __builtin_frexpf(amax / 448.0f, &ex);  // amax/448 = mant * 2^ex
+            s = __builtin_ldexpf(1.0f, mant == 0.5f ? ex - 1 : ex);
+            if (448.0f * s < amax) s *= 2.0f;
+          }
+          const float inv = 1.0f / s;
+          if (r < rows_valid) {
+            const size_t ro = (size_t)(row0 + r);
+#pragma unroll
+            for (int nt = 0; nt < CF::NT; ++nt) {
+              const int col = n0 + wn * CF::WN + nt * 32 + (lane & 31);
+              C8[ro * N + col] = (uint8_t)f32_to_e4m3(hv[mt][nt][i] * inv);
+            }
+            if (wn == 0 && (lane & 31) == 0) C8_sf[ro * (N / 128) + n0 / 128] = s;
+          }
+        }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < CF::MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < CF::NT; ++nt) {
+          const int col = n0 + wn * CF::WN + nt * 32 + (lane & 31);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = wm * 64 + mt * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3);
+            if (r < rows_valid) C16[(size_t)(row0 + r) * N + col] = f32_to_bf16_bits(acc[0][mt][nt][i]);
+          }
+        }
+    }
+  }
+}
+
+template <bool GATED, int BN>
+static moe_status_t launch_f8(const uint8_t* A, const float* A_sf, const int* cu, int M, int E,
+                              int Kd, int N, const uint8_t* B0, const uint8_t* B0_sf,
+                              const uint8_t* B1, const uint8_t* B1_sf, uint8_t* C8, float* C8_sf,
+                              uint16_t* C16, hipStream_t s) {
+  using CF = F8Cfg<GATED, BN>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_fp8_kernel<GATED, BN>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS_BYTES) != hipSuccess)
+      return MOE_EHIP;
+    attr_set = true;
+  }
+  ffn_fp8_kernel<GATED, BN><<<device_cu_count(), F8_THREADS, CF::LDS_BYTES, s>>>(
+      A, A_sf, cu, M, E, Kd, N, B0, B0_sf, B1, B1_sf, C8, C8_sf, C16);
+  return launch_status();
+}
+
+moe_status_t launch_ffn_gate_up_fp8(const void* x_perm, const float* x_sf, const int* cu, int M,
+                                    int E, int H, int Hp, const void* wg, const uint8_t* sg,
+                                    const void* wu, const uint8_t* su, void* h, float* h_sf,
+                                    hipStream_t s) {
+  if (M == 0) return MOE_OK;
+  return launch_f8<true, 128>(static_cast<const uint8_t*>(x_perm), x_sf, cu, M, E, H, Hp,
+                              static_cast<const uint8_t*>(wg), sg, static_cast<const uint8_t*>(wu),
+                              su, static_cast<uint8_t*>(h), h_sf, nullptr, s);
+}
+
+moe_status_t launch_ffn_down_fp8(const void* h, const float* h_sf, const int* cu, int M, int E,
+                                 int H, int Hp, const void* wd, const uint8_t* sd, void* y,
+                                 hipStream_t s) {
+  if (M == 0) return MOE_OK;
+  return launch_f8<false, 256>(static_cast<const uint8_t*>(h), h_sf, cu, M, E, Hp, H,
+                               static_cast<const uint8_t*>(wd), sd, nullptr, nullptr, nullptr,
+                               nullptr, static_cast<uint16_t*>(y), s);
+}
+
+}  // namespace moe

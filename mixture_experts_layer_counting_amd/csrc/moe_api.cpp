@@ -24,6 +24,11 @@ moe_status_t launch_ffn_gate_up_bf16(const void*, const int*, int, int, int, int
                                      const void*, void*, hipStream_t);
 moe_status_t launch_ffn_down_bf16(const void*, const int*, int, int, int, int, const void*, void*,
                                   hipStream_t);
+moe_status_t launch_ffn_gate_up_fp8(const void*, const float*, const int*, int, int, int, int,
+                                    const void*, const uint8_t*, const void*, const uint8_t*, void*,
+                                    float*, hipStream_t);
+moe_status_t launch_ffn_down_fp8(const void*, const float*, const int*, int, int, int, int,
+                                 const void*, const uint8_t*, void*, hipStream_t);
 moe_status_t launch_ffn_gate_up_f32(const void*, const int*, int, int, int, int, const void*,
                                     const void*, void*, hipStream_t);
 moe_status_t launch_ffn_down_f32(const void*, const int*, int, int, int, int, const void*, void*,
@@ -86,7 +91,10 @@ static moe_status_t check_ffn_dims(Path p, int64_t M, int E, int H, int Hp, bool
       if (gate_up) return (H % 64 == 0 && Hp % 128 == 0) ? MOE_OK : MOE_EUNSUPPORTED;
       return (H % 256 == 0 && Hp % 64 == 0) ? MOE_OK : MOE_EUNSUPPORTED;
     case PATH_FP8_MXFP4:
-      return MOE_EUNSUPPORTED;
+      if (E > 1024) return MOE_EUNSUPPORTED;
+      if ((int64_t)H * Hp >= (1ll << 31) || 256ll * (H > Hp ? H : Hp) >= (1ll << 31)) return MOE_EUNSUPPORTED;
+      if (gate_up) return (H % 128 == 0 && Hp % 128 == 0) ? MOE_OK : MOE_EUNSUPPORTED;
+      return (H % 256 == 0 && Hp % 128 == 0) ? MOE_OK : MOE_EUNSUPPORTED;
     default:
       return MOE_EUNSUPPORTED;
   }
@@ -171,10 +179,11 @@ moe_status_t moe_ffn_gate_up(const void* x_perm, const float* x_perm_sf, moe_dty
   if (st != MOE_OK) return st;
   if (!cu_seqlens) return MOE_EINVAL;
   if (M > 0 && (!x_perm || !w_gate || !w_up || !h)) return MOE_EINVAL;
-  (void)x_perm_sf;
-  (void)sf_gate;
-  (void)sf_up;
-  (void)h_sf;
+  if (p == PATH_FP8_MXFP4) {
+    if (M > 0 && (!x_perm_sf || !sf_gate || !sf_up || !h_sf)) return MOE_EINVAL;
+    return launch_ffn_gate_up_fp8(x_perm, x_perm_sf, cu_seqlens, M, E, H, Hp, w_gate, sf_gate, w_up,
+                                  sf_up, h, h_sf, stream);
+  }
   if (p == PATH_F32) return launch_ffn_gate_up_f32(x_perm, cu_seqlens, M, E, H, Hp, w_gate, w_up, h, stream);
   return launch_ffn_gate_up_bf16(x_perm, cu_seqlens, M, E, H, Hp, w_gate, w_up, h, stream);
 }
@@ -189,8 +198,10 @@ moe_status_t moe_ffn_down(const void* h, const float* h_sf, moe_dtype_t h_dtype,
   if (st != MOE_OK) return st;
   if (!cu_seqlens) return MOE_EINVAL;
   if (M > 0 && (!h || !w_down || !y_rows)) return MOE_EINVAL;
-  (void)h_sf;
-  (void)sf_down;
+  if (p == PATH_FP8_MXFP4) {
+    if (M > 0 && (!h_sf || !sf_down)) return MOE_EINVAL;
+    return launch_ffn_down_fp8(h, h_sf, cu_seqlens, M, E, H, Hp, w_down, sf_down, y_rows, stream);
+  }
   if (p == PATH_F32) return launch_ffn_down_f32(h, cu_seqlens, M, E, H, Hp, w_down, y_rows, stream);
   return launch_ffn_down_bf16(h, cu_seqlens, M, E, H, Hp, w_down, y_rows, stream);
 }

@@ -265,3 +265,49 @@ def test_c3_full_size_sampled():
 def test_c4_full_size_sampled(maxvio):
     say(f"c4 bf16 E=384 maxvio={maxvio}, full size")
     sampled_check(gen.config("c4", device=DEV, maxvio=maxvio))
+
+
+# ----------------------------------------------------------------------------- fp8 x MXFP4
+
+FP8_SMALL = [
+    dict(T=300, H=512, Hp=256, E=12, K=3, routing="skew", beta=0.5),
+    dict(T=600, H=256, Hp=384, E=24, K=4, routing="normal"),
+    dict(T=130, H=768, Hp=128, E=5, K=2, routing="balanced"),
+]
+
+
+@pytest.mark.parametrize("spec", FP8_SMALL, ids=lambda s: "T{T}_H{H}_Hp{Hp}_E{E}_K{K}_{routing}".format(**s))
+def test_small_fp8_mxfp4_layer(spec):
+    say(f"fp8 x mxfp4 small {spec}")
+    w = gen.make(**spec, act="fp8", wgt="mxfp4", out="bf16", cid=57, device=DEV)
+    r, ref = full_check(w)
+    # the requantised h: dequantised values within one e4m3 step, scales mostly identical
+    from _oracle_run import weight_fn, x_f64
+    x = x_f64(w)
+    fn = weight_fn(w)
+    cu = ref["cu_seqlens"]
+    tok = ref["row_src"] // w.K
+    h_gpu = O.decode_fp8_rows(host(r["h"]), host(r["h_sf"]))
+    sf_gpu = host(r["h_sf"]).astype(np.float64)
+    worst, same, n = 0.0, 0, 0
+    for e in range(w.E):
+        lo, hi = int(cu[e]), int(cu[e + 1])
+        if hi == lo:
+            continue
+        wg, wu, _ = fn(e)
+        xr = x[tok[lo:hi]]
+        g, u = xr @ wg, xr @ wu
+        h = g / (1 + np.exp(-g)) * u
+        hq, s = O.requant_fp8_1x128(h)
+        worst = max(worst, float(np.abs(h_gpu[lo:hi] - hq).max() / max(np.abs(h).max(), 1e-30)))
+        same += int((sf_gpu[lo:hi] == s).sum())
+        n += s.size
+    print(f"  h rel err {worst:.3e}, identical block scales {same}/{n}", flush=True)
+    assert worst <= 6e-2
+    assert same >= 0.99 * n
+
+
+@pytest.mark.slow
+def test_c5_full_size_sampled():
+    say("c5 fp8 x mxfp4 E=384 maxvio=1, full size")
+    sampled_check(gen.config("c5", device=DEV))
