@@ -126,9 +126,9 @@ def main():
     pos = torch.empty((T, K), **i32)
     row_src = torch.empty(M, **i32)
     x_perm = torch.empty((M, H), dtype=TD[w.act], device=dev)
-    x_perm_sf = torch.empty((M, H // 128), **f32) if w.act == "fp8" else None
+    x_perm_sf = torch.empty((H // 128, M), **f32) if w.act == "fp8" else None
     h = torch.empty((M, Hp), dtype=TD[hf], device=dev)
-    h_sf = torch.empty((M, Hp // 128), **f32) if w.act == "fp8" else None
+    h_sf = torch.empty((Hp // 128, M), **f32) if w.act == "fp8" else None
     y = torch.empty((M, H), dtype=TD[yf], device=dev)
     out = torch.empty((T, H), dtype=TD[w.out], device=dev)
     nws = moe.moe_permute_workspace_bytes(T, E, K)

@@ -67,7 +67,9 @@ typedef enum {
  *  MOE_MXFP4     OCP MX e2m1 codes, two per byte, with one e8m0 scale byte per 32 elements
  *                along the reduction dimension: value = e2m1(code) * 2^(scale - 127).
  *                Stored reduction-contiguous: byte j of output column n holds reduction
- *                index 2j in its low nibble and 2j+1 in its high nibble. */
+ *                index 2j in its low nibble and 2j+1 in its high nibble. Scale bytes are
+ *                stored block-major, [K/32][N] per expert, so the scales one K step needs
+ *                for consecutive columns are contiguous. */
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_dtype_t;
 
 /* How the K expert results of a token are summed.
@@ -110,7 +112,8 @@ MOE_API size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t K);
  *  row_src    [T*K] int32 out: flat index t*K + k of the copy stored in each row.
  *  row_w      [T*K] fp32 out (or NULL): topk_w of the copy stored in each row.
  *  x_perm     [T*K, H] out, format `act`: x_perm[pos[t,k]] = x[t], bit for bit.
- *  x_perm_sf  [T*K, H/128] fp32 out when act = FP8_E4M3.
+ *  x_perm_sf  [H/128, T*K] fp32 out when act = FP8_E4M3, block-major: x_perm_sf[b][r] is the
+ *             scale of block b of row r (the transpose of x_sf's layout).
  * Row order is a stable counting sort: the rows of expert e hold its copies in ascending
  * t*K + k. The result is deterministic. Limits: E <= 1024, K <= 32. */
 MOE_API moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t act,
@@ -125,11 +128,12 @@ MOE_API moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t a
  *     g = x_perm[r] . Wg[e],  u = x_perm[r] . Wu[e],  h[r] = silu(g) * u,
  * silu(z) = z / (1 + exp(-z)), accumulated in fp32.
  *  Formats: act F32 + wgt F32 -> h F32; act BF16 + wgt BF16 -> h BF16;
- *           act FP8_E4M3 + wgt MXFP4 -> h FP8_E4M3 with h_sf [M, Hp/128] fp32 power-of-two
+ *           act FP8_E4M3 + wgt MXFP4 -> h FP8_E4M3 with h_sf [Hp/128, M] (block-major) fp32
+ *           power-of-two
  *           scales (s = smallest power of two with 448*s >= block amax; code = e4m3fn
  *           round-to-nearest-even of h/s).
  *  F32/BF16 weights: w_gate, w_up [E, H, Hp] (g = x . W). MXFP4 weights: bytes [E, Hp, H/2]
- *  with sf_gate, sf_up [E, Hp, H/32].
+ *  with sf_gate, sf_up [E, H/32, Hp]; x_perm_sf [H/128, M].
  * One kernel launch; the tile schedule over the variable-size groups is derived on the device
  * from cu_seqlens. Needs H % 64 == 0 and Hp % 128 == 0 (BF16), H % 128 == 0 and
  * Hp % 128 == 0 (FP8/MXFP4); F32 has no multiple requirement. */
@@ -142,7 +146,7 @@ MOE_API moe_status_t moe_ffn_gate_up(const void* x_perm, const float* x_perm_sf,
 /* Second half of the grouped expert FFN: y_rows[r] = h[r] . Wd[e] for the rows of expert e.
  *  h_dtype F32 (wgt F32, out F32), BF16 (wgt BF16, out BF16) or FP8_E4M3 with h_sf
  *  (wgt MXFP4, out BF16). F32/BF16 w_down [E, Hp, H]; MXFP4 bytes [E, H, Hp/2] with
- *  sf_down [E, H, Hp/32]. Needs H % 256 == 0 and Hp % 64 == 0 (BF16), H % 128 == 0 and
+ *  sf_down [E, Hp/32, H]; h_sf [Hp/128, M]. Needs H % 256 == 0 and Hp % 64 == 0 (BF16), H % 128 == 0 and
  *  Hp % 128 == 0 (FP8/MXFP4). One kernel launch. */
 MOE_API moe_status_t moe_ffn_down(const void* h, const float* h_sf, moe_dtype_t h_dtype,
                           const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,

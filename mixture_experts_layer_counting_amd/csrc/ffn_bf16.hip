@@ -118,7 +118,8 @@ __device__ __forceinline__ void wait_barrier_dyn(int n) {
 template <bool GATED, int BN, int BK, int NS>
 __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
     const uint16_t* __restrict__ A, const int* __restrict__ cu, int M, int E, int Kd, int N,
-    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C) {
+    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C,
+    int n_fastest) {
   using CF = FbCfg<GATED, BN, BK, NS>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int* tstart = reinterpret_cast<int*>(smem + NS * CF::STAGE);
@@ -184,8 +185,10 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
     const int gbeg = cu[e];
     const int rows_e = cu[e + 1] - gbeg;
     const int mte = (rows_e + FB_BM - 1) / FB_BM;
-    const int ntile = lt / mte;
-    const int mtile = lt - ntile * mte;
+    // tile order inside an expert: m fastest (a weight panel's m-tiles are neighbours) or
+    // n fastest (neighbours cover whole weight rows, one m-tile at a time)
+    const int ntile = n_fastest ? lt % ntn : lt / mte;
+    const int mtile = n_fastest ? lt / ntn : lt - ntile * mte;
     const int row0 = gbeg + mtile * FB_BM;
     const int rows_valid = min(FB_BM, rows_e - mtile * FB_BM);
     const int n0 = ntile * BN;
@@ -270,6 +273,16 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
   }
 }
 
+// Tile order inside an expert group. MOE_FFN_ORDER = "m" | "n" overrides the default.
+static int tile_order_n_fastest(int M, int E) {
+  const char* p = std::getenv("MOE_FFN_ORDER");
+  if (p && p[0] == 'n') return 1;
+  if (p && p[0] == 'm') return 0;
+  (void)M;
+  (void)E;
+  return 0;
+}
+
 template <bool GATED, int BN, int BK, int NS>
 static moe_status_t launch_fb(const uint16_t* A, const int* cu, int M, int E, int Kd, int N,
                               const uint16_t* B0, const uint16_t* B1, uint16_t* C, hipStream_t s) {
@@ -282,7 +295,8 @@ static moe_status_t launch_fb(const uint16_t* A, const int* cu, int M, int E, in
     attr_set = true;
   }
   const int grid = device_cu_count();
-  ffn_bf16_kernel<GATED, BN, BK, NS><<<grid, FB_THREADS, CF::LDS_BYTES, s>>>(A, cu, M, E, Kd, N, B0, B1, C);
+  ffn_bf16_kernel<GATED, BN, BK, NS><<<grid, FB_THREADS, CF::LDS_BYTES, s>>>(A, cu, M, E, Kd, N, B0, B1, C,
+                                                                         tile_order_n_fastest(M, E));
   return launch_status();
 }
 

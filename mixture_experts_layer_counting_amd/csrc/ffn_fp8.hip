@@ -20,8 +20,9 @@
 // bf16 kernels. Block tile 256 rows x BN columns per weight matrix, K step 128. Activations are
 // staged [256][128 B] (16-byte chunk ^ (row/2 mod 8)); weights, stored reduction-contiguous
 // [N][K/2], are staged [BN][64 B] (chunk ^ (col/4 mod 4)). Both fragment reads are
-// ds_read_b128 without transposes. Per-stage scales are loaded straight into registers one
-// stage ahead.
+// ds_read_b128 without transposes. Scales are stored block-major (activations [K/128][M],
+// weights [E][K/32][N]) so each stage's scale loads are contiguous per wave; they go straight
+// into registers one stage ahead.
 #include "moe_common.h"
 #include "tile_sched.h"
 
@@ -122,7 +123,6 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
   const int nk = Kd / F8_BK;
   const int kbytes = Kd / 2;     // bytes per weight column
   const int ksf_b = Kd / 32;     // weight scale bytes per column
-  const int ksf_a = Kd / 128;    // activation scales per row
   const int G = gridDim.x;
   const int slot = xcd_slot(blockIdx.x, G);
   const uint32_t smem_lds = (uint32_t)(uintptr_t)(const MOE_LDS void*)smem;
@@ -181,19 +181,17 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     const uint32_t b_rem = (uint32_t)((size_t)(N - n0) * kbytes);
     const i32x4_t rB0 = f8_rsrc(B0 + wbase, b_rem);
     const i32x4_t rB1 = GATED ? f8_rsrc(B1 + wbase, b_rem) : rB0;
-    // scale rows of this lane: activations (per mt) and weight columns (per fragment)
+    // Scales are block-major: activations [Kd/128][M], weights [E][Kd/32][N]. For one stage a
+    // wave reads 32 consecutive rows (or columns) per load.
     const float* asf_row[CF::MT];
 #pragma unroll
-    for (int mt = 0; mt < CF::MT; ++mt) {
-      const int r = min(row0 + ar + mt * 32, M - 1);
-      asf_row[mt] = A_sf + (size_t)r * ksf_a;
-    }
+    for (int mt = 0; mt < CF::MT; ++mt) asf_row[mt] = A_sf + min(row0 + ar + mt * 32, M - 1);
     const uint8_t* bsf_col[CF::NF];
 #pragma unroll
     for (int f = 0; f < CF::NF; ++f) {
       const int nb = f / CF::NT, nt = f % CF::NT;
       const uint8_t* base = (GATED && nb) ? B1_sf : B0_sf;
-      bsf_col[f] = base + ((size_t)e * N + n0 + wn * CF::WN + nt * 32 + (lane & 31)) * ksf_b;
+      bsf_col[f] = base + (size_t)e * ksf_b * N + n0 + wn * CF::WN + nt * 32 + (lane & 31);
     }
 
     auto issue = [&](int kt) {
@@ -209,12 +207,18 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     };
     // per-stage scales: one activation exponent per mt (its 1x128 block), one dword of four
     // weight exponents per fragment (k-blocks 4kt..4kt+3 of the lane's column)
-    int sa_next[CF::MT], sb_next[CF::NF];
+    // raw values only: converting here would make the compiler wait for these loads (and, with
+    // in-order completion, for the DMA issued just before them) before the stage's MFMAs
+    float sa_next[CF::MT];
+    int sb_next[CF::NF][CF::KK];
     auto load_scales = [&](int kt) {
 #pragma unroll
-      for (int mt = 0; mt < CF::MT; ++mt) sa_next[mt] = pow2_to_e8m0(asf_row[mt][kt]);
+      for (int mt = 0; mt < CF::MT; ++mt) sa_next[mt] = asf_row[mt][(size_t)kt * M];
+      // weight k-block of MFMA step kk for this lane: 4kt + 2kk + G
 #pragma unroll
-      for (int f = 0; f < CF::NF; ++f) sb_next[f] = *reinterpret_cast<const int*>(bsf_col[f] + 4 * kt);
+      for (int f = 0; f < CF::NF; ++f)
+#pragma unroll
+        for (int kk = 0; kk < CF::KK; ++kk) sb_next[f][kk] = bsf_col[f][(size_t)(4 * kt + 2 * kk + g2) * N];
     };
 
     f32x16_t acc[CF::NB][CF::MT][CF::NT];
@@ -235,17 +239,19 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
       // Take this stage's scales now: their loads are complete (the barrier waited for every
       // outstanding vector-memory op), and consuming them here keeps the compiler's own wait
       // for them from landing after the next stage's loads are issued.
-      int sa[CF::MT], sb[CF::NF];
+      int sa[CF::MT], sb[CF::NF][CF::KK];
 #pragma unroll
       for (int mt = 0; mt < CF::MT; ++mt) {
-        sa[mt] = sa_next[mt];
-        asm volatile("" : : "v"(sa[mt]));
+        asm volatile("" : : "v"(sa_next[mt]));
+        sa[mt] = pow2_to_e8m0(sa_next[mt]);
       }
 #pragma unroll
-      for (int f = 0; f < CF::NF; ++f) {
-        sb[f] = sb_next[f];
-        asm volatile("" : : "v"(sb[f]));
-      }
+      for (int f = 0; f < CF::NF; ++f)
+#pragma unroll
+        for (int kk = 0; kk < CF::KK; ++kk) {
+          sb[f][kk] = sb_next[f][kk];
+          asm volatile("" : : "v"(sb[f][kk]));
+        }
       if (kt + 1 < nk) {
         issue(kt + 1);
         load_scales(kt + 1);
@@ -268,8 +274,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
             const i32x4_t bq = *reinterpret_cast<const i32x4_t*>(sb_l + nb * CF::B_BYTES + b_off[nt][kk]);
             const i32x4_t z = {0, 0, 0, 0};
             const i32x8_t bfr = __builtin_shufflevector(bq, z, 0, 1, 2, 3, 4, 5, 6, 7);
-            // weight scale byte for k-block 4kt + 2kk + G of this column
-            const int sbw = (sb[nb * CF::NT + nt] >> (8 * (2 * kk + g2))) & 0xff;
+            const int sbw = sb[nb * CF::NT + nt][kk];
 #pragma unroll
             for (int mt = 0; mt < CF::MT; ++mt)
               acc[nb][mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
               const int col = n0 + wn * CF::WN + nt * 32 + (lane & 31);
               C8[ro * N + col] = (uint8_t)f32_to_e4m3(hv[mt][nt][i] * inv);
             }
-            if (wn == 0 && (lane & 31) == 0) C8_sf[ro * (N / 128) + n0 / 128] = s;
+            if (wn == 0 && (lane & 31) == 0) C8_sf[(size_t)(n0 / 128) * M + ro] = s;  // [N/128][M]
           }
         }
     } else {

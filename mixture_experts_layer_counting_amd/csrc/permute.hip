@@ -239,7 +239,7 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
       const float v = x_sf[(size_t)(tb0 + j) * sf_per_row + c];
       for (int k = 0; k < K; ++k) {
         const int p = lpos[j * K + k];
-        if (p >= 0) x_perm_sf[(size_t)p * sf_per_row + c] = v;
+        if (p >= 0) x_perm_sf[(size_t)c * T * K + p] = v;  // block-major [H/128][T*K]
       }
     }
   }

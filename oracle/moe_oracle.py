@@ -81,14 +81,14 @@ def decode_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """One expert's MXFP4 matrix stored reduction-contiguous -> logical float64 W[k, n].
 
     ``packed`` [N, Kred/2]: byte j of row n holds k=2j (low nibble), k=2j+1 (high).
-    ``scales`` [N, Kred/32]: byte b scales k in [32b, 32b+32).
+    ``scales`` [Kred/32, N]: byte [b][n] scales k in [32b, 32b+32) of column n.
     """
     packed = np.asarray(packed, dtype=np.uint8)
     N, half = packed.shape
     codes = np.empty((N, 2 * half), dtype=np.uint8)
     codes[:, 0::2] = packed & 0xF
     codes[:, 1::2] = packed >> 4
-    vals = decode_e2m1(codes) * np.repeat(decode_e8m0(scales), 32, axis=1)
+    vals = decode_e2m1(codes) * np.repeat(decode_e8m0(np.asarray(scales).T), 32, axis=1)
     return vals.T
 
 

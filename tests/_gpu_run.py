@@ -35,14 +35,14 @@ def run_steps(w, with_row_w=True):
     r["row_src"] = torch.empty(M, **i32)
     r["row_w"] = torch.empty(M, **f32) if with_row_w else None
     r["x_perm"] = torch.empty((M, H), dtype=TORCH_DT[w.act], device=dev)
-    r["x_perm_sf"] = torch.empty((M, H // 128), **f32) if w.act == "fp8" else None
+    r["x_perm_sf"] = torch.empty((H // 128, M), **f32) if w.act == "fp8" else None
     nws = moe.moe_permute_workspace_bytes(T, E, K)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     moe.moe_permute(w.x, w.x_sf, DT[w.act], r["topk_idx"], r["topk_w"], T, H, E, K, r["counts"],
                     r["cu_seqlens"], r["pos"], r["row_src"], r["row_w"], r["x_perm"], r["x_perm_sf"],
                     ws, nws)
     r["h"] = torch.empty((M, Hp), dtype=TORCH_DT[h_fmt(w)], device=dev)
-    r["h_sf"] = torch.empty((M, Hp // 128), **f32) if w.act == "fp8" else None
+    r["h_sf"] = torch.empty((Hp // 128, M), **f32) if w.act == "fp8" else None
     moe.moe_ffn_gate_up(r["x_perm"], r["x_perm_sf"], DT[w.act], r["cu_seqlens"], M, E, H, Hp,
                         w.w_gate, w.w_up, w.sf_gate, w.sf_up, DT[w.wgt], r["h"], r["h_sf"])
     r["y_rows"] = torch.empty((M, H), dtype=TORCH_DT[y_fmt(w)], device=dev)

@@ -48,7 +48,7 @@ def check_x_perm(w, r, ref):
     xb = host(w.x)
     assert np.array_equal(host(r["x_perm"]), xb[ref["row_src"] // w.K])
     if w.x_sf is not None:
-        assert np.array_equal(host(r["x_perm_sf"]), host(w.x_sf)[ref["row_src"] // w.K])
+        assert np.array_equal(host(r["x_perm_sf"]), host(w.x_sf)[ref["row_src"] // w.K].T)
 
 
 def full_check(w, tol=None):
@@ -136,7 +136,7 @@ def test_permute_max_experts(act):
     row_src = torch.empty(M, dtype=torch.int32, device=DEV)
     row_w = torch.empty(M, dtype=torch.float32, device=DEV)
     xp = torch.empty((M, H), dtype=x.dtype, device=DEV)
-    xsf = torch.empty((M, H // 128), dtype=torch.float32, device=DEV) if act == "fp8" else None
+    xsf = torch.empty((H // 128, M), dtype=torch.float32, device=DEV) if act == "fp8" else None
     n = moe.moe_permute_workspace_bytes(T, E, K)
     ws = torch.empty(n, dtype=torch.uint8, device=DEV)
     dt = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "fp8": moe.MOE_FP8_E4M3}[act]
@@ -148,7 +148,7 @@ def test_permute_max_experts(act):
     assert np.array_equal(host(row_w), host(tw).ravel()[rs_ref])
     assert np.array_equal(host(xp), host(x)[rs_ref // K])
     if act == "fp8":
-        assert np.array_equal(host(xsf), host(x_sf)[rs_ref // K])
+        assert np.array_equal(host(xsf), host(x_sf)[rs_ref // K].T)
 
 
 def test_empty_batch():
@@ -287,8 +287,8 @@ def test_small_fp8_mxfp4_layer(spec):
     fn = weight_fn(w)
     cu = ref["cu_seqlens"]
     tok = ref["row_src"] // w.K
-    h_gpu = O.decode_fp8_rows(host(r["h"]), host(r["h_sf"]))
-    sf_gpu = host(r["h_sf"]).astype(np.float64)
+    h_gpu = O.decode_fp8_rows(host(r["h"]), host(r["h_sf"]).T)
+    sf_gpu = host(r["h_sf"]).T.astype(np.float64)
     worst, same, n = 0.0, 0, 0
     for e in range(w.E):
         lo, hi = int(cu[e]), int(cu[e + 1])

@@ -249,7 +249,7 @@ def test_mxfp4_decode_layout():
     Kred, N = 64, 3
     rng = np.random.default_rng(9)
     codes = rng.integers(0, 16, size=(Kred, N))
-    sbytes = np.array([[120, 130], [127, 100], [140, 127]], np.uint8)   # [N, Kred/32]
+    sbytes = np.array([[120, 127, 140], [130, 100, 127]], np.uint8)   # [Kred/32, N]
     packed = np.zeros((N, Kred // 2), np.uint8)
     for n in range(N):
         for k in range(Kred):
@@ -259,5 +259,5 @@ def test_mxfp4_decode_layout():
     for k in range(Kred):
         for n in range(N):
             c = int(codes[k, n])
-            v = (-1 if c & 8 else 1) * table[c & 7] * 2.0 ** (int(sbytes[n, k // 32]) - 127)
+            v = (-1 if c & 8 else 1) * table[c & 7] * 2.0 ** (int(sbytes[k // 32, n]) - 127)
             assert W[k, n] == v

@@ -62,7 +62,7 @@ def test_mxfp4_generator_exact_on_grid_and_nearest_off_grid():
     w = torch.from_numpy(rng.standard_normal((Kred, N)).astype(np.float32))
     packed, sb = _to_mxfp4(w)
     dec = O.decode_mxfp4(packed.numpy(), sb.numpy())
-    X = np.repeat(np.exp2(sb.numpy().astype(np.float64) - 127).T, 32, axis=0)
+    X = np.repeat(np.exp2(sb.numpy().astype(np.float64) - 127), 32, axis=0)
     v = w.numpy().astype(np.float64) / X
     grid = np.concatenate([-table[::-1], table])
     nearest = np.abs(np.clip(v, -6, 6)[..., None] - grid).min(axis=-1)

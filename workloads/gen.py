@@ -27,9 +27,9 @@ Storage layouts (row-major, dense):
 * fp32 / bf16 weights: ``w_gate``, ``w_up`` [E, H, Hp] and ``w_down`` [E, Hp, H]:
   logical W[e][k][n] with the reduction index k first (g = x.Wg, y = h.Wd).
 * MXFP4 weights are stored reduction-contiguous: gate/up bytes [E, Hp, H/2] with
-  scales [E, Hp, H/32]; down bytes [E, H, Hp/2] with scales [E, H, Hp/32]. Byte j of
+  scales [E, H/32, Hp]; down bytes [E, H, Hp/2] with scales [E, Hp/32, H]. Byte j of
   row n holds logical k = 2j in its low nibble and k = 2j+1 in its high nibble; scale
-  byte b covers k in [32b, 32b+32) and means 2^(b-127).
+  [b][n] covers k in [32b, 32b+32) of column n and means 2^(byte-127).
 """
 from __future__ import annotations
 
@@ -132,7 +132,7 @@ def _to_e4m3_blocked(x32: torch.Tensor):
 
 
 def _to_mxfp4(w_kn: torch.Tensor):
-    """Logical fp32 W [Kred, N] -> (packed bytes [N, Kred/2], e8m0 scales [N, Kred/32]).
+    """Logical fp32 W [Kred, N] -> (packed bytes [N, Kred/2], e8m0 scales [Kred/32, N]).
 
     OCP MX: per 32 reduction elements X = 2^(floor(log2 amax) - 2); element codes are
     e2m1 round-to-nearest-even of w/X, saturating at 6; amax = 0 -> scale byte 0.
@@ -153,7 +153,7 @@ def _to_mxfp4(w_kn: torch.Tensor):
     code = mag | ((v < 0).to(torch.uint8) << 3)
     code = code.reshape(N, Kred // 2, 2)
     packed = code[:, :, 0] | (code[:, :, 1] << 4)
-    return packed.contiguous(), sbyte.to(torch.uint8).contiguous()
+    return packed.contiguous(), sbyte.to(torch.uint8).t().contiguous()
 
 
 # ----------------------------------------------------------------------------- routing inputs
@@ -195,9 +195,9 @@ def _draw_weights(device, seed, cid, E, H, Hp, wgt):
         wg = torch.empty((E, Hp, H // 2), dtype=torch.uint8, device=device)
         wu = torch.empty((E, Hp, H // 2), dtype=torch.uint8, device=device)
         wd = torch.empty((E, H, Hp // 2), dtype=torch.uint8, device=device)
-        sg = torch.empty((E, Hp, H // 32), dtype=torch.uint8, device=device)
-        su = torch.empty((E, Hp, H // 32), dtype=torch.uint8, device=device)
-        sd = torch.empty((E, H, Hp // 32), dtype=torch.uint8, device=device)
+        sg = torch.empty((E, H // 32, Hp), dtype=torch.uint8, device=device)
+        su = torch.empty((E, H // 32, Hp), dtype=torch.uint8, device=device)
+        sd = torch.empty((E, Hp // 32, H), dtype=torch.uint8, device=device)
         for e in range(E):
             for tid, dw, ds, shp, std in ((2, wg, sg, (H, Hp), std_gu), (3, wu, su, (H, Hp), std_gu),
                                           (4, wd, sd, (Hp, H), std_d)):
