@@ -60,11 +60,18 @@ def copy_calibration(steps):
     n = 1 << 30
     src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
     dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
     for _ in range(steps):
         dst.copy_(src)
+    b.record()
     torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
     print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n,
-                      "launches": steps}), flush=True)
+                      "launches": steps + 1, "copy_ms": ms, "copy_gbs": 2 * n / ms / 1e6}), flush=True)
 
 
 def source_hash(*names):

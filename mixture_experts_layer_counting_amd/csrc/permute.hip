@@ -6,18 +6,22 @@
 // combine needs to restore token order. MoonEP "dispatch fwd" returns the same things for
 // one rank (tokens_per_expert, cu_seqlens, expert-grouped hidden rows and their weights).
 //
-// Row order inside an expert is ascending flat index t*K + k, i.e. a stable sort. Three
-// launches, none of them with atomics on global memory:
+// Row order inside an expert is ascending flat index t*K + k, i.e. a stable sort. No
+// atomics on global memory:
 //  1. hist:    one block per chunk of PERM_CHUNK tokens counts its copies per expert in
 //              LDS and writes them expert-major: hist[e][chunk].
 //  2. scan:    one wave per expert turns hist[e][*] into exclusive chunk offsets and the
 //              expert total (counts[e]).
 //  3. scatter: one block per PERM_TB tokens. It rebuilds cu_seqlens from counts in LDS,
 //              counts the copies of earlier tokens of its chunk, ranks its own copies
-//              with wave ballots (match by key bits + mbcnt) in flat order, writes pos /
-//              row_src / row_w, then copies each token row once from x to its K rows of
-//              x_perm with 16-byte loads and stores (HBM-bound part).
+//              with wave ballots (match by key bits + mbcnt) in flat order, and writes pos /
+//              row_src / row_w.
+//  4. copy:    one block per token copies its row once from x to its K rows of x_perm
+//              with 16-byte loads and stores (the HBM-bound part).
+//  (fp8 only) sf: gathers the 1x128 block scales into the block-major x_perm_sf.
 #include "moe_common.h"
+
+#include <algorithm>
 
 namespace moe {
 
@@ -105,20 +109,15 @@ struct VecT<1> {
   typedef unsigned char type;
 };
 
-template <int VB>
 __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
-    const unsigned char* __restrict__ x, const float* __restrict__ x_sf,
     const int* __restrict__ topk_idx, const float* __restrict__ topk_w, int T, int E, int K,
     int nch, const int* __restrict__ counts, const int* __restrict__ choff,
     int* __restrict__ cu_seqlens, int* __restrict__ pos, int* __restrict__ row_src,
-    float* __restrict__ row_w, unsigned char* __restrict__ x_perm, float* __restrict__ x_perm_sf,
-    int row_bytes, int sf_per_row, int key_bits, int* __restrict__ err) {
-  typedef typename VecT<VB>::type V;
+    float* __restrict__ row_w, int key_bits, int* __restrict__ err) {
   __shared__ int cu[PERM_MAX_E + 1];
   __shared__ int pre[PERM_MAX_E];
   __shared__ int wh[PERM_WAVES][PERM_MAX_E];
   __shared__ int wsum[PERM_WAVES];
-  __shared__ int lpos[PERM_TB * 32];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -203,7 +202,6 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
         }
       }
       pos[(size_t)tb0 * K + i] = p;
-      lpos[i] = p;
     }
     __syncthreads();
     // fold this group's counts into pre[] and clear wh for the next group
@@ -220,28 +218,42 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
     }
   }
 
-  // 4. copy each token row once to its K rows
+}
+
+// Copy each token row once from x to its K rows of x_perm (16-byte, 4-byte or 1-byte
+// accesses). One block per token keeps every CU busy on this HBM-bound copy.
+template <int VB>
+__global__ __launch_bounds__(256) void permute_copy_kernel(const unsigned char* __restrict__ x,
+                                                           const int* __restrict__ pos, int K,
+                                                           unsigned char* __restrict__ x_perm,
+                                                           int row_bytes) {
+  typedef typename VecT<VB>::type V;
+  __shared__ int p[32];
+  const int t = blockIdx.x;
+  if (threadIdx.x < K) p[threadIdx.x] = pos[(size_t)t * K + threadIdx.x];
+  __syncthreads();
   const int nv = row_bytes / VB;
-  const int ntok = tb1 - tb0;
-  for (int q = tid; q < ntok * nv; q += PERM_THREADS) {
-    const int j = q / nv;
-    const int c = q - j * nv;
-    const V v = reinterpret_cast<const V*>(x + (size_t)(tb0 + j) * row_bytes)[c];
-    for (int k = 0; k < K; ++k) {
-      const int p = lpos[j * K + k];
-      if (p >= 0) reinterpret_cast<V*>(x_perm + (size_t)p * row_bytes)[c] = v;
-    }
+  const V* src = reinterpret_cast<const V*>(x + (size_t)t * row_bytes);
+  for (int c = threadIdx.x; c < nv; c += blockDim.x) {
+    const V v = src[c];
+    for (int k = 0; k < K; ++k)
+      if (p[k] >= 0) reinterpret_cast<V*>(x_perm + (size_t)p[k] * row_bytes)[c] = v;
   }
-  if (x_sf) {
-    for (int q = tid; q < ntok * sf_per_row; q += PERM_THREADS) {
-      const int j = q / sf_per_row;
-      const int c = q - j * sf_per_row;
-      const float v = x_sf[(size_t)(tb0 + j) * sf_per_row + c];
-      for (int k = 0; k < K; ++k) {
-        const int p = lpos[j * K + k];
-        if (p >= 0) x_perm_sf[(size_t)c * T * K + p] = v;  // block-major [H/128][T*K]
-      }
-    }
+}
+
+// Block scales of the permuted rows, block-major [H/128][M]: consecutive threads write
+// consecutive rows (coalesced); the gathered reads of x_sf [T][H/128] stay in L2.
+__global__ __launch_bounds__(256) void permute_sf_kernel(const float* __restrict__ x_sf,
+                                                         const int* __restrict__ row_src,
+                                                         const int* __restrict__ cu_seqlens, int E,
+                                                         int K, int M, int nsf,
+                                                         float* __restrict__ x_perm_sf) {
+  const int rows = cu_seqlens[E];  // rows actually holding a copy
+  const size_t n = (size_t)nsf * M;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
+    const int c = (int)(i / M);
+    const int p = (int)(i - (size_t)c * M);
+    if (p < rows) x_perm_sf[i] = x_sf[(size_t)(row_src[p] / K) * nsf + c];
   }
 }
 
@@ -277,20 +289,23 @@ moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes,
   const int nblk = T > 0 ? (T + PERM_TB - 1) / PERM_TB : 1;
   const unsigned char* xb = static_cast<const unsigned char*>(x);
   unsigned char* xp = static_cast<unsigned char*>(x_perm);
-  const bool a16 = (row_bytes % 16 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)x_perm % 16 == 0);
-  const bool a4 = (row_bytes % 4 == 0) && ((uintptr_t)x % 4 == 0) && ((uintptr_t)x_perm % 4 == 0);
-  if (a16)
-    permute_scatter_kernel<16><<<nblk, PERM_THREADS, 0, s>>>(
-        xb, x_sf, topk_idx, topk_w, T, E, K, nch, counts, hist, cu_seqlens, pos, row_src, row_w,
-        xp, x_perm_sf, row_bytes, sf_per_row, key_bits, err);
-  else if (a4)
-    permute_scatter_kernel<4><<<nblk, PERM_THREADS, 0, s>>>(
-        xb, x_sf, topk_idx, topk_w, T, E, K, nch, counts, hist, cu_seqlens, pos, row_src, row_w,
-        xp, x_perm_sf, row_bytes, sf_per_row, key_bits, err);
-  else
-    permute_scatter_kernel<1><<<nblk, PERM_THREADS, 0, s>>>(
-        xb, x_sf, topk_idx, topk_w, T, E, K, nch, counts, hist, cu_seqlens, pos, row_src, row_w,
-        xp, x_perm_sf, row_bytes, sf_per_row, key_bits, err);
+  permute_scatter_kernel<<<nblk, PERM_THREADS, 0, s>>>(topk_idx, topk_w, T, E, K, nch, counts, hist,
+                                                       cu_seqlens, pos, row_src, row_w, key_bits, err);
+  if (T > 0) {
+    const bool a16 = (row_bytes % 16 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)x_perm % 16 == 0);
+    const bool a4 = (row_bytes % 4 == 0) && ((uintptr_t)x % 4 == 0) && ((uintptr_t)x_perm % 4 == 0);
+    if (a16)
+      permute_copy_kernel<16><<<T, 256, 0, s>>>(xb, pos, K, xp, row_bytes);
+    else if (a4)
+      permute_copy_kernel<4><<<T, 256, 0, s>>>(xb, pos, K, xp, row_bytes);
+    else
+      permute_copy_kernel<1><<<T, 256, 0, s>>>(xb, pos, K, xp, row_bytes);
+  }
+  if (x_sf && T > 0) {
+    const size_t n = (size_t)sf_per_row * T * K;
+    const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
+    permute_sf_kernel<<<blocks, 256, 0, s>>>(x_sf, row_src, cu_seqlens, E, K, T * K, sf_per_row, x_perm_sf);
+  }
   return launch_status();
 }
 
