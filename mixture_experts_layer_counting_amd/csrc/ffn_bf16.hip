@@ -16,7 +16,10 @@
 //    L2.
 //  * Block tile BM=256 rows x BN columns (per weight matrix), K step 64, two LDS stages.
 //    8 waves as 4 (rows) x 2 (columns), each wave 64 x BN/2 with MFMA 32x32x16 bf16 and
-//    fp32 accumulators (128 per lane).
+//    fp32 accumulators (128 per lane). A wave's two 32-row blocks are rows wm*32 + [0,32)
+//    and 128 + wm*32 + [0,32): with this interleave the padded rows of an expert's last tile
+//    fall evenly on the four SIMDs (waves w and w+4 share one), and a wave skips the MFMAs
+//    and fragment reads of any 32-row block that lies wholly past the group's rows.
 //  * A (activations, reduction-contiguous) is staged as [256][64] with the 16-byte chunk
 //    index XOR-swizzled by (row/2) mod 8 so ds_read_b128 of 16 consecutive rows is free of
 //    bank conflicts. B (weights [K][N], N contiguous) is staged in its global layout and
@@ -24,13 +27,14 @@
 //    segments are XOR-swizzled by 2*(row mod 4) so the four rows a transpose read touches
 //    land on distinct banks.
 //  * Global loads for step k+1 are issued before the MFMAs of step k; one barrier per step.
-//  * Rows past the expert's group are computed on whatever rows follow (clamped to M-1) and
-//    never stored.
+//  * The A descriptor's range ends at the group's last row of the tile, so rows past it read
+//    as zeros without memory traffic; they are never stored.
 #include "moe_common.h"
 #include "tile_sched.h"
 
 #include <cstdlib>
 #include <cstring>
+#include <type_traits>
 
 namespace moe {
 
@@ -165,8 +169,10 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
     b_mat[i] = nb;
   }
 
-  // ---- LDS -> MFMA fragments
-  const int a_fbase = (wm * 64 + (lane & 31)) * CF::A_ROW;
+  // ---- LDS -> MFMA fragments (block mt of this wave: rows mt*128 + wm*32 + lane%32; the
+  // swizzle term depends on lane%32 only, since 32 and 128 are multiples of A_SWZ_DIV*CPR)
+  static_assert((32 / CF::A_SWZ_DIV) % CF::CPR == 0, "row interleave must keep the A swizzle");
+  const int a_fbase = (wm * 32 + (lane & 31)) * CF::A_ROW;
   const int a_sw = ((lane & 31) / CF::A_SWZ_DIV) % CF::CPR;
   int a_fk[CF::KK];
 #pragma unroll
@@ -193,8 +199,10 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
     const int rows_valid = min(FB_BM, rows_e - mtile * FB_BM);
     const int n0 = ntile * BN;
 
-    const size_t a_rem = (size_t)(M - row0) * Kd * 2;
-    const i32x4_t rA = make_rsrc(A + (size_t)row0 * Kd, (uint32_t)(a_rem > 0x7fffffffu ? 0x7fffffffu : a_rem));
+    // rows [row0, row0 + rows_valid) only; rows_valid * Kd * 2 < 2^31 by the host checks
+    const i32x4_t rA = make_rsrc(A + (size_t)row0 * Kd, (uint32_t)rows_valid * (uint32_t)Kd * 2u);
+    // 32-row blocks of this wave that hold rows of the group (block 1 implies block 0)
+    const int nmt = __builtin_amdgcn_readfirstlane((wm * 32 < rows_valid) + (128 + wm * 32 < rows_valid));
     const size_t woff = (size_t)e * Kd * N + n0;
     const uint32_t b_rem = (uint32_t)(((size_t)Kd * N - n0) * 2);
     const i32x4_t rB0 = make_rsrc(B0 + woff, b_rem);
@@ -223,33 +231,43 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
 #pragma unroll
     for (int s = 0; s < NS - 1; ++s)
       if (s < nk) issue(s);
-    for (int kt = 0; kt < nk; ++kt) {
-      // stage kt has landed once at most (stages issued after it) * VM_PER_STAGE remain
-      wait_barrier_dyn<CF::VM_PER_STAGE*(NS - 2)>(min(NS - 2, nk - 1 - kt) * CF::VM_PER_STAGE);
-      if (kt + NS - 1 < nk) issue(kt + NS - 1);
-      const unsigned char* sa = smem + (kt % NS) * CF::STAGE;
-      const unsigned char* sb = sa + CF::A_BYTES;
+    // the K loop over the first MTV row blocks of this wave (MTV fixed at compile time; a
+    // wave with none still issues its loads and meets every barrier)
+    auto k_loop = [&](auto mtv) {
+      constexpr int MTV = decltype(mtv)::value;
+      for (int kt = 0; kt < nk; ++kt) {
+        // stage kt has landed once at most (stages issued after it) * VM_PER_STAGE remain
+        wait_barrier_dyn<CF::VM_PER_STAGE*(NS - 2)>(min(NS - 2, nk - 1 - kt) * CF::VM_PER_STAGE);
+        if (kt + NS - 1 < nk) issue(kt + NS - 1);
+        if constexpr (MTV > 0) {
+          const unsigned char* sa = smem + (kt % NS) * CF::STAGE;
+          const unsigned char* sb = sa + CF::A_BYTES;
 #pragma unroll
-      for (int kk = 0; kk < CF::KK; ++kk) {
-        bf16x8_t af[CF::MT];
+          for (int kk = 0; kk < CF::KK; ++kk) {
+            bf16x8_t af[MTV];
 #pragma unroll
-        for (int mt = 0; mt < CF::MT; ++mt)
-          af[mt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const i32x4_t*>(sa + a_fk[kk] + mt * 32 * CF::A_ROW));
+            for (int mt = 0; mt < MTV; ++mt)
+              af[mt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const i32x4_t*>(sa + a_fk[kk] + mt * 128 * CF::A_ROW));
 #pragma unroll
-        for (int nb = 0; nb < CF::NB; ++nb) {
+            for (int nb = 0; nb < CF::NB; ++nb) {
 #pragma unroll
-          for (int nt = 0; nt < CF::NT; ++nt) {
-            const unsigned char* p = sb + nb * CF::B_BYTES + b_fn[nt] + kk * 16 * CF::B_ROW;
-            const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(p));
-            const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(p + 4 * CF::B_ROW));
-            const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+              for (int nt = 0; nt < CF::NT; ++nt) {
+                const unsigned char* p = sb + nb * CF::B_BYTES + b_fn[nt] + kk * 16 * CF::B_ROW;
+                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(p));
+                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(p + 4 * CF::B_ROW));
+                const bf16x8_t bfr = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-            for (int mt = 0; mt < CF::MT; ++mt)
-              acc[nb][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfr, acc[nb][mt][nt], 0, 0, 0);
+                for (int mt = 0; mt < MTV; ++mt)
+                  acc[nb][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfr, acc[nb][mt][nt], 0, 0, 0);
+              }
+            }
           }
         }
       }
-    }
+    };
+    if (nmt == 2) k_loop(std::integral_constant<int, 2>{});
+    else if (nmt == 1) k_loop(std::integral_constant<int, 1>{});
+    else k_loop(std::integral_constant<int, 0>{});
 
     // epilogue: lane holds column lane%32 of rows 8*(i/4) + 4*(lane/32) + i%4
 #pragma unroll
@@ -259,7 +277,7 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
         const int col = n0 + wn * CF::WN + nt * 32 + (lane & 31);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int r = wm * 64 + mt * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
           if (r < rows_valid) {
             float v;
             if constexpr (GATED)

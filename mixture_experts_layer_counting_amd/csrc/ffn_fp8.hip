@@ -16,21 +16,27 @@
 // bytes, low nibble first; the scale register of lane (row or column, G) applies to k-block
 // [32G, 32G+32). Activation scales are per 128 k, so one exponent covers a whole K step.
 //
-// Same persistent, XCD-contiguous tile schedule and direct global->LDS double buffering as the
-// bf16 kernels. Block tile 256 rows x BN columns per weight matrix, K step 128. Activations are
-// staged [256][128 B] (16-byte chunk ^ (row/2 mod 8)); weights, stored reduction-contiguous
-// [N][K/2], are staged [BN][64 B] (chunk ^ (col/4 mod 4)). Both fragment reads are
-// ds_read_b128 without transposes. Scales are stored block-major (activations [K/128][M],
-// weights [E][K/32][N]) so each stage's scale loads are contiguous per wave; they go straight
-// into registers one stage ahead.
+// Same persistent, XCD-contiguous tile schedule and direct global->LDS staging as the bf16
+// kernels. Block tile 256 rows x BN columns per weight matrix, K step 128, three LDS stages
+// (two in flight while one is consumed: with fp4 weights a stage is short, and one stage in
+// flight leaves the HBM latency exposed). Activations are staged [256][128 B] (16-byte chunk
+// ^ (row/2 mod 8)); weights, stored reduction-contiguous [N][K/2], are staged [BN][64 B]
+// (chunk ^ (col/4 mod 4)). Both fragment reads are ds_read_b128 without transposes. Scales are
+// stored block-major (activations [K/128][M], weights [E][K/32][N]), so a stage's scales are
+// contiguous runs; they are staged in LDS with the tile data by the same direct loads, and all
+// of a stage's loads complete under one explicit wait. As in the bf16 kernels, a wave's two
+// 32-row blocks are rows wm*32 + [0,32) and 128 + wm*32 + [0,32), blocks wholly past the
+// group's rows skip their MFMAs, and the A descriptor ends at the group's last row.
 #include "moe_common.h"
 #include "tile_sched.h"
+
+#include <type_traits>
 
 namespace moe {
 
 constexpr int F8_BM = 256;
 constexpr int F8_BK = 128;  // reduction elements per stage
-constexpr int F8_NS = 2;
+constexpr int F8_NS = 3;
 constexpr int F8_THREADS = 512;
 constexpr int F8_MAX_E = 1024;
 
@@ -47,11 +53,18 @@ struct F8Cfg {
   static constexpr int B_ROW = F8_BK / 2;                  // 64 B per weight column
   static constexpr int B_BYTES = BN * B_ROW;               // per matrix
   static constexpr int B_LD = NB * B_BYTES / (1024 * 8);   // wave loads per stage (16 cols each)
-  static constexpr int STAGE = A_BYTES + NB * B_BYTES;
-  static constexpr int VM_PER_STAGE = A_LD + B_LD;
+  // per-stage scales: activations [256] fp32, weights [NB][4 k-blocks][BN] e8m0 bytes
+  static constexpr int SF_A = A_BYTES + NB * B_BYTES;
+  static constexpr int SF_B = SF_A + F8_BM * 4;
+  static constexpr int STAGE = SF_B + NB * 4 * BN;
+  static constexpr int VM_PER_STAGE = A_LD + B_LD + 1;  // + one scale load per wave
   static constexpr int SCHED_BYTES = (F8_MAX_E + 1 + 16) * 4;
   static constexpr int LDS_BYTES = F8_NS * STAGE + SCHED_BYTES;
   static_assert(A_LD >= 1 && B_LD >= 1, "tile too small");
+  // the scale loads: waves 0-3 take 64 activation rows each (4 B per lane), waves 4-7 take
+  // 256 bytes each of the weight scale block
+  static_assert(NB * 4 * BN == 4 * 256, "weight scale block must be four 256-byte loads");
+  static_assert(STAGE % 16 == 0, "stage alignment");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 
@@ -78,8 +91,21 @@ __device__ __forceinline__ void f8_dma16(i32x4_t rsrc_in, uint32_t lds_base, int
                : "memory", "m0");
 }
 
+// 4-byte variant: lane l writes LDS base + 4 l.
+__device__ __forceinline__ void f8_dma4(i32x4_t rsrc_in, uint32_t lds_base, int voff) {
+  i32x4_t rsrc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc_in[i]);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane((int)lds_base)), "v"(voff), "s"(rsrc)
+               : "memory", "m0");
+}
+
+// Wait until at most N of this wave's vector-memory loads are outstanding, then barrier.
+template <int N>
 __device__ __forceinline__ void f8_wait_barrier() {
-  asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" : : : "memory");
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
 // e8m0 byte of an fp32 power of two
@@ -145,11 +171,11 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     b_voff[i] = c * kbytes + (((lane & 3) ^ ((c >> 2) & 3)) << 4);
   }
 
-  // fragment offsets. A (fp8, 32x64 per MFMA): row wm*64 + mt*32 + lane%32, chunks 4kk + G
+  // fragment offsets. A (fp8, 32x64 per MFMA): row mt*128 + wm*32 + lane%32, chunks 4kk + G
   // and 4kk + 2 + G. B (fp4): column wn*WN + nt*32 + lane%32, chunk 2kk + G.
   const int g2 = lane >> 5;
-  const int ar = wm * 64 + (lane & 31);
-  const int a_sw = (ar >> 1) & 7;  // (mt*32)/2 is a multiple of 8: same swizzle for both mt
+  const int ar = wm * 32 + (lane & 31);
+  const int a_sw = (ar >> 1) & 7;  // (mt*128)/2 is a multiple of 8: same swizzle for both mt
   int a_off[CF::KK][2];
 #pragma unroll
   for (int kk = 0; kk < CF::KK; ++kk)
@@ -175,25 +201,13 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     const int rows_valid = min(F8_BM, rows_e - mtile * F8_BM);
     const int n0 = ntile * BN;
 
-    const size_t a_rem = (size_t)(M - row0) * Kd;
-    const i32x4_t rA = f8_rsrc(A + (size_t)row0 * Kd, (uint32_t)(a_rem > 0x7fffffffu ? 0x7fffffffu : a_rem));
+    // rows [row0, row0 + rows_valid) only; rows_valid * Kd < 2^31 by the host checks
+    const i32x4_t rA = f8_rsrc(A + (size_t)row0 * Kd, (uint32_t)rows_valid * (uint32_t)Kd);
+    const int nmt = __builtin_amdgcn_readfirstlane((wm * 32 < rows_valid) + (128 + wm * 32 < rows_valid));
     const size_t wbase = ((size_t)e * N + n0) * kbytes;
     const uint32_t b_rem = (uint32_t)((size_t)(N - n0) * kbytes);
     const i32x4_t rB0 = f8_rsrc(B0 + wbase, b_rem);
     const i32x4_t rB1 = GATED ? f8_rsrc(B1 + wbase, b_rem) : rB0;
-    // Scales are block-major: activations [Kd/128][M], weights [E][Kd/32][N]. For one stage a
-    // wave reads 32 consecutive rows (or columns) per load.
-    const float* asf_row[CF::MT];
-#pragma unroll
-    for (int mt = 0; mt < CF::MT; ++mt) asf_row[mt] = A_sf + min(row0 + ar + mt * 32, M - 1);
-    const uint8_t* bsf_col[CF::NF];
-#pragma unroll
-    for (int f = 0; f < CF::NF; ++f) {
-      const int nb = f / CF::NT, nt = f % CF::NT;
-      const uint8_t* base = (GATED && nb) ? B1_sf : B0_sf;
-      bsf_col[f] = base + (size_t)e * ksf_b * N + n0 + wn * CF::WN + nt * 32 + (lane & 31);
-    }
-
     auto issue = [&](int kt) {
       const uint32_t so = smem_lds + (uint32_t)((kt % F8_NS) * CF::STAGE);
 #pragma unroll
@@ -204,23 +218,23 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
         const bool second = GATED && (j / (CF::B_BYTES / 1024)) != 0;
         f8_dma16(second ? rB1 : rB0, so + CF::A_BYTES + j * 1024, b_voff[i], kt * (F8_BK / 2));
       }
+      if (wave < 4) {
+        // activation scales of block kt: rows row0 + 64 wave + lane; rows >= M read as zero
+        f8_dma4(f8_rsrc(A_sf + (size_t)kt * M, (uint32_t)M * 4u), so + CF::SF_A + wave * 256,
+                (row0 + wave * 64 + lane) * 4);
+      } else {
+        // weight scales of k-blocks 4kt..4kt+3, LDS [nb][kb][BN]: load j covers bytes
+        // 256 j .. 256 j + 255 of that block, i.e. matrix nb = j*256 / (4 BN), k-block rows of BN
+        const int j = wave - 4;
+        const int byte = j * 256 + lane * 4;
+        const int nb = byte / (4 * BN);
+        const int kb = (byte % (4 * BN)) / BN;
+        const int col = byte % BN;
+        const uint8_t* sfb = (GATED && nb) ? B1_sf : B0_sf;
+        f8_dma4(f8_rsrc(sfb + ((size_t)e * ksf_b + 4 * (size_t)kt) * N, (uint32_t)N * 4u),
+                so + CF::SF_B + j * 256, kb * N + n0 + col);
+      }
     };
-    // per-stage scales: one activation exponent per mt (its 1x128 block), one dword of four
-    // weight exponents per fragment (k-blocks 4kt..4kt+3 of the lane's column)
-    // raw values only: converting here would make the compiler wait for these loads (and, with
-    // in-order completion, for the DMA issued just before them) before the stage's MFMAs
-    float sa_next[CF::MT];
-    int sb_next[CF::NF][CF::KK];
-    auto load_scales = [&](int kt) {
-#pragma unroll
-      for (int mt = 0; mt < CF::MT; ++mt) sa_next[mt] = asf_row[mt][(size_t)kt * M];
-      // weight k-block of MFMA step kk for this lane: 4kt + 2kk + G
-#pragma unroll
-      for (int f = 0; f < CF::NF; ++f)
-#pragma unroll
-        for (int kk = 0; kk < CF::KK; ++kk) sb_next[f][kk] = bsf_col[f][(size_t)(4 * kt + 2 * kk + g2) * N];
-    };
-
     f32x16_t acc[CF::NB][CF::MT][CF::NT];
 #pragma unroll
     for (int nb = 0; nb < CF::NB; ++nb)
@@ -233,56 +247,57 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
 
     __syncthreads();
     issue(0);
-    load_scales(0);
-    for (int kt = 0; kt < nk; ++kt) {
-      f8_wait_barrier();
-      // Take this stage's scales now: their loads are complete (the barrier waited for every
-      // outstanding vector-memory op), and consuming them here keeps the compiler's own wait
-      // for them from landing after the next stage's loads are issued.
-      int sa[CF::MT], sb[CF::NF][CF::KK];
+    if (nk > 1) issue(1);
+    // the K loop over the first MTV row blocks of this wave (MTV fixed at compile time; a
+    // wave with none still issues its loads and meets every barrier)
+    auto k_loop = [&](auto mtv) {
+      constexpr int MTV = decltype(mtv)::value;
+      for (int kt = 0; kt < nk; ++kt) {
+        // stage kt complete for every wave; stage kt+1 (if any) may still be in flight. The
+        // barrier also means every wave is done with stage kt-1, whose buffer stage kt+2 reuses.
+        if (kt + 1 < nk) f8_wait_barrier<CF::VM_PER_STAGE>();
+        else f8_wait_barrier<0>();
+        if (kt + 2 < nk) issue(kt + 2);
+        if constexpr (MTV > 0) {
+          const unsigned char* sa_l = smem + (kt % F8_NS) * CF::STAGE;
+          const unsigned char* sb_l = sa_l + CF::A_BYTES;
+          // this stage's scales as e8m0 bytes: one per row block (the row's 1x128 block), and
+          // per fragment and MFMA step the byte of k-block 2kk + G of the lane's column
+          const float* sfa = reinterpret_cast<const float*>(sa_l + CF::SF_A);
+          const uint8_t* sfb = sa_l + CF::SF_B;
+          int sa[MTV];
 #pragma unroll
-      for (int mt = 0; mt < CF::MT; ++mt) {
-        asm volatile("" : : "v"(sa_next[mt]));
-        sa[mt] = pow2_to_e8m0(sa_next[mt]);
-      }
+          for (int mt = 0; mt < MTV; ++mt) sa[mt] = pow2_to_e8m0(sfa[ar + mt * 128]);
 #pragma unroll
-      for (int f = 0; f < CF::NF; ++f)
+          for (int kk = 0; kk < CF::KK; ++kk) {
+            i32x8_t af[MTV];
 #pragma unroll
-        for (int kk = 0; kk < CF::KK; ++kk) {
-          sb[f][kk] = sb_next[f][kk];
-          asm volatile("" : : "v"(sb[f][kk]));
-        }
-      if (kt + 1 < nk) {
-        issue(kt + 1);
-        load_scales(kt + 1);
-      }
-      const unsigned char* sa_l = smem + (kt % F8_NS) * CF::STAGE;
-      const unsigned char* sb_l = sa_l + CF::A_BYTES;
+            for (int mt = 0; mt < MTV; ++mt) {
+              const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(sa_l + a_off[kk][0] + mt * 128 * F8_BK);
+              const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(sa_l + a_off[kk][1] + mt * 128 * F8_BK);
+              af[mt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            }
 #pragma unroll
-      for (int kk = 0; kk < CF::KK; ++kk) {
-        i32x8_t af[CF::MT];
+            for (int nb = 0; nb < CF::NB; ++nb) {
 #pragma unroll
-        for (int mt = 0; mt < CF::MT; ++mt) {
-          const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(sa_l + a_off[kk][0] + mt * 32 * F8_BK);
-          const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(sa_l + a_off[kk][1] + mt * 32 * F8_BK);
-          af[mt] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        }
+              for (int nt = 0; nt < CF::NT; ++nt) {
+                const i32x4_t bq = *reinterpret_cast<const i32x4_t*>(sb_l + nb * CF::B_BYTES + b_off[nt][kk]);
+                const i32x4_t z = {0, 0, 0, 0};
+                const i32x8_t bfr = __builtin_shufflevector(bq, z, 0, 1, 2, 3, 4, 5, 6, 7);
+                const int sbw = sfb[(nb * 4 + 2 * kk + g2) * BN + wn * CF::WN + nt * 32 + (lane & 31)];
 #pragma unroll
-        for (int nb = 0; nb < CF::NB; ++nb) {
-#pragma unroll
-          for (int nt = 0; nt < CF::NT; ++nt) {
-            const i32x4_t bq = *reinterpret_cast<const i32x4_t*>(sb_l + nb * CF::B_BYTES + b_off[nt][kk]);
-            const i32x4_t z = {0, 0, 0, 0};
-            const i32x8_t bfr = __builtin_shufflevector(bq, z, 0, 1, 2, 3, 4, 5, 6, 7);
-            const int sbw = sb[nb * CF::NT + nt][kk];
-#pragma unroll
-            for (int mt = 0; mt < CF::MT; ++mt)
-              acc[nb][mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  af[mt], bfr, acc[nb][mt][nt], 0, 4, 0, sa[mt], 0, sbw);
+                for (int mt = 0; mt < MTV; ++mt)
+                  acc[nb][mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                      af[mt], bfr, acc[nb][mt][nt], 0, 4, 0, sa[mt], 0, sbw);
+              }
+            }
           }
         }
       }
-    }
+    };
+    if (nmt == 2) k_loop(std::integral_constant<int, 2>{});
+    else if (nmt == 1) k_loop(std::integral_constant<int, 1>{});
+    else k_loop(std::integral_constant<int, 0>{});
 
     if constexpr (GATED) {
       // SwiGLU, then per-row amax over this wave's 64 columns of the 128-column block; the two
@@ -311,14 +326,14 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
         for (int mt = 0; mt < CF::MT; ++mt)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            part[wn * 256 + wm * 64 + mt * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3)] = rmax[mt][i];
+            part[wn * 256 + mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3)] = rmax[mt][i];
       }
       __syncthreads();
 #pragma unroll
       for (int mt = 0; mt < CF::MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int r = wm * 64 + mt * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3);
+          const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3);
           const float amax = fmaxf(part[r], part[256 + r]);
           // smallest power of two s with 448 s >= amax (amax = 0 -> 1)
           float s = 1.0f;
@@ -347,7 +362,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
           const int col = n0 + wn * CF::WN + nt * 32 + (lane & 31);
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int r = wm * 64 + mt * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3);
+            const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3);
             if (r < rows_valid) C16[(size_t)(row0 + r) * N + col] = f32_to_bf16_bits(acc[0][mt][nt][i]);
           }
         }
