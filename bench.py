@@ -1,10 +1,15 @@
 """Benchmark of the MoE-layer hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2|c3|c4|c5] [--maxvio V]
+                    [--combine gather|scatter] [--xperm]
 
-One step = one pass of the whole path over one batch of synthetic input, through the C ABI:
-route -> permute -> gate/up + SwiGLU -> down -> combine (c3 passes its given routing and
-skips route). Inputs and weights are resident in HBM before the timed region starts.
+One step = one pass of the whole path over one batch of synthetic input, through the C ABI,
+in the order moe_layer_forward runs it: route -> permute metadata -> gate/up + SwiGLU with
+its rows gathered from x -> down -> combine (c3 passes its given routing and skips route).
+``--combine scatter`` fuses the weighted combine into the down projection (fp32 atomics into
+a zeroed accumulator, rounded once at the end); ``--xperm`` writes the permuted copy x_perm in
+the permute and reads it in gate/up instead of gathering. Inputs and weights are resident in
+HBM before the timed region starts.
 Prints ONE JSON line. ``value`` is tokens/s of the whole layer. ``roofline`` describes the
 dominant kernel (the gate/up grouped GEMM): its algorithmic flops or bytes per launch over
 its average duration measured with HIP events on the launch stream during the timed steps.
@@ -17,6 +22,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -49,6 +55,10 @@ def parse():
     ap.add_argument("--cpu-sample-experts", type=int, default=0,
                     help="experts in the oracle timing sample (0: whole layer when it is small)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--combine", default="gather", choices=["gather", "scatter"],
+                    help="deterministic gather-reduce (default) or the scatter-add fused into down")
+    ap.add_argument("--xperm", action="store_true",
+                    help="materialise x_perm in the permute instead of gathering rows in gate/up")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (known bytes) a few times, "
                          "to scale the FETCH_SIZE / WRITE_SIZE counters")
@@ -132,18 +142,21 @@ def main():
     cu = torch.empty(E + 1, **i32)
     pos = torch.empty((T, K), **i32)
     row_src = torch.empty(M, **i32)
-    x_perm = torch.empty((M, H), dtype=TD[w.act], device=dev)
-    x_perm_sf = torch.empty((H // 128, M), **f32) if w.act == "fp8" else None
+    scatter = args.combine == "scatter"
+    x_perm = torch.empty((M, H), dtype=TD[w.act], device=dev) if args.xperm else None
+    x_perm_sf = torch.empty((H // 128, M), **f32) if args.xperm and w.act == "fp8" else None
+    row_w = torch.empty(M, **f32) if scatter else None
     h = torch.empty((M, Hp), dtype=TD[hf], device=dev)
     h_sf = torch.empty((Hp // 128, M), **f32) if w.act == "fp8" else None
-    y = torch.empty((M, H), dtype=TD[yf], device=dev)
+    y = torch.empty((M, H), dtype=TD[yf], device=dev) if not scatter else None
     out = torch.empty((T, H), dtype=TD[w.out], device=dev)
+    acc = (out if w.out == "f32" else torch.empty((T, H), **f32)) if scatter else None
     nws = moe.moe_permute_workspace_bytes(T, E, K)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
-    stages = ["route", "permute", "gate_up", "down", "combine"]
+    stages = ["route", "permute", "gate_up", "down", "combine"]   # combine: acc zero + store (scatter)
     ev = {s: [] for s in stages}
 
     def step(record):
@@ -160,14 +173,27 @@ def main():
         if w.logits is not None:
             mark("route", lambda: moe.moe_route_topk(w.logits, T, E, K, topk_idx, topk_w, sh))
         mark("permute", lambda: moe.moe_permute(w.x, w.x_sf, DT[w.act], topk_idx, topk_w, T, H, E, K,
-                                                counts, cu, pos, row_src, None, x_perm, x_perm_sf,
+                                                counts, cu, pos, row_src, row_w, x_perm, x_perm_sf,
                                                 ws, nws, sh))
-        mark("gate_up", lambda: moe.moe_ffn_gate_up(x_perm, x_perm_sf, DT[w.act], cu, M, E, H, Hp,
-                                                    w.w_gate, w.w_up, w.sf_gate, w.sf_up, DT[w.wgt],
-                                                    h, h_sf, sh))
-        mark("down", lambda: moe.moe_ffn_down(h, h_sf, DT[hf], cu, M, E, H, Hp, w.w_down, w.sf_down,
-                                              DT[w.wgt], y, DT[yf], sh))
-        mark("combine", lambda: moe.moe_combine(y, DT[yf], pos, topk_w, T, H, K, out, DT[w.out], sh))
+        if args.xperm:
+            mark("gate_up", lambda: moe.moe_ffn_gate_up(x_perm, x_perm_sf, DT[w.act], cu, M, E, H, Hp,
+                                                        w.w_gate, w.w_up, w.sf_gate, w.sf_up,
+                                                        DT[w.wgt], h, h_sf, sh))
+        else:
+            mark("gate_up", lambda: moe.moe_ffn_gate_up_gather(w.x, w.x_sf, DT[w.act], row_src, T, K, cu,
+                                                               M, E, H, Hp, w.w_gate, w.w_up, w.sf_gate,
+                                                               w.sf_up, DT[w.wgt], h, h_sf, sh))
+        if not scatter:
+            mark("down", lambda: moe.moe_ffn_down(h, h_sf, DT[hf], cu, M, E, H, Hp, w.w_down, w.sf_down,
+                                                  DT[w.wgt], y, DT[yf], sh))
+            mark("combine", lambda: moe.moe_combine(y, DT[yf], pos, topk_w, T, H, K, out, DT[w.out], sh))
+        else:
+            mark("combine", lambda: acc.zero_())
+            mark("down", lambda: moe.moe_ffn_down_scatter(h, h_sf, DT[hf], cu, M, E, H, Hp, w.w_down,
+                                                          w.sf_down, DT[w.wgt], row_src, row_w, T, K,
+                                                          acc, sh))
+            if acc is not out:
+                mark("combine", lambda: out.copy_(acc))
 
     for _ in range(args.warmup):
         step(False)
@@ -178,8 +204,15 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
-    stage_ms = {s: (sum(a.elapsed_time(b) for a, b in ev[s]) / len(ev[s]) if ev[s] else 0.0)
-                for s in stages}
+    # per stage: total event time of the stage in a step (the scatter combine has two parts),
+    # median over the timed steps
+    def per_step(name):
+        if not ev[name]:
+            return 0.0
+        per = len(ev[name]) // args.steps
+        tot = [sum(a.elapsed_time(b) for a, b in ev[name][i * per:(i + 1) * per]) for i in range(args.steps)]
+        return float(statistics.median(tot))
+    stage_ms = {s: per_step(s) for s in stages}
 
     # ---------------------------------------------------------------- algorithmic units
     cnt = counts.cpu().numpy()
@@ -198,14 +231,21 @@ def main():
     dn_flops = 2.0 * M * H * Hp
     gu_bytes = M * H * ab + xsf_b + 2 * active * wmat + M * Hp * hb + hsf_b
     dn_bytes = M * Hp * hb + hsf_b + active * wmat + M * H * yb
-    perm_bytes = T * H * ab + M * H * ab + (T * (H // 128) * 4 + xsf_b if w.act == "fp8" else 0)
-    comb_bytes = M * H * yb + T * H * ob
+    # permute: topk_idx read; pos, row_src (and row_w from topk_w) written; + the row copy
+    perm_bytes = M * 4 + 2 * M * 4 + (2 * M * 4 if scatter else 0)
+    if args.xperm:
+        perm_bytes += T * H * ab + M * H * ab + (T * (H // 128) * 4 + xsf_b if w.act == "fp8" else 0)
+    if scatter:   # zero the fp32 accumulator, then round it once into out (bf16)
+        comb_bytes = T * H * 4 + ((T * H * 4 + T * H * ob) if w.out != "f32" else 0)
+        dn_bytes = M * Hp * hb + hsf_b + active * wmat + M * 4 * 2   # + the fp32 adds, M*H*4
+    else:
+        comb_bytes = M * H * yb + T * H * ob
     peak_flops = {"f32": PEAK_FP32_TFLOPS, "bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS}[w.act]
     gu_s = stage_ms["gate_up"] / 1e3
     t_mfma = gu_flops / (peak_flops * 1e12)
     t_hbm = gu_bytes / (PEAK_HBM_GBS * 1e9)
     khash = source_hash("ffn_bf16.hip", "tile_sched.h", "moe_common.h")
-    traffic = load_traffic("gate_up", args.config, khash)
+    traffic = load_traffic("gate_up" if args.xperm else "gate_up_gather", args.config, khash)
     if t_mfma >= t_hbm:
         roof = {"bound": "mfma", "achieved": gu_flops / gu_s / 1e12, "peak": peak_flops, "unit": "TFLOP/s"}
     else:
@@ -231,7 +271,8 @@ def main():
         "dtype": {"f32": "f32", "bf16": "bf16", "fp8": "fp8xmxfp4"}[w.act],
         "data": "synthetic (seeded; random-init weights of the stated shape)",
         "config": {"workload": f"{args.config}: {DESCR[args.config]}", "T": T, "H": H, "Hp": Hp,
-                   "E": E, "K": K, "act": w.act, "wgt": w.wgt},
+                   "E": E, "K": K, "act": w.act, "wgt": w.wgt, "combine": args.combine,
+                   "x_perm": "materialised" if args.xperm else "gathered in gate/up"},
         "grouped_ffn_tflops": ffn_tflops,
         "grouped_ffn_frac_of_mfma_peak": ffn_tflops / peak_flops,
         "stage_ms": stage_ms,

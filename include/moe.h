@@ -111,9 +111,13 @@ MOE_API size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t K);
  *  pos        [T, K] int32 out: row of copy (t, k); -1 for a dropped (invalid-id) copy.
  *  row_src    [T*K] int32 out: flat index t*K + k of the copy stored in each row.
  *  row_w      [T*K] fp32 out (or NULL): topk_w of the copy stored in each row.
- *  x_perm     [T*K, H] out, format `act`: x_perm[pos[t,k]] = x[t], bit for bit.
- *  x_perm_sf  [H/128, T*K] fp32 out when act = FP8_E4M3, block-major: x_perm_sf[b][r] is the
- *             scale of block b of row r (the transpose of x_sf's layout).
+ *  x_perm     [T*K, H] out, format `act`: x_perm[pos[t,k]] = x[t], bit for bit. May be NULL:
+ *             then only the routing metadata is produced (x, x_sf and x_perm_sf are not
+ *             touched), for consumers that gather rows through row_src, such as
+ *             moe_ffn_gate_up_gather.
+ *  x_perm_sf  [H/128, T*K] fp32 out when act = FP8_E4M3 and x_perm is given, block-major:
+ *             x_perm_sf[b][r] is the scale of block b of row r (the transpose of x_sf's
+ *             layout).
  * Row order is a stable counting sort: the rows of expert e hold its copies in ascending
  * t*K + k. The result is deterministic. Limits: E <= 1024, K <= 32. */
 MOE_API moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t act,
@@ -143,6 +147,22 @@ MOE_API moe_status_t moe_ffn_gate_up(const void* x_perm, const float* x_perm_sf,
                              const uint8_t* sf_gate, const uint8_t* sf_up, moe_dtype_t wgt,
                              void* h, float* h_sf, hipStream_t stream);
 
+/* moe_ffn_gate_up with its input rows gathered from the token matrix instead of a permuted
+ * copy ("Mixture of Kittens", Step 6 reads each expert's tokens through their indices; the
+ * DeepGEMM Mega-MoE how-to fuses dispatch into the expert GEMM): row r of expert e's group
+ * is x[row_src[r] / K], so
+ *     h[r] = silu(x[row_src[r]/K] . Wg[e]) * (x[row_src[r]/K] . Wu[e]),
+ * bitwise the same h as moe_ffn_gate_up on the x_perm that moe_permute would write.
+ *  x [T, H] of format `act`; x_sf [T, H/128] fp32 (FP8_E4M3, the token layout of
+ *  moe_permute's x_sf); row_src [M] from moe_permute; other arguments as moe_ffn_gate_up.
+ * Needs M <= T*K and T*H*bytes(act) < 2^31 (MOE_EUNSUPPORTED otherwise). */
+MOE_API moe_status_t moe_ffn_gate_up_gather(const void* x, const float* x_sf, moe_dtype_t act,
+                                    const int32_t* row_src, int32_t T, int32_t K,
+                                    const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
+                                    int32_t Hp, const void* w_gate, const void* w_up,
+                                    const uint8_t* sf_gate, const uint8_t* sf_up, moe_dtype_t wgt,
+                                    void* h, float* h_sf, hipStream_t stream);
+
 /* Second half of the grouped expert FFN: y_rows[r] = h[r] . Wd[e] for the rows of expert e.
  *  h_dtype F32 (wgt F32, out F32), BF16 (wgt BF16, out BF16) or FP8_E4M3 with h_sf
  *  (wgt MXFP4, out BF16). F32/BF16 w_down [E, Hp, H]; MXFP4 bytes [E, H, Hp/2] with
@@ -152,6 +172,20 @@ MOE_API moe_status_t moe_ffn_down(const void* h, const float* h_sf, moe_dtype_t 
                           const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
                           int32_t Hp, const void* w_down, const uint8_t* sf_down,
                           moe_dtype_t wgt, void* y_rows, moe_dtype_t out, hipStream_t stream);
+
+/* moe_ffn_down with the weighted combine fused into its epilogue (DeepGEMM Mega-MoE how-to:
+ * combine fused into the expert kernel; MoonEP "combine fwd" weights the rows): for every row
+ * r of expert e's group,
+ *     acc[row_src[r] / K] += row_w[r] * (h[r] . Wd[e]),
+ * added with fp32 atomics, so the order of the K additions of a token (and its last bit) may
+ * vary between runs. acc [T, H] fp32 is accumulated into: the caller zeroes it first.
+ * row_src, row_w [M] from moe_permute. Formats and limits as moe_ffn_down (y_rows is not
+ * written). */
+MOE_API moe_status_t moe_ffn_down_scatter(const void* h, const float* h_sf, moe_dtype_t h_dtype,
+                                  const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
+                                  int32_t Hp, const void* w_down, const uint8_t* sf_down,
+                                  moe_dtype_t wgt, const int32_t* row_src, const float* row_w,
+                                  int32_t T, int32_t K, float* acc, hipStream_t stream);
 
 /* Scratch bytes moe_grouped_ffn needs (the intermediate h and its scales). */
 MOE_API size_t moe_grouped_ffn_workspace_bytes(int32_t M, int32_t Hp, moe_dtype_t act, moe_dtype_t wgt);
@@ -181,12 +215,18 @@ MOE_API size_t moe_layer_workspace_bytes(const moe_layer_desc_t* d);
 /* The whole layer on one stream, no host synchronisation ("Distributed expert parallelism",
  * "The dispatch-compute-combine lifecycle", without the exchanges):
  *   route (skipped when logits == NULL: topk_idx_in / topk_w_in are used instead)
- *   -> permute -> gate/up + SwiGLU -> down -> combine.
+ *   -> permute metadata (counts, cu_seqlens, pos, row_src)
+ *   -> gate/up + SwiGLU, its rows gathered from x (moe_ffn_gate_up_gather; with the
+ *      environment variable MOE_LAYER_XPERM=1, or when T*H*bytes(act) >= 2^31, x_perm is
+ *      written by moe_permute and read instead: same result, bit for bit)
+ *   -> d->combine == MOE_COMBINE_GATHER: down -> y_rows -> moe_combine (deterministic);
+ *      d->combine == MOE_COMBINE_SCATTER_ATOMIC: down with the weighted scatter-add fused
+ *      into its epilogue (moe_ffn_down_scatter) into an fp32 accumulator (the output itself
+ *      when d->out is F32, else a workspace buffer rounded once into out at the end).
  *  x [T, H] (format d->act, with x_sf for FP8_E4M3); logits [T, E] fp32 or NULL;
  *  topk_idx_in / topk_w_in [T, K] when logits == NULL; weights as for moe_grouped_ffn;
- *  out [T, H] of d->out. `ws` must hold moe_layer_workspace_bytes(d) bytes; all
- *  intermediates (routing, counts, cu_seqlens, pos, row_src, x_perm, h, y_rows) live there,
- *  at offsets reported by moe_layer_workspace_layout. */
+ *  out [T, H] of d->out, 16-byte aligned. `ws` must hold moe_layer_workspace_bytes(d) bytes;
+ *  the intermediates live there, at offsets reported by moe_layer_workspace_layout. */
 MOE_API moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const void* x, const float* x_sf,
                                const float* logits, const int32_t* topk_idx_in,
                                const float* topk_w_in, const void* w_gate, const void* w_up,
@@ -196,9 +236,10 @@ MOE_API moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const void* x,
 
 /* Byte offsets of the intermediates inside the moe_layer_forward workspace, for inspection.
  * offsets[i] (i in order): 0 topk_idx, 1 topk_w, 2 counts, 3 cu_seqlens, 4 pos, 5 row_src,
- * 6 row_w, 7 x_perm, 8 x_perm_sf, 9 h, 10 h_sf, 11 y_rows, 12 permute scratch,
- * 13 fp32 accumulator (scatter combine). Unused entries are set to SIZE_MAX. Writes
- * n <= 14 entries; returns MOE_EINVAL for an invalid `d`. Host-only. */
+ * 6 row_w (scatter combine), 7 x_perm and 8 x_perm_sf (only when x_perm is written),
+ * 9 h, 10 h_sf, 11 y_rows (gather combine), 12 permute scratch, 13 fp32 accumulator (scatter
+ * combine with a BF16 output). Unused entries are set to SIZE_MAX. Writes n <= 14 entries;
+ * returns MOE_EINVAL for an invalid `d`. Host-only; the sizes depend on MOE_LAYER_XPERM. */
 MOE_API moe_status_t moe_layer_workspace_layout(const moe_layer_desc_t* d, size_t* offsets, int32_t n);
 
 /* Static text for a status code. */

@@ -28,7 +28,8 @@ WS_FIELDS = ("topk_idx", "topk_w", "counts", "cu_seqlens", "pos", "row_src", "ro
              "x_perm_sf", "h", "h_sf", "y_rows", "permute_scratch", "acc_f32")
 
 EXPORTS = ("moe_route_topk", "moe_permute_workspace_bytes", "moe_permute", "moe_ffn_gate_up",
-           "moe_ffn_down", "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn", "moe_combine",
+           "moe_ffn_gate_up_gather", "moe_ffn_down", "moe_ffn_down_scatter",
+           "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn", "moe_combine",
            "moe_layer_workspace_bytes", "moe_layer_forward", "moe_layer_workspace_layout",
            "moe_status_str")
 
@@ -58,6 +59,10 @@ _SIGS = {
     "moe_permute_workspace_bytes": (_S, [_I, _I, _I]),
     "moe_permute": (_I, [_P, _P, _E, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
     "moe_ffn_gate_up": (_I, [_P, _P, _E, _P, _I, _I, _I, _I, _P, _P, _P, _P, _E, _P, _P, _P]),
+    "moe_ffn_gate_up_gather": (_I, [_P, _P, _E, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _E,
+                                    _P, _P, _P]),
+    "moe_ffn_down_scatter": (_I, [_P, _P, _E, _P, _I, _I, _I, _I, _P, _P, _E, _P, _P, _I, _I, _P,
+                                  _P]),
     "moe_ffn_down": (_I, [_P, _P, _E, _P, _I, _I, _I, _I, _P, _P, _E, _P, _E, _P]),
     "moe_grouped_ffn_workspace_bytes": (_S, [_I, _I, _E, _E]),
     "moe_grouped_ffn": (_I, [_P, _P, _E, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _E, _P, _E,
@@ -138,6 +143,21 @@ def moe_ffn_gate_up(x_perm, x_perm_sf, act, cu_seqlens, M, E, H, Hp, w_gate, w_u
     _check(lib().moe_ffn_gate_up(_ptr(x_perm), _ptr(x_perm_sf), act, _ptr(cu_seqlens), M, E, H, Hp,
                                  _ptr(w_gate), _ptr(w_up), _ptr(sf_gate), _ptr(sf_up), wgt, _ptr(h),
                                  _ptr(h_sf), _stream(stream)), "moe_ffn_gate_up")
+
+
+def moe_ffn_gate_up_gather(x, x_sf, act, row_src, T, K, cu_seqlens, M, E, H, Hp, w_gate, w_up,
+                           sf_gate, sf_up, wgt, h, h_sf, stream=None):
+    _check(lib().moe_ffn_gate_up_gather(_ptr(x), _ptr(x_sf), act, _ptr(row_src), T, K,
+                                        _ptr(cu_seqlens), M, E, H, Hp, _ptr(w_gate), _ptr(w_up),
+                                        _ptr(sf_gate), _ptr(sf_up), wgt, _ptr(h), _ptr(h_sf),
+                                        _stream(stream)), "moe_ffn_gate_up_gather")
+
+
+def moe_ffn_down_scatter(h, h_sf, h_dtype, cu_seqlens, M, E, H, Hp, w_down, sf_down, wgt, row_src,
+                         row_w, T, K, acc, stream=None):
+    _check(lib().moe_ffn_down_scatter(_ptr(h), _ptr(h_sf), h_dtype, _ptr(cu_seqlens), M, E, H, Hp,
+                                      _ptr(w_down), _ptr(sf_down), wgt, _ptr(row_src), _ptr(row_w),
+                                      T, K, _ptr(acc), _stream(stream)), "moe_ffn_down_scatter")
 
 
 def moe_ffn_down(h, h_sf, h_dtype, cu_seqlens, M, E, H, Hp, w_down, sf_down, wgt, y_rows, out,

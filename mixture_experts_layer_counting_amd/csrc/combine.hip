@@ -128,4 +128,50 @@ moe_status_t launch_combine(const void* y, moe_dtype_t yt, const int* pos, const
   return MOE_EUNSUPPORTED;
 }
 
+// ---- fp32 accumulator of the fused scatter-add combine --------------------------------
+// (the down projection adds row_w * y of every row into acc[token] with fp32 atomics; the
+// accumulator starts at zero and is rounded once into the output format at the end)
+
+__global__ __launch_bounds__(256) void acc_zero_kernel(float* __restrict__ acc, size_t n) {
+  const size_t n4 = n / 4;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+    reinterpret_cast<float4*>(acc)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (size_t i = n4 * 4 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) acc[i] = 0.f;
+}
+
+__global__ __launch_bounds__(256) void acc_store_bf16_kernel(const float* __restrict__ acc,
+                                                             uint16_t* __restrict__ out, size_t n) {
+  const size_t n8 = n / 8;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
+    float f[8];
+    load8(acc + 8 * i, f);
+    store8(out + 8 * i, f);
+  }
+  for (size_t i = n8 * 8 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
+    out[i] = f32_to_bf16_bits(acc[i]);
+}
+
+static int stream_grid(size_t items) {
+  const size_t cap = (size_t)device_cu_count() * 8;
+  const size_t need = (items + 255) / 256;
+  return (int)(need < cap ? (need > 0 ? need : 1) : cap);
+}
+
+moe_status_t launch_acc_zero(float* acc, size_t n, hipStream_t s) {
+  if (n == 0) return MOE_OK;
+  if ((uintptr_t)acc % 16) return MOE_EINVAL;
+  acc_zero_kernel<<<stream_grid(n / 4), 256, 0, s>>>(acc, n);
+  return launch_status();
+}
+
+moe_status_t launch_acc_store(const float* acc, size_t n, void* out, moe_dtype_t ot, hipStream_t s) {
+  if (n == 0) return MOE_OK;
+  if (ot != MOE_BF16) return MOE_EUNSUPPORTED;
+  if ((uintptr_t)acc % 16 || (uintptr_t)out % 16) return MOE_EINVAL;
+  acc_store_bf16_kernel<<<stream_grid(n / 8), 256, 0, s>>>(acc, static_cast<uint16_t*>(out), n);
+  return launch_status();
+}
+
 }  // namespace moe

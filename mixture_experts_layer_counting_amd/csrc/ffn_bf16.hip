@@ -27,8 +27,13 @@
 //    segments are XOR-swizzled by 2*(row mod 4) so the four rows a transpose read touches
 //    land on distinct banks.
 //  * Global loads for step k+1 are issued before the MFMAs of step k; one barrier per step.
-//  * The A descriptor's range ends at the group's last row of the tile, so rows past it read
-//    as zeros without memory traffic; they are never stored.
+//  * Rows past the group's last row of the tile are loaded out of the A descriptor's range,
+//    so they read as zeros without memory traffic; they are never stored.
+//  * Optional row maps ("Mixture of Kittens", Step 6 gathers its inputs by token index and
+//    scatters its outputs; the survey's fused layer): with `a_src`, A row r of the group is
+//    row a_src[r] / a_k of A (the token matrix x, no permuted copy); with `s_acc`, the down
+//    epilogue adds s_w[r] * y[r] into s_acc[s_src[r] / s_k] with fp32 atomics instead of
+//    storing y (the weighted combine fused into the down projection).
 #include "moe_common.h"
 #include "tile_sched.h"
 
@@ -119,11 +124,13 @@ __device__ __forceinline__ void wait_barrier_dyn(int n) {
   }
 }
 
-template <bool GATED, int BN, int BK, int NS>
+// MAPPED selects the row maps at compile time: gate/up gathers its A rows, down scatters
+// into the accumulator; the plain instantiations carry neither.
+template <bool GATED, int BN, int BK, int NS, bool MAPPED>
 __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
     const uint16_t* __restrict__ A, const int* __restrict__ cu, int M, int E, int Kd, int N,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C,
-    int n_fastest) {
+    int n_fastest, RowMaps maps) {
   using CF = FbCfg<GATED, BN, BK, NS>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int* tstart = reinterpret_cast<int*>(smem + NS * CF::STAGE);
@@ -144,12 +151,14 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
   // chunk p ^ ((r / A_SWZ_DIV) % CPR), so 16 consecutive rows of one chunk hit 16 distinct
   // bank groups. Wave load j (j = wave + 8 i) fills rows [j*A_RPL, (j+1)*A_RPL), lane l ->
   // row j*A_RPL + l / CPR, slot l % CPR.
-  int a_voff[CF::A_LD], a_ldo[CF::A_LD];
+  // (when gathering, a_voff is reset per tile from the tile's source rows)
+  int a_voff[CF::A_LD], a_ldo[CF::A_LD], a_row[CF::A_LD];
 #pragma unroll
   for (int i = 0; i < CF::A_LD; ++i) {
     const int j = wave + 8 * i;
     const int r = j * CF::A_RPL + lane / CF::CPR;
     const int p = lane % CF::CPR;
+    a_row[i] = r;
     a_voff[i] = r * Kd * 2 + ((p ^ ((r / CF::A_SWZ_DIV) % CF::CPR)) << 4);
     a_ldo[i] = j * 1024;
   }
@@ -199,8 +208,25 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
     const int rows_valid = min(FB_BM, rows_e - mtile * FB_BM);
     const int n0 = ntile * BN;
 
-    // rows [row0, row0 + rows_valid) only; rows_valid * Kd * 2 < 2^31 by the host checks
-    const i32x4_t rA = make_rsrc(A + (size_t)row0 * Kd, (uint32_t)rows_valid * (uint32_t)Kd * 2u);
+    // A rows of this tile: rows past rows_valid get an offset past the descriptor's range.
+    // Plain: the descriptor starts at row row0 and spans rows_valid rows (< 2^31 bytes by the
+    // host checks). Gathered: it spans all a_rows rows of A (< 2^31 bytes, host checks).
+    i32x4_t rA;
+    int a_off[CF::A_LD];
+    if constexpr (GATED && MAPPED) {
+      // the chunk part of a_voff is (a_voff - row * Kd * 2); the row part is replaced by the
+      // source row's offset
+      rA = make_rsrc(A, (uint32_t)maps.a_rows * (uint32_t)Kd * 2u);
+#pragma unroll
+      for (int i = 0; i < CF::A_LD; ++i)
+        a_off[i] = a_row[i] < rows_valid
+                       ? (maps.a_src[row0 + a_row[i]] / maps.a_k - a_row[i]) * Kd * 2 + a_voff[i]
+                       : (int)0x80000000u;
+    } else {
+      rA = make_rsrc(A + (size_t)row0 * Kd, (uint32_t)rows_valid * (uint32_t)Kd * 2u);
+#pragma unroll
+      for (int i = 0; i < CF::A_LD; ++i) a_off[i] = a_voff[i];
+    }
     // 32-row blocks of this wave that hold rows of the group (block 1 implies block 0)
     const int nmt = __builtin_amdgcn_readfirstlane((wm * 32 < rows_valid) + (128 + wm * 32 < rows_valid));
     const size_t woff = (size_t)e * Kd * N + n0;
@@ -211,7 +237,7 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
     auto issue = [&](int kt) {  // A_LD + B_LD direct loads per lane for stage kt
       const uint32_t so = smem_lds + (uint32_t)((kt % NS) * CF::STAGE);
 #pragma unroll
-      for (int i = 0; i < CF::A_LD; ++i) lds_dma16(rA, so + a_ldo[i], a_voff[i], kt * BK * 2);
+      for (int i = 0; i < CF::A_LD; ++i) lds_dma16(rA, so + a_ldo[i], a_off[i], kt * BK * 2);
 #pragma unroll
       for (int i = 0; i < CF::B_LD; ++i)
         lds_dma16(b_mat[i] ? rB1 : rB0, so + b_ldo[i], b_voff[i], kt * BK * N * 2);
@@ -270,24 +296,40 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
     else k_loop(std::integral_constant<int, 0>{});
 
     // epilogue: lane holds column lane%32 of rows 8*(i/4) + 4*(lane/32) + i%4
+    if constexpr (!GATED && MAPPED) {
 #pragma unroll
-    for (int mt = 0; mt < CF::MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < CF::NT; ++nt) {
-        const int col = n0 + wn * CF::WN + nt * 32 + (lane & 31);
+      for (int mt = 0; mt < CF::MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
           if (r < rows_valid) {
-            float v;
-            if constexpr (GATED)
-              v = silu_f32(acc[0][mt][nt][i]) * acc[1][mt][nt][i];
-            else
-              v = acc[0][mt][nt][i];
-            C[(size_t)(row0 + r) * N + col] = f32_to_bf16_bits(v);
+            const int gr = row0 + r;
+            float* dst = maps.s_acc + (size_t)(maps.s_src[gr] / maps.s_k) * N + n0 + wn * CF::WN + (lane & 31);
+            const float w = maps.s_w[gr];
+#pragma unroll
+            for (int nt = 0; nt < CF::NT; ++nt) unsafeAtomicAdd(dst + nt * 32, w * acc[0][mt][nt][i]);
           }
         }
-      }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < CF::MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < CF::NT; ++nt) {
+          const int col = n0 + wn * CF::WN + nt * 32 + (lane & 31);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            if (r < rows_valid) {
+              float v;
+              if constexpr (GATED)
+                v = silu_f32(acc[0][mt][nt][i]) * acc[1][mt][nt][i];
+              else
+                v = acc[0][mt][nt][i];
+              C[(size_t)(row0 + r) * N + col] = f32_to_bf16_bits(v);
+            }
+          }
+        }
+    }
   }
 }
 
@@ -301,21 +343,31 @@ static int tile_order_n_fastest(int M, int E) {
   return 0;
 }
 
-template <bool GATED, int BN, int BK, int NS>
-static moe_status_t launch_fb(const uint16_t* A, const int* cu, int M, int E, int Kd, int N,
-                              const uint16_t* B0, const uint16_t* B1, uint16_t* C, hipStream_t s) {
+template <bool GATED, int BN, int BK, int NS, bool MAPPED>
+static moe_status_t launch_fb_k(const uint16_t* A, const int* cu, int M, int E, int Kd, int N,
+                                const uint16_t* B0, const uint16_t* B1, uint16_t* C,
+                                const RowMaps& maps, hipStream_t s) {
   using CF = FbCfg<GATED, BN, BK, NS>;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_kernel<GATED, BN, BK, NS>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_kernel<GATED, BN, BK, NS, MAPPED>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS_BYTES) != hipSuccess)
       return MOE_EHIP;
     attr_set = true;
   }
   const int grid = device_cu_count();
-  ffn_bf16_kernel<GATED, BN, BK, NS><<<grid, FB_THREADS, CF::LDS_BYTES, s>>>(A, cu, M, E, Kd, N, B0, B1, C,
-                                                                         tile_order_n_fastest(M, E));
+  ffn_bf16_kernel<GATED, BN, BK, NS, MAPPED><<<grid, FB_THREADS, CF::LDS_BYTES, s>>>(
+      A, cu, M, E, Kd, N, B0, B1, C, tile_order_n_fastest(M, E), maps);
   return launch_status();
+}
+
+template <bool GATED, int BN, int BK, int NS>
+static moe_status_t launch_fb(const uint16_t* A, const int* cu, int M, int E, int Kd, int N,
+                              const uint16_t* B0, const uint16_t* B1, uint16_t* C,
+                              const RowMaps& maps, hipStream_t s) {
+  const bool mapped = GATED ? maps.a_src != nullptr : maps.s_acc != nullptr;
+  if (mapped) return launch_fb_k<GATED, BN, BK, NS, true>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
+  return launch_fb_k<GATED, BN, BK, NS, false>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
 }
 
 // K-step / LDS-stage pipeline variant: MOE_FFN_PIPE = "64x2" (default) or "32x4".
@@ -330,24 +382,27 @@ static int pipe_variant() {
 
 template <bool GATED, int BN>
 static moe_status_t launch_fb_any(const uint16_t* A, const int* cu, int M, int E, int Kd, int N,
-                                  const uint16_t* B0, const uint16_t* B1, uint16_t* C, hipStream_t s) {
-  if (pipe_variant() == 1) return launch_fb<GATED, BN, 32, 4>(A, cu, M, E, Kd, N, B0, B1, C, s);
-  return launch_fb<GATED, BN, 64, 2>(A, cu, M, E, Kd, N, B0, B1, C, s);
+                                  const uint16_t* B0, const uint16_t* B1, uint16_t* C,
+                                  const RowMaps& maps, hipStream_t s) {
+  if (pipe_variant() == 1) return launch_fb<GATED, BN, 32, 4>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
+  return launch_fb<GATED, BN, 64, 2>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
 }
 
-moe_status_t launch_ffn_gate_up_bf16(const void* x_perm, const int* cu, int M, int E, int H, int Hp,
-                                     const void* wg, const void* wu, void* h, hipStream_t s) {
+moe_status_t launch_ffn_gate_up_bf16(const void* a, const int* cu, int M, int E, int H, int Hp,
+                                     const void* wg, const void* wu, void* h, const RowMaps& maps,
+                                     hipStream_t s) {
   if (M == 0) return MOE_OK;
-  return launch_fb_any<true, 128>(static_cast<const uint16_t*>(x_perm), cu, M, E, H, Hp,
-                              static_cast<const uint16_t*>(wg), static_cast<const uint16_t*>(wu),
-                              static_cast<uint16_t*>(h), s);
+  return launch_fb_any<true, 128>(static_cast<const uint16_t*>(a), cu, M, E, H, Hp,
+                                  static_cast<const uint16_t*>(wg), static_cast<const uint16_t*>(wu),
+                                  static_cast<uint16_t*>(h), maps, s);
 }
 
 moe_status_t launch_ffn_down_bf16(const void* h, const int* cu, int M, int E, int H, int Hp,
-                                  const void* wd, void* y, hipStream_t s) {
+                                  const void* wd, void* y, const RowMaps& maps, hipStream_t s) {
   if (M == 0) return MOE_OK;
   return launch_fb_any<false, 256>(static_cast<const uint16_t*>(h), cu, M, E, Hp, H,
-                               static_cast<const uint16_t*>(wd), nullptr, static_cast<uint16_t*>(y), s);
+                                   static_cast<const uint16_t*>(wd), nullptr,
+                                   static_cast<uint16_t*>(y), maps, s);
 }
 
 }  // namespace moe

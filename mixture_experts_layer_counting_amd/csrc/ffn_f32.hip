@@ -3,7 +3,9 @@
 // Same operation and schedule as the bf16 kernels ("Mixture of Kittens", Step 1: expert =
 // Down(SwiGLU(Up x, Gate x)); "Distributed expert parallelism", "Grouped expert
 // computation"): a persistent loop over 64x64 output tiles of every expert's row group,
-// 16-deep K steps staged in LDS, 4x4 outputs per thread, any H / Hp (edges masked).
+// 16-deep K steps staged in LDS, 4x4 outputs per thread, any H / Hp (edges masked). The
+// optional row maps gather A rows by token index and scatter row_w * y into an fp32
+// accumulator, as in the bf16 kernels.
 #include "moe_common.h"
 #include "tile_sched.h"
 
@@ -18,12 +20,14 @@ constexpr int FF_MAX_E = 512;  // 2 * threads
 template <bool GATED>
 __global__ __launch_bounds__(FF_THREADS) void ffn_f32_kernel(
     const float* __restrict__ A, const int* __restrict__ cu, int M, int E, int Kd, int N,
-    const float* __restrict__ B0, const float* __restrict__ B1, float* __restrict__ C) {
+    const float* __restrict__ B0, const float* __restrict__ B1, float* __restrict__ C,
+    RowMaps maps) {
   constexpr int NB = GATED ? 2 : 1;
   __shared__ int tstart[FF_MAX_E + 1];
   __shared__ int wsum[FF_THREADS / 64];
   __shared__ float sA[FF_BK][FF_BM + 1];
   __shared__ float sB[NB][FF_BK][FF_BN];
+  __shared__ int sRow[FF_BM];  // source row of A for each tile row
   const int tid = threadIdx.x;
   const int ntn = (N + FF_BN - 1) / FF_BN;
   const int total = build_tile_prefix<FF_BM, FF_THREADS>(cu, E, ntn, tstart, wsum);
@@ -39,6 +43,10 @@ __global__ __launch_bounds__(FF_THREADS) void ffn_f32_kernel(
     const int n0 = ntile * FF_BN;
     const float* W0 = B0 + (size_t)e * Kd * N;
     const float* W1 = GATED ? B1 + (size_t)e * Kd * N : nullptr;
+    __syncthreads();  // previous tile's readers of sRow are done
+    for (int r = tid; r < FF_BM; r += FF_THREADS)
+      sRow[r] = r < rows_valid ? (maps.a_src ? maps.a_src[row0 + r] / maps.a_k : row0 + r) : 0;
+    __syncthreads();
     float acc[NB][4][4];
     for (int b = 0; b < NB; ++b)
       for (int i = 0; i < 4; ++i)
@@ -46,7 +54,7 @@ __global__ __launch_bounds__(FF_THREADS) void ffn_f32_kernel(
     for (int k0 = 0; k0 < Kd; k0 += FF_BK) {
       for (int q = tid; q < FF_BM * FF_BK; q += FF_THREADS) {
         const int r = q / FF_BK, k = q % FF_BK;
-        sA[k][r] = (r < rows_valid && k0 + k < Kd) ? A[(size_t)(row0 + r) * Kd + k0 + k] : 0.f;
+        sA[k][r] = (r < rows_valid && k0 + k < Kd) ? A[(size_t)sRow[r] * Kd + k0 + k] : 0.f;
       }
       for (int q = tid; q < FF_BK * FF_BN; q += FF_THREADS) {
         const int k = q / FF_BN, n = q % FF_BN;
@@ -77,27 +85,31 @@ __global__ __launch_bounds__(FF_THREADS) void ffn_f32_kernel(
           v = silu_f32(acc[0][i][j]) * acc[1][i][j];
         else
           v = acc[0][i][j];
-        C[(size_t)(row0 + r) * N + n] = v;
+        if (!GATED && maps.s_acc)
+          unsafeAtomicAdd(maps.s_acc + (size_t)(maps.s_src[row0 + r] / maps.s_k) * N + n, maps.s_w[row0 + r] * v);
+        else
+          C[(size_t)(row0 + r) * N + n] = v;
       }
     }
   }
 }
 
-moe_status_t launch_ffn_gate_up_f32(const void* x_perm, const int* cu, int M, int E, int H, int Hp,
-                                    const void* wg, const void* wu, void* h, hipStream_t s) {
+moe_status_t launch_ffn_gate_up_f32(const void* a, const int* cu, int M, int E, int H, int Hp,
+                                    const void* wg, const void* wu, void* h, const RowMaps& maps,
+                                    hipStream_t s) {
   if (M == 0) return MOE_OK;
   ffn_f32_kernel<true><<<device_cu_count(), FF_THREADS, 0, s>>>(
-      static_cast<const float*>(x_perm), cu, M, E, H, Hp, static_cast<const float*>(wg),
-      static_cast<const float*>(wu), static_cast<float*>(h));
+      static_cast<const float*>(a), cu, M, E, H, Hp, static_cast<const float*>(wg),
+      static_cast<const float*>(wu), static_cast<float*>(h), maps);
   return launch_status();
 }
 
 moe_status_t launch_ffn_down_f32(const void* h, const int* cu, int M, int E, int H, int Hp,
-                                 const void* wd, void* y, hipStream_t s) {
+                                 const void* wd, void* y, const RowMaps& maps, hipStream_t s) {
   if (M == 0) return MOE_OK;
   ffn_f32_kernel<false><<<device_cu_count(), FF_THREADS, 0, s>>>(
       static_cast<const float*>(h), cu, M, E, Hp, H, static_cast<const float*>(wd), nullptr,
-      static_cast<float*>(y));
+      static_cast<float*>(y), maps);
   return launch_status();
 }
 

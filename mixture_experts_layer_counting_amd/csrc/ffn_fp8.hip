@@ -26,7 +26,10 @@
 // contiguous runs; they are staged in LDS with the tile data by the same direct loads, and all
 // of a stage's loads complete under one explicit wait. As in the bf16 kernels, a wave's two
 // 32-row blocks are rows wm*32 + [0,32) and 128 + wm*32 + [0,32), blocks wholly past the
-// group's rows skip their MFMAs, and the A descriptor ends at the group's last row.
+// group's rows skip their MFMAs, and rows past the group's last row load as zeros from past
+// the A descriptor's range. The optional row maps (gathering A rows and their scales from
+// the token matrix x [T, H] with x_sf [T, H/128]; scattering row_w * y into an fp32
+// accumulator) work as in the bf16 kernels.
 #include "moe_common.h"
 #include "tile_sched.h"
 
@@ -92,13 +95,14 @@ __device__ __forceinline__ void f8_dma16(i32x4_t rsrc_in, uint32_t lds_base, int
 }
 
 // 4-byte variant: lane l writes LDS base + 4 l.
-__device__ __forceinline__ void f8_dma4(i32x4_t rsrc_in, uint32_t lds_base, int voff) {
+__device__ __forceinline__ void f8_dma4(i32x4_t rsrc_in, uint32_t lds_base, int voff, int soff) {
   i32x4_t rsrc;
 #pragma unroll
   for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc_in[i]);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
                :
-               : "s"(__builtin_amdgcn_readfirstlane((int)lds_base)), "v"(voff), "s"(rsrc)
+               : "s"(__builtin_amdgcn_readfirstlane((int)lds_base)), "v"(voff), "s"(rsrc),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
                : "memory", "m0");
 }
 
@@ -128,12 +132,13 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return sgn | code;
 }
 
-template <bool GATED, int BN>
+// MAPPED: gate/up gathers its A rows and scales, down scatters (compile-time, as in bf16)
+template <bool GATED, int BN, bool MAPPED>
 __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ A_sf, const int* __restrict__ cu,
     int M, int E, int Kd, int N, const uint8_t* __restrict__ B0, const uint8_t* __restrict__ B0_sf,
     const uint8_t* __restrict__ B1, const uint8_t* __restrict__ B1_sf, uint8_t* __restrict__ C8,
-    float* __restrict__ C8_sf, uint16_t* __restrict__ C16) {
+    float* __restrict__ C8_sf, uint16_t* __restrict__ C16, RowMaps maps) {
   using CF = F8Cfg<GATED, BN>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int* tstart = reinterpret_cast<int*>(smem + F8_NS * CF::STAGE);
@@ -155,12 +160,15 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
 
   // global -> LDS coordinates. A wave load j (= wave + 8 i) covers rows 8j..8j+7 (128 B each):
   // lane -> row 8j + lane/8, slot lane%8 holds chunk slot ^ ((row/2) % 8).
-  int a_voff[CF::A_LD];
+  // (when gathering, the row part of a_voff is replaced per tile by the source row's offset)
+  int a_voff[CF::A_LD], a_row[CF::A_LD];
 #pragma unroll
   for (int i = 0; i < CF::A_LD; ++i) {
     const int r = (wave + 8 * i) * 8 + (lane >> 3);
+    a_row[i] = r;
     a_voff[i] = r * Kd + (((lane & 7) ^ ((r >> 1) & 7)) << 4);
   }
+  const int nsf = Kd / 128;  // activation scale blocks per row
   // B wave load j covers columns 16j'..16j'+15 (64 B each) of matrix j / (B_BYTES/1024):
   // lane -> column lane/4, slot lane%4 holds chunk slot ^ ((col/4) % 4).
   int b_voff[CF::B_LD];
@@ -201,8 +209,25 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     const int rows_valid = min(F8_BM, rows_e - mtile * F8_BM);
     const int n0 = ntile * BN;
 
-    // rows [row0, row0 + rows_valid) only; rows_valid * Kd < 2^31 by the host checks
-    const i32x4_t rA = f8_rsrc(A + (size_t)row0 * Kd, (uint32_t)rows_valid * (uint32_t)Kd);
+    // A rows of this tile (see the bf16 kernels): rows past rows_valid load past the range.
+    // The activation-scale load of waves 0-3 covers tile rows 64 wave + lane.
+    i32x4_t rA;
+    int a_ld_off[CF::A_LD];
+    int sc_voff = 0;
+    const int sc_row = (wave & 3) * 64 + lane;
+    if constexpr (GATED && MAPPED) {
+      rA = f8_rsrc(A, (uint32_t)maps.a_rows * (uint32_t)Kd);
+#pragma unroll
+      for (int i = 0; i < CF::A_LD; ++i)
+        a_ld_off[i] = a_row[i] < rows_valid ? (maps.a_src[row0 + a_row[i]] / maps.a_k - a_row[i]) * Kd + a_voff[i]
+                                         : (int)0x80000000u;
+      sc_voff = sc_row < rows_valid ? (maps.a_src[row0 + sc_row] / maps.a_k) * nsf * 4 : (int)0x80000000u;
+    } else {
+      rA = f8_rsrc(A + (size_t)row0 * Kd, (uint32_t)rows_valid * (uint32_t)Kd);
+#pragma unroll
+      for (int i = 0; i < CF::A_LD; ++i) a_ld_off[i] = a_voff[i];
+      sc_voff = (row0 + sc_row) * 4;
+    }
     const int nmt = __builtin_amdgcn_readfirstlane((wm * 32 < rows_valid) + (128 + wm * 32 < rows_valid));
     const size_t wbase = ((size_t)e * N + n0) * kbytes;
     const uint32_t b_rem = (uint32_t)((size_t)(N - n0) * kbytes);
@@ -211,7 +236,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     auto issue = [&](int kt) {
       const uint32_t so = smem_lds + (uint32_t)((kt % F8_NS) * CF::STAGE);
 #pragma unroll
-      for (int i = 0; i < CF::A_LD; ++i) f8_dma16(rA, so + (wave + 8 * i) * 1024, a_voff[i], kt * F8_BK);
+      for (int i = 0; i < CF::A_LD; ++i) f8_dma16(rA, so + (wave + 8 * i) * 1024, a_ld_off[i], kt * F8_BK);
 #pragma unroll
       for (int i = 0; i < CF::B_LD; ++i) {
         const int j = wave + 8 * i;
@@ -219,9 +244,13 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
         f8_dma16(second ? rB1 : rB0, so + CF::A_BYTES + j * 1024, b_voff[i], kt * (F8_BK / 2));
       }
       if (wave < 4) {
-        // activation scales of block kt: rows row0 + 64 wave + lane; rows >= M read as zero
-        f8_dma4(f8_rsrc(A_sf + (size_t)kt * M, (uint32_t)M * 4u), so + CF::SF_A + wave * 256,
-                (row0 + wave * 64 + lane) * 4);
+        // activation scales of block kt for tile rows 64 wave + lane. Plain: block-major
+        // [Kd/128][M], rows >= M read as zero. Gathered: x_sf [a_rows][Kd/128] of the row's token.
+        if constexpr (GATED && MAPPED)
+          f8_dma4(f8_rsrc(A_sf, (uint32_t)maps.a_rows * (uint32_t)nsf * 4u), so + CF::SF_A + wave * 256,
+                  sc_voff, kt * 4);
+        else
+          f8_dma4(f8_rsrc(A_sf + (size_t)kt * M, (uint32_t)M * 4u), so + CF::SF_A + wave * 256, sc_voff, 0);
       } else {
         // weight scales of k-blocks 4kt..4kt+3, LDS [nb][kb][BN]: load j covers bytes
         // 256 j .. 256 j + 255 of that block, i.e. matrix nb = j*256 / (4 BN), k-block rows of BN
@@ -232,7 +261,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
         const int col = byte % BN;
         const uint8_t* sfb = (GATED && nb) ? B1_sf : B0_sf;
         f8_dma4(f8_rsrc(sfb + ((size_t)e * ksf_b + 4 * (size_t)kt) * N, (uint32_t)N * 4u),
-                so + CF::SF_B + j * 256, kb * N + n0 + col);
+                so + CF::SF_B + j * 256, kb * N + n0 + col, 0);
       }
     };
     f32x16_t acc[CF::NB][CF::MT][CF::NT];
@@ -354,6 +383,20 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
             if (wn == 0 && (lane & 31) == 0) C8_sf[(size_t)(n0 / 128) * M + ro] = s;  // [N/128][M]
           }
         }
+    } else if constexpr (MAPPED) {
+#pragma unroll
+      for (int mt = 0; mt < CF::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3);
+          if (r < rows_valid) {
+            const int gr = row0 + r;
+            float* dst = maps.s_acc + (size_t)(maps.s_src[gr] / maps.s_k) * N + n0 + wn * CF::WN + (lane & 31);
+            const float w = maps.s_w[gr];
+#pragma unroll
+            for (int nt = 0; nt < CF::NT; ++nt) unsafeAtomicAdd(dst + nt * 32, w * acc[0][mt][nt][i]);
+          }
+        }
     } else {
 #pragma unroll
       for (int mt = 0; mt < CF::MT; ++mt)
@@ -370,41 +413,52 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
   }
 }
 
-template <bool GATED, int BN>
-static moe_status_t launch_f8(const uint8_t* A, const float* A_sf, const int* cu, int M, int E,
+template <bool GATED, int BN, bool MAPPED>
+static moe_status_t launch_f8_k(const uint8_t* A, const float* A_sf, const int* cu, int M, int E,
                               int Kd, int N, const uint8_t* B0, const uint8_t* B0_sf,
                               const uint8_t* B1, const uint8_t* B1_sf, uint8_t* C8, float* C8_sf,
-                              uint16_t* C16, hipStream_t s) {
+                              uint16_t* C16, const RowMaps& maps, hipStream_t s) {
   using CF = F8Cfg<GATED, BN>;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_fp8_kernel<GATED, BN>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_fp8_kernel<GATED, BN, MAPPED>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS_BYTES) != hipSuccess)
       return MOE_EHIP;
     attr_set = true;
   }
-  ffn_fp8_kernel<GATED, BN><<<device_cu_count(), F8_THREADS, CF::LDS_BYTES, s>>>(
-      A, A_sf, cu, M, E, Kd, N, B0, B0_sf, B1, B1_sf, C8, C8_sf, C16);
+  ffn_fp8_kernel<GATED, BN, MAPPED><<<device_cu_count(), F8_THREADS, CF::LDS_BYTES, s>>>(
+      A, A_sf, cu, M, E, Kd, N, B0, B0_sf, B1, B1_sf, C8, C8_sf, C16, maps);
   return launch_status();
+}
+
+template <bool GATED, int BN>
+static moe_status_t launch_f8(const uint8_t* A, const float* A_sf, const int* cu, int M, int E,
+                              int Kd, int N, const uint8_t* B0, const uint8_t* B0_sf,
+                              const uint8_t* B1, const uint8_t* B1_sf, uint8_t* C8, float* C8_sf,
+                              uint16_t* C16, const RowMaps& maps, hipStream_t s) {
+  const bool mapped = GATED ? maps.a_src != nullptr : maps.s_acc != nullptr;
+  if (mapped)
+    return launch_f8_k<GATED, BN, true>(A, A_sf, cu, M, E, Kd, N, B0, B0_sf, B1, B1_sf, C8, C8_sf, C16, maps, s);
+  return launch_f8_k<GATED, BN, false>(A, A_sf, cu, M, E, Kd, N, B0, B0_sf, B1, B1_sf, C8, C8_sf, C16, maps, s);
 }
 
 moe_status_t launch_ffn_gate_up_fp8(const void* x_perm, const float* x_sf, const int* cu, int M,
                                     int E, int H, int Hp, const void* wg, const uint8_t* sg,
                                     const void* wu, const uint8_t* su, void* h, float* h_sf,
-                                    hipStream_t s) {
+                                    const RowMaps& maps, hipStream_t s) {
   if (M == 0) return MOE_OK;
   return launch_f8<true, 128>(static_cast<const uint8_t*>(x_perm), x_sf, cu, M, E, H, Hp,
                               static_cast<const uint8_t*>(wg), sg, static_cast<const uint8_t*>(wu),
-                              su, static_cast<uint8_t*>(h), h_sf, nullptr, s);
+                              su, static_cast<uint8_t*>(h), h_sf, nullptr, maps, s);
 }
 
 moe_status_t launch_ffn_down_fp8(const void* h, const float* h_sf, const int* cu, int M, int E,
                                  int H, int Hp, const void* wd, const uint8_t* sd, void* y,
-                                 hipStream_t s) {
+                                 const RowMaps& maps, hipStream_t s) {
   if (M == 0) return MOE_OK;
   return launch_f8<false, 256>(static_cast<const uint8_t*>(h), h_sf, cu, M, E, Hp, H,
                                static_cast<const uint8_t*>(wd), sd, nullptr, nullptr, nullptr,
-                               nullptr, static_cast<uint16_t*>(y), s);
+                               nullptr, static_cast<uint16_t*>(y), maps, s);
 }
 
 }  // namespace moe

@@ -21,18 +21,20 @@ moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes, co
 moe_status_t launch_combine(const void*, moe_dtype_t, const int*, const float*, int, int, int,
                             void*, moe_dtype_t, hipStream_t);
 moe_status_t launch_ffn_gate_up_bf16(const void*, const int*, int, int, int, int, const void*,
-                                     const void*, void*, hipStream_t);
+                                     const void*, void*, const RowMaps&, hipStream_t);
 moe_status_t launch_ffn_down_bf16(const void*, const int*, int, int, int, int, const void*, void*,
-                                  hipStream_t);
+                                  const RowMaps&, hipStream_t);
 moe_status_t launch_ffn_gate_up_fp8(const void*, const float*, const int*, int, int, int, int,
                                     const void*, const uint8_t*, const void*, const uint8_t*, void*,
-                                    float*, hipStream_t);
+                                    float*, const RowMaps&, hipStream_t);
 moe_status_t launch_ffn_down_fp8(const void*, const float*, const int*, int, int, int, int,
-                                 const void*, const uint8_t*, void*, hipStream_t);
+                                 const void*, const uint8_t*, void*, const RowMaps&, hipStream_t);
 moe_status_t launch_ffn_gate_up_f32(const void*, const int*, int, int, int, int, const void*,
-                                    const void*, void*, hipStream_t);
+                                    const void*, void*, const RowMaps&, hipStream_t);
 moe_status_t launch_ffn_down_f32(const void*, const int*, int, int, int, int, const void*, void*,
-                                 hipStream_t);
+                                 const RowMaps&, hipStream_t);
+moe_status_t launch_acc_zero(float* acc, size_t n, hipStream_t s);
+moe_status_t launch_acc_store(const float* acc, size_t n, void* out, moe_dtype_t out_dtype, hipStream_t s);
 
 int device_cu_count() {
   static int cache[64] = {0};
@@ -144,11 +146,12 @@ moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t act,
   const int eb = act_bytes(act);
   if (eb == 0) return MOE_EUNSUPPORTED;
   if (!counts || !cu_seqlens) return MOE_EINVAL;
-  if (T > 0 && (!x || !topk_idx || !pos || !row_src || !x_perm)) return MOE_EINVAL;
+  if (T > 0 && (!topk_idx || !pos || !row_src)) return MOE_EINVAL;
+  if (T > 0 && x_perm && !x) return MOE_EINVAL;
   if (row_w && T > 0 && !topk_w) return MOE_EINVAL;
   if (act == MOE_FP8_E4M3) {
     if (H % 128) return MOE_EUNSUPPORTED;
-    if (T > 0 && (!x_sf || !x_perm_sf)) return MOE_EINVAL;
+    if (T > 0 && x_perm && (!x_sf || !x_perm_sf)) return MOE_EINVAL;
   }
   if ((int64_t)T * K > std::numeric_limits<int32_t>::max() / 2) return MOE_EUNSUPPORTED;
   const size_t need = permute_ws_bytes(T, E, K);
@@ -156,10 +159,10 @@ moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t act,
   poison(ws, ws_bytes, stream);
   const bool validate = env_flag("MOE_VALIDATE");
   int* err = nullptr;
-  moe_status_t st = launch_permute(x, act == MOE_FP8_E4M3 ? x_sf : nullptr, eb, topk_idx, topk_w,
-                                   T, H, E, K, counts, cu_seqlens, pos, row_src, row_w, x_perm,
-                                   act == MOE_FP8_E4M3 ? x_perm_sf : nullptr, ws, validate, &err,
-                                   stream);
+  const bool sf = act == MOE_FP8_E4M3 && x_perm;
+  moe_status_t st = launch_permute(x, sf ? x_sf : nullptr, eb, topk_idx, topk_w, T, H, E, K, counts,
+                                   cu_seqlens, pos, row_src, row_w, x_perm, sf ? x_perm_sf : nullptr,
+                                   ws, validate, &err, stream);
   if (st != MOE_OK || !validate) return st;
   int h_err = 0;
   if (hipMemcpyAsync(&h_err, err, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess ||
@@ -182,10 +185,39 @@ moe_status_t moe_ffn_gate_up(const void* x_perm, const float* x_perm_sf, moe_dty
   if (p == PATH_FP8_MXFP4) {
     if (M > 0 && (!x_perm_sf || !sf_gate || !sf_up || !h_sf)) return MOE_EINVAL;
     return launch_ffn_gate_up_fp8(x_perm, x_perm_sf, cu_seqlens, M, E, H, Hp, w_gate, sf_gate, w_up,
-                                  sf_up, h, h_sf, stream);
+                                  sf_up, h, h_sf, RowMaps{}, stream);
   }
-  if (p == PATH_F32) return launch_ffn_gate_up_f32(x_perm, cu_seqlens, M, E, H, Hp, w_gate, w_up, h, stream);
-  return launch_ffn_gate_up_bf16(x_perm, cu_seqlens, M, E, H, Hp, w_gate, w_up, h, stream);
+  if (p == PATH_F32)
+    return launch_ffn_gate_up_f32(x_perm, cu_seqlens, M, E, H, Hp, w_gate, w_up, h, RowMaps{}, stream);
+  return launch_ffn_gate_up_bf16(x_perm, cu_seqlens, M, E, H, Hp, w_gate, w_up, h, RowMaps{}, stream);
+}
+
+moe_status_t moe_ffn_gate_up_gather(const void* x, const float* x_sf, moe_dtype_t act,
+                                    const int32_t* row_src, int32_t T, int32_t K,
+                                    const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
+                                    int32_t Hp, const void* w_gate, const void* w_up,
+                                    const uint8_t* sf_gate, const uint8_t* sf_up, moe_dtype_t wgt,
+                                    void* h, float* h_sf, hipStream_t stream) {
+  const Path p = ffn_path(act, wgt);
+  if (p == PATH_NONE) return MOE_EUNSUPPORTED;
+  if (T < 0 || K < 1 || (int64_t)M > (int64_t)T * K) return MOE_EINVAL;
+  moe_status_t st = check_ffn_dims(p, M, E, H, Hp, true);
+  if (st != MOE_OK) return st;
+  // the gathered rows are addressed with 32-bit byte offsets into x
+  if ((int64_t)T * H * act_bytes(act) >= (1ll << 31)) return MOE_EUNSUPPORTED;
+  if (!cu_seqlens) return MOE_EINVAL;
+  if (M > 0 && (!x || !row_src || !w_gate || !w_up || !h)) return MOE_EINVAL;
+  RowMaps maps;
+  maps.a_src = row_src;
+  maps.a_k = K;
+  maps.a_rows = T;
+  if (p == PATH_FP8_MXFP4) {
+    if (M > 0 && (!x_sf || !sf_gate || !sf_up || !h_sf)) return MOE_EINVAL;
+    return launch_ffn_gate_up_fp8(x, x_sf, cu_seqlens, M, E, H, Hp, w_gate, sf_gate, w_up, sf_up, h,
+                                  h_sf, maps, stream);
+  }
+  if (p == PATH_F32) return launch_ffn_gate_up_f32(x, cu_seqlens, M, E, H, Hp, w_gate, w_up, h, maps, stream);
+  return launch_ffn_gate_up_bf16(x, cu_seqlens, M, E, H, Hp, w_gate, w_up, h, maps, stream);
 }
 
 moe_status_t moe_ffn_down(const void* h, const float* h_sf, moe_dtype_t h_dtype,
@@ -200,10 +232,36 @@ moe_status_t moe_ffn_down(const void* h, const float* h_sf, moe_dtype_t h_dtype,
   if (M > 0 && (!h || !w_down || !y_rows)) return MOE_EINVAL;
   if (p == PATH_FP8_MXFP4) {
     if (M > 0 && (!h_sf || !sf_down)) return MOE_EINVAL;
-    return launch_ffn_down_fp8(h, h_sf, cu_seqlens, M, E, H, Hp, w_down, sf_down, y_rows, stream);
+    return launch_ffn_down_fp8(h, h_sf, cu_seqlens, M, E, H, Hp, w_down, sf_down, y_rows, RowMaps{},
+                               stream);
   }
-  if (p == PATH_F32) return launch_ffn_down_f32(h, cu_seqlens, M, E, H, Hp, w_down, y_rows, stream);
-  return launch_ffn_down_bf16(h, cu_seqlens, M, E, H, Hp, w_down, y_rows, stream);
+  if (p == PATH_F32) return launch_ffn_down_f32(h, cu_seqlens, M, E, H, Hp, w_down, y_rows, RowMaps{}, stream);
+  return launch_ffn_down_bf16(h, cu_seqlens, M, E, H, Hp, w_down, y_rows, RowMaps{}, stream);
+}
+
+moe_status_t moe_ffn_down_scatter(const void* h, const float* h_sf, moe_dtype_t h_dtype,
+                                  const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
+                                  int32_t Hp, const void* w_down, const uint8_t* sf_down,
+                                  moe_dtype_t wgt, const int32_t* row_src, const float* row_w,
+                                  int32_t T, int32_t K, float* acc, hipStream_t stream) {
+  const Path p = ffn_path(h_dtype, wgt);
+  if (p == PATH_NONE) return MOE_EUNSUPPORTED;
+  if (T < 0 || K < 1 || (int64_t)M > (int64_t)T * K) return MOE_EINVAL;
+  moe_status_t st = check_ffn_dims(p, M, E, H, Hp, false);
+  if (st != MOE_OK) return st;
+  if (!cu_seqlens) return MOE_EINVAL;
+  if (M > 0 && (!h || !w_down || !row_src || !row_w || !acc)) return MOE_EINVAL;
+  RowMaps maps;
+  maps.s_src = row_src;
+  maps.s_w = row_w;
+  maps.s_k = K;
+  maps.s_acc = acc;
+  if (p == PATH_FP8_MXFP4) {
+    if (M > 0 && (!h_sf || !sf_down)) return MOE_EINVAL;
+    return launch_ffn_down_fp8(h, h_sf, cu_seqlens, M, E, H, Hp, w_down, sf_down, nullptr, maps, stream);
+  }
+  if (p == PATH_F32) return launch_ffn_down_f32(h, cu_seqlens, M, E, H, Hp, w_down, nullptr, maps, stream);
+  return launch_ffn_down_bf16(h, cu_seqlens, M, E, H, Hp, w_down, nullptr, maps, stream);
 }
 
 size_t moe_grouped_ffn_workspace_bytes(int32_t M, int32_t Hp, moe_dtype_t act, moe_dtype_t wgt) {
@@ -259,6 +317,13 @@ enum {
   WS_X_PERM_SF, WS_H, WS_H_SF, WS_Y, WS_PERM_SCRATCH, WS_ACC, WS_N
 };
 
+// Whether moe_layer_forward writes the permuted copy x_perm (and gate/up reads it) or gate/up
+// gathers its rows from x through row_src. Gathering is the default; MOE_LAYER_XPERM=1 forces
+// the copy, and so does an x too large for 32-bit row offsets.
+static bool layer_materializes(const moe_layer_desc_t* d) {
+  return env_flag("MOE_LAYER_XPERM") || (int64_t)d->T * d->H * act_bytes(d->act) >= (1ll << 31);
+}
+
 static moe_status_t layer_layout(const moe_layer_desc_t* d, size_t* off, size_t* total) {
   if (!d) return MOE_EINVAL;
   if (d->T < 0 || d->H < 1 || d->Hp < 1 || d->E < 1 || d->K < 1 || d->K > d->E) return MOE_EINVAL;
@@ -267,26 +332,28 @@ static moe_status_t layer_layout(const moe_layer_desc_t* d, size_t* off, size_t*
   if (d->combine != MOE_COMBINE_GATHER && d->combine != MOE_COMBINE_SCATTER_ATOMIC) return MOE_EINVAL;
   const size_t T = d->T, H = d->H, Hp = d->Hp, E = d->E, K = d->K, M = T * K;
   const size_t ab = act_bytes(d->act), hb = act_bytes(h_dtype_of(p)), yb = act_bytes(y_dtype_of(p));
+  const bool mat = layer_materializes(d), scatter = d->combine == MOE_COMBINE_SCATTER_ATOMIC;
+  const bool fp8 = p == PATH_FP8_MXFP4;
   size_t sz[WS_N] = {0};
-  sz[WS_TOPK_IDX] = M * 4;
-  sz[WS_TOPK_W] = M * 4;
-  sz[WS_COUNTS] = E * 4;
-  sz[WS_CU] = (E + 1) * 4;
-  sz[WS_POS] = M * 4;
-  sz[WS_ROW_SRC] = M * 4;
-  sz[WS_ROW_W] = M * 4;
-  sz[WS_X_PERM] = M * H * ab;
-  sz[WS_X_PERM_SF] = p == PATH_FP8_MXFP4 ? M * (H / 128) * 4 : 0;
-  sz[WS_H] = M * Hp * hb;
-  sz[WS_H_SF] = p == PATH_FP8_MXFP4 ? M * (Hp / 128) * 4 : 0;
-  sz[WS_Y] = M * H * yb;
-  sz[WS_PERM_SCRATCH] = permute_ws_bytes(d->T, d->E, d->K);
-  sz[WS_ACC] = d->combine == MOE_COMBINE_SCATTER_ATOMIC ? T * H * 4 : 0;
+  bool used[WS_N] = {false};
+  auto want = [&](int i, size_t bytes) { sz[i] = bytes; used[i] = true; };
+  want(WS_TOPK_IDX, M * 4);
+  want(WS_TOPK_W, M * 4);
+  want(WS_COUNTS, E * 4);
+  want(WS_CU, (E + 1) * 4);
+  want(WS_POS, M * 4);
+  want(WS_ROW_SRC, M * 4);
+  if (scatter) want(WS_ROW_W, M * 4);
+  if (mat) want(WS_X_PERM, M * H * ab);
+  if (mat && fp8) want(WS_X_PERM_SF, M * (H / 128) * 4);
+  want(WS_H, M * Hp * hb);
+  if (fp8) want(WS_H_SF, M * (Hp / 128) * 4);
+  if (!scatter) want(WS_Y, M * H * yb);
+  want(WS_PERM_SCRATCH, permute_ws_bytes(d->T, d->E, d->K));
+  if (scatter && d->out != MOE_F32) want(WS_ACC, T * H * 4);  // fp32 out accumulates in place
   size_t o = 0;
   for (int i = 0; i < WS_N; ++i) {
-    const bool used = sz[i] > 0 || i == WS_TOPK_IDX || i == WS_TOPK_W || i == WS_POS ||
-                      i == WS_ROW_SRC || i == WS_ROW_W || i == WS_X_PERM || i == WS_H || i == WS_Y;
-    if (!used) {
+    if (!used[i]) {
       off[i] = SIZE_MAX;
       continue;
     }
@@ -325,7 +392,6 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const void* x, const f
   st = check_ffn_dims(p, (int64_t)d->T * d->K, d->E, d->H, d->Hp, true);
   if (st == MOE_OK) st = check_ffn_dims(p, (int64_t)d->T * d->K, d->E, d->H, d->Hp, false);
   if (st != MOE_OK) return st;
-  if (d->combine != MOE_COMBINE_GATHER) return MOE_EUNSUPPORTED;
   if (d->T > 0 && (!x || !out || !w_gate || !w_up || !w_down)) return MOE_EINVAL;
   if (d->T > 0 && !logits && (!topk_idx_in || !topk_w_in)) return MOE_EINVAL;
   poison(ws, ws_bytes, stream);
@@ -345,19 +411,37 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const void* x, const f
   int32_t* cu = static_cast<int32_t*>(at(WS_CU));
   int32_t* pos = static_cast<int32_t*>(at(WS_POS));
   int32_t* row_src = static_cast<int32_t*>(at(WS_ROW_SRC));
+  float* row_w = static_cast<float*>(at(WS_ROW_W));
+  float* h_sf = static_cast<float*>(at(WS_H_SF));
+  const bool mat = layer_materializes(d), scatter = d->combine == MOE_COMBINE_SCATTER_ATOMIC;
   const size_t perm_ws = permute_ws_bytes(T, E, K);
-  st = moe_permute(x, x_sf, d->act, topk_idx, topk_w, T, H, E, K, counts, cu, pos, row_src, nullptr,
+  st = moe_permute(x, x_sf, d->act, topk_idx, topk_w, T, H, E, K, counts, cu, pos, row_src, row_w,
                    at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)), at(WS_PERM_SCRATCH), perm_ws,
                    stream);
   if (st != MOE_OK) return st;
-  st = moe_ffn_gate_up(at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)), d->act, cu, M, E, H, Hp,
-                       w_gate, w_up, sf_gate, sf_up, d->wgt, at(WS_H), static_cast<float*>(at(WS_H_SF)),
-                       stream);
+  if (mat)
+    st = moe_ffn_gate_up(at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)), d->act, cu, M, E, H, Hp,
+                         w_gate, w_up, sf_gate, sf_up, d->wgt, at(WS_H), h_sf, stream);
+  else
+    st = moe_ffn_gate_up_gather(x, x_sf, d->act, row_src, T, K, cu, M, E, H, Hp, w_gate, w_up, sf_gate,
+                                sf_up, d->wgt, at(WS_H), h_sf, stream);
   if (st != MOE_OK) return st;
-  st = moe_ffn_down(at(WS_H), static_cast<float*>(at(WS_H_SF)), h_dtype_of(p), cu, M, E, H, Hp, w_down,
-                    sf_down, d->wgt, at(WS_Y), y_dtype_of(p), stream);
+  if (!scatter) {
+    st = moe_ffn_down(at(WS_H), h_sf, h_dtype_of(p), cu, M, E, H, Hp, w_down, sf_down, d->wgt, at(WS_Y),
+                      y_dtype_of(p), stream);
+    if (st != MOE_OK) return st;
+    return moe_combine(at(WS_Y), y_dtype_of(p), pos, topk_w, T, H, K, out, d->out, stream);
+  }
+  // weighted scatter-add fused into the down projection, into an fp32 accumulator
+  float* acc = d->out == MOE_F32 ? static_cast<float*>(out) : static_cast<float*>(at(WS_ACC));
+  const size_t n = (size_t)T * H;
+  if (n == 0) return MOE_OK;
+  st = launch_acc_zero(acc, n, stream);
   if (st != MOE_OK) return st;
-  return moe_combine(at(WS_Y), y_dtype_of(p), pos, topk_w, T, H, K, out, d->out, stream);
+  st = moe_ffn_down_scatter(at(WS_H), h_sf, h_dtype_of(p), cu, M, E, H, Hp, w_down, sf_down, d->wgt,
+                            row_src, row_w, T, K, acc, stream);
+  if (st != MOE_OK || d->out == MOE_F32) return st;
+  return launch_acc_store(acc, n, out, d->out, stream);
 }
 
 }  // extern "C"

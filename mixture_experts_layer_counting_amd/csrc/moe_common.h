@@ -34,6 +34,20 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 bool env_flag(const char* name);
 
+// Optional row maps of a grouped-FFN launch; null pointers select the plain layout.
+//  gather  (gate/up): A row of group row r is row a_src[r] / a_k of A, which has a_rows rows.
+//  scatter (down):    instead of storing y[r], add s_w[r] * y[r] to row s_src[r] / s_k of the
+//                     fp32 accumulator s_acc (fp32 atomics).
+struct RowMaps {
+  const int* a_src = nullptr;
+  int a_k = 1;
+  int a_rows = 0;
+  const int* s_src = nullptr;
+  const float* s_w = nullptr;
+  int s_k = 1;
+  float* s_acc = nullptr;
+};
+
 // ---- device helpers -----------------------------------------------------------------
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {

@@ -291,7 +291,7 @@ moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes,
   unsigned char* xp = static_cast<unsigned char*>(x_perm);
   permute_scatter_kernel<<<nblk, PERM_THREADS, 0, s>>>(topk_idx, topk_w, T, E, K, nch, counts, hist,
                                                        cu_seqlens, pos, row_src, row_w, key_bits, err);
-  if (T > 0) {
+  if (T > 0 && x_perm) {
     const bool a16 = (row_bytes % 16 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)x_perm % 16 == 0);
     const bool a4 = (row_bytes % 4 == 0) && ((uintptr_t)x % 4 == 0) && ((uintptr_t)x_perm % 4 == 0);
     if (a16)
@@ -301,7 +301,7 @@ moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes,
     else
       permute_copy_kernel<1><<<T, 256, 0, s>>>(xb, pos, K, xp, row_bytes);
   }
-  if (x_sf && T > 0) {
+  if (x_sf && x_perm_sf && T > 0) {
     const size_t n = (size_t)sf_per_row * T * K;
     const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
     permute_sf_kernel<<<blocks, 256, 0, s>>>(x_sf, row_src, cu_seqlens, E, K, T * K, sf_per_row, x_perm_sf);

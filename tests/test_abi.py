@@ -101,20 +101,52 @@ def test_layer_workspace_sizes_and_layout():
     d = moe.LayerDesc(8192, 7168, 2048, 384, 8, moe.MOE_BF16, moe.MOE_BF16, moe.MOE_BF16, 0)
     n = moe.moe_layer_workspace_bytes(d)
     M = 8192 * 8
-    big = M * 7168 * 2 * 2 + M * 2048 * 2          # x_perm + y_rows + h
+    big = M * 7168 * 2 + M * 2048 * 2              # y_rows + h (gate/up gathers from x)
     assert big < n < big + 8 * 2 ** 20
     lay = moe.moe_layer_workspace_layout(d)
     used = [v for v in lay.values() if v is not None]
     assert used == sorted(used) and all(v % 256 == 0 for v in used)
-    assert lay["x_perm_sf"] is None and lay["h_sf"] is None and lay["acc_f32"] is None
+    assert lay["x_perm"] is None and lay["x_perm_sf"] is None and lay["row_w"] is None
+    assert lay["h_sf"] is None and lay["acc_f32"] is None
     assert lay["y_rows"] + M * 7168 * 2 <= n
+    os.environ["MOE_LAYER_XPERM"] = "1"       # the materialised permuted copy
+    try:
+        n_mat = moe.moe_layer_workspace_bytes(d)
+        lay_mat = moe.moe_layer_workspace_layout(d)
+    finally:
+        del os.environ["MOE_LAYER_XPERM"]
+    assert lay_mat["x_perm"] is not None and big + M * 7168 * 2 < n_mat < big + M * 7168 * 2 + 8 * 2 ** 20
+    sc = moe.LayerDesc(8192, 7168, 2048, 384, 8, moe.MOE_BF16, moe.MOE_BF16, moe.MOE_BF16,
+                       moe.MOE_COMBINE_SCATTER_ATOMIC)
+    lay_sc = moe.moe_layer_workspace_layout(sc)
+    assert lay_sc["y_rows"] is None and lay_sc["row_w"] is not None and lay_sc["acc_f32"] is not None
+    assert moe.moe_layer_workspace_bytes(sc) < M * 2048 * 2 + 8192 * 7168 * 4 + 8 * 2 ** 20
+    sc32 = moe.LayerDesc(64, 128, 64, 8, 2, moe.MOE_F32, moe.MOE_F32, moe.MOE_F32, 1)
+    assert moe.moe_layer_workspace_layout(sc32)["acc_f32"] is None   # accumulates into out
     bad = moe.LayerDesc(8, 128, 64, 4, 5, moe.MOE_F32, moe.MOE_F32, moe.MOE_F32, 0)   # K > E
     assert moe.moe_layer_workspace_bytes(bad) == 0
     mixed = moe.LayerDesc(8, 128, 64, 4, 2, moe.MOE_BF16, moe.MOE_F32, moe.MOE_BF16, 0)
     assert moe.moe_layer_workspace_bytes(mixed) == 0
     fp8 = moe.LayerDesc(64, 256, 128, 4, 2, moe.MOE_FP8_E4M3, moe.MOE_MXFP4, moe.MOE_BF16, 0)
     lay8 = moe.moe_layer_workspace_layout(fp8)
-    assert lay8["x_perm_sf"] is not None and lay8["h_sf"] is not None
+    assert lay8["x_perm_sf"] is None and lay8["h_sf"] is not None
+
+
+def test_gather_and_scatter_argument_checks():
+    g = moe.moe_ffn_gate_up_gather
+    # (x, x_sf, act, row_src, T, K, cu, M, E, H, Hp, wg, wu, sfg, sfu, wgt, h, h_sf)
+    _expect(moe.MOE_EINVAL, g, 16, None, moe.MOE_BF16, 16, 4, 2, 16, 9, 4, 128, 128, 16, 16, None,
+            None, moe.MOE_BF16, 16, None, 0)                              # M > T*K
+    _expect(moe.MOE_EINVAL, g, 16, None, moe.MOE_BF16, None, 4, 2, 16, 8, 4, 128, 128, 16, 16, None,
+            None, moe.MOE_BF16, 16, None, 0)                              # NULL row_src
+    _expect(moe.MOE_EUNSUPPORTED, g, 16, None, moe.MOE_BF16, 16, 2 ** 20, 2, 16, 8, 4, 1024, 128, 16,
+            16, None, None, moe.MOE_BF16, 16, None, 0)                    # x past 2 GiB
+    d = moe.moe_ffn_down_scatter
+    # (h, h_sf, h_dtype, cu, M, E, H, Hp, wd, sfd, wgt, row_src, row_w, T, K, acc)
+    _expect(moe.MOE_EINVAL, d, 16, None, moe.MOE_BF16, 16, 8, 4, 256, 128, 16, None, moe.MOE_BF16,
+            16, 16, 4, 2, None, 0)                                        # NULL accumulator
+    _expect(moe.MOE_EUNSUPPORTED, d, 16, None, moe.MOE_BF16, 16, 8, 4, 128, 128, 16, None,
+            moe.MOE_BF16, 16, 16, 4, 2, 16, 0)                            # H % 256
 
 
 def test_layer_forward_rejects_small_workspace():

@@ -311,3 +311,124 @@ def test_small_fp8_mxfp4_layer(spec):
 def test_c5_full_size_sampled():
     say("c5 fp8 x mxfp4 E=384 maxvio=1, full size")
     sampled_check(gen.config("c5", device=DEV))
+
+
+# ----------------------------------------------------------------------------- row maps
+
+GATHER_CASES = [
+    ("f32", dict(T=333, H=200, Hp=72, E=9, K=3, routing="skew", beta=0.5)),
+    ("bf16", dict(T=600, H=512, Hp=256, E=32, K=6, routing="skew", beta=3.0)),
+    ("fp8", dict(T=300, H=512, Hp=256, E=12, K=3, routing="skew", beta=0.5)),
+]
+FMT = {"f32": ("f32", "f32"), "bf16": ("bf16", "bf16"), "fp8": ("mxfp4", "bf16")}
+
+
+def make_case(act, spec, cid):
+    wgt, out = FMT[act]
+    return gen.make(**spec, act=act, wgt=wgt, out=out, cid=cid, device=DEV)
+
+
+@pytest.mark.parametrize("act,spec", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+def test_gate_up_gather_is_bitwise_the_permuted_path(act, spec):
+    say(f"gate/up gathered from x vs from x_perm, {act} {spec}")
+    w = make_case(act, spec, 60)
+    r = run_steps(w)
+    M = w.T * w.K
+    from _gpu_run import DT, TORCH_DT, h_fmt
+    h2 = torch.empty_like(r["h"])
+    h2_sf = torch.empty_like(r["h_sf"]) if r["h_sf"] is not None else None
+    moe.moe_ffn_gate_up_gather(w.x, w.x_sf, DT[w.act], r["row_src"], w.T, w.K, r["cu_seqlens"], M, w.E,
+                               w.H, w.Hp, w.w_gate, w.w_up, w.sf_gate, w.sf_up, DT[w.wgt], h2, h2_sf)
+    torch.cuda.synchronize()
+    rows = int(host(r["cu_seqlens"])[-1])
+    assert np.array_equal(host(h2)[:rows], host(r["h"])[:rows])
+    if h2_sf is not None:
+        assert np.array_equal(host(h2_sf)[:, :rows], host(r["h_sf"])[:, :rows])
+
+
+@pytest.mark.parametrize("act,spec", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+def test_layer_with_and_without_x_perm_bitwise(act, spec):
+    say(f"layer: MOE_LAYER_XPERM=1 vs the gathered default, {act}")
+    w = make_case(act, spec, 61)
+    out_g, _, lay_g = run_layer(w)
+    os.environ["MOE_LAYER_XPERM"] = "1"
+    try:
+        out_m, _, lay_m = run_layer(w)
+    finally:
+        del os.environ["MOE_LAYER_XPERM"]
+    torch.cuda.synchronize()
+    assert lay_g["x_perm"] is None and lay_m["x_perm"] is not None
+    assert np.array_equal(host(out_g), host(out_m))
+
+
+def decode_out(w, t):
+    b = host(t)
+    return b.astype(np.float64) if w.out == "f32" else O.decode_bf16(b)
+
+
+@pytest.mark.parametrize("act,spec", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+def test_down_scatter_entry_point(act, spec):
+    say(f"moe_ffn_down_scatter into a zeroed fp32 accumulator, {act}")
+    w = make_case(act, spec, 62)
+    r = run_steps(w)
+    ref = oracle_layer(w)
+    from _gpu_run import DT, h_fmt
+    M = w.T * w.K
+    acc = torch.zeros((w.T, w.H), dtype=torch.float32, device=DEV)
+    moe.moe_ffn_down_scatter(r["h"], r["h_sf"], DT[h_fmt(w)], r["cu_seqlens"], M, w.E, w.H, w.Hp,
+                             w.w_down, w.sf_down, DT[w.wgt], r["row_src"], r["row_w"], w.T, w.K, acc)
+    torch.cuda.synchronize()
+    e = rel_err(host(acc).astype(np.float64), ref["out"])
+    # against the deterministic gather combine of the same y (before its bf16 rounding of y)
+    e_g = rel_err(host(acc).astype(np.float64), decode_out(w, r["out"]))
+    print(f"  acc rel err vs oracle {e:.3e}, vs gather combine {e_g:.3e}", flush=True)
+    assert e <= TOL[w.act]
+
+
+@pytest.mark.parametrize("act,spec", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
+def test_layer_scatter_combine(act, spec):
+    say(f"layer with MOE_COMBINE_SCATTER_ATOMIC, {act}")
+    w = make_case(act, spec, 63)
+    out, ws, lay = run_layer(w, combine=moe.MOE_COMBINE_SCATTER_ATOMIC)
+    torch.cuda.synchronize()
+    assert lay["y_rows"] is None and lay["row_w"] is not None
+    assert (lay["acc_f32"] is None) == (w.out == "f32")
+    ref = oracle_layer(w)
+    e = rel_err(decode_out(w, out), ref["out"])
+    print(f"  out rel err {e:.3e}", flush=True)
+    assert e <= TOL[w.act]
+
+
+def test_layer_scatter_combine_empty_experts_and_t0():
+    say("scatter combine: many empty experts, then T=0")
+    w = gen.make(T=97, H=256, Hp=128, E=40, K=2, routing="skew", beta=4.0, act="bf16", wgt="bf16",
+                 out="bf16", cid=64, device=DEV)
+    out, _, _ = run_layer(w, combine=moe.MOE_COMBINE_SCATTER_ATOMIC)
+    torch.cuda.synchronize()
+    assert rel_err(decode_out(w, out), oracle_layer(w)["out"]) <= TOL["bf16"]
+    w0 = gen.make(T=0, H=256, Hp=128, E=8, K=2, routing="normal", cid=64, device=DEV)
+    out0, _, _ = run_layer(w0, combine=moe.MOE_COMBINE_SCATTER_ATOMIC)
+    torch.cuda.synchronize()
+    assert out0.shape == (0, 256)
+
+
+def sampled_layer_check(w, combine, n_tokens=4):
+    """Full size through moe_layer_forward: out[t] for a few tokens from the oracle."""
+    out, ws, lay = run_layer(w, combine=combine)
+    torch.cuda.synchronize()
+    ref = oracle_routing(w)
+    tokens = sorted({0, 1, w.T // 2, w.T - 1})[:n_tokens]
+    want = oracle_tokens(w, tokens, ref)
+    o = decode_out(w, out)
+    errs = [rel_err(o[t], want[t]) for t in tokens]
+    print(f"  tokens {tokens} rel errs {[f'{e:.2e}' for e in errs]}", flush=True)
+    assert max(errs) <= TOL[w.act]
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("cfg", ["c3", "c5"])
+def test_full_size_layer_gather_and_scatter(cfg):
+    say(f"{cfg} full size through moe_layer_forward: gathered gate/up, both combines")
+    w = gen.config(cfg, device=DEV)
+    sampled_layer_check(w, moe.MOE_COMBINE_GATHER)
+    sampled_layer_check(w, moe.MOE_COMBINE_SCATTER_ATOMIC)
