@@ -57,6 +57,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--combine", default="gather", choices=["gather", "scatter"],
                     help="deterministic gather-reduce (default) or the scatter-add fused into down")
+    ap.add_argument("--shared-hs", type=int, default=0,
+                    help="also time moe_layer_forward and moe_layer_forward_shared (a shared "
+                         "expert of this intermediate size on a side stream); reported under "
+                         "'fused', the headline value stays the routed layer")
     ap.add_argument("--xperm", action="store_true",
                     help="materialise x_perm in the permute instead of gathering rows in gate/up")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -127,7 +131,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     moe.lib()   # fail loudly if the HIP library is missing
-    w = gen.config(args.config, device=dev, maxvio=args.maxvio if args.config == "c4" else None)
+    w = gen.config(args.config, device=dev, maxvio=args.maxvio if args.config == "c4" else None,
+                   shared_hs=args.shared_hs)
     T, H, Hp, E, K = w.T, w.H, w.Hp, w.E, w.K
     M = T * K
     DT = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "fp8": moe.MOE_FP8_E4M3, "mxfp4": moe.MOE_MXFP4}
@@ -287,9 +292,56 @@ def main():
                     "maxvio_target": w.meta.get("maxvio_target")},
         "roofline": roof,
     }
+    if args.shared_hs:
+        line["fused"] = time_fused(w, args, moe, torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args, out)
     print(json.dumps(line), flush=True)
+
+
+def time_fused(w, args, moe, torch):
+    """Whole-layer entry points timed end to end (events on the launch stream): the routed
+    layer alone, and with a shared expert of size Hs on a side stream (overlapped) or on the
+    same stream (serial)."""
+    DT = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "fp8": moe.MOE_FP8_E4M3, "mxfp4": moe.MOE_MXFP4}
+    comb = moe.MOE_COMBINE_SCATTER_ATOMIC if args.combine == "scatter" else moe.MOE_COMBINE_GATHER
+    d = moe.LayerDesc(w.T, w.H, w.Hp, w.E, w.K, DT[w.act], DT[w.wgt], DT[w.out], comb)
+    n = max(moe.moe_layer_shared_workspace_bytes(d, w.Hs), moe.moe_layer_workspace_bytes(d))
+    ws = torch.empty(n, dtype=torch.uint8, device=w.x.device)
+    out = torch.empty((w.T, w.H), dtype={"f32": torch.float32, "bf16": torch.bfloat16}[w.out],
+                      device=w.x.device)
+    side = torch.cuda.Stream()
+    stream = torch.cuda.current_stream()
+
+    def routed():
+        moe.moe_layer_forward(d, w.x, w.x_sf, w.logits, w.topk_idx, w.topk_w, w.w_gate, w.w_up,
+                              w.w_down, w.sf_gate, w.sf_up, w.sf_down, out, ws, n)
+
+    def shared(side_stream):
+        moe.moe_layer_forward_shared(d, w.Hs, w.x, w.x_sf, w.x_shared, w.logits, w.topk_idx, w.topk_w,
+                                     w.w_gate, w.w_up, w.w_down, w.sf_gate, w.sf_up, w.sf_down,
+                                     w.ws_gate, w.ws_up, w.ws_down, out, ws, n, side_stream=side_stream)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
+
+    ms_routed = timed(routed)
+    ms_serial = timed(lambda: shared(None))
+    ms_side = timed(lambda: shared(side))
+    return {"Hs": w.Hs, "ms_layer_forward": ms_routed, "ms_layer_forward_shared_serial": ms_serial,
+            "ms_layer_forward_shared_side_stream": ms_side,
+            "shared_expert_ms_hidden": ms_serial - ms_side,
+            "tokens_per_s_with_shared": w.T / (ms_side / 1e3)}
 
 
 def cpu_baseline(w, args, gpu_out):

@@ -209,6 +209,16 @@ MOE_API moe_status_t moe_combine(const void* y_rows, moe_dtype_t y_dtype, const 
                          const float* topk_w, int32_t T, int32_t H, int32_t K, void* out,
                          moe_dtype_t out_dtype, hipStream_t stream);
 
+/* moe_combine with the shared expert's output added to each token ("Mixture of Kittens",
+ * Step 1, "The Math": MoE(x) = SharedExpert(x) + sum_k w_k * RoutedExpert_k(x)):
+ *   out[t] = (sum_{k=0..K-1} topk_w[t,k] * y_rows[pos[t,k]]) + shared_y[t],
+ * summed in fp32 (k in increasing order, then the shared row) and rounded once.
+ *  shared_y [T, H] of y_dtype. Deterministic. */
+MOE_API moe_status_t moe_combine_shared(const void* y_rows, moe_dtype_t y_dtype, const int32_t* pos,
+                                const float* topk_w, int32_t T, int32_t H, int32_t K,
+                                const void* shared_y, void* out, moe_dtype_t out_dtype,
+                                hipStream_t stream);
+
 /* Workspace bytes of moe_layer_forward for `d` (0 if `d` is invalid). */
 MOE_API size_t moe_layer_workspace_bytes(const moe_layer_desc_t* d);
 
@@ -233,6 +243,36 @@ MOE_API moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const void* x,
                                const void* w_down, const uint8_t* sf_gate, const uint8_t* sf_up,
                                const uint8_t* sf_down, void* out, void* ws, size_t ws_bytes,
                                hipStream_t stream);
+
+/* Workspace bytes of moe_layer_forward_shared for `d` and shared intermediate size Hs (0 if
+ * invalid): the moe_layer_forward workspace followed by h_s [T, Hs], y_s [T, H] (bf16, fp32
+ * for an F32 layer) and a two-entry cu_seqlens. */
+MOE_API size_t moe_layer_shared_workspace_bytes(const moe_layer_desc_t* d, int32_t Hs);
+
+/* moe_layer_forward plus a shared expert ("Mixture of Kittens", Step 1: every token also
+ * goes through one shared expert whose output is added to the weighted routed sum):
+ *   out[t] = SharedExpert(xs[t]) + sum_k topk_w[t,k] * Expert_{topk_idx[t,k]}(x[t]),
+ *   SharedExpert(v) = (silu(v . Ws_gate) * (v . Ws_up)) . Ws_down.
+ * The shared expert runs in BF16 (F32 for an F32 layer) even when the routed experts are
+ * FP8 x MXFP4 ("Mixture of Kittens", Step 8: the shared expert stays in BF16); it is one
+ * grouped-GEMM group of all T rows. Its input xs is x_shared [T, H] when given, else x
+ * (x_shared is required for an FP8_E4M3 layer: the BF16 activations). Weights ws_gate,
+ * ws_up [H, Hs], ws_down [Hs, H] in that format; needs the moe_ffn_gate_up / moe_ffn_down
+ * limits with Hp = Hs. Its output is added in the combine (gather: moe_combine_shared;
+ * scatter: to the fp32 accumulator before the rounding).
+ * side_stream: when non-NULL and different from `stream`, the shared expert runs there,
+ * overlapping the routed path ("Mixture of Kittens", Step 9: the shared expert FFN overlaps
+ * the first dispatch); the call orders it after the work already on `stream` and makes
+ * `stream` wait for it before the combine, so completion on `stream` covers everything.
+ * Calls that overlap on one device must not share side_stream. */
+MOE_API moe_status_t moe_layer_forward_shared(const moe_layer_desc_t* d, int32_t Hs, const void* x,
+                                      const float* x_sf, const void* x_shared, const float* logits,
+                                      const int32_t* topk_idx_in, const float* topk_w_in,
+                                      const void* w_gate, const void* w_up, const void* w_down,
+                                      const uint8_t* sf_gate, const uint8_t* sf_up,
+                                      const uint8_t* sf_down, const void* ws_gate,
+                                      const void* ws_up, const void* ws_down, void* out, void* ws,
+                                      size_t ws_bytes, hipStream_t stream, hipStream_t side_stream);
 
 /* Byte offsets of the intermediates inside the moe_layer_forward workspace, for inspection.
  * offsets[i] (i in order): 0 topk_idx, 1 topk_w, 2 counts, 3 cu_seqlens, 4 pos, 5 row_src,

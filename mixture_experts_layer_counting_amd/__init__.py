@@ -30,7 +30,8 @@ WS_FIELDS = ("topk_idx", "topk_w", "counts", "cu_seqlens", "pos", "row_src", "ro
 EXPORTS = ("moe_route_topk", "moe_permute_workspace_bytes", "moe_permute", "moe_ffn_gate_up",
            "moe_ffn_gate_up_gather", "moe_ffn_down", "moe_ffn_down_scatter",
            "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn", "moe_combine",
-           "moe_layer_workspace_bytes", "moe_layer_forward", "moe_layer_workspace_layout",
+           "moe_combine_shared", "moe_layer_workspace_bytes", "moe_layer_forward",
+           "moe_layer_shared_workspace_bytes", "moe_layer_forward_shared", "moe_layer_workspace_layout",
            "moe_status_str")
 
 
@@ -72,6 +73,10 @@ _SIGS = {
     "moe_layer_forward": (_I, [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                _P, _P, _P, _S, _P]),
     "moe_layer_workspace_layout": (_I, [ctypes.POINTER(LayerDesc), ctypes.POINTER(_S), _I]),
+    "moe_combine_shared": (_I, [_P, _E, _P, _P, _I, _I, _I, _P, _P, _E, _P]),
+    "moe_layer_shared_workspace_bytes": (_S, [ctypes.POINTER(LayerDesc), _I]),
+    "moe_layer_forward_shared": (_I, [ctypes.POINTER(LayerDesc), _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                                      _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P, _P]),
     "moe_status_str": (ctypes.c_char_p, [_I]),
 }
 
@@ -203,3 +208,28 @@ def moe_layer_forward(desc: LayerDesc, x, x_sf, logits, topk_idx_in, topk_w_in, 
                                    _ptr(w_down), _ptr(sf_gate), _ptr(sf_up), _ptr(sf_down),
                                    _ptr(out), _ptr(ws), ws_bytes, _stream(stream)),
            "moe_layer_forward")
+
+
+def moe_combine_shared(y_rows, y_dtype, pos, topk_w, T, H, K, shared_y, out, out_dtype, stream=None):
+    _check(lib().moe_combine_shared(_ptr(y_rows), y_dtype, _ptr(pos), _ptr(topk_w), T, H, K,
+                                    _ptr(shared_y), _ptr(out), out_dtype, _stream(stream)),
+           "moe_combine_shared")
+
+
+def moe_layer_shared_workspace_bytes(desc: LayerDesc, Hs) -> int:
+    return int(lib().moe_layer_shared_workspace_bytes(ctypes.byref(desc), Hs))
+
+
+def moe_layer_forward_shared(desc: LayerDesc, Hs, x, x_sf, x_shared, logits, topk_idx_in, topk_w_in,
+                             w_gate, w_up, w_down, sf_gate, sf_up, sf_down, ws_gate, ws_up, ws_down,
+                             out, ws, ws_bytes, stream=None, side_stream=None):
+    """``side_stream``: a torch stream (or raw handle) for the shared expert, or None to run
+    it on ``stream``."""
+    side = None if side_stream is None else (side_stream.cuda_stream if hasattr(side_stream, "cuda_stream")
+                                             else side_stream)
+    _check(lib().moe_layer_forward_shared(ctypes.byref(desc), Hs, _ptr(x), _ptr(x_sf), _ptr(x_shared),
+                                          _ptr(logits), _ptr(topk_idx_in), _ptr(topk_w_in), _ptr(w_gate),
+                                          _ptr(w_up), _ptr(w_down), _ptr(sf_gate), _ptr(sf_up),
+                                          _ptr(sf_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down),
+                                          _ptr(out), _ptr(ws), ws_bytes, _stream(stream), side),
+           "moe_layer_forward_shared")

@@ -7,7 +7,9 @@
 // FMA) and is rounded once, so the output is bitwise reproducible.
 //
 // One block per token; each thread owns 16-byte column chunks and keeps the K row loads
-// of a chunk in flight together. HBM-bound: M*H*b read + T*H*b written.
+// of a chunk in flight together. HBM-bound: M*H*b read + T*H*b written. An optional addend
+// row per token (the shared expert's output: "Mixture of Kittens", Step 1, MoE(x) =
+// SharedExpert(x) + the weighted routed sum) is added after the k sum, before the rounding.
 #include "moe_common.h"
 
 namespace moe {
@@ -44,7 +46,8 @@ template <typename YT, typename OT, int KMAX>
 __global__ __launch_bounds__(128) void combine_kernel(const YT* __restrict__ y_rows,
                                                       const int* __restrict__ pos,
                                                       const float* __restrict__ topk_w, int T,
-                                                      int H, int K, OT* __restrict__ out) {
+                                                      int H, int K, const YT* __restrict__ add,
+                                                      OT* __restrict__ out) {
   const int t = blockIdx.x;
   int p[KMAX];
   float w[KMAX];
@@ -65,6 +68,12 @@ __global__ __launch_bounds__(128) void combine_kernel(const YT* __restrict__ y_r
         for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[k], v[i], acc[i]);
       }
     }
+    if (add) {
+      float v[8];
+      load8(add + (size_t)t * H + c * 8, v);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += v[i];
+    }
     store8(out + (size_t)t * H + c * 8, acc);
   }
 }
@@ -75,6 +84,7 @@ __global__ __launch_bounds__(128) void combine_scalar_kernel(const YT* __restric
                                                              const int* __restrict__ pos,
                                                              const float* __restrict__ topk_w,
                                                              int T, int H, int K,
+                                                             const YT* __restrict__ add,
                                                              OT* __restrict__ out) {
   const int t = blockIdx.x;
   for (int c = threadIdx.x; c < H; c += blockDim.x) {
@@ -89,6 +99,12 @@ __global__ __launch_bounds__(128) void combine_scalar_kernel(const YT* __restric
         v = y_rows[(size_t)p * H + c];
       acc = fmaf(topk_w[(size_t)t * K + k], v, acc);
     }
+    if (add) {
+      if constexpr (sizeof(YT) == 2)
+        acc += bf16_bits_to_f32(add[(size_t)t * H + c]);
+      else
+        acc += add[(size_t)t * H + c];
+    }
     if constexpr (sizeof(OT) == 2)
       out[(size_t)t * H + c] = f32_to_bf16_bits(acc);
     else
@@ -98,33 +114,35 @@ __global__ __launch_bounds__(128) void combine_scalar_kernel(const YT* __restric
 
 template <typename YT, typename OT>
 static moe_status_t dispatch_combine(const void* y, const int* pos, const float* w, int T, int H,
-                                     int K, void* out, hipStream_t s) {
+                                     int K, const void* add, void* out, hipStream_t s) {
   const YT* yr = static_cast<const YT*>(y);
+  const YT* ad = static_cast<const YT*>(add);
   OT* o = static_cast<OT*>(out);
-  const bool vec = (H % 8 == 0) && ((uintptr_t)y % 16 == 0) && ((uintptr_t)out % 16 == 0);
+  const bool vec = (H % 8 == 0) && ((uintptr_t)y % 16 == 0) && ((uintptr_t)out % 16 == 0) &&
+                   ((uintptr_t)add % 16 == 0);
   if (!vec) {
-    combine_scalar_kernel<YT, OT><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, o);
+    combine_scalar_kernel<YT, OT><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, ad, o);
   } else if (K <= 2) {
-    combine_kernel<YT, OT, 2><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, o);
+    combine_kernel<YT, OT, 2><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, ad, o);
   } else if (K <= 4) {
-    combine_kernel<YT, OT, 4><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, o);
+    combine_kernel<YT, OT, 4><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, ad, o);
   } else if (K <= 8) {
-    combine_kernel<YT, OT, 8><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, o);
+    combine_kernel<YT, OT, 8><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, ad, o);
   } else if (K <= 16) {
-    combine_kernel<YT, OT, 16><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, o);
+    combine_kernel<YT, OT, 16><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, ad, o);
   } else {
-    combine_kernel<YT, OT, 32><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, o);
+    combine_kernel<YT, OT, 32><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, ad, o);
   }
   return launch_status();
 }
 
 moe_status_t launch_combine(const void* y, moe_dtype_t yt, const int* pos, const float* w, int T,
-                            int H, int K, void* out, moe_dtype_t ot, hipStream_t s) {
+                            int H, int K, const void* add, void* out, moe_dtype_t ot, hipStream_t s) {
   if (T == 0 || H == 0) return MOE_OK;
-  if (yt == MOE_BF16 && ot == MOE_BF16) return dispatch_combine<uint16_t, uint16_t>(y, pos, w, T, H, K, out, s);
-  if (yt == MOE_BF16 && ot == MOE_F32) return dispatch_combine<uint16_t, float>(y, pos, w, T, H, K, out, s);
-  if (yt == MOE_F32 && ot == MOE_F32) return dispatch_combine<float, float>(y, pos, w, T, H, K, out, s);
-  if (yt == MOE_F32 && ot == MOE_BF16) return dispatch_combine<float, uint16_t>(y, pos, w, T, H, K, out, s);
+  if (yt == MOE_BF16 && ot == MOE_BF16) return dispatch_combine<uint16_t, uint16_t>(y, pos, w, T, H, K, add, out, s);
+  if (yt == MOE_BF16 && ot == MOE_F32) return dispatch_combine<uint16_t, float>(y, pos, w, T, H, K, add, out, s);
+  if (yt == MOE_F32 && ot == MOE_F32) return dispatch_combine<float, float>(y, pos, w, T, H, K, add, out, s);
+  if (yt == MOE_F32 && ot == MOE_BF16) return dispatch_combine<float, uint16_t>(y, pos, w, T, H, K, add, out, s);
   return MOE_EUNSUPPORTED;
 }
 
@@ -140,17 +158,37 @@ __global__ __launch_bounds__(256) void acc_zero_kernel(float* __restrict__ acc, 
   for (size_t i = n4 * 4 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) acc[i] = 0.f;
 }
 
-__global__ __launch_bounds__(256) void acc_store_bf16_kernel(const float* __restrict__ acc,
-                                                             uint16_t* __restrict__ out, size_t n) {
+// out = round(acc + add): add (nullable) has the format of y (bf16 or fp32); out may alias
+// acc when both are fp32.
+template <typename AT, typename OT>
+__global__ __launch_bounds__(256) void acc_store_kernel(const float* acc, const AT* __restrict__ add,
+                                                        OT* out, size_t n) {
   const size_t n8 = n / 8;
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8; i += stride) {
     float f[8];
     load8(acc + 8 * i, f);
+    if (add) {
+      float a[8];
+      load8(add + 8 * i, a);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f[j] += a[j];
+    }
     store8(out + 8 * i, f);
   }
-  for (size_t i = n8 * 8 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
-    out[i] = f32_to_bf16_bits(acc[i]);
+  for (size_t i = n8 * 8 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    float v = acc[i];
+    if (add) {
+      if constexpr (sizeof(AT) == 2)
+        v += bf16_bits_to_f32(add[i]);
+      else
+        v += add[i];
+    }
+    if constexpr (sizeof(OT) == 2)
+      out[i] = f32_to_bf16_bits(v);
+    else
+      out[i] = v;
+  }
 }
 
 static int stream_grid(size_t items) {
@@ -166,11 +204,32 @@ moe_status_t launch_acc_zero(float* acc, size_t n, hipStream_t s) {
   return launch_status();
 }
 
-moe_status_t launch_acc_store(const float* acc, size_t n, void* out, moe_dtype_t ot, hipStream_t s) {
+moe_status_t launch_acc_store(const float* acc, size_t n, const void* add, moe_dtype_t add_dtype,
+                              void* out, moe_dtype_t ot, hipStream_t s) {
   if (n == 0) return MOE_OK;
-  if (ot != MOE_BF16) return MOE_EUNSUPPORTED;
-  if ((uintptr_t)acc % 16 || (uintptr_t)out % 16) return MOE_EINVAL;
-  acc_store_bf16_kernel<<<stream_grid(n / 8), 256, 0, s>>>(acc, static_cast<uint16_t*>(out), n);
+  if ((uintptr_t)acc % 16 || (uintptr_t)out % 16 || (uintptr_t)add % 16) return MOE_EINVAL;
+  const int g = stream_grid(n / 8);
+  if (ot == MOE_BF16 && add_dtype == MOE_BF16)
+    acc_store_kernel<uint16_t, uint16_t><<<g, 256, 0, s>>>(acc, static_cast<const uint16_t*>(add),
+                                                           static_cast<uint16_t*>(out), n);
+  else if (ot == MOE_F32 && add_dtype == MOE_F32)
+    acc_store_kernel<float, float><<<g, 256, 0, s>>>(acc, static_cast<const float*>(add),
+                                                     static_cast<float*>(out), n);
+  else
+    return MOE_EUNSUPPORTED;
+  return launch_status();
+}
+
+// cu_seqlens of one group holding all T rows (the shared expert run as a one-group launch)
+__global__ void dense_cu_kernel(int* cu, int T) {
+  if (threadIdx.x == 0) {
+    cu[0] = 0;
+    cu[1] = T;
+  }
+}
+
+moe_status_t launch_dense_cu(int* cu, int T, hipStream_t s) {
+  dense_cu_kernel<<<1, 64, 0, s>>>(cu, T);
   return launch_status();
 }
 

@@ -19,7 +19,7 @@ moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes, co
                             float* x_perm_sf, void* ws, bool validate, int** err_out,
                             hipStream_t s);
 moe_status_t launch_combine(const void*, moe_dtype_t, const int*, const float*, int, int, int,
-                            void*, moe_dtype_t, hipStream_t);
+                            const void*, void*, moe_dtype_t, hipStream_t);
 moe_status_t launch_ffn_gate_up_bf16(const void*, const int*, int, int, int, int, const void*,
                                      const void*, void*, const RowMaps&, hipStream_t);
 moe_status_t launch_ffn_down_bf16(const void*, const int*, int, int, int, int, const void*, void*,
@@ -34,7 +34,9 @@ moe_status_t launch_ffn_gate_up_f32(const void*, const int*, int, int, int, int,
 moe_status_t launch_ffn_down_f32(const void*, const int*, int, int, int, int, const void*, void*,
                                  const RowMaps&, hipStream_t);
 moe_status_t launch_acc_zero(float* acc, size_t n, hipStream_t s);
-moe_status_t launch_acc_store(const float* acc, size_t n, void* out, moe_dtype_t out_dtype, hipStream_t s);
+moe_status_t launch_acc_store(const float* acc, size_t n, const void* add, moe_dtype_t add_dtype,
+                              void* out, moe_dtype_t out_dtype, hipStream_t s);
+moe_status_t launch_dense_cu(int* cu, int T, hipStream_t s);
 
 int device_cu_count() {
   static int cache[64] = {0};
@@ -309,7 +311,19 @@ moe_status_t moe_combine(const void* y_rows, moe_dtype_t y_dtype, const int32_t*
   if ((y_dtype != MOE_F32 && y_dtype != MOE_BF16) || (out_dtype != MOE_F32 && out_dtype != MOE_BF16))
     return MOE_EUNSUPPORTED;
   if (T > 0 && (!y_rows || !pos || !topk_w || !out)) return MOE_EINVAL;
-  return launch_combine(y_rows, y_dtype, pos, topk_w, T, H, K, out, out_dtype, stream);
+  return launch_combine(y_rows, y_dtype, pos, topk_w, T, H, K, nullptr, out, out_dtype, stream);
+}
+
+moe_status_t moe_combine_shared(const void* y_rows, moe_dtype_t y_dtype, const int32_t* pos,
+                                const float* topk_w, int32_t T, int32_t H, int32_t K,
+                                const void* shared_y, void* out, moe_dtype_t out_dtype,
+                                hipStream_t stream) {
+  if (T < 0 || H < 1 || K < 1) return MOE_EINVAL;
+  if (K > 32) return MOE_EUNSUPPORTED;
+  if ((y_dtype != MOE_F32 && y_dtype != MOE_BF16) || (out_dtype != MOE_F32 && out_dtype != MOE_BF16))
+    return MOE_EUNSUPPORTED;
+  if (T > 0 && (!y_rows || !pos || !topk_w || !out || !shared_y)) return MOE_EINVAL;
+  return launch_combine(y_rows, y_dtype, pos, topk_w, T, H, K, shared_y, out, out_dtype, stream);
 }
 
 enum {
@@ -364,6 +378,31 @@ static moe_status_t layer_layout(const moe_layer_desc_t* d, size_t* off, size_t*
   return MOE_OK;
 }
 
+// The shared expert runs in bf16 (fp32 in the fp32 layer) whatever the routed format
+// ("Mixture of Kittens", Step 8: the shared expert stays in BF16).
+static Path shared_path(const moe_layer_desc_t* d) {
+  return ffn_path(d->act, d->wgt) == PATH_F32 ? PATH_F32 : PATH_BF16;
+}
+
+// Workspace of moe_layer_forward_shared: the routed layout, then h_s [T, Hs], y_s [T, H] and
+// the one-group cu_seqlens [2].
+static moe_status_t shared_layout(const moe_layer_desc_t* d, int32_t Hs, size_t* off, size_t* total,
+                                  size_t* h_s, size_t* y_s, size_t* cu_s) {
+  if (Hs < 1) return MOE_EINVAL;
+  const moe_status_t st = layer_layout(d, off, total);
+  if (st != MOE_OK) return st;
+  const Path sp = shared_path(d);
+  const size_t eb = sp == PATH_F32 ? 4 : 2, T = d->T, H = d->H;
+  size_t o = align_up(*total, 256);
+  *h_s = o;
+  o = align_up(o + T * (size_t)Hs * eb, 256);
+  *y_s = o;
+  o = align_up(o + T * H * eb, 256);
+  *cu_s = o;
+  *total = o + 256;
+  return MOE_OK;
+}
+
 size_t moe_layer_workspace_bytes(const moe_layer_desc_t* d) {
   size_t off[WS_N], total = 0;
   return layer_layout(d, off, &total) == MOE_OK ? total : 0;
@@ -378,14 +417,43 @@ moe_status_t moe_layer_workspace_layout(const moe_layer_desc_t* d, size_t* offse
   return MOE_OK;
 }
 
-moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const void* x, const float* x_sf,
-                               const float* logits, const int32_t* topk_idx_in,
-                               const float* topk_w_in, const void* w_gate, const void* w_up,
-                               const void* w_down, const uint8_t* sf_gate, const uint8_t* sf_up,
-                               const uint8_t* sf_down, void* out, void* ws, size_t ws_bytes,
-                               hipStream_t stream) {
-  size_t off[WS_N], total = 0;
-  moe_status_t st = layer_layout(d, off, &total);
+}  // extern "C"
+
+namespace moe {
+
+// Per-device events that order the shared expert's side stream with the main stream
+// (created once per device, kept for the process lifetime).
+static moe_status_t side_events(hipEvent_t** ev) {
+  static hipEvent_t cache[64][2];
+  static bool made[64] = {false};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return MOE_EHIP;
+  if (!made[dev]) {
+    for (int i = 0; i < 2; ++i)
+      if (hipEventCreateWithFlags(&cache[dev][i], hipEventDisableTiming) != hipSuccess) return MOE_EHIP;
+    made[dev] = true;
+  }
+  *ev = cache[dev];
+  return MOE_OK;
+}
+
+struct SharedArgs {
+  int32_t Hs = 0;
+  const void* x_shared = nullptr;
+  const void *w_gate = nullptr, *w_up = nullptr, *w_down = nullptr;
+  hipStream_t side = nullptr;
+};
+
+static moe_status_t layer_forward_impl(const moe_layer_desc_t* d, const void* x, const float* x_sf,
+                                       const float* logits, const int32_t* topk_idx_in,
+                                       const float* topk_w_in, const void* w_gate, const void* w_up,
+                                       const void* w_down, const uint8_t* sf_gate,
+                                       const uint8_t* sf_up, const uint8_t* sf_down,
+                                       const SharedArgs* sh, void* out, void* ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  size_t off[WS_N], total = 0, h_s_off = 0, y_s_off = 0, cu_s_off = 0;
+  moe_status_t st = sh ? shared_layout(d, sh->Hs, off, &total, &h_s_off, &y_s_off, &cu_s_off)
+                       : layer_layout(d, off, &total);
   if (st != MOE_OK) return st;
   if (!ws || ws_bytes < total) return MOE_EWORKSPACE;
   const Path p = ffn_path(d->act, d->wgt);
@@ -394,10 +462,50 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const void* x, const f
   if (st != MOE_OK) return st;
   if (d->T > 0 && (!x || !out || !w_gate || !w_up || !w_down)) return MOE_EINVAL;
   if (d->T > 0 && !logits && (!topk_idx_in || !topk_w_in)) return MOE_EINVAL;
+  const Path sp = sh ? shared_path(d) : PATH_NONE;
+  const void* xs = nullptr;
+  if (sh) {
+    st = check_ffn_dims(sp, d->T, 1, d->H, sh->Hs, true);
+    if (st == MOE_OK) st = check_ffn_dims(sp, d->T, 1, d->H, sh->Hs, false);
+    if (st != MOE_OK) return st;
+    xs = sh->x_shared ? sh->x_shared : (p == PATH_FP8_MXFP4 ? nullptr : x);
+    if (d->T > 0 && (!xs || !sh->w_gate || !sh->w_up || !sh->w_down)) return MOE_EINVAL;
+  }
   poison(ws, ws_bytes, stream);
   char* base = static_cast<char*>(ws);
   auto at = [&](int i) -> void* { return off[i] == SIZE_MAX ? nullptr : base + off[i]; };
   const int T = d->T, E = d->E, K = d->K, H = d->H, Hp = d->Hp, M = T * K;
+
+  // shared expert (one group of all T rows), on the side stream when one is given
+  void* y_s = sh ? base + y_s_off : nullptr;
+  hipEvent_t* ev = nullptr;
+  const bool side = sh && sh->side && sh->side != stream && T > 0;
+  if (sh && T > 0) {
+    hipStream_t ss = stream;
+    if (side) {
+      st = side_events(&ev);
+      if (st != MOE_OK) return st;
+      if (hipEventRecord(ev[0], stream) != hipSuccess || hipStreamWaitEvent(sh->side, ev[0], 0) != hipSuccess)
+        return MOE_EHIP;
+      ss = sh->side;
+    }
+    int32_t* cu_s = reinterpret_cast<int32_t*>(base + cu_s_off);
+    const moe_dtype_t sdt = sp == PATH_F32 ? MOE_F32 : MOE_BF16;
+    st = launch_dense_cu(cu_s, T, ss);
+    if (st == MOE_OK)
+      st = moe_ffn_gate_up(xs, nullptr, sdt, cu_s, T, 1, H, sh->Hs, sh->w_gate, sh->w_up, nullptr,
+                           nullptr, sdt, base + h_s_off, nullptr, ss);
+    if (st == MOE_OK)
+      st = moe_ffn_down(base + h_s_off, nullptr, sdt, cu_s, T, 1, H, sh->Hs, sh->w_down, nullptr, sdt,
+                        y_s, sdt, ss);
+    if (st != MOE_OK) return st;
+    if (side && hipEventRecord(ev[1], sh->side) != hipSuccess) return MOE_EHIP;
+  }
+  auto join_side = [&]() -> moe_status_t {
+    if (side && hipStreamWaitEvent(stream, ev[1], 0) != hipSuccess) return MOE_EHIP;
+    return MOE_OK;
+  };
+
   int32_t* topk_idx = static_cast<int32_t*>(at(WS_TOPK_IDX));
   float* topk_w = static_cast<float*>(at(WS_TOPK_W));
   if (logits) {
@@ -429,8 +537,9 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const void* x, const f
   if (!scatter) {
     st = moe_ffn_down(at(WS_H), h_sf, h_dtype_of(p), cu, M, E, H, Hp, w_down, sf_down, d->wgt, at(WS_Y),
                       y_dtype_of(p), stream);
+    if (st == MOE_OK) st = join_side();
     if (st != MOE_OK) return st;
-    return moe_combine(at(WS_Y), y_dtype_of(p), pos, topk_w, T, H, K, out, d->out, stream);
+    return launch_combine(at(WS_Y), y_dtype_of(p), pos, topk_w, T, H, K, y_s, out, d->out, stream);
   }
   // weighted scatter-add fused into the down projection, into an fp32 accumulator
   float* acc = d->out == MOE_F32 ? static_cast<float*>(out) : static_cast<float*>(at(WS_ACC));
@@ -440,8 +549,48 @@ moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const void* x, const f
   if (st != MOE_OK) return st;
   st = moe_ffn_down_scatter(at(WS_H), h_sf, h_dtype_of(p), cu, M, E, H, Hp, w_down, sf_down, d->wgt,
                             row_src, row_w, T, K, acc, stream);
-  if (st != MOE_OK || d->out == MOE_F32) return st;
-  return launch_acc_store(acc, n, out, d->out, stream);
+  if (st == MOE_OK) st = join_side();
+  if (st != MOE_OK) return st;
+  if (d->out == MOE_F32 && !y_s) return MOE_OK;
+  return launch_acc_store(acc, n, y_s, y_dtype_of(p), out, d->out, stream);
+}
+
+}  // namespace moe
+
+extern "C" {
+
+moe_status_t moe_layer_forward(const moe_layer_desc_t* d, const void* x, const float* x_sf,
+                               const float* logits, const int32_t* topk_idx_in,
+                               const float* topk_w_in, const void* w_gate, const void* w_up,
+                               const void* w_down, const uint8_t* sf_gate, const uint8_t* sf_up,
+                               const uint8_t* sf_down, void* out, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  return layer_forward_impl(d, x, x_sf, logits, topk_idx_in, topk_w_in, w_gate, w_up, w_down, sf_gate,
+                            sf_up, sf_down, nullptr, out, ws, ws_bytes, stream);
+}
+
+size_t moe_layer_shared_workspace_bytes(const moe_layer_desc_t* d, int32_t Hs) {
+  size_t off[WS_N], total = 0, a, b, c;
+  return shared_layout(d, Hs, off, &total, &a, &b, &c) == MOE_OK ? total : 0;
+}
+
+moe_status_t moe_layer_forward_shared(const moe_layer_desc_t* d, int32_t Hs, const void* x,
+                                      const float* x_sf, const void* x_shared, const float* logits,
+                                      const int32_t* topk_idx_in, const float* topk_w_in,
+                                      const void* w_gate, const void* w_up, const void* w_down,
+                                      const uint8_t* sf_gate, const uint8_t* sf_up,
+                                      const uint8_t* sf_down, const void* ws_gate,
+                                      const void* ws_up, const void* ws_down, void* out, void* ws,
+                                      size_t ws_bytes, hipStream_t stream, hipStream_t side_stream) {
+  SharedArgs sh;
+  sh.Hs = Hs;
+  sh.x_shared = x_shared;
+  sh.w_gate = ws_gate;
+  sh.w_up = ws_up;
+  sh.w_down = ws_down;
+  sh.side = side_stream;
+  return layer_forward_impl(d, x, x_sf, logits, topk_idx_in, topk_w_in, w_gate, w_up, w_down, sf_gate,
+                            sf_up, sf_down, &sh, out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -274,6 +274,27 @@ def layer(x: np.ndarray, E: int, K: int, weights: WeightFn, *, logits: Optional[
                 out=out, maxvio=maxvio(counts, T, K, E))
 
 
+def shared_expert(xs: np.ndarray, wg: np.ndarray, wu: np.ndarray, wd: np.ndarray) -> np.ndarray:
+    """The shared expert on every token ("Mixture of Kittens", Step 1, "The Math": the layer
+    output is SharedExpert(x) plus the weighted sum of the routed experts; the shared expert
+    is an FFN of the same SwiGLU form, applied to all tokens). ``xs`` [T, H] float64 (the
+    activations the shared expert reads: bf16 even in a low-precision layer, Step 8), weights
+    Ws_gate, Ws_up [H, Hs], Ws_down [Hs, H] float64. No requantisation of its h (bf16 path)."""
+    return expert_ffn(xs, wg, wu, wd, False)[1]
+
+
+def layer_with_shared(x: np.ndarray, xs: np.ndarray, E: int, K: int, weights: WeightFn,
+                      shared_weights: Tuple[np.ndarray, np.ndarray, np.ndarray],
+                      **kw) -> Dict[str, np.ndarray]:
+    """``layer`` plus the shared expert's output added to every token's combined row
+    ("Mixture of Kittens", Step 1, "The Math")."""
+    res = layer(x, E, K, weights, **kw)
+    ys = shared_expert(np.asarray(xs, np.float64), *shared_weights)
+    res["y_shared"] = ys
+    res["out"] = res["out"] + ys
+    return res
+
+
 def layer_token_loop(x: np.ndarray, idx: np.ndarray, w: np.ndarray, weights: WeightFn,
                      fp8_requant: bool = False) -> np.ndarray:
     """Independent formulation with no permutation at all:

@@ -66,3 +66,16 @@ def run_layer(w, combine=moe.MOE_COMBINE_GATHER):
     moe.moe_layer_forward(d, w.x, w.x_sf, w.logits, w.topk_idx, w.topk_w, w.w_gate, w.w_up,
                           w.w_down, w.sf_gate, w.sf_up, w.sf_down, out, ws, nbytes)
     return out, ws, moe.moe_layer_workspace_layout(d)
+
+
+def run_layer_shared(w, combine=moe.MOE_COMBINE_GATHER, side_stream=None):
+    """moe_layer_forward_shared; returns (out, workspace tensor)."""
+    d = layer_desc(w, combine)
+    nbytes = moe.moe_layer_shared_workspace_bytes(d, w.Hs)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=w.x.device)
+    out = torch.empty((w.T, w.H), dtype=TORCH_DT[w.out], device=w.x.device)
+    moe.moe_layer_forward_shared(d, w.Hs, w.x, w.x_sf, w.x_shared, w.logits, w.topk_idx, w.topk_w,
+                                 w.w_gate, w.w_up, w.w_down, w.sf_gate, w.sf_up, w.sf_down,
+                                 w.ws_gate, w.ws_up, w.ws_down, out, ws, nbytes,
+                                 side_stream=side_stream)
+    return out, ws

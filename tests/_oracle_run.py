@@ -40,6 +40,27 @@ def oracle_layer(w, experts=None):
                    topk_w=b["topk_w"], fp8_requant=(w.act == "fp8"), experts=experts)
 
 
+def shared_weights_f64(w):
+    def dec(t):
+        bits = to_numpy_bits(t)
+        return np.asarray(bits, np.float64) if bits.dtype == np.float32 else O.decode_bf16(bits)
+    return dec(w.ws_gate), dec(w.ws_up), dec(w.ws_down)
+
+
+def shared_input_f64(w, b=None):
+    """The activations the shared expert reads: x_shared (bf16) for an fp8 layer, else x."""
+    if w.x_shared is not None:
+        return O.decode_bf16(to_numpy_bits(w.x_shared))
+    return x_f64(w, b)
+
+
+def oracle_layer_shared(w):
+    b = host_bits(w)
+    return O.layer_with_shared(x_f64(w, b), shared_input_f64(w, b), w.E, w.K, weight_fn(w),
+                               shared_weights_f64(w), logits=b["logits"], topk_idx=b["topk_idx"],
+                               topk_w=b["topk_w"], fp8_requant=(w.act == "fp8"))
+
+
 def oracle_routing(w):
     """Integer results only (routing, counts, offsets, permutation)."""
     b = host_bits(w)

@@ -432,3 +432,52 @@ def test_full_size_layer_gather_and_scatter(cfg):
     w = gen.config(cfg, device=DEV)
     sampled_layer_check(w, moe.MOE_COMBINE_GATHER)
     sampled_layer_check(w, moe.MOE_COMBINE_SCATTER_ATOMIC)
+
+
+# ----------------------------------------------------------------------------- shared expert
+
+SHARED_CASES = [
+    ("f32", dict(T=333, H=200, Hp=72, E=9, K=3, routing="skew", beta=0.5), 96),
+    ("bf16", dict(T=600, H=512, Hp=256, E=32, K=6, routing="skew", beta=3.0), 384),
+    ("fp8", dict(T=300, H=512, Hp=256, E=12, K=3, routing="skew", beta=0.5), 256),
+]
+
+
+@pytest.mark.parametrize("act,spec,hs", SHARED_CASES, ids=[c[0] for c in SHARED_CASES])
+def test_layer_shared_expert(act, spec, hs):
+    say(f"layer + shared expert (Hs={hs}), {act}: one stream, side stream, scatter combine")
+    from _gpu_run import run_layer_shared
+    from _oracle_run import oracle_layer_shared
+    wgt, outf = FMT[act]
+    w = gen.make(**spec, act=act, wgt=wgt, out=outf, cid=65, device=DEV, shared_hs=hs)
+    ref = oracle_layer_shared(w)
+    out1, _ = run_layer_shared(w)
+    side = torch.cuda.Stream()
+    out2, _ = run_layer_shared(w, side_stream=side)
+    out3, _ = run_layer_shared(w, combine=moe.MOE_COMBINE_SCATTER_ATOMIC, side_stream=side)
+    torch.cuda.synchronize()
+    e1 = rel_err(decode_out(w, out1), ref["out"])
+    e3 = rel_err(decode_out(w, out3), ref["out"])
+    es = rel_err(decode_out(w, out1), ref["out"] - ref["y_shared"])   # without the shared part
+    print(f"  out rel err {e1:.3e} (scatter {e3:.3e}); without the shared term it would be {es:.3e}",
+          flush=True)
+    assert np.array_equal(host(out1), host(out2))          # the side stream changes nothing
+    assert e1 <= TOL[w.act] and e3 <= TOL[w.act]
+    assert es > 10 * TOL[w.act]                              # the shared term is really there
+
+
+def test_combine_shared_entry_point():
+    say("moe_combine_shared = moe_combine + the shared row, bitwise on exact inputs")
+    T, H, K = 64, 256, 2
+    g = torch.Generator(device="cpu").manual_seed(3)
+    # values on a coarse grid so the fp32 sums are exact in any order
+    y = (torch.randint(-64, 64, (T * K, H), generator=g).float() / 64).to(DEV)
+    add = (torch.randint(-64, 64, (T, H), generator=g).float() / 64).to(DEV)
+    pos = torch.randperm(T * K, generator=g).view(T, K).int().to(DEV)
+    tw = torch.full((T, K), 0.5, device=DEV)
+    out = torch.empty((T, H), device=DEV)
+    base = torch.empty((T, H), device=DEV)
+    moe.moe_combine_shared(y, moe.MOE_F32, pos, tw, T, H, K, add, out, moe.MOE_F32)
+    moe.moe_combine(y, moe.MOE_F32, pos, tw, T, H, K, base, moe.MOE_F32)
+    torch.cuda.synchronize()
+    assert torch.equal(out, base + add)

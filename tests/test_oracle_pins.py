@@ -196,6 +196,38 @@ def test_layer_equals_direct_expert_loop(T, H, Hp, E, K, seed):
     assert np.abs(res["out"] - ref).max() <= 1e-12 * scale
 
 
+def test_shared_expert_hand_computable_and_added():
+    """Shared expert with H = Hs and Ws_gate = a I, Ws_up = I, Ws_down = P (a permutation):
+    SharedExpert(x) = P-permuted silu(a x) * x elementwise, and it is added to the routed
+    sum (MoE(x) = SharedExpert(x) + sum_k w_k Expert_k(x), "Mixture of Kittens", Step 1)."""
+    x = np.array([[1.0, -2.0, 0.0], [0.5, 3.0, -1.0]])
+    a = 2.0
+    P = np.array([[0, 1.0, 0], [0, 0, 1.0], [1.0, 0, 0]])     # column j of the output = input j-1
+    ys = O.shared_expert(x, a * np.eye(3), np.eye(3), P)
+    s = lambda z: z / (1 + math.exp(-z))
+    elem = np.array([[s(a * v) * v for v in row] for row in x])
+    np.testing.assert_allclose(ys, elem[:, [2, 0, 1]], rtol=1e-15)
+    # routed part: one expert with zero down weights contributes nothing, so out == ys
+    zero = (np.eye(3), np.eye(3), np.zeros((3, 3)))
+    res = O.layer_with_shared(x, x, 1, 1, lambda e: zero, (a * np.eye(3), np.eye(3), P),
+                              topk_idx=np.zeros((2, 1), np.int32), topk_w=np.ones((2, 1)))
+    np.testing.assert_allclose(res["out"], elem[:, [2, 0, 1]], rtol=1e-15)
+
+
+def test_shared_expert_equal_to_the_routed_one_doubles_the_output():
+    """E=1, K=1 (weight 1) and shared weights equal to the expert's: out = 2 x dense FFN
+    (the shared output is added, not overwritten or dropped)."""
+    rng = np.random.default_rng(7)
+    T, H, Hs = 9, 8, 4
+    x = rng.standard_normal((T, H))
+    wg, wu, wd = rng.standard_normal((H, Hs)), rng.standard_normal((H, Hs)), rng.standard_normal((Hs, H))
+    res = O.layer_with_shared(x, x, 1, 1, lambda e: (wg, wu, wd), (wg, wu, wd),
+                              topk_idx=np.zeros((T, 1), np.int32), topk_w=np.ones((T, 1)))
+    g, u = x @ wg, x @ wu
+    dense = (g / (1 + np.exp(-g)) * u) @ wd
+    np.testing.assert_allclose(res["out"], 2 * dense, rtol=1e-12, atol=1e-12)
+
+
 # ----------------------------------------------------------------------------- formats
 
 def test_e2m1_and_e8m0_tables():

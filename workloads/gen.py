@@ -17,7 +17,7 @@ Recipe (all draws seeded; every tensor is reproducible on its own):
   part of the layer.
 
 tensor_id: 0 x, 1 logits / router matrix, 2 W_gate, 3 W_up, 4 W_down,
-5 skew permutation, 6 Dirichlet combine weights.
+5 skew permutation, 6 Dirichlet combine weights, 7/8/9 shared-expert W_gate/W_up/W_down.
 
 Storage layouts (row-major, dense):
 
@@ -90,6 +90,16 @@ class Workload:
     sf_up: Optional[torch.Tensor]
     sf_down: Optional[torch.Tensor]
     meta: dict
+    # optional shared expert: bf16 (fp32 in an fp32 layer) weights [H, Hs], [H, Hs], [Hs, H]
+    # and, for an fp8 layer, the bf16 activations it reads (the same draw as x, before fp8)
+    ws_gate: Optional[torch.Tensor] = None
+    ws_up: Optional[torch.Tensor] = None
+    ws_down: Optional[torch.Tensor] = None
+    x_shared: Optional[torch.Tensor] = None
+
+    @property
+    def Hs(self) -> int:
+        return 0 if self.ws_gate is None else int(self.ws_gate.shape[1])
 
     @property
     def M(self) -> int:
@@ -211,7 +221,7 @@ def _draw_weights(device, seed, cid, E, H, Hp, wgt):
 
 # ----------------------------------------------------------------------------- public
 def make(*, T, H, Hp, E, K, act="bf16", wgt="bf16", out="bf16", routing="normal",
-         beta=0.0, maxvio=None, seed=0, cid=99, device="cpu", name=None) -> Workload:
+         beta=0.0, maxvio=None, seed=0, cid=99, device="cpu", name=None, shared_hs=0) -> Workload:
     """Draw one workload. ``routing`` is one of:
 
     * ``"xwr"``: logits = x . Wr computed once in fp64 and rounded to fp32, Wr N(0, 1/H);
@@ -258,15 +268,28 @@ def make(*, T, H, Hp, E, K, act="bf16", wgt="bf16", out="bf16", routing="normal"
         raise ValueError(routing)
 
     wg, wu, wd, sg, su, sd = _draw_weights(device, seed, cid, E, H, Hp, wgt)
+    shared = {}
+    if shared_hs:
+        sdt = torch.float32 if act == "f32" else torch.bfloat16
+        for key, tid, shp, std in (("ws_gate", 7, (H, shared_hs), 1.0 / math.sqrt(H)),
+                                   ("ws_up", 8, (H, shared_hs), 1.0 / math.sqrt(H)),
+                                   ("ws_down", 9, (shared_hs, H), 1.0 / math.sqrt(shared_hs))):
+            g = _torch_gen(device, seed, cid, tid, 0)
+            shared[key] = (torch.randn(shp, generator=g, device=device) * std).to(sdt)
+        if act == "fp8":
+            shared["x_shared"] = x32.to(torch.bfloat16).to(device)
     return Workload(name=name or f"custom_T{T}_H{H}_Hp{Hp}_E{E}_K{K}_{act}_{wgt}",
                     T=T, H=H, Hp=Hp, E=E, K=K, act=act, wgt=wgt, out=out,
                     x=x, x_sf=x_sf, logits=logits, topk_idx=topk_idx, topk_w=topk_w,
                     w_gate=wg, w_up=wu, w_down=wd, sf_gate=sg, sf_up=su, sf_down=sd,
-                    meta=dict(routing=routing, beta=beta, maxvio_target=maxvio, seed=seed, cid=cid))
+                    meta=dict(routing=routing, beta=beta, maxvio_target=maxvio, seed=seed, cid=cid),
+                    **shared)
 
 
-def config(name: str, device="cpu", maxvio: Optional[float] = None, seed: int = 0) -> Workload:
-    """One of the five named workloads at full size (c4 takes a maxvio target; c5 uses 1)."""
+def config(name: str, device="cpu", maxvio: Optional[float] = None, seed: int = 0,
+           shared_hs: int = 0) -> Workload:
+    """One of the five named workloads at full size (c4 takes a maxvio target; c5 uses 1).
+    ``shared_hs`` > 0 adds a shared expert of that intermediate size."""
     s = dict(_SHAPES[name])
     routing = s.pop("routing")
     beta = 0.0
@@ -278,7 +301,7 @@ def config(name: str, device="cpu", maxvio: Optional[float] = None, seed: int = 
         beta = skew_beta(s["T"], s["E"], s["K"], maxvio, lowp=(name == "c5"))
     label = name if maxvio is None or name == "c5" else f"{name}_maxvio{maxvio:g}"
     return make(**s, routing=routing, beta=beta, maxvio=maxvio, seed=seed,
-                cid=_CONFIG_ID[name], device=device, name=label)
+                cid=_CONFIG_ID[name], device=device, name=label, shared_hs=shared_hs)
 
 
 def to_numpy_bits(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
