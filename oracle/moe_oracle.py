@@ -141,6 +141,41 @@ def requant_fp8_1x128(h: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
     return (q * s[:, :, None]).reshape(R, C), s
 
 
+def encode_e4m3fn(v: np.ndarray) -> np.ndarray:
+    """e4m3fn values (already on the grid, |v| <= 448) -> codes uint8. The sign bit is the
+    value's (so -0.0 -> 0x80); magnitudes >= 2^-6 are normal (exponent field floor(log2|v|)
+    + 7, 3 mantissa bits), smaller ones subnormal (mantissa |v| / 2^-9)."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    sign = np.where(np.signbit(v), 0x80, 0).astype(np.int64)
+    with np.errstate(divide="ignore"):
+        p = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    p = np.where(np.exp2(p) > a, p - 1, p)
+    p = np.where(np.exp2(p + 1) <= a, p + 1, p)
+    normal = a >= 2.0 ** -6
+    mant_n = np.round((a / np.exp2(p) - 1.0) * 8).astype(np.int64)
+    code_n = ((p.astype(np.int64) + 7) << 3) | mant_n
+    code_s = np.round(a / 2.0 ** -9).astype(np.int64)
+    code = np.where(normal, code_n, code_s)
+    if np.any(code > 0x7E) or np.any(round_e4m3fn(v) != v):
+        raise ValueError("value not representable in e4m3fn")
+    return (sign | code).astype(np.uint8)
+
+
+def quantize_fp8_1x128(x: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Activation quantisation ("Mixture of Kittens", Step 8: activations are quantised
+    to fp8 before the GEMMs, with the quantisation fused into dispatch): rows of x [R, C]
+    -> (e4m3fn codes uint8 [R, C], power-of-two scales [R, C/128]) by the 1x128 rule of
+    ``requant_fp8_1x128`` (decision on the fp32 value)."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float64)
+    R, C = x32.shape
+    blocks = x32.reshape(R, C // 128, 128)
+    s = fp8_block_scale(np.abs(blocks).max(axis=2))
+    q = round_e4m3fn(blocks / s[:, :, None])
+    # a block of zeros keeps the signs of its zeros; others round ties to even
+    return encode_e4m3fn(q.reshape(R, C)), s
+
+
 # ----------------------------------------------------------------------------- routing
 
 
@@ -194,6 +229,38 @@ def permute(topk_idx: np.ndarray, E: int) -> Tuple[np.ndarray, np.ndarray]:
             pos[t, k] = r
             row_src[r] = t * K + k
     return pos, row_src
+
+
+def padded_offsets(counts: np.ndarray, pad: int) -> np.ndarray:
+    """cu_seqlens [E+1] when every expert's group is padded up to a multiple of ``pad``
+    rows (MoonEP "API walkthrough": token_padding and a padded cu_seqlens; "Distributed
+    expert parallelism", "Static-capacity versus dropless dispatch": groups padded to
+    hardware-friendly multiples). The counts themselves stay the real ones."""
+    cu = np.zeros(len(counts) + 1, dtype=np.int64)
+    for e, c in enumerate(counts):
+        cu[e + 1] = cu[e] + (int(c) + pad - 1) // pad * pad
+    return cu
+
+
+def permute_padded(topk_idx: np.ndarray, E: int, pad: int) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """``permute`` into padded groups: expert e's copies fill rows cu[e] .. cu[e]+counts[e]-1
+    (same stable order) and the rest of its group is padding (row_src = -1). Returns
+    (pos [T, K], row_src [capacity], cu [E+1]) with capacity = T*K + E*(pad-1), the static
+    buffer size that any routing fits."""
+    idx = np.asarray(topk_idx)
+    T, K = idx.shape
+    counts, _ = count_offsets(idx, E)
+    cu = padded_offsets(counts, pad)
+    fill = cu[:-1].copy()
+    pos = np.empty((T, K), dtype=np.int64)
+    row_src = np.full(T * K + E * (pad - 1), -1, dtype=np.int64)
+    for t in range(T):
+        for k in range(K):
+            e = int(idx[t, k])
+            pos[t, k] = fill[e]
+            row_src[fill[e]] = t * K + k
+            fill[e] += 1
+    return pos, row_src, cu
 
 
 def maxvio(counts: np.ndarray, T: int, K: int, E: int) -> float:

@@ -228,6 +228,61 @@ def test_shared_expert_equal_to_the_routed_one_doubles_the_output():
     np.testing.assert_allclose(res["out"], 2 * dense, rtol=1e-12, atol=1e-12)
 
 
+# ----------------------------------------------------------------------------- padding, quantisation
+
+def test_padded_offsets_four_rank_example_and_closed_forms():
+    ex = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "four_rank_example.json")))
+    counts = np.array(ex["counts"])
+    # pad 2: each group rounded up to even -> [2,2,0,2,0,2,2,0]
+    assert O.padded_offsets(counts, 2).tolist() == [0, 2, 4, 4, 6, 6, 8, 10, 10]
+    assert O.padded_offsets(counts, 1).tolist() == ex["cu_seqlens"]
+    rng = np.random.default_rng(11)
+    c = rng.integers(0, 300, size=37)
+    cu = O.padded_offsets(c, 128)
+    sizes = np.diff(cu)
+    assert np.all(sizes % 128 == 0) and np.all(sizes >= c) and np.all(sizes - c < 128)
+    assert np.all((sizes == 0) == (c == 0))
+
+
+def test_permute_padded_matches_unpadded_within_groups():
+    rng = np.random.default_rng(12)
+    T, K, E, pad = 50, 3, 7, 8
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    pos, rs = O.permute(idx, E)
+    ppos, prs, cu = O.permute_padded(idx, E, pad)
+    counts, cu0 = O.count_offsets(idx, E)
+    assert len(prs) == T * K + E * (pad - 1)
+    for e in range(E):   # same copies, same order, shifted to the padded group start
+        assert np.array_equal(prs[cu[e]:cu[e] + counts[e]], rs[cu0[e]:cu0[e + 1]])
+        assert np.all(prs[cu[e] + counts[e]:cu[e + 1]] == -1)
+    assert np.all(prs[cu[-1]:] == -1)
+    flat = np.arange(T * K).reshape(T, K)
+    assert np.array_equal(prs[ppos], flat)    # exact inversion
+
+
+def test_encode_e4m3fn_inverts_decode_for_every_code():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(O.encode_e4m3fn(O.decode_e4m3fn(codes)), codes)
+    assert O.encode_e4m3fn(np.array([-0.0]))[0] == 0x80
+    with pytest.raises(ValueError):
+        O.encode_e4m3fn(np.array([0.3]))          # not on the grid
+
+
+def test_quantize_fp8_matches_requant_and_torch():
+    rng = np.random.default_rng(13)
+    x = rng.standard_normal((6, 384)) * np.exp2(rng.integers(-8, 8, size=(6, 1)))
+    x[2, :128] = 0.0                                   # an all-zero block: scale 1, codes 0
+    codes, s = O.quantize_fp8_1x128(x)
+    vals, s2 = O.requant_fp8_1x128(x)
+    assert np.array_equal(s, s2)
+    assert np.array_equal(O.decode_e4m3fn(codes) * np.repeat(s, 128, axis=1), vals)
+    assert np.all(codes[2, :128] == 0) and s[2, 0] == 1.0
+    # torch's float8_e4m3fn cast of the same exact fp32 quotients gives the same bytes
+    q32 = torch.from_numpy((x.astype(np.float32).astype(np.float64) / np.repeat(s, 128, axis=1)).astype(np.float32))
+    tb = q32.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(tb, codes)
+
+
 # ----------------------------------------------------------------------------- formats
 
 def test_e2m1_and_e8m0_tables():
