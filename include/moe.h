@@ -80,7 +80,9 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_
 typedef enum { MOE_COMBINE_GATHER = 0, MOE_COMBINE_SCATTER_ATOMIC = 1 } moe_combine_t;
 
 /* Whole-layer description. Supported (act, wgt, out) combinations:
- *  (F32, F32, F32), (BF16, BF16, BF16), (FP8_E4M3, MXFP4, BF16). */
+ *  (F32, F32, F32), (BF16, BF16, BF16), (FP8_E4M3, MXFP4, BF16), and (BF16, MXFP4, BF16):
+ *  BF16 activations quantised on entry to FP8_E4M3 with 1x128 scales (moe_quantize_fp8),
+ *  then the FP8_E4M3 x MXFP4 path. */
 typedef struct {
   int32_t T, H, Hp, E, K;
   moe_dtype_t act, wgt, out;
@@ -126,6 +128,39 @@ MOE_API moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t a
                          int32_t* pos, int32_t* row_src, float* row_w, void* x_perm,
                          float* x_perm_sf, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* The static-capacity (padded) variant of moe_permute (MoonEP "API walkthrough": buffer
+ * token_padding and a padded cu_seqlens; "Distributed expert parallelism", "Static-capacity
+ * versus dropless dispatch" and "Hidden padding in metrics"): every expert group is padded
+ * up to a multiple of `pad` rows inside a static buffer of moe_padded_capacity(T, E, K, pad)
+ * = T*K + E*(pad-1) rows, which holds any routing.
+ *  counts      [E] out: the real copies per expert (log these beside the padded sizes).
+ *  cu_seqlens  [E+1] out: padded group offsets, cu[e+1] - cu[e] = ceil(counts[e]/pad)*pad.
+ *  row_src, row_w [capacity] out: real rows as in moe_permute; padding rows (inside the
+ *              groups and past cu[E]) hold row_src = -1 and row_w = 0.
+ *  x_perm      [capacity, H] out or NULL: real rows as in moe_permute, padding rows inside
+ *              the groups zero; x_perm_sf [H/128, capacity] (FP8) with scale 1 for them.
+ * The grouped FFN entry points accept the padded cu_seqlens with M = capacity; padding rows
+ * compute zeros (and are skipped by the gather and scatter row maps, which read
+ * row_src = -1 as a padding row). Other arguments and limits as moe_permute; pad >= 1
+ * (pad = 1 is moe_permute). */
+MOE_API int64_t moe_padded_capacity(int32_t T, int32_t E, int32_t K, int32_t pad);
+MOE_API moe_status_t moe_permute_padded(const void* x, const float* x_sf, moe_dtype_t act,
+                                const int32_t* topk_idx, const float* topk_w, int32_t T, int32_t H,
+                                int32_t E, int32_t K, int32_t pad, int32_t* counts,
+                                int32_t* cu_seqlens, int32_t* pos, int32_t* row_src, float* row_w,
+                                void* x_perm, float* x_perm_sf, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* Activation quantisation to FP8_E4M3 with 1x128 power-of-two scales ("Mixture of
+ * Kittens", Step 8: activations are quantised for the fp8 GEMMs, fused into dispatch):
+ * for each row r and block b of 128 columns, s[r][b] = the smallest power of two with
+ * 448*s >= max |x[r][128b..128b+127]| (1 for an all-zero block) and
+ * q[r][c] = e4m3fn round-to-nearest-even(x[r][c] / s[r][b]) (an exact zero gives code 0).
+ *  x [R, C] of x_dtype (BF16 or F32), 16-byte aligned, C % 128 == 0;
+ *  q [R, C] codes out (8-byte aligned); sf [R, C/128] fp32 out (the x_sf layout). */
+MOE_API moe_status_t moe_quantize_fp8(const void* x, moe_dtype_t x_dtype, int32_t R, int32_t C,
+                              uint8_t* q, float* sf, hipStream_t stream);
+
 /* First half of the grouped expert FFN ("Mixture of Kittens", Step 1; "Distributed expert
  * parallelism", "Grouped expert computation"): for every expert e and its rows
  * r in [cu_seqlens[e], cu_seqlens[e+1]):
@@ -154,8 +189,9 @@ MOE_API moe_status_t moe_ffn_gate_up(const void* x_perm, const float* x_perm_sf,
  *     h[r] = silu(x[row_src[r]/K] . Wg[e]) * (x[row_src[r]/K] . Wu[e]),
  * bitwise the same h as moe_ffn_gate_up on the x_perm that moe_permute would write.
  *  x [T, H] of format `act`; x_sf [T, H/128] fp32 (FP8_E4M3, the token layout of
- *  moe_permute's x_sf); row_src [M] from moe_permute; other arguments as moe_ffn_gate_up.
- * Needs M <= T*K and T*H*bytes(act) < 2^31 (MOE_EUNSUPPORTED otherwise). */
+ *  moe_permute's x_sf); row_src [M] from moe_permute or moe_permute_padded (a row with
+ *  row_src = -1 is a padding row and reads zeros); other arguments as moe_ffn_gate_up.
+ * Needs T*H*bytes(act) < 2^31 (MOE_EUNSUPPORTED otherwise). */
 MOE_API moe_status_t moe_ffn_gate_up_gather(const void* x, const float* x_sf, moe_dtype_t act,
                                     const int32_t* row_src, int32_t T, int32_t K,
                                     const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
@@ -179,8 +215,8 @@ MOE_API moe_status_t moe_ffn_down(const void* h, const float* h_sf, moe_dtype_t 
  *     acc[row_src[r] / K] += row_w[r] * (h[r] . Wd[e]),
  * added with fp32 atomics, so the order of the K additions of a token (and its last bit) may
  * vary between runs. acc [T, H] fp32 is accumulated into: the caller zeroes it first.
- * row_src, row_w [M] from moe_permute. Formats and limits as moe_ffn_down (y_rows is not
- * written). */
+ * row_src, row_w [M] from moe_permute or moe_permute_padded (rows with row_src = -1 are
+ * skipped). Formats and limits as moe_ffn_down (y_rows is not written). */
 MOE_API moe_status_t moe_ffn_down_scatter(const void* h, const float* h_sf, moe_dtype_t h_dtype,
                                   const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
                                   int32_t Hp, const void* w_down, const uint8_t* sf_down,
@@ -278,7 +314,8 @@ MOE_API moe_status_t moe_layer_forward_shared(const moe_layer_desc_t* d, int32_t
  * offsets[i] (i in order): 0 topk_idx, 1 topk_w, 2 counts, 3 cu_seqlens, 4 pos, 5 row_src,
  * 6 row_w (scatter combine), 7 x_perm and 8 x_perm_sf (only when x_perm is written),
  * 9 h, 10 h_sf, 11 y_rows (gather combine), 12 permute scratch, 13 fp32 accumulator (scatter
- * combine with a BF16 output). Unused entries are set to SIZE_MAX. Writes n <= 14 entries;
+ * combine with a BF16 output), 14 x_q and 15 x_q_sf (the quantised activations of a
+ * (BF16, MXFP4) layer). Unused entries are set to SIZE_MAX. Writes n <= 16 entries;
  * returns MOE_EINVAL for an invalid `d`. Host-only; the sizes depend on MOE_LAYER_XPERM. */
 MOE_API moe_status_t moe_layer_workspace_layout(const moe_layer_desc_t* d, size_t* offsets, int32_t n);
 

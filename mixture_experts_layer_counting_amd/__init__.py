@@ -25,9 +25,10 @@ MOE_COMBINE_GATHER, MOE_COMBINE_SCATTER_ATOMIC = range(2)
 
 # offsets reported by moe_layer_workspace_layout, in order
 WS_FIELDS = ("topk_idx", "topk_w", "counts", "cu_seqlens", "pos", "row_src", "row_w", "x_perm",
-             "x_perm_sf", "h", "h_sf", "y_rows", "permute_scratch", "acc_f32")
+             "x_perm_sf", "h", "h_sf", "y_rows", "permute_scratch", "acc_f32", "x_q", "x_q_sf")
 
-EXPORTS = ("moe_route_topk", "moe_permute_workspace_bytes", "moe_permute", "moe_ffn_gate_up",
+EXPORTS = ("moe_route_topk", "moe_permute_workspace_bytes", "moe_permute", "moe_padded_capacity",
+           "moe_permute_padded", "moe_quantize_fp8", "moe_ffn_gate_up",
            "moe_ffn_gate_up_gather", "moe_ffn_down", "moe_ffn_down_scatter",
            "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn", "moe_combine",
            "moe_combine_shared", "moe_layer_workspace_bytes", "moe_layer_forward",
@@ -60,6 +61,10 @@ _SIGS = {
     "moe_permute_workspace_bytes": (_S, [_I, _I, _I]),
     "moe_permute": (_I, [_P, _P, _E, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
     "moe_ffn_gate_up": (_I, [_P, _P, _E, _P, _I, _I, _I, _I, _P, _P, _P, _P, _E, _P, _P, _P]),
+    "moe_padded_capacity": (ctypes.c_int64, [_I, _I, _I, _I]),
+    "moe_permute_padded": (_I, [_P, _P, _E, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
+                                _P, _S, _P]),
+    "moe_quantize_fp8": (_I, [_P, _E, _I, _I, _P, _P, _P]),
     "moe_ffn_gate_up_gather": (_I, [_P, _P, _E, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _E,
                                     _P, _P, _P]),
     "moe_ffn_down_scatter": (_I, [_P, _P, _E, _P, _I, _I, _I, _I, _P, _P, _E, _P, _P, _I, _I, _P,
@@ -141,6 +146,23 @@ def moe_permute(x, x_sf, act, topk_idx, topk_w, T, H, E, K, counts, cu_seqlens, 
                              _ptr(counts), _ptr(cu_seqlens), _ptr(pos), _ptr(row_src), _ptr(row_w),
                              _ptr(x_perm), _ptr(x_perm_sf), _ptr(ws), ws_bytes, _stream(stream)),
            "moe_permute")
+
+
+def moe_padded_capacity(T, E, K, pad) -> int:
+    return int(lib().moe_padded_capacity(T, E, K, pad))
+
+
+def moe_permute_padded(x, x_sf, act, topk_idx, topk_w, T, H, E, K, pad, counts, cu_seqlens, pos,
+                       row_src, row_w, x_perm, x_perm_sf, ws, ws_bytes, stream=None):
+    _check(lib().moe_permute_padded(_ptr(x), _ptr(x_sf), act, _ptr(topk_idx), _ptr(topk_w), T, H, E,
+                                    K, pad, _ptr(counts), _ptr(cu_seqlens), _ptr(pos), _ptr(row_src),
+                                    _ptr(row_w), _ptr(x_perm), _ptr(x_perm_sf), _ptr(ws), ws_bytes,
+                                    _stream(stream)), "moe_permute_padded")
+
+
+def moe_quantize_fp8(x, x_dtype, R, C, q, sf, stream=None):
+    _check(lib().moe_quantize_fp8(_ptr(x), x_dtype, R, C, _ptr(q), _ptr(sf), _stream(stream)),
+           "moe_quantize_fp8")
 
 
 def moe_ffn_gate_up(x_perm, x_perm_sf, act, cu_seqlens, M, E, H, Hp, w_gate, w_up, sf_gate, sf_up,

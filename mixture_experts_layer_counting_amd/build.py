@@ -17,8 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 
-SOURCES = ["route_topk.hip", "permute.hip", "combine.hip", "ffn_f32.hip", "ffn_bf16.hip",
-           "ffn_fp8.hip", "moe_api.cpp"]
+SOURCES = ["route_topk.hip", "permute.hip", "combine.hip", "quant.hip", "ffn_f32.hip",
+           "ffn_bf16.hip", "ffn_fp8.hip", "moe_api.cpp"]
 
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

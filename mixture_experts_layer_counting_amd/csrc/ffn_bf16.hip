@@ -30,10 +30,11 @@
 //  * Rows past the group's last row of the tile are loaded out of the A descriptor's range,
 //    so they read as zeros without memory traffic; they are never stored.
 //  * Optional row maps ("Mixture of Kittens", Step 6 gathers its inputs by token index and
-//    scatters its outputs; the survey's fused layer): with `a_src`, A row r of the group is
+//    scatters its outputs): with `a_src`, A row r of the group is
 //    row a_src[r] / a_k of A (the token matrix x, no permuted copy); with `s_acc`, the down
 //    epilogue adds s_w[r] * y[r] into s_acc[s_src[r] / s_k] with fp32 atomics instead of
-//    storing y (the weighted combine fused into the down projection).
+//    storing y (the weighted combine fused into the down projection). A negative source
+//    index marks a padding row of a padded layout: it gathers zeros and scatters nothing.
 #include "moe_common.h"
 #include "tile_sched.h"
 
@@ -218,10 +219,10 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
       // source row's offset
       rA = make_rsrc(A, (uint32_t)maps.a_rows * (uint32_t)Kd * 2u);
 #pragma unroll
-      for (int i = 0; i < CF::A_LD; ++i)
-        a_off[i] = a_row[i] < rows_valid
-                       ? (maps.a_src[row0 + a_row[i]] / maps.a_k - a_row[i]) * Kd * 2 + a_voff[i]
-                       : (int)0x80000000u;
+      for (int i = 0; i < CF::A_LD; ++i) {
+        const int src = a_row[i] < rows_valid ? maps.a_src[row0 + a_row[i]] : -1;  // -1: padding row
+        a_off[i] = src >= 0 ? (src / maps.a_k - a_row[i]) * Kd * 2 + a_voff[i] : (int)0x80000000u;
+      }
     } else {
       rA = make_rsrc(A + (size_t)row0 * Kd, (uint32_t)rows_valid * (uint32_t)Kd * 2u);
 #pragma unroll
@@ -302,9 +303,10 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          if (r < rows_valid) {
+          const int src = r < rows_valid ? maps.s_src[row0 + r] : -1;  // -1: padding row
+          if (src >= 0) {
             const int gr = row0 + r;
-            float* dst = maps.s_acc + (size_t)(maps.s_src[gr] / maps.s_k) * N + n0 + wn * CF::WN + (lane & 31);
+            float* dst = maps.s_acc + (size_t)(src / maps.s_k) * N + n0 + wn * CF::WN + (lane & 31);
             const float w = maps.s_w[gr];
 #pragma unroll
             for (int nt = 0; nt < CF::NT; ++nt) unsafeAtomicAdd(dst + nt * 32, w * acc[0][mt][nt][i]);

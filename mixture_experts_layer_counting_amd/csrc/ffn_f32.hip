@@ -45,7 +45,7 @@ __global__ __launch_bounds__(FF_THREADS) void ffn_f32_kernel(
     const float* W1 = GATED ? B1 + (size_t)e * Kd * N : nullptr;
     __syncthreads();  // previous tile's readers of sRow are done
     for (int r = tid; r < FF_BM; r += FF_THREADS)
-      sRow[r] = r < rows_valid ? (maps.a_src ? maps.a_src[row0 + r] / maps.a_k : row0 + r) : 0;
+      sRow[r] = r < rows_valid ? (maps.a_src ? maps.a_src[row0 + r] : (row0 + r) * maps.a_k) : -1;
     __syncthreads();
     float acc[NB][4][4];
     for (int b = 0; b < NB; ++b)
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(FF_THREADS) void ffn_f32_kernel(
     for (int k0 = 0; k0 < Kd; k0 += FF_BK) {
       for (int q = tid; q < FF_BM * FF_BK; q += FF_THREADS) {
         const int r = q / FF_BK, k = q % FF_BK;
-        sA[k][r] = (r < rows_valid && k0 + k < Kd) ? A[(size_t)sRow[r] * Kd + k0 + k] : 0.f;
+        sA[k][r] = (sRow[r] >= 0 && k0 + k < Kd) ? A[(size_t)(sRow[r] / maps.a_k) * Kd + k0 + k] : 0.f;
       }
       for (int q = tid; q < FF_BK * FF_BN; q += FF_THREADS) {
         const int k = q / FF_BN, n = q % FF_BN;
@@ -85,9 +85,10 @@ __global__ __launch_bounds__(FF_THREADS) void ffn_f32_kernel(
           v = silu_f32(acc[0][i][j]) * acc[1][i][j];
         else
           v = acc[0][i][j];
-        if (!GATED && maps.s_acc)
-          unsafeAtomicAdd(maps.s_acc + (size_t)(maps.s_src[row0 + r] / maps.s_k) * N + n, maps.s_w[row0 + r] * v);
-        else
+        if (!GATED && maps.s_acc) {
+          const int src = maps.s_src[row0 + r];  // -1: padding row
+          if (src >= 0) unsafeAtomicAdd(maps.s_acc + (size_t)(src / maps.s_k) * N + n, maps.s_w[row0 + r] * v);
+        } else
           C[(size_t)(row0 + r) * N + n] = v;
       }
     }

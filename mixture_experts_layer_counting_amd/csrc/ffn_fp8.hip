@@ -112,27 +112,6 @@ __device__ __forceinline__ void f8_wait_barrier() {
   asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-// e8m0 byte of an fp32 power of two
-__device__ __forceinline__ int pow2_to_e8m0(float s) { return (__float_as_uint(s) >> 23) & 0xff; }
-
-// fp32 -> OCP e4m3fn code, round to nearest even; |v| <= 448 by construction of the scale.
-__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sgn = (u >> 24) & 0x80u;
-  const float a = __builtin_fabsf(v);
-  uint32_t code;
-  if (a < 0.015625f) {  // below 2^-6: subnormal grid of step 2^-9 (code 8 is 2^-6 itself)
-    code = (uint32_t)__builtin_rintf(a * 512.0f);
-  } else {
-    const uint32_t m = u & 0x7fffffffu;
-    const uint32_t r = (m + 0x7ffffu + ((m >> 20) & 1u)) >> 20;  // keep 3 mantissa bits, RNE
-    code = r - ((127u - 7u) << 3);
-    if (code > 0x7eu) code = 0x7eu;                               // saturate at 448
-  }
-  return sgn | code;
-}
-
-// MAPPED: gate/up gathers its A rows and scales, down scatters (compile-time, as in bf16)
 template <bool GATED, int BN, bool MAPPED>
 __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ A_sf, const int* __restrict__ cu,
@@ -218,10 +197,12 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     if constexpr (GATED && MAPPED) {
       rA = f8_rsrc(A, (uint32_t)maps.a_rows * (uint32_t)Kd);
 #pragma unroll
-      for (int i = 0; i < CF::A_LD; ++i)
-        a_ld_off[i] = a_row[i] < rows_valid ? (maps.a_src[row0 + a_row[i]] / maps.a_k - a_row[i]) * Kd + a_voff[i]
-                                         : (int)0x80000000u;
-      sc_voff = sc_row < rows_valid ? (maps.a_src[row0 + sc_row] / maps.a_k) * nsf * 4 : (int)0x80000000u;
+      for (int i = 0; i < CF::A_LD; ++i) {
+        const int src = a_row[i] < rows_valid ? maps.a_src[row0 + a_row[i]] : -1;  // -1: padding row
+        a_ld_off[i] = src >= 0 ? (src / maps.a_k - a_row[i]) * Kd + a_voff[i] : (int)0x80000000u;
+      }
+      const int ssrc = sc_row < rows_valid ? maps.a_src[row0 + sc_row] : -1;
+      sc_voff = ssrc >= 0 ? (ssrc / maps.a_k) * nsf * 4 : (int)0x80000000u;
     } else {
       rA = f8_rsrc(A + (size_t)row0 * Kd, (uint32_t)rows_valid * (uint32_t)Kd);
 #pragma unroll
@@ -364,14 +345,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
         for (int i = 0; i < 16; ++i) {
           const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3);
           const float amax = fmaxf(part[r], part[256 + r]);
-          // smallest power of two s with 448 s >= amax (amax = 0 -> 1)
-          float s = 1.0f;
-          if (amax > 0.f) {
-            int ex;
-            const float mant = __builtin_frexpf(amax / 448.0f, &ex);  // amax/448 = mant * 2^ex
-            s = __builtin_ldexpf(1.0f, mant == 0.5f ? ex - 1 : ex);
-            if (448.0f * s < amax) s *= 2.0f;
-          }
+          const float s = fp8_pow2_scale(amax);
           const float inv = 1.0f / s;
           if (r < rows_valid) {
             const size_t ro = (size_t)(row0 + r);
@@ -389,9 +363,10 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3);
-          if (r < rows_valid) {
+          const int src = r < rows_valid ? maps.s_src[row0 + r] : -1;  // -1: padding row
+          if (src >= 0) {
             const int gr = row0 + r;
-            float* dst = maps.s_acc + (size_t)(maps.s_src[gr] / maps.s_k) * N + n0 + wn * CF::WN + (lane & 31);
+            float* dst = maps.s_acc + (size_t)(src / maps.s_k) * N + n0 + wn * CF::WN + (lane & 31);
             const float w = maps.s_w[gr];
 #pragma unroll
             for (int nt = 0; nt < CF::NT; ++nt) unsafeAtomicAdd(dst + nt * 32, w * acc[0][mt][nt][i]);

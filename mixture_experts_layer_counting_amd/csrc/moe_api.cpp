@@ -16,8 +16,10 @@ size_t permute_ws_bytes(int T, int E, int K);
 moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes, const int* topk_idx,
                             const float* topk_w, int T, int H, int E, int K, int* counts,
                             int* cu_seqlens, int* pos, int* row_src, float* row_w, void* x_perm,
-                            float* x_perm_sf, void* ws, bool validate, int** err_out,
-                            hipStream_t s);
+                            float* x_perm_sf, void* ws, bool validate, int pad, int cap,
+                            int** err_out, hipStream_t s);
+moe_status_t launch_quantize_fp8(const void* x, moe_dtype_t xt, int R, int C, void* q, float* sf,
+                                 hipStream_t s);
 moe_status_t launch_combine(const void*, moe_dtype_t, const int*, const float*, int, int, int,
                             const void*, void*, moe_dtype_t, hipStream_t);
 moe_status_t launch_ffn_gate_up_bf16(const void*, const int*, int, int, int, int, const void*,
@@ -138,12 +140,13 @@ size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t K) {
   return permute_ws_bytes(T, E, K);
 }
 
-moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t act,
-                         const int32_t* topk_idx, const float* topk_w, int32_t T, int32_t H,
-                         int32_t E, int32_t K, int32_t* counts, int32_t* cu_seqlens,
-                         int32_t* pos, int32_t* row_src, float* row_w, void* x_perm,
-                         float* x_perm_sf, void* ws, size_t ws_bytes, hipStream_t stream) {
-  if (T < 0 || H < 1 || E < 1 || K < 1) return MOE_EINVAL;
+static moe_status_t permute_impl(const void* x, const float* x_sf, moe_dtype_t act,
+                                 const int32_t* topk_idx, const float* topk_w, int32_t T, int32_t H,
+                                 int32_t E, int32_t K, int32_t pad, int32_t* counts,
+                                 int32_t* cu_seqlens, int32_t* pos, int32_t* row_src, float* row_w,
+                                 void* x_perm, float* x_perm_sf, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  if (T < 0 || H < 1 || E < 1 || K < 1 || pad < 1) return MOE_EINVAL;
   if (E > 1024 || K > 32) return MOE_EUNSUPPORTED;
   const int eb = act_bytes(act);
   if (eb == 0) return MOE_EUNSUPPORTED;
@@ -155,7 +158,8 @@ moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t act,
     if (H % 128) return MOE_EUNSUPPORTED;
     if (T > 0 && x_perm && (!x_sf || !x_perm_sf)) return MOE_EINVAL;
   }
-  if ((int64_t)T * K > std::numeric_limits<int32_t>::max() / 2) return MOE_EUNSUPPORTED;
+  const int64_t cap = (int64_t)T * K + (int64_t)E * (pad - 1);
+  if (cap > std::numeric_limits<int32_t>::max() / 2) return MOE_EUNSUPPORTED;
   const size_t need = permute_ws_bytes(T, E, K);
   if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
   poison(ws, ws_bytes, stream);
@@ -164,13 +168,46 @@ moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t act,
   const bool sf = act == MOE_FP8_E4M3 && x_perm;
   moe_status_t st = launch_permute(x, sf ? x_sf : nullptr, eb, topk_idx, topk_w, T, H, E, K, counts,
                                    cu_seqlens, pos, row_src, row_w, x_perm, sf ? x_perm_sf : nullptr,
-                                   ws, validate, &err, stream);
+                                   ws, validate, pad, (int)cap, &err, stream);
   if (st != MOE_OK || !validate) return st;
   int h_err = 0;
   if (hipMemcpyAsync(&h_err, err, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess)
     return MOE_EHIP;
   return h_err ? MOE_EINVAL : MOE_OK;
+}
+
+moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t act,
+                         const int32_t* topk_idx, const float* topk_w, int32_t T, int32_t H,
+                         int32_t E, int32_t K, int32_t* counts, int32_t* cu_seqlens,
+                         int32_t* pos, int32_t* row_src, float* row_w, void* x_perm,
+                         float* x_perm_sf, void* ws, size_t ws_bytes, hipStream_t stream) {
+  return permute_impl(x, x_sf, act, topk_idx, topk_w, T, H, E, K, 1, counts, cu_seqlens, pos, row_src,
+                      row_w, x_perm, x_perm_sf, ws, ws_bytes, stream);
+}
+
+int64_t moe_padded_capacity(int32_t T, int32_t E, int32_t K, int32_t pad) {
+  if (T < 0 || E < 1 || K < 1 || pad < 1) return -1;
+  return (int64_t)T * K + (int64_t)E * (pad - 1);
+}
+
+moe_status_t moe_permute_padded(const void* x, const float* x_sf, moe_dtype_t act,
+                                const int32_t* topk_idx, const float* topk_w, int32_t T, int32_t H,
+                                int32_t E, int32_t K, int32_t pad, int32_t* counts,
+                                int32_t* cu_seqlens, int32_t* pos, int32_t* row_src, float* row_w,
+                                void* x_perm, float* x_perm_sf, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  return permute_impl(x, x_sf, act, topk_idx, topk_w, T, H, E, K, pad, counts, cu_seqlens, pos, row_src,
+                      row_w, x_perm, x_perm_sf, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_quantize_fp8(const void* x, moe_dtype_t x_dtype, int32_t R, int32_t C, uint8_t* q,
+                              float* sf, hipStream_t stream) {
+  if (R < 0 || C < 1) return MOE_EINVAL;
+  if (C % 128 || (x_dtype != MOE_BF16 && x_dtype != MOE_F32)) return MOE_EUNSUPPORTED;
+  if (R > 0 && (!x || !q || !sf)) return MOE_EINVAL;
+  if ((uintptr_t)x % 16 || (uintptr_t)q % 8) return MOE_EINVAL;
+  return launch_quantize_fp8(x, x_dtype, R, C, q, sf, stream);
 }
 
 moe_status_t moe_ffn_gate_up(const void* x_perm, const float* x_perm_sf, moe_dtype_t act,
@@ -202,7 +239,7 @@ moe_status_t moe_ffn_gate_up_gather(const void* x, const float* x_sf, moe_dtype_
                                     void* h, float* h_sf, hipStream_t stream) {
   const Path p = ffn_path(act, wgt);
   if (p == PATH_NONE) return MOE_EUNSUPPORTED;
-  if (T < 0 || K < 1 || (int64_t)M > (int64_t)T * K) return MOE_EINVAL;
+  if (T < 0 || K < 1) return MOE_EINVAL;
   moe_status_t st = check_ffn_dims(p, M, E, H, Hp, true);
   if (st != MOE_OK) return st;
   // the gathered rows are addressed with 32-bit byte offsets into x
@@ -248,7 +285,7 @@ moe_status_t moe_ffn_down_scatter(const void* h, const float* h_sf, moe_dtype_t 
                                   int32_t T, int32_t K, float* acc, hipStream_t stream) {
   const Path p = ffn_path(h_dtype, wgt);
   if (p == PATH_NONE) return MOE_EUNSUPPORTED;
-  if (T < 0 || K < 1 || (int64_t)M > (int64_t)T * K) return MOE_EINVAL;
+  if (T < 0 || K < 1) return MOE_EINVAL;
   moe_status_t st = check_ffn_dims(p, M, E, H, Hp, false);
   if (st != MOE_OK) return st;
   if (!cu_seqlens) return MOE_EINVAL;
@@ -328,24 +365,33 @@ moe_status_t moe_combine_shared(const void* y_rows, moe_dtype_t y_dtype, const i
 
 enum {
   WS_TOPK_IDX, WS_TOPK_W, WS_COUNTS, WS_CU, WS_POS, WS_ROW_SRC, WS_ROW_W, WS_X_PERM,
-  WS_X_PERM_SF, WS_H, WS_H_SF, WS_Y, WS_PERM_SCRATCH, WS_ACC, WS_N
+  WS_X_PERM_SF, WS_H, WS_H_SF, WS_Y, WS_PERM_SCRATCH, WS_ACC, WS_XQ, WS_XQ_SF, WS_N
 };
+
+// A BF16 layer with MXFP4 experts quantises its activations to fp8 (1x128 scales) once on
+// entry and then runs the fp8 x MXFP4 path ("Mixture of Kittens", Step 8).
+static bool layer_quantizes(const moe_layer_desc_t* d) {
+  return d->act == MOE_BF16 && d->wgt == MOE_MXFP4;
+}
+static moe_dtype_t layer_act(const moe_layer_desc_t* d) {
+  return layer_quantizes(d) ? MOE_FP8_E4M3 : d->act;
+}
 
 // Whether moe_layer_forward writes the permuted copy x_perm (and gate/up reads it) or gate/up
 // gathers its rows from x through row_src. Gathering is the default; MOE_LAYER_XPERM=1 forces
 // the copy, and so does an x too large for 32-bit row offsets.
 static bool layer_materializes(const moe_layer_desc_t* d) {
-  return env_flag("MOE_LAYER_XPERM") || (int64_t)d->T * d->H * act_bytes(d->act) >= (1ll << 31);
+  return env_flag("MOE_LAYER_XPERM") || (int64_t)d->T * d->H * act_bytes(layer_act(d)) >= (1ll << 31);
 }
 
 static moe_status_t layer_layout(const moe_layer_desc_t* d, size_t* off, size_t* total) {
   if (!d) return MOE_EINVAL;
   if (d->T < 0 || d->H < 1 || d->Hp < 1 || d->E < 1 || d->K < 1 || d->K > d->E) return MOE_EINVAL;
-  const Path p = ffn_path(d->act, d->wgt);
+  const Path p = ffn_path(layer_act(d), d->wgt);
   if (p == PATH_NONE || d->out != y_dtype_of(p)) return MOE_EUNSUPPORTED;
   if (d->combine != MOE_COMBINE_GATHER && d->combine != MOE_COMBINE_SCATTER_ATOMIC) return MOE_EINVAL;
   const size_t T = d->T, H = d->H, Hp = d->Hp, E = d->E, K = d->K, M = T * K;
-  const size_t ab = act_bytes(d->act), hb = act_bytes(h_dtype_of(p)), yb = act_bytes(y_dtype_of(p));
+  const size_t ab = act_bytes(layer_act(d)), hb = act_bytes(h_dtype_of(p)), yb = act_bytes(y_dtype_of(p));
   const bool mat = layer_materializes(d), scatter = d->combine == MOE_COMBINE_SCATTER_ATOMIC;
   const bool fp8 = p == PATH_FP8_MXFP4;
   size_t sz[WS_N] = {0};
@@ -365,6 +411,11 @@ static moe_status_t layer_layout(const moe_layer_desc_t* d, size_t* off, size_t*
   if (!scatter) want(WS_Y, M * H * yb);
   want(WS_PERM_SCRATCH, permute_ws_bytes(d->T, d->E, d->K));
   if (scatter && d->out != MOE_F32) want(WS_ACC, T * H * 4);  // fp32 out accumulates in place
+  if (layer_quantizes(d)) {
+    if (H % 128) return MOE_EUNSUPPORTED;
+    want(WS_XQ, T * H);
+    want(WS_XQ_SF, T * (H / 128) * 4);
+  }
   size_t o = 0;
   for (int i = 0; i < WS_N; ++i) {
     if (!used[i]) {
@@ -381,7 +432,7 @@ static moe_status_t layer_layout(const moe_layer_desc_t* d, size_t* off, size_t*
 // The shared expert runs in bf16 (fp32 in the fp32 layer) whatever the routed format
 // ("Mixture of Kittens", Step 8: the shared expert stays in BF16).
 static Path shared_path(const moe_layer_desc_t* d) {
-  return ffn_path(d->act, d->wgt) == PATH_F32 ? PATH_F32 : PATH_BF16;
+  return ffn_path(layer_act(d), d->wgt) == PATH_F32 ? PATH_F32 : PATH_BF16;
 }
 
 // Workspace of moe_layer_forward_shared: the routed layout, then h_s [T, Hs], y_s [T, H] and
@@ -456,7 +507,8 @@ static moe_status_t layer_forward_impl(const moe_layer_desc_t* d, const void* x,
                        : layer_layout(d, off, &total);
   if (st != MOE_OK) return st;
   if (!ws || ws_bytes < total) return MOE_EWORKSPACE;
-  const Path p = ffn_path(d->act, d->wgt);
+  const Path p = ffn_path(layer_act(d), d->wgt);
+  const moe_dtype_t act = layer_act(d);
   st = check_ffn_dims(p, (int64_t)d->T * d->K, d->E, d->H, d->Hp, true);
   if (st == MOE_OK) st = check_ffn_dims(p, (int64_t)d->T * d->K, d->E, d->H, d->Hp, false);
   if (st != MOE_OK) return st;
@@ -468,13 +520,21 @@ static moe_status_t layer_forward_impl(const moe_layer_desc_t* d, const void* x,
     st = check_ffn_dims(sp, d->T, 1, d->H, sh->Hs, true);
     if (st == MOE_OK) st = check_ffn_dims(sp, d->T, 1, d->H, sh->Hs, false);
     if (st != MOE_OK) return st;
-    xs = sh->x_shared ? sh->x_shared : (p == PATH_FP8_MXFP4 ? nullptr : x);
+    xs = sh->x_shared ? sh->x_shared : (d->act == MOE_FP8_E4M3 ? nullptr : x);
     if (d->T > 0 && (!xs || !sh->w_gate || !sh->w_up || !sh->w_down)) return MOE_EINVAL;
   }
   poison(ws, ws_bytes, stream);
   char* base = static_cast<char*>(ws);
   auto at = [&](int i) -> void* { return off[i] == SIZE_MAX ? nullptr : base + off[i]; };
   const int T = d->T, E = d->E, K = d->K, H = d->H, Hp = d->Hp, M = T * K;
+  if (layer_quantizes(d) && T > 0) {
+    // activation quantisation on entry: the routed experts read the fp8 rows from here on
+    st = moe_quantize_fp8(x, MOE_BF16, T, H, static_cast<uint8_t*>(at(WS_XQ)),
+                          static_cast<float*>(at(WS_XQ_SF)), stream);
+    if (st != MOE_OK) return st;
+    x = at(WS_XQ);
+    x_sf = static_cast<float*>(at(WS_XQ_SF));
+  }
 
   // shared expert (one group of all T rows), on the side stream when one is given
   void* y_s = sh ? base + y_s_off : nullptr;
@@ -523,15 +583,15 @@ static moe_status_t layer_forward_impl(const moe_layer_desc_t* d, const void* x,
   float* h_sf = static_cast<float*>(at(WS_H_SF));
   const bool mat = layer_materializes(d), scatter = d->combine == MOE_COMBINE_SCATTER_ATOMIC;
   const size_t perm_ws = permute_ws_bytes(T, E, K);
-  st = moe_permute(x, x_sf, d->act, topk_idx, topk_w, T, H, E, K, counts, cu, pos, row_src, row_w,
+  st = moe_permute(x, x_sf, act, topk_idx, topk_w, T, H, E, K, counts, cu, pos, row_src, row_w,
                    at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)), at(WS_PERM_SCRATCH), perm_ws,
                    stream);
   if (st != MOE_OK) return st;
   if (mat)
-    st = moe_ffn_gate_up(at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)), d->act, cu, M, E, H, Hp,
+    st = moe_ffn_gate_up(at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)), act, cu, M, E, H, Hp,
                          w_gate, w_up, sf_gate, sf_up, d->wgt, at(WS_H), h_sf, stream);
   else
-    st = moe_ffn_gate_up_gather(x, x_sf, d->act, row_src, T, K, cu, M, E, H, Hp, w_gate, w_up, sf_gate,
+    st = moe_ffn_gate_up_gather(x, x_sf, act, row_src, T, K, cu, M, E, H, Hp, w_gate, w_up, sf_gate,
                                 sf_up, d->wgt, at(WS_H), h_sf, stream);
   if (st != MOE_OK) return st;
   if (!scatter) {

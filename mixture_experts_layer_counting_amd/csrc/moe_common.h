@@ -68,6 +68,40 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
+// ---- OCP 8-bit formats -----------------------------------------------------------------
+
+// e8m0 byte of an fp32 power of two
+__device__ __forceinline__ int pow2_to_e8m0(float s) { return (__float_as_uint(s) >> 23) & 0xff; }
+
+// fp32 -> OCP e4m3fn code, round to nearest even; |v| <= 448 by construction of the scale.
+// An exact zero (either sign) gives code 0.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sgn = (u >> 24) & 0x80u;
+  const float a = __builtin_fabsf(v);
+  if (a == 0.0f) return 0u;
+  uint32_t code;
+  if (a < 0.015625f) {  // below 2^-6: subnormal grid of step 2^-9 (code 8 is 2^-6 itself)
+    code = (uint32_t)__builtin_rintf(a * 512.0f);
+  } else {
+    const uint32_t m = u & 0x7fffffffu;
+    const uint32_t r = (m + 0x7ffffu + ((m >> 20) & 1u)) >> 20;  // keep 3 mantissa bits, RNE
+    code = r - ((127u - 7u) << 3);
+    if (code > 0x7eu) code = 0x7eu;                               // saturate at 448
+  }
+  return sgn | code;
+}
+
+// Scale of a 1x128 block: the smallest power of two s with 448 s >= amax (amax = 0 -> 1).
+__device__ __forceinline__ float fp8_pow2_scale(float amax) {
+  if (!(amax > 0.f)) return 1.0f;
+  int ex;
+  const float mant = __builtin_frexpf(amax / 448.0f, &ex);  // amax/448 = mant * 2^ex
+  float s = __builtin_ldexpf(1.0f, mant == 0.5f ? ex - 1 : ex);
+  if (448.0f * s < amax) s *= 2.0f;
+  return s;
+}
+
 // Wave-uniform broadcast from lane `src`.
 __device__ __forceinline__ int wave_bcast(int v, int src) { return __shfl(v, src, MOE_WAVE); }
 

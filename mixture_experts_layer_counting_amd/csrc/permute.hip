@@ -19,6 +19,11 @@
 //  4. copy:    one block per token copies its row once from x to its K rows of x_perm
 //              with 16-byte loads and stores (the HBM-bound part).
 //  (fp8 only) sf: gathers the 1x128 block scales into the block-major x_perm_sf.
+// Padded variant (MoonEP "API walkthrough": token_padding and padded cu_seqlens;
+// "Distributed expert parallelism", "Static-capacity versus dropless dispatch"): every
+// group is rounded up to a multiple of `pad` rows inside a static buffer of
+// T*K + E*(pad-1) rows. counts stay the real ones; cu_seqlens is padded; padding rows have
+// row_src = -1, row_w = 0, zero activations and scale 1.
 #include "moe_common.h"
 
 #include <algorithm>
@@ -113,7 +118,7 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
     const int* __restrict__ topk_idx, const float* __restrict__ topk_w, int T, int E, int K,
     int nch, const int* __restrict__ counts, const int* __restrict__ choff,
     int* __restrict__ cu_seqlens, int* __restrict__ pos, int* __restrict__ row_src,
-    float* __restrict__ row_w, int key_bits, int* __restrict__ err) {
+    float* __restrict__ row_w, int key_bits, int pad, int* __restrict__ err) {
   __shared__ int cu[PERM_MAX_E + 1];
   __shared__ int pre[PERM_MAX_E];
   __shared__ int wh[PERM_WAVES][PERM_MAX_E];
@@ -130,7 +135,7 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = tid * 4 + j;
-      loc[j] = e < E ? counts[e] : 0;
+      loc[j] = e < E ? (counts[e] + pad - 1) / pad * pad : 0;  // group rows (padded)
       sum += loc[j];
     }
     const int incl = wave_incl_scan(sum);
@@ -253,7 +258,36 @@ __global__ __launch_bounds__(256) void permute_sf_kernel(const float* __restrict
   for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
     const int c = (int)(i / M);
     const int p = (int)(i - (size_t)c * M);
-    if (p < rows) x_perm_sf[i] = x_sf[(size_t)(row_src[p] / K) * nsf + c];
+    if (p < rows) {
+      const int src = row_src[p];
+      x_perm_sf[i] = src >= 0 ? x_sf[(size_t)(src / K) * nsf + c] : 1.0f;  // padding: scale 1
+    }
+  }
+}
+
+// Padded layout: mark every row of the static buffer as padding before the scatter fills
+// the real ones.
+__global__ __launch_bounds__(256) void permute_pad_fill_kernel(int* __restrict__ row_src,
+                                                               float* __restrict__ row_w, int cap) {
+  for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < cap; r += gridDim.x * blockDim.x) {
+    row_src[r] = -1;
+    if (row_w) row_w[r] = 0.f;
+  }
+}
+
+// Padded layout: zero the activation rows of padding rows inside the groups.
+__global__ __launch_bounds__(256) void permute_zero_pad_kernel(const int* __restrict__ row_src,
+                                                               const int* __restrict__ cu_seqlens,
+                                                               int E, unsigned char* __restrict__ x_perm,
+                                                               int row_bytes) {
+  const int r = blockIdx.x;
+  if (r >= cu_seqlens[E] || row_src[r] >= 0) return;
+  unsigned char* dst = x_perm + (size_t)r * row_bytes;
+  if (row_bytes % 16 == 0 && (uintptr_t)dst % 16 == 0) {
+    for (int c = threadIdx.x; c < row_bytes / 16; c += blockDim.x)
+      reinterpret_cast<int4*>(dst)[c] = make_int4(0, 0, 0, 0);
+  } else {
+    for (int c = threadIdx.x; c < row_bytes; c += blockDim.x) dst[c] = 0;
   }
 }
 
@@ -266,8 +300,8 @@ size_t permute_ws_bytes(int T, int E, int K) {
 moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes,
                             const int* topk_idx, const float* topk_w, int T, int H, int E, int K,
                             int* counts, int* cu_seqlens, int* pos, int* row_src, float* row_w,
-                            void* x_perm, float* x_perm_sf, void* ws, bool validate,
-                            int** err_out, hipStream_t s) {
+                            void* x_perm, float* x_perm_sf, void* ws, bool validate, int pad,
+                            int cap, int** err_out, hipStream_t s) {
   const int nch = (T + PERM_CHUNK - 1) / PERM_CHUNK;
   int* hist = static_cast<int*>(ws);
   int* err = reinterpret_cast<int*>(static_cast<char*>(ws) +
@@ -289,8 +323,11 @@ moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes,
   const int nblk = T > 0 ? (T + PERM_TB - 1) / PERM_TB : 1;
   const unsigned char* xb = static_cast<const unsigned char*>(x);
   unsigned char* xp = static_cast<unsigned char*>(x_perm);
+  if (pad > 1 && cap > 0)
+    permute_pad_fill_kernel<<<std::min((cap + 255) / 256, 1024), 256, 0, s>>>(row_src, row_w, cap);
   permute_scatter_kernel<<<nblk, PERM_THREADS, 0, s>>>(topk_idx, topk_w, T, E, K, nch, counts, hist,
-                                                       cu_seqlens, pos, row_src, row_w, key_bits, err);
+                                                       cu_seqlens, pos, row_src, row_w, key_bits, pad,
+                                                       err);
   if (T > 0 && x_perm) {
     const bool a16 = (row_bytes % 16 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)x_perm % 16 == 0);
     const bool a4 = (row_bytes % 4 == 0) && ((uintptr_t)x % 4 == 0) && ((uintptr_t)x_perm % 4 == 0);
@@ -301,10 +338,12 @@ moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes,
     else
       permute_copy_kernel<1><<<T, 256, 0, s>>>(xb, pos, K, xp, row_bytes);
   }
+  if (T > 0 && x_perm && pad > 1)
+    permute_zero_pad_kernel<<<cap, 256, 0, s>>>(row_src, cu_seqlens, E, xp, row_bytes);
   if (x_sf && x_perm_sf && T > 0) {
-    const size_t n = (size_t)sf_per_row * T * K;
+    const size_t n = (size_t)sf_per_row * cap;
     const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
-    permute_sf_kernel<<<blocks, 256, 0, s>>>(x_sf, row_src, cu_seqlens, E, K, T * K, sf_per_row, x_perm_sf);
+    permute_sf_kernel<<<blocks, 256, 0, s>>>(x_sf, row_src, cu_seqlens, E, K, cap, sf_per_row, x_perm_sf);
   }
   return launch_status();
 }

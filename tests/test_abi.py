@@ -135,8 +135,8 @@ def test_layer_workspace_sizes_and_layout():
 def test_gather_and_scatter_argument_checks():
     g = moe.moe_ffn_gate_up_gather
     # (x, x_sf, act, row_src, T, K, cu, M, E, H, Hp, wg, wu, sfg, sfu, wgt, h, h_sf)
-    _expect(moe.MOE_EINVAL, g, 16, None, moe.MOE_BF16, 16, 4, 2, 16, 9, 4, 128, 128, 16, 16, None,
-            None, moe.MOE_BF16, 16, None, 0)                              # M > T*K
+    _expect(moe.MOE_EINVAL, g, 16, None, moe.MOE_BF16, 16, -4, 2, 16, 8, 4, 128, 128, 16, 16, None,
+            None, moe.MOE_BF16, 16, None, 0)                              # T < 0
     _expect(moe.MOE_EINVAL, g, 16, None, moe.MOE_BF16, None, 4, 2, 16, 8, 4, 128, 128, 16, 16, None,
             None, moe.MOE_BF16, 16, None, 0)                              # NULL row_src
     _expect(moe.MOE_EUNSUPPORTED, g, 16, None, moe.MOE_BF16, 16, 2 ** 20, 2, 16, 8, 4, 1024, 128, 16,

@@ -481,3 +481,127 @@ def test_combine_shared_entry_point():
     moe.moe_combine(y, moe.MOE_F32, pos, tw, T, H, K, base, moe.MOE_F32)
     torch.cuda.synchronize()
     assert torch.equal(out, base + add)
+
+
+# ----------------------------------------------------------------------------- quantisation, padding
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_quantize_fp8_bit_exact(dt):
+    say(f"moe_quantize_fp8 from {dt}: codes and scales bit-exact")
+    g = torch.Generator(device="cpu").manual_seed(21)
+    R, C = 333, 768
+    x = torch.randn(R, C, generator=g) * torch.exp2(torch.randint(-12, 12, (R, 1), generator=g).float())
+    x[5, :128] = 0.0                     # all-zero block
+    x[6, 128:256] = 1e-30                # tiny block (subnormal scale range)
+    x[7, 0] = 448.0 * 2 ** 10            # block amax exactly on a power-of-two boundary
+    xt = x.to(torch.bfloat16 if dt == "bf16" else torch.float32)
+    xd = xt.to(DEV)
+    q = torch.empty((R, C), dtype=torch.uint8, device=DEV)
+    sf = torch.empty((R, C // 128), dtype=torch.float32, device=DEV)
+    moe.moe_quantize_fp8(xd, moe.MOE_BF16 if dt == "bf16" else moe.MOE_F32, R, C, q, sf)
+    torch.cuda.synchronize()
+    xv = O.decode_bf16(host(xt)) if dt == "bf16" else host(xt).astype(np.float64)
+    codes, s = O.quantize_fp8_1x128(xv)
+    assert np.array_equal(host(sf).astype(np.float64), s)
+    assert np.array_equal(host(q), codes)
+
+
+def padded_steps(w, pad, gather):
+    """Padded permute -> grouped FFN over the padded groups (M = capacity) -> combine."""
+    from _gpu_run import DT, TORCH_DT, h_fmt, y_fmt
+    T, H, Hp, E, K = w.T, w.H, w.Hp, w.E, w.K
+    cap = moe.moe_padded_capacity(T, E, K, pad)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    f32 = dict(dtype=torch.float32, device=DEV)
+    r = dict(counts=torch.empty(E, **i32), cu_seqlens=torch.empty(E + 1, **i32),
+             pos=torch.empty((T, K), **i32), row_src=torch.empty(cap, **i32), row_w=torch.empty(cap, **f32))
+    r["x_perm"] = None if gather else torch.empty((cap, H), dtype=TORCH_DT[w.act], device=DEV)
+    r["x_perm_sf"] = None if gather or w.act != "fp8" else torch.empty((H // 128, cap), **f32)
+    nws = moe.moe_permute_workspace_bytes(T, E, K)
+    ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
+    moe.moe_permute_padded(w.x, w.x_sf, DT[w.act], w.topk_idx, w.topk_w, T, H, E, K, pad, r["counts"],
+                           r["cu_seqlens"], r["pos"], r["row_src"], r["row_w"], r["x_perm"], r["x_perm_sf"],
+                           ws, nws)
+    r["h"] = torch.empty((cap, Hp), dtype=TORCH_DT[h_fmt(w)], device=DEV)
+    r["h_sf"] = torch.empty((Hp // 128, cap), **f32) if w.act == "fp8" else None
+    if gather:
+        moe.moe_ffn_gate_up_gather(w.x, w.x_sf, DT[w.act], r["row_src"], T, K, r["cu_seqlens"], cap, E, H,
+                                   Hp, w.w_gate, w.w_up, w.sf_gate, w.sf_up, DT[w.wgt], r["h"], r["h_sf"])
+    else:
+        moe.moe_ffn_gate_up(r["x_perm"], r["x_perm_sf"], DT[w.act], r["cu_seqlens"], cap, E, H, Hp,
+                            w.w_gate, w.w_up, w.sf_gate, w.sf_up, DT[w.wgt], r["h"], r["h_sf"])
+    r["y_rows"] = torch.empty((cap, H), dtype=TORCH_DT[y_fmt(w)], device=DEV)
+    moe.moe_ffn_down(r["h"], r["h_sf"], DT[h_fmt(w)], r["cu_seqlens"], cap, E, H, Hp, w.w_down, w.sf_down,
+                     DT[w.wgt], r["y_rows"], DT[y_fmt(w)])
+    r["out"] = torch.empty((T, H), dtype=TORCH_DT[w.out], device=DEV)
+    moe.moe_combine(r["y_rows"], DT[y_fmt(w)], r["pos"], w.topk_w, T, H, K, r["out"], DT[w.out])
+    r["acc"] = torch.zeros((T, H), **f32)
+    moe.moe_ffn_down_scatter(r["h"], r["h_sf"], DT[h_fmt(w)], r["cu_seqlens"], cap, E, H, Hp, w.w_down,
+                             w.sf_down, DT[w.wgt], r["row_src"], r["row_w"], T, K, r["acc"])
+    return r, cap
+
+
+PAD_CASES = [("bf16", 128, False), ("bf16", 128, True), ("fp8", 128, False), ("fp8", 64, True),
+             ("f32", 16, True)]
+
+
+@pytest.mark.parametrize("act,pad,gather", PAD_CASES, ids=[f"{a}_pad{p}_{'gather' if g else 'xperm'}"
+                                                          for a, p, g in PAD_CASES])
+def test_padded_layout_and_results(act, pad, gather):
+    say(f"padded permute (pad {pad}), {act}, {'gathered' if gather else 'materialised'} rows")
+    spec = {"f32": dict(T=333, H=200, Hp=72, E=9, K=3), "bf16": dict(T=600, H=512, Hp=256, E=32, K=6),
+            "fp8": dict(T=300, H=512, Hp=256, E=12, K=3)}[act]
+    w = make_case(act, dict(spec, routing="balanced"), 66)
+    idx = host(w.topk_idx)
+    # skew the given routing so groups are ragged and some experts are empty
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.choice(w.E // 2 + 1, w.K, replace=False) for _ in range(w.T)]).astype(np.int32)
+    w.topk_idx = torch.from_numpy(idx).to(DEV)
+    r, cap = padded_steps(w, pad, gather)
+    base = run_steps(w)
+    torch.cuda.synchronize()
+    ppos, prs, pcu = O.permute_padded(idx, w.E, pad)
+    counts, _ = O.count_offsets(idx, w.E)
+    assert cap == len(prs)
+    assert np.array_equal(host(r["counts"]), counts)
+    assert np.array_equal(host(r["cu_seqlens"]), pcu)
+    assert np.array_equal(host(r["pos"]), ppos)
+    assert np.array_equal(host(r["row_src"]), prs)
+    tw = host(w.topk_w).ravel()
+    assert np.array_equal(host(r["row_w"]), np.where(prs >= 0, tw[np.maximum(prs, 0)], 0).astype(np.float32))
+    if not gather:
+        xp = host(r["x_perm"])[:pcu[-1]]
+        real = prs[:pcu[-1]] >= 0
+        assert np.array_equal(xp[real], host(w.x)[prs[:pcu[-1]][real] // w.K])
+        assert not xp[~real].any()
+        if w.act == "fp8":
+            sfp = host(r["x_perm_sf"])[:, :pcu[-1]].T
+            assert np.array_equal(sfp[real], host(w.x_sf)[prs[:pcu[-1]][real] // w.K])
+            assert np.all(sfp[~real] == 1.0)
+    # per-row results do not depend on where a group starts: same output, bit for bit
+    assert np.array_equal(host(r["out"]), host(base["out"]))
+    ref = oracle_layer(w)
+    assert rel_err(host(r["acc"]).astype(np.float64), ref["out"]) <= TOL[w.act]
+
+
+@pytest.mark.parametrize("spec", FP8_SMALL[:2], ids=lambda s: "T{T}_H{H}_Hp{Hp}_E{E}_K{K}_{routing}".format(**s))
+def test_layer_bf16_activations_mxfp4_experts(spec):
+    say(f"(BF16, MXFP4) layer: quantised on entry, {spec}")
+    w = gen.make(**spec, act="bf16", wgt="mxfp4", out="bf16", cid=67, device=DEV)
+    out, ws, lay = run_layer(w)
+    torch.cuda.synchronize()
+    assert lay["x_q"] is not None and lay["x_q_sf"] is not None
+    # the oracle quantises the same bf16 values with its own 1x128 rule, then runs the fp8 layer
+    from _oracle_run import weight_fn
+    b = host(w.x)
+    codes, s = O.quantize_fp8_1x128(O.decode_bf16(b))
+    xq = O.decode_fp8_rows(codes, s)
+    bits = {"logits": host(w.logits), "topk_idx": host(w.topk_idx), "topk_w": host(w.topk_w)}
+    ref = O.layer(xq, w.E, w.K, weight_fn(w), logits=bits["logits"], topk_idx=bits["topk_idx"],
+                  topk_w=bits["topk_w"], fp8_requant=True)
+    e = rel_err(decode_out(w, out), ref["out"])
+    print(f"  out rel err {e:.3e}", flush=True)
+    assert e <= TOL["fp8"]
+    # and the quantised activations in the workspace are the oracle's bytes
+    n = w.T * w.H
+    assert np.array_equal(host(ws[lay["x_q"]:lay["x_q"] + n]).reshape(w.T, w.H), codes)
