@@ -61,6 +61,10 @@ def parse():
                     help="also time moe_layer_forward and moe_layer_forward_shared (a shared "
                          "expert of this intermediate size on a side stream); reported under "
                          "'fused', the headline value stays the routed layer")
+    ap.add_argument("--pad", type=int, default=1,
+                    help="static-capacity layout: pad every expert group to a multiple of this many rows")
+    ap.add_argument("--bf16-input", action="store_true",
+                    help="c5 only: bf16 activations quantised to fp8 1x128 inside the timed step")
     ap.add_argument("--xperm", action="store_true",
                     help="materialise x_perm in the permute instead of gathering rows in gate/up")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -131,10 +135,18 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     moe.lib()   # fail loudly if the HIP library is missing
+    quant = args.bf16_input and args.config == "c5"
     w = gen.config(args.config, device=dev, maxvio=args.maxvio if args.config == "c4" else None,
-                   shared_hs=args.shared_hs)
+                   shared_hs=args.shared_hs, act="bf16" if quant else None)
     T, H, Hp, E, K = w.T, w.H, w.Hp, w.E, w.K
     M = T * K
+    pad = max(args.pad, 1)
+    MR = moe.moe_padded_capacity(T, E, K, pad)   # rows of the permuted buffers (M when pad = 1)
+    x_in, x_in_sf = w.x, w.x_sf
+    if quant:   # the layer's own activation format from here on: fp8 with 1x128 scales
+        xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        xq_sf = torch.empty((T, H // 128), dtype=torch.float32, device=dev)
+        w.act, w.x, w.x_sf = "fp8", xq, xq_sf
     DT = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "fp8": moe.MOE_FP8_E4M3, "mxfp4": moe.MOE_MXFP4}
     TD = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
     hf = "fp8" if w.act == "fp8" else w.act
@@ -146,14 +158,14 @@ def main():
     counts = torch.empty(E, **i32)
     cu = torch.empty(E + 1, **i32)
     pos = torch.empty((T, K), **i32)
-    row_src = torch.empty(M, **i32)
+    row_src = torch.empty(MR, **i32)
     scatter = args.combine == "scatter"
-    x_perm = torch.empty((M, H), dtype=TD[w.act], device=dev) if args.xperm else None
-    x_perm_sf = torch.empty((H // 128, M), **f32) if args.xperm and w.act == "fp8" else None
-    row_w = torch.empty(M, **f32) if scatter else None
-    h = torch.empty((M, Hp), dtype=TD[hf], device=dev)
-    h_sf = torch.empty((Hp // 128, M), **f32) if w.act == "fp8" else None
-    y = torch.empty((M, H), dtype=TD[yf], device=dev) if not scatter else None
+    x_perm = torch.empty((MR, H), dtype=TD[w.act], device=dev) if args.xperm else None
+    x_perm_sf = torch.empty((H // 128, MR), **f32) if args.xperm and w.act == "fp8" else None
+    row_w = torch.empty(MR, **f32) if scatter else None
+    h = torch.empty((MR, Hp), dtype=TD[hf], device=dev)
+    h_sf = torch.empty((Hp // 128, MR), **f32) if w.act == "fp8" else None
+    y = torch.empty((MR, H), dtype=TD[yf], device=dev) if not scatter else None
     out = torch.empty((T, H), dtype=TD[w.out], device=dev)
     acc = (out if w.out == "f32" else torch.empty((T, H), **f32)) if scatter else None
     nws = moe.moe_permute_workspace_bytes(T, E, K)
@@ -161,7 +173,7 @@ def main():
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
-    stages = ["route", "permute", "gate_up", "down", "combine"]   # combine: acc zero + store (scatter)
+    stages = ["quantize", "route", "permute", "gate_up", "down", "combine"]   # combine: acc zero + store (scatter)
     ev = {s: [] for s in stages}
 
     def step(record):
@@ -175,26 +187,28 @@ def main():
                 ev[name].append((a, b))
             else:
                 fn()
+        if quant:
+            mark("quantize", lambda: moe.moe_quantize_fp8(x_in, moe.MOE_BF16, T, H, xq, xq_sf, sh))
         if w.logits is not None:
             mark("route", lambda: moe.moe_route_topk(w.logits, T, E, K, topk_idx, topk_w, sh))
-        mark("permute", lambda: moe.moe_permute(w.x, w.x_sf, DT[w.act], topk_idx, topk_w, T, H, E, K,
-                                                counts, cu, pos, row_src, row_w, x_perm, x_perm_sf,
-                                                ws, nws, sh))
+        mark("permute", lambda: moe.moe_permute_padded(w.x, w.x_sf, DT[w.act], topk_idx, topk_w, T, H, E, K,
+                                                       pad, counts, cu, pos, row_src, row_w, x_perm,
+                                                       x_perm_sf, ws, nws, sh))
         if args.xperm:
-            mark("gate_up", lambda: moe.moe_ffn_gate_up(x_perm, x_perm_sf, DT[w.act], cu, M, E, H, Hp,
+            mark("gate_up", lambda: moe.moe_ffn_gate_up(x_perm, x_perm_sf, DT[w.act], cu, MR, E, H, Hp,
                                                         w.w_gate, w.w_up, w.sf_gate, w.sf_up,
                                                         DT[w.wgt], h, h_sf, sh))
         else:
             mark("gate_up", lambda: moe.moe_ffn_gate_up_gather(w.x, w.x_sf, DT[w.act], row_src, T, K, cu,
-                                                               M, E, H, Hp, w.w_gate, w.w_up, w.sf_gate,
+                                                               MR, E, H, Hp, w.w_gate, w.w_up, w.sf_gate,
                                                                w.sf_up, DT[w.wgt], h, h_sf, sh))
         if not scatter:
-            mark("down", lambda: moe.moe_ffn_down(h, h_sf, DT[hf], cu, M, E, H, Hp, w.w_down, w.sf_down,
+            mark("down", lambda: moe.moe_ffn_down(h, h_sf, DT[hf], cu, MR, E, H, Hp, w.w_down, w.sf_down,
                                                   DT[w.wgt], y, DT[yf], sh))
             mark("combine", lambda: moe.moe_combine(y, DT[yf], pos, topk_w, T, H, K, out, DT[w.out], sh))
         else:
             mark("combine", lambda: acc.zero_())
-            mark("down", lambda: moe.moe_ffn_down_scatter(h, h_sf, DT[hf], cu, M, E, H, Hp, w.w_down,
+            mark("down", lambda: moe.moe_ffn_down_scatter(h, h_sf, DT[hf], cu, MR, E, H, Hp, w.w_down,
                                                           w.sf_down, DT[w.wgt], row_src, row_w, T, K,
                                                           acc, sh))
             if acc is not out:
@@ -277,7 +291,9 @@ def main():
         "data": "synthetic (seeded; random-init weights of the stated shape)",
         "config": {"workload": f"{args.config}: {DESCR[args.config]}", "T": T, "H": H, "Hp": Hp,
                    "E": E, "K": K, "act": w.act, "wgt": w.wgt, "combine": args.combine,
-                   "x_perm": "materialised" if args.xperm else "gathered in gate/up"},
+                   "x_perm": "materialised" if args.xperm else "gathered in gate/up",
+                   "pad": pad, "input": "bf16, quantised in the step" if quant else w.act},
+        "rows": {"real": int(cnt.sum()), "in_groups": int(cu[-1].item()), "buffer": int(MR)},
         "grouped_ffn_tflops": ffn_tflops,
         "grouped_ffn_frac_of_mfma_peak": ffn_tflops / peak_flops,
         "stage_ms": stage_ms,

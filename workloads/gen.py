@@ -287,10 +287,13 @@ def make(*, T, H, Hp, E, K, act="bf16", wgt="bf16", out="bf16", routing="normal"
 
 
 def config(name: str, device="cpu", maxvio: Optional[float] = None, seed: int = 0,
-           shared_hs: int = 0) -> Workload:
+           shared_hs: int = 0, act: Optional[str] = None) -> Workload:
     """One of the five named workloads at full size (c4 takes a maxvio target; c5 uses 1).
-    ``shared_hs`` > 0 adds a shared expert of that intermediate size."""
+    ``shared_hs`` > 0 adds a shared expert of that intermediate size; ``act`` overrides the
+    activation format (e.g. bf16 activations for the MXFP4 workload, quantised by the layer)."""
     s = dict(_SHAPES[name])
+    if act is not None:
+        s["act"] = act
     routing = s.pop("routing")
     beta = 0.0
     if routing == "skew":
