@@ -65,6 +65,8 @@ def parse():
                     help="static-capacity layout: pad every expert group to a multiple of this many rows")
     ap.add_argument("--bf16-input", action="store_true",
                     help="c5 only: bf16 activations quantised to fp8 1x128 inside the timed step")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of replays of the step captured as a HIP graph")
     ap.add_argument("--xperm", action="store_true",
                     help="materialise x_perm in the permute instead of gathering rows in gate/up")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -188,29 +190,29 @@ def main():
             else:
                 fn()
         if quant:
-            mark("quantize", lambda: moe.moe_quantize_fp8(x_in, moe.MOE_BF16, T, H, xq, xq_sf, sh))
+            mark("quantize", lambda: moe.moe_quantize_fp8(x_in, moe.MOE_BF16, T, H, xq, xq_sf, None))
         if w.logits is not None:
-            mark("route", lambda: moe.moe_route_topk(w.logits, T, E, K, topk_idx, topk_w, sh))
+            mark("route", lambda: moe.moe_route_topk(w.logits, T, E, K, topk_idx, topk_w, None))
         mark("permute", lambda: moe.moe_permute_padded(w.x, w.x_sf, DT[w.act], topk_idx, topk_w, T, H, E, K,
                                                        pad, counts, cu, pos, row_src, row_w, x_perm,
-                                                       x_perm_sf, ws, nws, sh))
+                                                       x_perm_sf, ws, nws, None))
         if args.xperm:
             mark("gate_up", lambda: moe.moe_ffn_gate_up(x_perm, x_perm_sf, DT[w.act], cu, MR, E, H, Hp,
                                                         w.w_gate, w.w_up, w.sf_gate, w.sf_up,
-                                                        DT[w.wgt], h, h_sf, sh))
+                                                        DT[w.wgt], h, h_sf, None))
         else:
             mark("gate_up", lambda: moe.moe_ffn_gate_up_gather(w.x, w.x_sf, DT[w.act], row_src, T, K, cu,
                                                                MR, E, H, Hp, w.w_gate, w.w_up, w.sf_gate,
-                                                               w.sf_up, DT[w.wgt], h, h_sf, sh))
+                                                               w.sf_up, DT[w.wgt], h, h_sf, None))
         if not scatter:
             mark("down", lambda: moe.moe_ffn_down(h, h_sf, DT[hf], cu, MR, E, H, Hp, w.w_down, w.sf_down,
-                                                  DT[w.wgt], y, DT[yf], sh))
-            mark("combine", lambda: moe.moe_combine(y, DT[yf], pos, topk_w, T, H, K, out, DT[w.out], sh))
+                                                  DT[w.wgt], y, DT[yf], None))
+            mark("combine", lambda: moe.moe_combine(y, DT[yf], pos, topk_w, T, H, K, out, DT[w.out], None))
         else:
             mark("combine", lambda: acc.zero_())
             mark("down", lambda: moe.moe_ffn_down_scatter(h, h_sf, DT[hf], cu, MR, E, H, Hp, w.w_down,
                                                           w.sf_down, DT[w.wgt], row_src, row_w, T, K,
-                                                          acc, sh))
+                                                          acc, None))
             if acc is not out:
                 mark("combine", lambda: out.copy_(acc))
 
@@ -222,6 +224,32 @@ def main():
         step(True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    ms_step_eager = elapsed * 1e3 / args.steps
+    eager_out = out.clone()
+    # Headline timing: the same step captured once as a HIP graph and replayed, so the host
+    # launch gaps between its kernels are gone (every kernel of the step still runs each
+    # replay). The per-stage times above come from the eager pass.
+    graph_check = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(False)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step(False)
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        graph_check = bool(torch.equal(out, eager_out)) if not scatter else \
+            float((out.float() - eager_out.float()).abs().max() / eager_out.float().abs().max().clamp_min(1e-30))
     ms_step = elapsed * 1e3 / args.steps
     # per stage: total event time of the stage in a step (the scatter combine has two parts),
     # median over the timed steps
@@ -284,6 +312,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_eager": ms_step_eager,
+        "timing": "HIP graph replay of the whole step" if not args.no_graph else "eager launches",
+        "graph_replay_matches_eager": graph_check,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -127,6 +127,26 @@ __device__ __forceinline__ void wait_barrier_dyn(int n) {
 
 // MAPPED selects the row maps at compile time: gate/up gathers its A rows, down scatters
 // into the accumulator; the plain instantiations carry neither.
+// Wait until at most N of this wave's vector-memory operations are outstanding (no barrier).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// n in [0, N] at run time, uniform over the wave: dispatch to the immediates N, N-1, ..., 0
+template <int N>
+__device__ __forceinline__ void wait_vm_dyn(int n) {
+  if constexpr (N > 0) {
+    if (n >= N) {
+      wait_vm<N>();
+      return;
+    }
+    wait_vm_dyn<N - 1>(n);
+  } else {
+    wait_vm<0>();
+  }
+}
+
 template <bool GATED, int BN, int BK, int NS, bool MAPPED>
 __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
     const uint16_t* __restrict__ A, const int* __restrict__ cu, int M, int E, int Kd, int N,
@@ -335,6 +355,262 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
   }
 }
 
+// ---- ping-pong schedule ---------------------------------------------------------------
+// Same tiles, LDS layout, fragments and epilogue as ffn_bf16_kernel with BK = 64 and two
+// stages. The eight waves form two groups of four, waves 0-3 and 4-7, so each SIMD holds
+// one wave of each. Time is cut into slots, one per half K step and group, separated by
+// workgroup barriers; in every slot one wave of a SIMD runs the 16 MFMAs of a half step from
+// fragments already in its registers while its partner reads the fragments of its next half
+// step from LDS (and, in group 0, issues the direct global->LDS loads of the next stage).
+// With the plain schedule both waves of a SIMD waited for the same stage and
+// then computed together, so load time and compute time added up.
+//
+//   group 0: read h0(kt) | compute h0(kt) | read h1(kt) | compute h1(kt) | read h0(kt+1) ...
+//   group 1:   (wait)    | read h0(kt)    | compute h0  | read h1(kt)    | compute h1 ...
+// Both groups execute the same instruction sequence; group 1 passes one extra barrier at the
+// start (and group 0 one at the end), which is all that offsets them. Group 0 issues the
+// direct loads of stage kt+1 while reading half 0 of stage kt (the buffer's previous stage,
+// kt-1, has then been read by both groups) and waits for them before the last barrier of
+// stage kt, so loads have four slots to land. Every barrier is preceded by lgkmcnt(0), so no
+// LDS read of a buffer is in flight when a later slot refills it.
+__device__ __forceinline__ void pp_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <bool GATED, int BN, int BK, int NS, bool MAPPED>
+__global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
+    const uint16_t* __restrict__ A, const int* __restrict__ cu, int M, int E, int Kd, int N,
+    const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C,
+    int n_fastest, RowMaps maps) {
+  using CF = FbCfg<GATED, BN, BK, NS>;
+  constexpr int KH = 2;                                   // MFMA k-steps per slot
+  constexpr int UPS = CF::KK / KH;                        // slots (units) per stage: 2 or 1
+  constexpr int A_LDP = CF::A_BYTES / (1024 * 4);         // A loads per group-0 wave per stage
+  constexpr int B_LDP = CF::NB * CF::B_BYTES / (1024 * 4);
+  constexpr int VMG = A_LDP + B_LDP;
+  constexpr int PER_MAT = CF::B_BYTES / 1024;             // 1 KiB weight loads per matrix
+  constexpr int NF = CF::NB * CF::NT;                     // B fragments per k-step
+  static_assert(CF::KK % KH == 0 && PER_MAT % 4 == 0 && A_LDP >= 1, "ping-pong tiling");
+  static_assert(VMG * (NS - 1) < 64, "vmcnt range");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  int* tstart = reinterpret_cast<int*>(smem + NS * CF::STAGE);
+  int* wsum = tstart + FB_MAX_E + 1;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1;
+  const int wn = wave & 1;
+  const bool g0 = wave < 4;
+  const int gw = wave & 3;
+  const int ntn = N / BN;
+  const int total = build_tile_prefix<FB_BM, FB_THREADS>(cu, E, ntn, tstart, wsum);
+  const int nk = Kd / BK;
+  const int G = gridDim.x;
+  const int slot = xcd_slot(blockIdx.x, G);
+
+  // loads of group-0 wave gw: A load j = gw + 4i fills rows [8j, 8j+8); weight load
+  // j = gw + 4i fills B_RPL rows of matrix j / PER_MAT. The weight offsets differ only by
+  // whole rows, uniform over the wave, so they ride in the scalar offset.
+  int a_row[A_LDP], a_voff[A_LDP];
+#pragma unroll
+  for (int i = 0; i < A_LDP; ++i) {
+    const int j = gw + 4 * i;
+    const int r = j * CF::A_RPL + lane / CF::CPR;
+    const int p = lane % CF::CPR;
+    a_row[i] = r;
+    a_voff[i] = r * Kd * 2 + ((p ^ ((r / CF::A_SWZ_DIV) % CF::CPR)) << 4);
+  }
+  int b_voff0;
+  {
+    const int r = gw * CF::B_RPL + lane / (64 / CF::B_RPL);
+    const int q = lane % (64 / CF::B_RPL);
+    const int sgm = (q >> 1) ^ ((r & 3) << 1);
+    b_voff0 = r * N * 2 + ((sgm << 1) + (q & 1)) * 16;
+  }
+
+  // LDS -> fragment offsets (as in ffn_bf16_kernel)
+  const int a_fbase = (wm * 32 + (lane & 31)) * CF::A_ROW;
+  const int a_sw = ((lane & 31) / CF::A_SWZ_DIV) % CF::CPR;
+  int a_fk[CF::KK];
+#pragma unroll
+  for (int kk = 0; kk < CF::KK; ++kk) a_fk[kk] = a_fbase + ((((kk << 1) | (lane >> 5)) ^ a_sw) << 4);
+  const int g = lane >> 4, jj = lane & 15;
+  const int bP = (wn * CF::WN) / 16 + (g & 1);
+  const int b_fbase = (8 * (g >> 1) + (jj >> 2)) * CF::B_ROW + 8 * (jj & 3) + ((bP ^ ((jj >> 2) << 1)) << 5);
+  const uint32_t smem_lds = lds_addr(smem);
+
+  for (int t = slot; t < total; t += G) {
+    const int e = find_expert(tstart, E, t);
+    const int lt = t - tstart[e];
+    const int gbeg = cu[e];
+    const int rows_e = cu[e + 1] - gbeg;
+    const int mte = (rows_e + FB_BM - 1) / FB_BM;
+    const int ntile = n_fastest ? lt % ntn : lt / mte;
+    const int mtile = n_fastest ? lt / ntn : lt - ntile * mte;
+    const int row0 = gbeg + mtile * FB_BM;
+    const int rows_valid = min(FB_BM, rows_e - mtile * FB_BM);
+    const int n0 = ntile * BN;
+
+    i32x4_t rA;
+    int a_off[A_LDP];
+    if constexpr (GATED && MAPPED) {
+      rA = make_rsrc(A, (uint32_t)maps.a_rows * (uint32_t)Kd * 2u);
+#pragma unroll
+      for (int i = 0; i < A_LDP; ++i) {
+        const int src = a_row[i] < rows_valid ? maps.a_src[row0 + a_row[i]] : -1;  // -1: padding row
+        a_off[i] = src >= 0 ? (src / maps.a_k - a_row[i]) * Kd * 2 + a_voff[i] : (int)0x80000000u;
+      }
+    } else {
+      rA = make_rsrc(A + (size_t)row0 * Kd, (uint32_t)rows_valid * (uint32_t)Kd * 2u);
+#pragma unroll
+      for (int i = 0; i < A_LDP; ++i) a_off[i] = a_voff[i];
+    }
+    const size_t woff = (size_t)e * Kd * N + n0;
+    const uint32_t b_rem = (uint32_t)(((size_t)Kd * N - n0) * 2);
+    const i32x4_t rB0 = make_rsrc(B0 + woff, b_rem);
+    const i32x4_t rB1 = GATED ? make_rsrc(B1 + woff, b_rem) : rB0;
+    const int nmt = __builtin_amdgcn_readfirstlane((wm * 32 < rows_valid) + (128 + wm * 32 < rows_valid));
+
+    auto issue = [&](int kt) __attribute__((always_inline)) {  // group 0 only: this wave's share of stage kt
+      const uint32_t so = smem_lds + (uint32_t)((kt % NS) * CF::STAGE);
+#pragma unroll
+      for (int i = 0; i < A_LDP; ++i) lds_dma16(rA, so + (gw + 4 * i) * 1024, a_off[i], kt * BK * 2);
+#pragma unroll
+      for (int i = 0; i < B_LDP; ++i) {
+        const int j = gw + 4 * i;  // j / PER_MAT == (4 i) / PER_MAT since gw < 4
+        const int rows = ((4 * i) % PER_MAT) * CF::B_RPL;
+        lds_dma16(((4 * i) / PER_MAT) ? rB1 : rB0, so + CF::A_BYTES + j * 1024, b_voff0,
+                  kt * BK * N * 2 + rows * N * 2);
+      }
+    };
+
+    f32x16_t acc[CF::NB][CF::MT][CF::NT];
+#pragma unroll
+    for (int nb = 0; nb < CF::NB; ++nb)
+#pragma unroll
+      for (int mt = 0; mt < CF::MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < CF::NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[nb][mt][nt][i] = 0.f;
+
+    auto run = [&](auto mtv) __attribute__((always_inline)) {
+      constexpr int MTV = decltype(mtv)::value;
+      bf16x8_t fa[CF::MT > 0 ? CF::MT : 1][KH];
+      bf16x8_t fb[NF][KH];
+      // read the fragments of half HF of stage kt
+      auto mread = [&](int kt, auto hfc) __attribute__((always_inline)) {
+        constexpr int HF = decltype(hfc)::value;
+        if constexpr (MTV > 0) {
+          const unsigned char* sa = smem + (kt % NS) * CF::STAGE;
+          const unsigned char* sb = sa + CF::A_BYTES;
+#pragma unroll
+          for (int q = 0; q < KH; ++q) {
+            const int kk = HF * KH + q;
+#pragma unroll
+            for (int mt = 0; mt < MTV; ++mt)
+              fa[mt][q] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const i32x4_t*>(sa + a_fk[kk] + mt * 128 * CF::A_ROW));
+#pragma unroll
+            for (int nb = 0; nb < CF::NB; ++nb)
+#pragma unroll
+              for (int nt = 0; nt < CF::NT; ++nt) {
+                const unsigned char* p = sb + nb * CF::B_BYTES + (b_fbase ^ (nt << 6)) + kk * 16 * CF::B_ROW;
+                const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(p));
+                const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(p + 4 * CF::B_ROW));
+                fb[nb * CF::NT + nt][q] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+              }
+          }
+        }
+      };
+      auto compute = [&]() __attribute__((always_inline)) {
+        if constexpr (MTV > 0) {
+#pragma unroll
+          for (int q = 0; q < KH; ++q)
+#pragma unroll
+            for (int nb = 0; nb < CF::NB; ++nb)
+#pragma unroll
+              for (int nt = 0; nt < CF::NT; ++nt)
+#pragma unroll
+                for (int mt = 0; mt < MTV; ++mt)
+                  acc[nb][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt][q], fb[nb * CF::NT + nt][q],
+                                                                            acc[nb][mt][nt], 0, 0, 0);
+        }
+      };
+      constexpr std::integral_constant<int, 0> H0{};
+      constexpr std::integral_constant<int, 1> H1{};
+      // Both groups run the same sequence (read, barrier, compute, barrier per slot);
+      // group 1 starts one barrier later, which puts it one slot behind group 0.
+      if (g0) {
+        // every buffer is free at the start: stages 0 .. NS-1 go out now
+        for (int st = 0; st < NS && st < nk; ++st) issue(st);
+        wait_vm_dyn<VMG * (NS - 1)>(min(NS - 1, nk - 1) * VMG);   // stage 0 landed
+      }
+      pp_barrier();                 // stage 0 has landed for everyone
+      if (!g0) pp_barrier();        // group 1: one slot behind
+      for (int kt = 0; kt < nk; ++kt) {
+        mread(kt, H0);
+        // buffer (kt+NS-1) % NS held stage kt-1, whose last reader (group 1) is done
+        if (g0 && kt >= 1 && kt + NS - 1 < nk) issue(kt + NS - 1);
+        pp_barrier();
+        compute();
+        if constexpr (UPS == 2) {
+          pp_barrier();
+          mread(kt, H1);
+          pp_barrier();
+          compute();
+        }
+        // stage kt+1 landed before it is read (younger stages may stay in flight)
+        if (g0 && kt + 1 < nk) wait_vm_dyn<VMG * (NS - 2)>(min(NS - 2, nk - 2 - kt) * VMG);
+        pp_barrier();
+      }
+      if (g0) pp_barrier();         // same number of barriers in both groups
+    };
+    __syncthreads();  // previous tile's readers are done with every stage
+    if (nmt == 2) run(std::integral_constant<int, 2>{});
+    else if (nmt == 1) run(std::integral_constant<int, 1>{});
+    else run(std::integral_constant<int, 0>{});
+
+    // epilogue (as in ffn_bf16_kernel)
+    if constexpr (!GATED && MAPPED) {
+#pragma unroll
+      for (int mt = 0; mt < CF::MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          const int src = r < rows_valid ? maps.s_src[row0 + r] : -1;
+          if (src >= 0) {
+            float* dst = maps.s_acc + (size_t)(src / maps.s_k) * N + n0 + wn * CF::WN + (lane & 31);
+            const float w = maps.s_w[row0 + r];
+#pragma unroll
+            for (int nt = 0; nt < CF::NT; ++nt) unsafeAtomicAdd(dst + nt * 32, w * acc[0][mt][nt][i]);
+          }
+        }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < CF::MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < CF::NT; ++nt) {
+          const int col = n0 + wn * CF::WN + nt * 32 + (lane & 31);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+            if (r < rows_valid) {
+              float v;
+              if constexpr (GATED)
+                v = silu_f32(acc[0][mt][nt][i]) * acc[1][mt][nt][i];
+              else
+                v = acc[0][mt][nt][i];
+              C[(size_t)(row0 + r) * N + col] = f32_to_bf16_bits(v);
+            }
+          }
+        }
+    }
+  }
+}
+
 // Tile order inside an expert group. MOE_FFN_ORDER = "m" | "n" overrides the default.
 static int tile_order_n_fastest(int M, int E) {
   const char* p = std::getenv("MOE_FFN_ORDER");
@@ -372,14 +648,34 @@ static moe_status_t launch_fb(const uint16_t* A, const int* cu, int M, int E, in
   return launch_fb_k<GATED, BN, BK, NS, false>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
 }
 
-// K-step / LDS-stage pipeline variant: MOE_FFN_PIPE = "64x2" (default) or "32x4".
+// K-step / LDS-stage pipeline variant. Default: the ping-pong schedule with K step 32 and
+// four stages (fastest on every measured shape). MOE_FFN_PIPE = "64x2" or "32x4" selects the
+// plain schedule with that K step and stage count, "pp" the ping-pong one with K step 64 and
+// two stages.
 static int pipe_variant() {
   static int v = -1;
   if (v < 0) {
     const char* p = std::getenv("MOE_FFN_PIPE");
-    v = (p && !std::strcmp(p, "32x4")) ? 1 : 0;
+    v = !p ? 3 : !std::strcmp(p, "64x2") ? 0 : !std::strcmp(p, "32x4") ? 1 : !std::strcmp(p, "pp") ? 2 : 3;
   }
   return v;
+}
+
+template <bool GATED, int BN, int BK, int NS, bool MAPPED>
+static moe_status_t launch_pp_k(const uint16_t* A, const int* cu, int M, int E, int Kd, int N,
+                                const uint16_t* B0, const uint16_t* B1, uint16_t* C,
+                                const RowMaps& maps, hipStream_t s) {
+  using CF = FbCfg<GATED, BN, BK, NS>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_pp_kernel<GATED, BN, BK, NS, MAPPED>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS_BYTES) != hipSuccess)
+      return MOE_EHIP;
+    attr_set = true;
+  }
+  ffn_bf16_pp_kernel<GATED, BN, BK, NS, MAPPED><<<device_cu_count(), FB_THREADS, CF::LDS_BYTES, s>>>(
+      A, cu, M, E, Kd, N, B0, B1, C, tile_order_n_fastest(M, E), maps);
+  return launch_status();
 }
 
 template <bool GATED, int BN>
@@ -387,6 +683,15 @@ static moe_status_t launch_fb_any(const uint16_t* A, const int* cu, int M, int E
                                   const uint16_t* B0, const uint16_t* B1, uint16_t* C,
                                   const RowMaps& maps, hipStream_t s) {
   if (pipe_variant() == 1) return launch_fb<GATED, BN, 32, 4>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
+  if (pipe_variant() >= 2) {
+    const bool mapped = GATED ? maps.a_src != nullptr : maps.s_acc != nullptr;
+    if (pipe_variant() == 3) {
+      if (mapped) return launch_pp_k<GATED, BN, 32, 4, true>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
+      return launch_pp_k<GATED, BN, 32, 4, false>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
+    }
+    if (mapped) return launch_pp_k<GATED, BN, 64, 2, true>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
+    return launch_pp_k<GATED, BN, 64, 2, false>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
+  }
   return launch_fb<GATED, BN, 64, 2>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
 }
 
