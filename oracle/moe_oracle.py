@@ -362,6 +362,88 @@ def layer_with_shared(x: np.ndarray, xs: np.ndarray, E: int, K: int, weights: We
     return res
 
 
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d silu(z) / dz = sigma(z) * (1 + z * (1 - sigma(z)))."""
+    sg = 1.0 / (1.0 + np.exp(-z))
+    return sg * (1.0 + z * (1.0 - sg))
+
+
+def layer_backward(x: np.ndarray, E: int, K: int, weights: WeightFn, dout: np.ndarray, *,
+                   logits: Optional[np.ndarray] = None, topk_idx: Optional[np.ndarray] = None,
+                   topk_w: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+    """Gradients of the layer output ``out`` (see ``layer``) for an upstream gradient
+    ``dout`` [T, H], in float64, following the forward steps backwards (MoonEP "API
+    walkthrough": combine bwd, the expert GEMMs' dgrad and wgrad, dispatch bwd):
+
+    * combine bwd: dy[r] = w[t,k] * dout[t] for the row r = pos[t,k]; the gradient of a
+      routing weight is dw[t,k] = <dout[t], y[pos[t,k]]>;
+    * down: dh = dy . Wd^T, dWd[e] = h_e^T . dy_e;
+    * SwiGLU: dg = dh * u * silu'(g), du = dh * silu(g);
+    * gate/up: dx_rows = dg . Wg^T + du . Wu^T, dWg[e] = x_e^T . dg_e, dWu[e] = x_e^T . du_e;
+    * dispatch bwd: dx[t] = sum_k dx_rows[pos[t,k]];
+    * routing (logits given): the weights are a softmax over the K selected logits, so
+      dlogits[t, e_k] = w_k (dw_k - sum_j w_j dw_j) and 0 for the other experts.
+
+    Returns dx [T, H], dWg/dWu [E, H, Hp], dWd [E, Hp, H], dw [T, K], dlogits [T, E] (when
+    logits are given) and the per-row intermediates dy, dh, dg, du, dx_rows."""
+    x = np.asarray(x, dtype=np.float64)
+    dout = np.asarray(dout, dtype=np.float64)
+    T, H = x.shape
+    if logits is not None:
+        idx, w = route_topk(logits, K)
+    else:
+        idx, w = np.asarray(topk_idx, np.int32), np.asarray(topk_w, np.float64)
+    counts, cu = count_offsets(idx, E)
+    pos, row_src = permute(idx, E)
+    tok = row_src // K
+    wr = np.asarray(w).ravel()[row_src]
+    M = T * K
+    dy = wr[:, None] * dout[tok]
+    dx_rows = np.zeros((M, H))
+    dw = np.zeros((T, K))
+    Hp = None
+    dWg = dWu = dWd = None
+    dh_all = dg_all = du_all = None
+    for e in range(E):
+        lo, hi = int(cu[e]), int(cu[e + 1])
+        wg, wu, wd = weights(e)
+        if Hp is None:
+            Hp = wg.shape[1]
+            dWg, dWu = np.zeros((E, H, Hp)), np.zeros((E, H, Hp))
+            dWd = np.zeros((E, Hp, H))
+            dh_all, dg_all, du_all = np.zeros((M, Hp)), np.zeros((M, Hp)), np.zeros((M, Hp))
+        if hi == lo:
+            continue
+        xe = x[tok[lo:hi]]
+        g, u = xe @ wg, xe @ wu
+        h = silu(g) * u
+        ye = h @ wd
+        # routing-weight gradient of the rows of this expert
+        rs = row_src[lo:hi]
+        dw[rs // K, rs % K] = np.sum(dout[tok[lo:hi]] * ye, axis=1)
+        dye = dy[lo:hi]
+        dh = dye @ wd.T
+        dWd[e] = h.T @ dye
+        dg = dh * u * silu_grad(g)
+        du = dh * silu(g)
+        dx_rows[lo:hi] = dg @ wg.T + du @ wu.T
+        dWg[e] = xe.T @ dg
+        dWu[e] = xe.T @ du
+        dh_all[lo:hi], dg_all[lo:hi], du_all[lo:hi] = dh, dg, du
+    dx = np.zeros((T, H))
+    for k in range(K):
+        dx += dx_rows[pos[:, k]]
+    res = dict(dx=dx, dWg=dWg, dWu=dWu, dWd=dWd, dw=dw, dy=dy, dh=dh_all, dg=dg_all, du=du_all,
+               dx_rows=dx_rows, topk_idx=idx, topk_w=w, pos=pos, row_src=row_src, cu_seqlens=cu)
+    if logits is not None:
+        Et = np.asarray(logits).shape[1]
+        dl = np.zeros((T, Et))
+        s = np.sum(w * dw, axis=1, keepdims=True)
+        np.put_along_axis(dl, idx.astype(np.int64), w * (dw - s), axis=1)
+        res["dlogits"] = dl
+    return res
+
+
 def layer_token_loop(x: np.ndarray, idx: np.ndarray, w: np.ndarray, weights: WeightFn,
                      fp8_requant: bool = False) -> np.ndarray:
     """Independent formulation with no permutation at all:

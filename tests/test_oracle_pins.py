@@ -228,6 +228,71 @@ def test_shared_expert_equal_to_the_routed_one_doubles_the_output():
     np.testing.assert_allclose(res["out"], 2 * dense, rtol=1e-12, atol=1e-12)
 
 
+# ----------------------------------------------------------------------------- backward
+
+def _fd_layer(T=5, H=6, Hp=4, E=3, K=2, seed=21):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, H))
+    W = [[rng.standard_normal((H, Hp)) / 2, rng.standard_normal((H, Hp)) / 2, rng.standard_normal((Hp, H)) / 2]
+         for _ in range(E)]
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    dout = rng.standard_normal((T, H))
+    return x, W, lg, dout
+
+
+def test_backward_matches_finite_differences():
+    """Every gradient of layer_backward against central differences of the fp64 forward
+    (loss = <dout, out>); routing is held by giving the forward the same top-k ids."""
+    T, H, Hp, E, K = 5, 6, 4, 3, 2
+    x, W, lg, dout = _fd_layer(T, H, Hp, E, K)
+    idx, w = O.route_topk(lg, K)
+    fn = lambda e: tuple(W[e])
+    g = O.layer_backward(x, E, K, fn, dout, topk_idx=idx, topk_w=w)
+    loss = lambda xx, WW, ww: float(np.sum(dout * O.layer(xx, E, K, lambda e: tuple(WW[e]),
+                                                            topk_idx=idx, topk_w=ww)["out"]))
+    eps = 1e-6
+    def fd(f, arr, index):
+        a = arr.copy(); a[index] += eps; up = f(a)
+        a = arr.copy(); a[index] -= eps; dn = f(a)
+        return (up - dn) / (2 * eps)
+    rng = np.random.default_rng(0)
+    for _ in range(6):
+        i = (rng.integers(T), rng.integers(H))
+        assert abs(fd(lambda a: loss(a, W, w), x, i) - g["dx"][i]) < 1e-6
+        i = (rng.integers(T), rng.integers(K))
+        assert abs(fd(lambda a: loss(x, W, a), w, i) - g["dw"][i]) < 1e-6
+        for m, key in enumerate(("dWg", "dWu", "dWd")):
+            e = int(rng.integers(E))
+            shp = W[e][m].shape
+            i = (int(rng.integers(shp[0])), int(rng.integers(shp[1])))
+            def f(a, e=e, m=m):
+                WW = [list(t) for t in W]
+                WW[e][m] = a
+                return loss(x, WW, w)
+            assert abs(fd(f, W[e][m], i) - g[key][e][i]) < 1e-6
+
+
+def test_backward_logit_gradient_through_topk_softmax():
+    T, H, Hp, E, K = 5, 6, 4, 3, 2
+    x, W, lg, dout = _fd_layer(T, H, Hp, E, K, seed=22)
+    lg64 = lg.astype(np.float64)
+    g = O.layer_backward(x, E, K, lambda e: tuple(W[e]), dout, logits=lg)
+    idx = g["topk_idx"]
+    def loss(l):
+        # the same selection, weights from the perturbed logits (softmax over the selected K)
+        sel = np.take_along_axis(l, idx.astype(np.int64), axis=1)
+        z = np.exp(sel - sel.max(axis=1, keepdims=True))
+        ww = z / z.sum(axis=1, keepdims=True)
+        return float(np.sum(dout * O.layer(x, E, K, lambda e: tuple(W[e]), topk_idx=idx, topk_w=ww)["out"]))
+    eps = 1e-6
+    for t in range(T):
+        for e in range(E):
+            a = lg64.copy(); a[t, e] += eps; up = loss(a)
+            a = lg64.copy(); a[t, e] -= eps; dn = loss(a)
+            assert abs((up - dn) / (2 * eps) - g["dlogits"][t, e]) < 1e-6
+    assert np.allclose(g["dlogits"].sum(axis=1), 0.0, atol=1e-12)   # softmax invariance
+
+
 # ----------------------------------------------------------------------------- padding, quantisation
 
 def test_padded_offsets_four_rank_example_and_closed_forms():
