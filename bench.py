@@ -67,6 +67,8 @@ def parse():
                     help="c5 only: bf16 activations quantised to fp8 1x128 inside the timed step")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of replays of the step captured as a HIP graph")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time moe_layer_backward (bf16 layers), reported under 'backward'")
     ap.add_argument("--xperm", action="store_true",
                     help="materialise x_perm in the permute instead of gathering rows in gate/up")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -341,6 +343,8 @@ def main():
     }
     if args.shared_hs:
         line["fused"] = time_fused(w, args, moe, torch)
+    if args.backward and w.act == "bf16" and w.wgt == "bf16":
+        line["backward"] = time_backward(w, args, moe, torch)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, args, out)
     print(json.dumps(line), flush=True)
@@ -389,6 +393,55 @@ def time_fused(w, args, moe, torch):
             "ms_layer_forward_shared_side_stream": ms_side,
             "shared_expert_ms_hidden": ms_serial - ms_side,
             "tokens_per_s_with_shared": w.T / (ms_side / 1e3)}
+
+
+def time_backward(w, args, moe, torch):
+    """moe_layer_backward end to end (forward recomputed inside), HIP events around graph
+    replays. Work: the recomputed forward (6 M H H') + down dgrad (2 M H H') + gate/up
+    dgrad (4 M H H') + the three weight gradients (6 M H H') = 18 M H H' flops."""
+    dev = w.x.device
+    d = moe.LayerDesc(w.T, w.H, w.Hp, w.E, w.K, moe.MOE_BF16, moe.MOE_BF16, moe.MOE_BF16, 0)
+    n = moe.moe_layer_backward_workspace_bytes(d)
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+    g = torch.Generator(device="cpu").manual_seed(8)
+    dout = torch.randn((w.T, w.H), generator=g).to(torch.bfloat16).to(dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    dx = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=dev)
+    dwg = torch.empty((w.E, w.H, w.Hp), **f32)
+    dwu = torch.empty((w.E, w.H, w.Hp), **f32)
+    dwd = torch.empty((w.E, w.Hp, w.H), **f32)
+    dtw = torch.empty((w.T, w.K), **f32)
+    dl = torch.empty((w.T, w.E), **f32) if w.logits is not None else None
+
+    def run():
+        moe.moe_layer_backward(d, w.x, w.logits, w.topk_idx, w.topk_w, w.w_gate, w.w_up, w.w_down, dout, dx,
+                               dwg, dwu, dwd, dtw, dl, ws, n)
+    for _ in range(max(args.warmup, 1)):
+        run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        run()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    graph.replay()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(args.steps):
+        graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.steps
+    flops = 18.0 * w.T * w.K * w.H * w.Hp
+    return {"ms": ms, "tokens_per_s": w.T / (ms / 1e3), "tflops": flops / (ms / 1e3) / 1e12,
+            "frac_of_mfma_peak": flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS,
+            "work": "forward recomputed + dgrad + wgrad (18 M H H' flops), bf16, HIP graph replay"}
 
 
 def cpu_baseline(w, args, gpu_out):

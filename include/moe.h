@@ -240,6 +240,7 @@ MOE_API moe_status_t moe_grouped_ffn(const void* x_perm, const float* x_perm_sf,
  * MoonEP "combine fwd"): out[t] = sum_{k=0..K-1} topk_w[t,k] * y_rows[pos[t,k]], summed in
  * fp32 in increasing k and rounded once to `out_dtype`; rows with pos < 0 are skipped.
  *  y_rows [T*K, H] of y_dtype (F32 or BF16); out [T, H] of out_dtype (F32 or BF16).
+ *  topk_w may be NULL: unit weights (the sum of a token's rows, as in the dispatch backward).
  * Deterministic: the same inputs give bitwise the same output. */
 MOE_API moe_status_t moe_combine(const void* y_rows, moe_dtype_t y_dtype, const int32_t* pos,
                          const float* topk_w, int32_t T, int32_t H, int32_t K, void* out,
@@ -309,6 +310,33 @@ MOE_API moe_status_t moe_layer_forward_shared(const moe_layer_desc_t* d, int32_t
                                       const uint8_t* sf_down, const void* ws_gate,
                                       const void* ws_up, const void* ws_down, void* out, void* ws,
                                       size_t ws_bytes, hipStream_t stream, hipStream_t side_stream);
+
+/* Workspace bytes of moe_layer_backward for `d` (0 if invalid or unsupported). */
+MOE_API size_t moe_layer_backward_workspace_bytes(const moe_layer_desc_t* d);
+
+/* Gradients of the layer (moe_layer_forward with the gather combine) for an upstream gradient
+ * dout, following MoonEP's "API walkthrough" order backwards: the forward is recomputed with
+ * x_perm, g = x.Wg and u = x.Wu kept, then
+ *   combine bwd  dy[r] = w[t,k] * dout[t] (r = pos[t,k]), d_topk_w[t,k] = <dout[t], y[r]>
+ *   down         dh = dy . Wd[e]^T (with the SwiGLU backward fused:
+ *                dg = dh * u * silu'(g), du = dh * silu(g)),  dWd[e] = h_e^T . dy_e
+ *   gate/up      dx_rows = dg . Wg[e]^T + du . Wu[e]^T,  dWg[e] = x_e^T . dg_e, dWu[e] = x_e^T . du_e
+ *   dispatch bwd dx[t] = sum_k dx_rows[pos[t,k]]
+ *   routing      (logits given and d_logits non-NULL) the weights are a softmax over the K
+ *                selected logits: d_logits[t, e_k] = w_k (d_topk_w_k - sum_j w_j d_topk_w_j),
+ *                0 for the other experts.
+ * BF16 layers only (d->act = wgt = out = BF16, gather combine); H % 256 == 0, Hp % 256 == 0.
+ * Intermediates are bf16, accumulation fp32.
+ *  x, dout, dx [T, H] bf16; logits or topk_idx_in / topk_w_in as in moe_layer_forward;
+ *  dw_gate, dw_up [E, H, Hp] and dw_down [E, Hp, H] fp32 out (written, not accumulated; zero
+ *  for experts without rows); d_topk_w [T, K] fp32 out (may be NULL); d_logits [T, E] fp32
+ *  out or NULL. */
+MOE_API moe_status_t moe_layer_backward(const moe_layer_desc_t* d, const void* x, const float* logits,
+                                const int32_t* topk_idx_in, const float* topk_w_in,
+                                const void* w_gate, const void* w_up, const void* w_down,
+                                const void* dout, void* dx, float* dw_gate, float* dw_up,
+                                float* dw_down, float* d_topk_w, float* d_logits, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
 
 /* Byte offsets of the intermediates inside the moe_layer_forward workspace, for inspection.
  * offsets[i] (i in order): 0 topk_idx, 1 topk_w, 2 counts, 3 cu_seqlens, 4 pos, 5 row_src,

@@ -33,6 +33,7 @@ EXPORTS = ("moe_route_topk", "moe_permute_workspace_bytes", "moe_permute", "moe_
            "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn", "moe_combine",
            "moe_combine_shared", "moe_layer_workspace_bytes", "moe_layer_forward",
            "moe_layer_shared_workspace_bytes", "moe_layer_forward_shared", "moe_layer_workspace_layout",
+           "moe_layer_backward_workspace_bytes", "moe_layer_backward",
            "moe_status_str")
 
 
@@ -79,6 +80,9 @@ _SIGS = {
                                _P, _P, _P, _S, _P]),
     "moe_layer_workspace_layout": (_I, [ctypes.POINTER(LayerDesc), ctypes.POINTER(_S), _I]),
     "moe_combine_shared": (_I, [_P, _E, _P, _P, _I, _I, _I, _P, _P, _E, _P]),
+    "moe_layer_backward_workspace_bytes": (_S, [ctypes.POINTER(LayerDesc)]),
+    "moe_layer_backward": (_I, [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                _P, _P, _P, _S, _P]),
     "moe_layer_shared_workspace_bytes": (_S, [ctypes.POINTER(LayerDesc), _I]),
     "moe_layer_forward_shared": (_I, [ctypes.POINTER(LayerDesc), _I, _P, _P, _P, _P, _P, _P, _P, _P,
                                       _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P, _P]),
@@ -255,3 +259,16 @@ def moe_layer_forward_shared(desc: LayerDesc, Hs, x, x_sf, x_shared, logits, top
                                           _ptr(sf_down), _ptr(ws_gate), _ptr(ws_up), _ptr(ws_down),
                                           _ptr(out), _ptr(ws), ws_bytes, _stream(stream), side),
            "moe_layer_forward_shared")
+
+
+def moe_layer_backward_workspace_bytes(desc: LayerDesc) -> int:
+    return int(lib().moe_layer_backward_workspace_bytes(ctypes.byref(desc)))
+
+
+def moe_layer_backward(desc: LayerDesc, x, logits, topk_idx_in, topk_w_in, w_gate, w_up, w_down, dout,
+                       dx, dw_gate, dw_up, dw_down, d_topk_w, d_logits, ws, ws_bytes, stream=None):
+    _check(lib().moe_layer_backward(ctypes.byref(desc), _ptr(x), _ptr(logits), _ptr(topk_idx_in),
+                                    _ptr(topk_w_in), _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(dout),
+                                    _ptr(dx), _ptr(dw_gate), _ptr(dw_up), _ptr(dw_down), _ptr(d_topk_w),
+                                    _ptr(d_logits), _ptr(ws), ws_bytes, _stream(stream)),
+           "moe_layer_backward")

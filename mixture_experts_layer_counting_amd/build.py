@@ -18,7 +18,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
 
 SOURCES = ["route_topk.hip", "permute.hip", "combine.hip", "quant.hip", "ffn_f32.hip",
-           "ffn_bf16.hip", "ffn_fp8.hip", "moe_api.cpp"]
+           "ffn_bf16.hip", "ffn_fp8.hip", "ffn_bwd.hip", "moe_api.cpp"]
 
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -54,7 +54,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const YT* __restrict__ y_r
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
     p[k] = k < K ? pos[(size_t)t * K + k] : -1;
-    w[k] = k < K ? topk_w[(size_t)t * K + k] : 0.f;
+    w[k] = k < K ? (topk_w ? topk_w[(size_t)t * K + k] : 1.0f) : 0.f;  // NULL: unit weights
   }
   const int nchunk = H / 8;
   for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(128) void combine_scalar_kernel(const YT* __restric
         v = bf16_bits_to_f32(y_rows[(size_t)p * H + c]);
       else
         v = y_rows[(size_t)p * H + c];
-      acc = fmaf(topk_w[(size_t)t * K + k], v, acc);
+      acc = fmaf(topk_w ? topk_w[(size_t)t * K + k] : 1.0f, v, acc);
     }
     if (add) {
       if constexpr (sizeof(YT) == 2)

@@ -35,6 +35,7 @@
 //    epilogue adds s_w[r] * y[r] into s_acc[s_src[r] / s_k] with fp32 atomics instead of
 //    storing y (the weighted combine fused into the down projection). A negative source
 //    index marks a padding row of a padded layout: it gathers zeros and scatters nothing.
+#include "lds_dma.h"
 #include "moe_common.h"
 #include "tile_sched.h"
 
@@ -73,79 +74,6 @@ struct FbCfg {
   static_assert(VM_PER_STAGE * (NS - 2) < 16, "vmcnt wait count out of range");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
-
-// Buffer descriptor (base, range in bytes; raw, stride 0) in scalar registers.
-__device__ __forceinline__ i32x4_t make_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4_t r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff);
-  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-  r[3] = 0x00020000;
-  return r;
-}
-
-// Direct global->LDS load of 16 bytes per lane (buffer_load_dwordx4 ... lds): lane l's bytes
-// land at lds_base + 16*l, offsets past the descriptor's range write zeros. Written as asm so
-// the compiler does not add a full vmcnt(0) wait before every later LDS read; completion is
-// tracked explicitly with wait_barrier<N>() below. No output registers.
-__device__ __forceinline__ void lds_dma16(i32x4_t rsrc_in, uint32_t lds_base, int voff, int soff) {
-  i32x4_t rsrc;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc_in[i]);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane((int)lds_base)), "v"(voff), "s"(rsrc),
-                 "s"(__builtin_amdgcn_readfirstlane(soff))
-               : "memory", "m0");
-}
-
-// Wait until at most N of this wave's vector-memory operations are outstanding, then
-// barrier the workgroup. The memory clobber keeps LDS reads on their side of the barrier.
-template <int N>
-__device__ __forceinline__ void wait_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const MOE_LDS void*)p;
-}
-
-template <int N>
-__device__ __forceinline__ void wait_barrier_dyn(int n) {
-  // n in [0, N]: dispatch to the compile-time immediates
-  if constexpr (N > 0) {
-    if (n >= N) {
-      wait_barrier<N>();
-      return;
-    }
-    wait_barrier_dyn<N - 1>(n);
-  } else {
-    wait_barrier<0>();
-  }
-}
-
-// MAPPED selects the row maps at compile time: gate/up gathers its A rows, down scatters
-// into the accumulator; the plain instantiations carry neither.
-// Wait until at most N of this wave's vector-memory operations are outstanding (no barrier).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-// n in [0, N] at run time, uniform over the wave: dispatch to the immediates N, N-1, ..., 0
-template <int N>
-__device__ __forceinline__ void wait_vm_dyn(int n) {
-  if constexpr (N > 0) {
-    if (n >= N) {
-      wait_vm<N>();
-      return;
-    }
-    wait_vm_dyn<N - 1>(n);
-  } else {
-    wait_vm<0>();
-  }
-}
 
 template <bool GATED, int BN, int BK, int NS, bool MAPPED>
 __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
@@ -343,10 +271,15 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
             const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
             if (r < rows_valid) {
               float v;
-              if constexpr (GATED)
+              if constexpr (GATED) {
                 v = silu_f32(acc[0][mt][nt][i]) * acc[1][mt][nt][i];
-              else
+                if (maps.save_g) {
+                  maps.save_g[(size_t)(row0 + r) * N + col] = f32_to_bf16_bits(acc[0][mt][nt][i]);
+                  maps.save_u[(size_t)(row0 + r) * N + col] = f32_to_bf16_bits(acc[1][mt][nt][i]);
+                }
+              } else {
                 v = acc[0][mt][nt][i];
+              }
               C[(size_t)(row0 + r) * N + col] = f32_to_bf16_bits(v);
             }
           }
@@ -599,10 +532,15 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
             const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
             if (r < rows_valid) {
               float v;
-              if constexpr (GATED)
+              if constexpr (GATED) {
                 v = silu_f32(acc[0][mt][nt][i]) * acc[1][mt][nt][i];
-              else
+                if (maps.save_g) {
+                  maps.save_g[(size_t)(row0 + r) * N + col] = f32_to_bf16_bits(acc[0][mt][nt][i]);
+                  maps.save_u[(size_t)(row0 + r) * N + col] = f32_to_bf16_bits(acc[1][mt][nt][i]);
+                }
+              } else {
                 v = acc[0][mt][nt][i];
+              }
               C[(size_t)(row0 + r) * N + col] = f32_to_bf16_bits(v);
             }
           }

@@ -39,6 +39,17 @@ moe_status_t launch_acc_zero(float* acc, size_t n, hipStream_t s);
 moe_status_t launch_acc_store(const float* acc, size_t n, const void* add, moe_dtype_t add_dtype,
                               void* out, moe_dtype_t out_dtype, hipStream_t s);
 moe_status_t launch_dense_cu(int* cu, int T, hipStream_t s);
+moe_status_t launch_bwd_down_swiglu(const void* dy, const int* cu, int M, int E, int H, int Hp,
+                                    const void* wd, const void* g, const void* u, void* dg, void* du,
+                                    hipStream_t s);
+moe_status_t launch_bwd_gate_up(const void* dg, const void* du, const int* cu, int M, int E, int H,
+                                int Hp, const void* wg, const void* wu, void* dx_rows, hipStream_t s);
+moe_status_t launch_bwd_wgrad(const void* A, const void* B, const int* cu, int E, int Md, int Nd,
+                              float* W, hipStream_t s);
+moe_status_t launch_combine_bwd(const void* dout, const void* y, const int* pos, const float* w,
+                                int T, int H, int K, void* dy, float* dw, hipStream_t s);
+moe_status_t launch_route_bwd(const int* idx, const float* w, const float* dw, int T, int E, int K,
+                              float* dl, hipStream_t s);
 
 int device_cu_count() {
   static int cache[64] = {0};
@@ -347,7 +358,7 @@ moe_status_t moe_combine(const void* y_rows, moe_dtype_t y_dtype, const int32_t*
   if (K > 32) return MOE_EUNSUPPORTED;
   if ((y_dtype != MOE_F32 && y_dtype != MOE_BF16) || (out_dtype != MOE_F32 && out_dtype != MOE_BF16))
     return MOE_EUNSUPPORTED;
-  if (T > 0 && (!y_rows || !pos || !topk_w || !out)) return MOE_EINVAL;
+  if (T > 0 && (!y_rows || !pos || !out)) return MOE_EINVAL;   // topk_w NULL: unit weights
   return launch_combine(y_rows, y_dtype, pos, topk_w, T, H, K, nullptr, out, out_dtype, stream);
 }
 
@@ -651,6 +662,112 @@ moe_status_t moe_layer_forward_shared(const moe_layer_desc_t* d, int32_t Hs, con
   sh.side = side_stream;
   return layer_forward_impl(d, x, x_sf, logits, topk_idx_in, topk_w_in, w_gate, w_up, w_down, sf_gate,
                             sf_up, sf_down, &sh, out, ws, ws_bytes, stream);
+}
+
+// ---- layer backward ---------------------------------------------------------------------
+
+enum {
+  BW_TOPK_IDX, BW_TOPK_W, BW_COUNTS, BW_CU, BW_POS, BW_ROW_SRC, BW_ROW_W, BW_X_PERM, BW_G, BW_U,
+  BW_H, BW_Y, BW_DY, BW_DG, BW_DU, BW_DW, BW_PERM_SCRATCH, BW_N
+};
+
+static moe_status_t bwd_check(const moe_layer_desc_t* d) {
+  if (!d) return MOE_EINVAL;
+  if (d->T < 0 || d->H < 1 || d->Hp < 1 || d->E < 1 || d->K < 1 || d->K > d->E) return MOE_EINVAL;
+  if (d->act != MOE_BF16 || d->wgt != MOE_BF16 || d->out != MOE_BF16) return MOE_EUNSUPPORTED;
+  if (d->E > 1024 || d->K > 32) return MOE_EUNSUPPORTED;
+  if (d->H % 256 || d->Hp % 256) return MOE_EUNSUPPORTED;
+  if ((int64_t)d->T * d->K * (d->H > d->Hp ? d->H : d->Hp) * 2 >= (1ll << 31)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+static moe_status_t bwd_layout(const moe_layer_desc_t* d, size_t* off, size_t* total) {
+  const moe_status_t st = bwd_check(d);
+  if (st != MOE_OK) return st;
+  const size_t T = d->T, H = d->H, Hp = d->Hp, E = d->E, K = d->K, M = T * K;
+  size_t sz[BW_N] = {M * 4, M * 4, E * 4, (E + 1) * 4, M * 4, M * 4, M * 4, M * H * 2, M * Hp * 2,
+                     M * Hp * 2, M * Hp * 2, M * H * 2, M * H * 2, M * Hp * 2, M * Hp * 2, M * 4,
+                     permute_ws_bytes(d->T, d->E, d->K)};
+  size_t o = 0;
+  for (int i = 0; i < BW_N; ++i) {
+    off[i] = o;
+    o = align_up(o + sz[i], 256);
+  }
+  *total = o + 256;
+  return MOE_OK;
+}
+
+size_t moe_layer_backward_workspace_bytes(const moe_layer_desc_t* d) {
+  size_t off[BW_N], total = 0;
+  return bwd_layout(d, off, &total) == MOE_OK ? total : 0;
+}
+
+moe_status_t moe_layer_backward(const moe_layer_desc_t* d, const void* x, const float* logits,
+                                const int32_t* topk_idx_in, const float* topk_w_in,
+                                const void* w_gate, const void* w_up, const void* w_down,
+                                const void* dout, void* dx, float* dw_gate, float* dw_up,
+                                float* dw_down, float* d_topk_w, float* d_logits, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
+  size_t off[BW_N], total = 0;
+  moe_status_t st = bwd_layout(d, off, &total);
+  if (st != MOE_OK) return st;
+  if (!ws || ws_bytes < total) return MOE_EWORKSPACE;
+  if (!dw_gate || !dw_up || !dw_down || !w_gate || !w_up || !w_down) return MOE_EINVAL;
+  if (d->T > 0 && (!x || !dout || !dx)) return MOE_EINVAL;
+  if (d->T > 0 && !logits && (!topk_idx_in || !topk_w_in)) return MOE_EINVAL;
+  poison(ws, ws_bytes, stream);
+  char* base = static_cast<char*>(ws);
+  auto at = [&](int i) -> void* { return base + off[i]; };
+  const int T = d->T, E = d->E, K = d->K, H = d->H, Hp = d->Hp, M = T * K;
+  int32_t* topk_idx = static_cast<int32_t*>(at(BW_TOPK_IDX));
+  float* topk_w = static_cast<float*>(at(BW_TOPK_W));
+  if (logits) {
+    st = moe_route_topk(logits, T, E, K, topk_idx, topk_w, stream);
+    if (st != MOE_OK) return st;
+  } else {
+    topk_idx = const_cast<int32_t*>(topk_idx_in);
+    topk_w = const_cast<float*>(topk_w_in);
+  }
+  int32_t* cu = static_cast<int32_t*>(at(BW_CU));
+  int32_t* pos = static_cast<int32_t*>(at(BW_POS));
+  int32_t* row_src = static_cast<int32_t*>(at(BW_ROW_SRC));
+  float* row_w = static_cast<float*>(at(BW_ROW_W));
+  st = moe_permute(x, nullptr, MOE_BF16, topk_idx, topk_w, T, H, E, K, static_cast<int32_t*>(at(BW_COUNTS)),
+                   cu, pos, row_src, row_w, at(BW_X_PERM), nullptr, at(BW_PERM_SCRATCH),
+                   permute_ws_bytes(T, E, K), stream);
+  if (st != MOE_OK) return st;
+  // forward recomputed, keeping g and u
+  RowMaps save;
+  save.save_g = static_cast<uint16_t*>(at(BW_G));
+  save.save_u = static_cast<uint16_t*>(at(BW_U));
+  if (M > 0) {
+    st = launch_ffn_gate_up_bf16(at(BW_X_PERM), cu, M, E, H, Hp, w_gate, w_up, at(BW_H), save, stream);
+    if (st == MOE_OK) st = launch_ffn_down_bf16(at(BW_H), cu, M, E, H, Hp, w_down, at(BW_Y), RowMaps{}, stream);
+    if (st != MOE_OK) return st;
+  }
+  // combine backward: dy and the routing-weight gradient (then the top-k softmax backward)
+  float* dw = d_topk_w ? d_topk_w : static_cast<float*>(at(BW_DW));
+  st = launch_combine_bwd(dout, at(BW_Y), pos, topk_w, T, H, K, at(BW_DY), dw, stream);
+  if (st == MOE_OK && logits && d_logits) st = launch_route_bwd(topk_idx, topk_w, dw, T, E, K, d_logits, stream);
+  if (st != MOE_OK) return st;
+  // down: dh with the SwiGLU backward fused (dg, du), and dWd = h^T dy
+  if (M > 0) {
+    st = launch_bwd_down_swiglu(at(BW_DY), cu, M, E, H, Hp, w_down, at(BW_G), at(BW_U), at(BW_DG), at(BW_DU),
+                                stream);
+    if (st != MOE_OK) return st;
+  }
+  st = launch_bwd_wgrad(at(BW_H), at(BW_DY), cu, E, Hp, H, dw_down, stream);
+  if (st != MOE_OK) return st;
+  // gate/up: dx_rows = dg Wg^T + du Wu^T (into the y buffer, no longer needed), the weights'
+  // gradients, then the dispatch backward (unit-weight combine of dx_rows)
+  if (M > 0) {
+    st = launch_bwd_gate_up(at(BW_DG), at(BW_DU), cu, M, E, H, Hp, w_gate, w_up, at(BW_Y), stream);
+    if (st != MOE_OK) return st;
+  }
+  st = launch_bwd_wgrad(at(BW_X_PERM), at(BW_DG), cu, E, H, Hp, dw_gate, stream);
+  if (st == MOE_OK) st = launch_bwd_wgrad(at(BW_X_PERM), at(BW_DU), cu, E, H, Hp, dw_up, stream);
+  if (st != MOE_OK) return st;
+  return launch_combine(at(BW_Y), MOE_BF16, pos, nullptr, T, H, K, nullptr, dx, MOE_BF16, stream);
 }
 
 }  // extern "C"

@@ -46,6 +46,9 @@ struct RowMaps {
   const float* s_w = nullptr;
   int s_k = 1;
   float* s_acc = nullptr;
+  // gate/up only: also store g = x.Wg and u = x.Wu (bf16, [rows, N]) for the backward
+  uint16_t* save_g = nullptr;
+  uint16_t* save_u = nullptr;
 };
 
 // ---- device helpers -----------------------------------------------------------------

@@ -605,3 +605,77 @@ def test_layer_bf16_activations_mxfp4_experts(spec):
     # and the quantised activations in the workspace are the oracle's bytes
     n = w.T * w.H
     assert np.array_equal(host(ws[lay["x_q"]:lay["x_q"] + n]).reshape(w.T, w.H), codes)
+
+
+# ----------------------------------------------------------------------------- backward
+
+BWD_CASES = [
+    dict(T=300, H=512, Hp=256, E=12, K=3, routing="normal"),
+    dict(T=600, H=256, Hp=512, E=32, K=4, routing="skew", beta=3.0),   # empty experts
+    dict(T=130, H=768, Hp=256, E=5, K=2, routing="balanced"),          # given routing
+]
+
+
+def run_backward(w, dout):
+    from _gpu_run import layer_desc
+    d = layer_desc(w)
+    n = moe.moe_layer_backward_workspace_bytes(d)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    f32 = dict(dtype=torch.float32, device=DEV)
+    r = dict(dx=torch.empty((w.T, w.H), dtype=torch.bfloat16, device=DEV),
+             dWg=torch.full((w.E, w.H, w.Hp), float("nan"), **f32),
+             dWu=torch.full((w.E, w.H, w.Hp), float("nan"), **f32),
+             dWd=torch.full((w.E, w.Hp, w.H), float("nan"), **f32),
+             dw=torch.empty((w.T, w.K), **f32),
+             dl=torch.empty((w.T, w.E), **f32) if w.logits is not None else None)
+    moe.moe_layer_backward(d, w.x, w.logits, w.topk_idx, w.topk_w, w.w_gate, w.w_up, w.w_down, dout,
+                           r["dx"], r["dWg"], r["dWu"], r["dWd"], r["dw"], r["dl"], ws, n)
+    return r
+
+
+def check_backward(w, dout, tol=2e-2):
+    r = run_backward(w, dout)
+    torch.cuda.synchronize()
+    from _oracle_run import weight_fn
+    b = {"logits": host(w.logits), "topk_idx": host(w.topk_idx), "topk_w": host(w.topk_w)}
+    ref = O.layer_backward(O.decode_bf16(host(w.x)), w.E, w.K, weight_fn(w), O.decode_bf16(host(dout)),
+                           logits=b["logits"], topk_idx=b["topk_idx"], topk_w=b["topk_w"])
+    errs = {"dx": rel_err(O.decode_bf16(host(r["dx"])), ref["dx"]),
+            "dWg": rel_err(host(r["dWg"]), ref["dWg"]), "dWu": rel_err(host(r["dWu"]), ref["dWu"]),
+            "dWd": rel_err(host(r["dWd"]), ref["dWd"]), "dw": rel_err(host(r["dw"]), ref["dw"])}
+    if r["dl"] is not None:
+        errs["dlogits"] = rel_err(host(r["dl"]), ref["dlogits"])
+    print("  " + "  ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= tol, (k, v)
+    # experts without rows get exactly zero weight gradients
+    counts = np.diff(ref["cu_seqlens"])
+    for e in np.nonzero(counts == 0)[0]:
+        assert not host(r["dWg"])[e].any() and not host(r["dWd"])[e].any()
+    return r, ref
+
+
+@pytest.mark.parametrize("spec", BWD_CASES, ids=lambda s: "T{T}_H{H}_Hp{Hp}_E{E}_K{K}_{routing}".format(**s))
+def test_layer_backward(spec):
+    say(f"layer backward {spec}")
+    w = gen.make(**spec, act="bf16", wgt="bf16", out="bf16", cid=70, device=DEV)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    dout = torch.randn((w.T, w.H), generator=g).to(torch.bfloat16).to(DEV)
+    check_backward(w, dout)
+
+
+def test_layer_backward_c2_full():
+    say("layer backward, c2 full size (oracle backward over every expert)")
+    w = gen.config("c2", device=DEV)
+    g = torch.Generator(device="cpu").manual_seed(8)
+    dout = torch.randn((w.T, w.H), generator=g).to(torch.bfloat16).to(DEV)
+    check_backward(w, dout)
+
+
+def test_layer_backward_t0():
+    say("layer backward, T=0: zero weight gradients")
+    w = gen.make(T=0, H=256, Hp=256, E=4, K=2, routing="normal", cid=71, device=DEV)
+    dout = torch.empty((0, 256), dtype=torch.bfloat16, device=DEV)
+    r = run_backward(w, dout)
+    torch.cuda.synchronize()
+    assert not r["dWg"].any() and not r["dWu"].any() and not r["dWd"].any()
