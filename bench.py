@@ -293,7 +293,7 @@ def main():
     gu_s = stage_ms["gate_up"] / 1e3
     t_mfma = gu_flops / (peak_flops * 1e12)
     t_hbm = gu_bytes / (PEAK_HBM_GBS * 1e9)
-    khash = source_hash("ffn_bf16.hip", "tile_sched.h", "moe_common.h")
+    khash = source_hash("ffn_bf16.hip", "tile_sched.h", "moe_common.h", "lds_dma.h")
     traffic = load_traffic("gate_up" if args.xperm else "gate_up_gather", args.config, khash)
     if t_mfma >= t_hbm:
         roof = {"bound": "mfma", "achieved": gu_flops / gu_s / 1e12, "peak": peak_flops, "unit": "TFLOP/s"}

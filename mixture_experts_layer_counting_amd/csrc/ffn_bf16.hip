@@ -153,8 +153,9 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
     // n fastest (neighbours cover whole weight rows, one m-tile at a time)
     const int ntile = n_fastest ? lt % ntn : lt / mte;
     const int mtile = n_fastest ? lt / ntn : lt - ntile * mte;
-    const int row0 = gbeg + mtile * FB_BM;
-    const int rows_valid = min(FB_BM, rows_e - mtile * FB_BM);
+    const int chunk = even_chunk(rows_e, mte);
+    const int row0 = gbeg + mtile * chunk;
+    const int rows_valid = min(chunk, rows_e - mtile * chunk);
     const int n0 = ntile * BN;
 
     // A rows of this tile: rows past rows_valid get an offset past the descriptor's range.
@@ -306,6 +307,13 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
 // kt-1, has then been read by both groups) and waits for them before the last barrier of
 // stage kt, so loads have four slots to land. Every barrier is preceded by lgkmcnt(0), so no
 // LDS read of a buffer is in flight when a later slot refills it.
+// Four consecutive bf16 values (rounded to nearest even) as one 8-byte store; p is 8-byte aligned.
+__device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, float c, float d) {
+  const uint32_t lo = (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+  const uint32_t hi = (uint32_t)f32_to_bf16_bits(c) | ((uint32_t)f32_to_bf16_bits(d) << 16);
+  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+}
+
 __device__ __forceinline__ void pp_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
@@ -325,6 +333,11 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
   constexpr int VMG = A_LDP + B_LDP;
   constexpr int PER_MAT = CF::B_BYTES / 1024;             // 1 KiB weight loads per matrix
   constexpr int NF = CF::NB * CF::NT;                     // B fragments per k-step
+  // Operand order of the MFMA. With the weight fragment first the accumulator comes out
+  // transposed: lane l holds one output row (l % 32 of the 32-row block) and four runs of four
+  // consecutive columns, which the epilogue writes as 8-byte stores. The scatter epilogue keeps
+  // the other order, where the 32 lanes of a row add into 32 consecutive floats of one token.
+  constexpr bool ROW_LANES = !(!GATED && MAPPED);
   static_assert(CF::KK % KH == 0 && PER_MAT % 4 == 0 && A_LDP >= 1, "ping-pong tiling");
   static_assert(VMG * (NS - 1) < 64, "vmcnt range");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -383,8 +396,9 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
     const int mte = (rows_e + FB_BM - 1) / FB_BM;
     const int ntile = n_fastest ? lt % ntn : lt / mte;
     const int mtile = n_fastest ? lt / ntn : lt - ntile * mte;
-    const int row0 = gbeg + mtile * FB_BM;
-    const int rows_valid = min(FB_BM, rows_e - mtile * FB_BM);
+    const int chunk = even_chunk(rows_e, mte);
+    const int row0 = gbeg + mtile * chunk;
+    const int rows_valid = min(chunk, rows_e - mtile * chunk);
     const int n0 = ntile * BN;
 
     i32x4_t rA;
@@ -467,9 +481,14 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
 #pragma unroll
               for (int nt = 0; nt < CF::NT; ++nt)
 #pragma unroll
-                for (int mt = 0; mt < MTV; ++mt)
-                  acc[nb][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt][q], fb[nb * CF::NT + nt][q],
-                                                                            acc[nb][mt][nt], 0, 0, 0);
+                for (int mt = 0; mt < MTV; ++mt) {
+                  if constexpr (ROW_LANES)
+                    acc[nb][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb * CF::NT + nt][q], fa[mt][q],
+                                                                              acc[nb][mt][nt], 0, 0, 0);
+                  else
+                    acc[nb][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt][q], fb[nb * CF::NT + nt][q],
+                                                                              acc[nb][mt][nt], 0, 0, 0);
+                }
         }
       };
       constexpr std::integral_constant<int, 0> H0{};
@@ -506,7 +525,7 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
     else if (nmt == 1) run(std::integral_constant<int, 1>{});
     else run(std::integral_constant<int, 0>{});
 
-    // epilogue (as in ffn_bf16_kernel)
+    // epilogue
     if constexpr (!GATED && MAPPED) {
 #pragma unroll
       for (int mt = 0; mt < CF::MT; ++mt)
@@ -522,29 +541,34 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
           }
         }
     } else {
+      // row-lane layout: block (mt, nt) holds row mt*128 + wm*32 + lane%32 in this lane, and
+      // columns nt*32 + 8j + 4(lane/32) + c in acc[..][4j + c], j, c = 0..3
+      const int col_l = n0 + wn * CF::WN + 4 * (lane >> 5);
 #pragma unroll
-      for (int mt = 0; mt < CF::MT; ++mt)
+      for (int mt = 0; mt < CF::MT; ++mt) {
+        const int r = mt * 128 + wm * 32 + (lane & 31);
+        if (r < rows_valid) {
+          const size_t ro = (size_t)(row0 + r) * N + col_l;
 #pragma unroll
-        for (int nt = 0; nt < CF::NT; ++nt) {
-          const int col = n0 + wn * CF::WN + nt * 32 + (lane & 31);
+          for (int nt = 0; nt < CF::NT; ++nt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-            if (r < rows_valid) {
-              float v;
+            for (int j = 0; j < 4; ++j) {
+              const size_t o = ro + nt * 32 + 8 * j;
+              const f32x16_t& a0 = acc[0][mt][nt];
               if constexpr (GATED) {
-                v = silu_f32(acc[0][mt][nt][i]) * acc[1][mt][nt][i];
+                const f32x16_t& a1 = acc[1][mt][nt];
+                store_bf16x4(C + o, silu_f32(a0[4 * j]) * a1[4 * j], silu_f32(a0[4 * j + 1]) * a1[4 * j + 1],
+                             silu_f32(a0[4 * j + 2]) * a1[4 * j + 2], silu_f32(a0[4 * j + 3]) * a1[4 * j + 3]);
                 if (maps.save_g) {
-                  maps.save_g[(size_t)(row0 + r) * N + col] = f32_to_bf16_bits(acc[0][mt][nt][i]);
-                  maps.save_u[(size_t)(row0 + r) * N + col] = f32_to_bf16_bits(acc[1][mt][nt][i]);
+                  store_bf16x4(maps.save_g + o, a0[4 * j], a0[4 * j + 1], a0[4 * j + 2], a0[4 * j + 3]);
+                  store_bf16x4(maps.save_u + o, a1[4 * j], a1[4 * j + 1], a1[4 * j + 2], a1[4 * j + 3]);
                 }
               } else {
-                v = acc[0][mt][nt][i];
+                store_bf16x4(C + o, a0[4 * j], a0[4 * j + 1], a0[4 * j + 2], a0[4 * j + 3]);
               }
-              C[(size_t)(row0 + r) * N + col] = f32_to_bf16_bits(v);
             }
-          }
         }
+      }
     }
   }
 }

@@ -92,8 +92,9 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dgrad_kernel(
     const int mte = (rows_e + BW_TILE - 1) / BW_TILE;
     const int ntile = lt / mte;
     const int mtile = lt - ntile * mte;
-    const int row0 = gbeg + mtile * BW_TILE;
-    const int rows_valid = min(BW_TILE, rows_e - mtile * BW_TILE);
+    const int chunk = even_chunk(rows_e, mte);
+    const int row0 = gbeg + mtile * chunk;
+    const int rows_valid = min(chunk, rows_e - mtile * chunk);
     const int n0 = ntile * BW_TILE;
     const uint32_t a_bytes = (uint32_t)rows_valid * (uint32_t)Kd * 2u;  // rows past: zeros
     const i32x4_t rA0 = make_rsrc(A0 + (size_t)row0 * Kd, a_bytes);

@@ -184,8 +184,9 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     const int mte = (rows_e + F8_BM - 1) / F8_BM;
     const int ntile = lt / mte;
     const int mtile = lt - ntile * mte;
-    const int row0 = gbeg + mtile * F8_BM;
-    const int rows_valid = min(F8_BM, rows_e - mtile * F8_BM);
+    const int chunk = even_chunk(rows_e, mte);
+    const int row0 = gbeg + mtile * chunk;
+    const int rows_valid = min(chunk, rows_e - mtile * chunk);
     const int n0 = ntile * BN;
 
     // A rows of this tile (see the bf16 kernels): rows past rows_valid load past the range.

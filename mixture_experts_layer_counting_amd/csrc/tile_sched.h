@@ -58,6 +58,16 @@ __device__ __forceinline__ int find_expert(const int* tstart, int E, int t) {
   return lo;
 }
 
+// Rows per m-tile when an expert's rows_e rows are spread evenly over its mte = ceil(rows_e / bm)
+// tiles: ceil(rows_e / mte) rounded up to whole 32-row blocks. That is at most bm, and since
+// (mte - 1) * bm < rows_e the last tile keeps at least one row. The tiles of one expert then
+// run the same number of 32-row MFMA blocks and stream the shared weight panel in step, so
+// the panel is fetched from HBM once and reused from L2 instead of being re-read by a
+// straggler tile that has fallen behind.
+__device__ __forceinline__ int even_chunk(int rows_e, int mte) {
+  return ((rows_e + mte - 1) / mte + 31) & ~31;
+}
+
 // Block slot for the persistent loop: blocks are dispatched round-robin over the 8 XCDs,
 // so block b runs on XCD b % 8; giving XCD x the contiguous slots [x*G/8, (x+1)*G/8)
 // keeps neighbouring tiles (same expert, same weight panel) in one L2.
