@@ -307,11 +307,26 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
 // kt-1, has then been read by both groups) and waits for them before the last barrier of
 // stage kt, so loads have four slots to land. Every barrier is preceded by lgkmcnt(0), so no
 // LDS read of a buffer is in flight when a later slot refills it.
-// Four consecutive bf16 values (rounded to nearest even) as one 8-byte store; p is 8-byte aligned.
-__device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, float c, float d) {
-  const uint32_t lo = (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
-  const uint32_t hi = (uint32_t)f32_to_bf16_bits(c) | ((uint32_t)f32_to_bf16_bits(d) << 16);
-  *reinterpret_cast<uint2*>(p) = make_uint2(lo, hi);
+// Sixteen columns of one row of a row-lane 32x32 block, as bf16 (rounded to nearest even).
+// Lane l holds row l % 32: v0..v3 are columns 4(l / 32) + 0..3 and v4..v7 columns
+// 8 + 4(l / 32) + 0..3. v_permlane32_swap trades the second group of the lower half for the
+// first group of the upper half, after which lane l < 32 holds columns 0..7 and lane l + 32
+// columns 8..15: the 16 bytes this lane writes at its column 8(l / 32). All 64 lanes must be
+// active.
+__device__ __forceinline__ uint4 pack_row16(float v0, float v1, float v2, float v3, float v4, float v5,
+                                            float v6, float v7) {
+  const uint32_t a0 = pack_bf16x2(v0, v1), a1 = pack_bf16x2(v2, v3);
+  const uint32_t b0 = pack_bf16x2(v4, v5), b1 = pack_bf16x2(v6, v7);
+  // swap(x, y) returns (x of lanes 0..31 | y of lanes 0..31, x of lanes 32..63 | y of lanes
+  // 32..63): the lower half keeps x and receives the upper half's x as the second result; the
+  // upper half receives the lower half's y as the first result and keeps y
+  const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+  return make_uint4(s0[0], s1[0], s0[1], s1[1]);
+}
+
+__device__ __forceinline__ uint4 pack_row16(const f32x16_t& a, int i0) {
+  return pack_row16(a[i0], a[i0 + 1], a[i0 + 2], a[i0 + 3], a[i0 + 4], a[i0 + 5], a[i0 + 6], a[i0 + 7]);
 }
 
 __device__ __forceinline__ void pp_barrier() {
@@ -388,7 +403,14 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
   const int b_fbase = (8 * (g >> 1) + (jj >> 2)) * CF::B_ROW + 8 * (jj & 3) + ((bP ^ ((jj >> 2) << 1)) << 5);
   const uint32_t smem_lds = lds_addr(smem);
 
-  for (int t = slot; t < total; t += G) {
+  // one output tile: its expert, rows, columns and load descriptors
+  struct Tile {
+    int row0, rows_valid, n0, nmt;
+    i32x4_t rA, rB0, rB1;
+    int a_off[A_LDP];
+  };
+  auto decode = [&](int t) __attribute__((always_inline)) {
+    Tile d;
     const int e = find_expert(tstart, E, t);
     const int lt = t - tstart[e];
     const int gbeg = cu[e];
@@ -397,42 +419,53 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
     const int ntile = n_fastest ? lt % ntn : lt / mte;
     const int mtile = n_fastest ? lt / ntn : lt - ntile * mte;
     const int chunk = even_chunk(rows_e, mte);
-    const int row0 = gbeg + mtile * chunk;
-    const int rows_valid = min(chunk, rows_e - mtile * chunk);
-    const int n0 = ntile * BN;
-
-    i32x4_t rA;
-    int a_off[A_LDP];
+    d.row0 = gbeg + mtile * chunk;
+    d.rows_valid = min(chunk, rows_e - mtile * chunk);
+    d.n0 = ntile * BN;
     if constexpr (GATED && MAPPED) {
-      rA = make_rsrc(A, (uint32_t)maps.a_rows * (uint32_t)Kd * 2u);
+      d.rA = make_rsrc(A, (uint32_t)maps.a_rows * (uint32_t)Kd * 2u);
 #pragma unroll
       for (int i = 0; i < A_LDP; ++i) {
-        const int src = a_row[i] < rows_valid ? maps.a_src[row0 + a_row[i]] : -1;  // -1: padding row
-        a_off[i] = src >= 0 ? (src / maps.a_k - a_row[i]) * Kd * 2 + a_voff[i] : (int)0x80000000u;
+        const int src = a_row[i] < d.rows_valid ? maps.a_src[d.row0 + a_row[i]] : -1;  // -1: padding row
+        d.a_off[i] = src >= 0 ? (src / maps.a_k - a_row[i]) * Kd * 2 + a_voff[i] : (int)0x80000000u;
       }
     } else {
-      rA = make_rsrc(A + (size_t)row0 * Kd, (uint32_t)rows_valid * (uint32_t)Kd * 2u);
+      d.rA = make_rsrc(A + (size_t)d.row0 * Kd, (uint32_t)d.rows_valid * (uint32_t)Kd * 2u);
 #pragma unroll
-      for (int i = 0; i < A_LDP; ++i) a_off[i] = a_voff[i];
+      for (int i = 0; i < A_LDP; ++i) d.a_off[i] = a_voff[i];
     }
-    const size_t woff = (size_t)e * Kd * N + n0;
-    const uint32_t b_rem = (uint32_t)(((size_t)Kd * N - n0) * 2);
-    const i32x4_t rB0 = make_rsrc(B0 + woff, b_rem);
-    const i32x4_t rB1 = GATED ? make_rsrc(B1 + woff, b_rem) : rB0;
-    const int nmt = __builtin_amdgcn_readfirstlane((wm * 32 < rows_valid) + (128 + wm * 32 < rows_valid));
+    const size_t woff = (size_t)e * Kd * N + d.n0;
+    const uint32_t b_rem = (uint32_t)(((size_t)Kd * N - d.n0) * 2);
+    d.rB0 = make_rsrc(B0 + woff, b_rem);
+    d.rB1 = GATED ? make_rsrc(B1 + woff, b_rem) : d.rB0;
+    d.nmt = __builtin_amdgcn_readfirstlane((wm * 32 < d.rows_valid) + (128 + wm * 32 < d.rows_valid));
+    return d;
+  };
+  // group 0 only: this wave's share of stage kt of tile d
+  auto issue = [&](const Tile& d, int kt) __attribute__((always_inline)) {
+    const uint32_t so = smem_lds + (uint32_t)((kt % NS) * CF::STAGE);
+#pragma unroll
+    for (int i = 0; i < A_LDP; ++i) lds_dma16(d.rA, so + (gw + 4 * i) * 1024, d.a_off[i], kt * BK * 2);
+#pragma unroll
+    for (int i = 0; i < B_LDP; ++i) {
+      const int j = gw + 4 * i;  // j / PER_MAT == (4 i) / PER_MAT since gw < 4
+      const int rows = ((4 * i) % PER_MAT) * CF::B_RPL;
+      lds_dma16(((4 * i) / PER_MAT) ? d.rB1 : d.rB0, so + CF::A_BYTES + j * 1024, b_voff0,
+                kt * BK * N * 2 + rows * N * 2);
+    }
+  };
 
-    auto issue = [&](int kt) __attribute__((always_inline)) {  // group 0 only: this wave's share of stage kt
-      const uint32_t so = smem_lds + (uint32_t)((kt % NS) * CF::STAGE);
-#pragma unroll
-      for (int i = 0; i < A_LDP; ++i) lds_dma16(rA, so + (gw + 4 * i) * 1024, a_off[i], kt * BK * 2);
-#pragma unroll
-      for (int i = 0; i < B_LDP; ++i) {
-        const int j = gw + 4 * i;  // j / PER_MAT == (4 i) / PER_MAT since gw < 4
-        const int rows = ((4 * i) % PER_MAT) * CF::B_RPL;
-        lds_dma16(((4 * i) / PER_MAT) ? rB1 : rB0, so + CF::A_BYTES + j * 1024, b_voff0,
-                  kt * BK * N * 2 + rows * N * 2);
-      }
-    };
+  // The first NS stages of a tile go out as soon as the buffers are free: for the first tile
+  // here, for the others right after the previous tile's last MFMA read, so that they land
+  // while that tile's outputs are being written.
+  Tile cur;
+  if (slot < total) {
+    cur = decode(slot);
+    if (g0)
+      for (int st = 0; st < NS && st < nk; ++st) issue(cur, st);
+  }
+  for (int t = slot; t < total; t += G) {
+    const int row0 = cur.row0, rows_valid = cur.rows_valid, n0 = cur.n0, nmt = cur.nmt;
 
     f32x16_t acc[CF::NB][CF::MT][CF::NT];
 #pragma unroll
@@ -495,17 +528,16 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
       constexpr std::integral_constant<int, 1> H1{};
       // Both groups run the same sequence (read, barrier, compute, barrier per slot);
       // group 1 starts one barrier later, which puts it one slot behind group 0.
-      if (g0) {
-        // every buffer is free at the start: stages 0 .. NS-1 go out now
-        for (int st = 0; st < NS && st < nk; ++st) issue(st);
-        wait_vm_dyn<VMG * (NS - 1)>(min(NS - 1, nk - 1) * VMG);   // stage 0 landed
-      }
+      // stages 0 .. NS-1 are in flight; stage 0 has landed once at most the younger ones are
+      // outstanding (the previous tile's output stores, issued after them, can only add to
+      // the count, so they never end the wait early)
+      if (g0) wait_vm_dyn<VMG * (NS - 1)>(min(NS - 1, nk - 1) * VMG);
       pp_barrier();                 // stage 0 has landed for everyone
       if (!g0) pp_barrier();        // group 1: one slot behind
       for (int kt = 0; kt < nk; ++kt) {
         mread(kt, H0);
         // buffer (kt+NS-1) % NS held stage kt-1, whose last reader (group 1) is done
-        if (g0 && kt >= 1 && kt + NS - 1 < nk) issue(kt + NS - 1);
+        if (g0 && kt >= 1 && kt + NS - 1 < nk) issue(cur, kt + NS - 1);
         pp_barrier();
         compute();
         if constexpr (UPS == 2) {
@@ -520,10 +552,16 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
       }
       if (g0) pp_barrier();         // same number of barriers in both groups
     };
-    __syncthreads();  // previous tile's readers are done with every stage
     if (nmt == 2) run(std::integral_constant<int, 2>{});
     else if (nmt == 1) run(std::integral_constant<int, 1>{});
     else run(std::integral_constant<int, 0>{});
+    // The last barrier of run() follows every LDS read of this tile in both groups, so every
+    // buffer is free: the next tile's first stages go out before this tile's stores.
+    if (t + G < total) {
+      cur = decode(t + G);
+      if (g0)
+        for (int st = 0; st < NS && st < nk; ++st) issue(cur, st);
+    }
 
     // epilogue
     if constexpr (!GATED && MAPPED) {
@@ -543,31 +581,38 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
     } else {
       // row-lane layout: block (mt, nt) holds row mt*128 + wm*32 + lane%32 in this lane, and
       // columns nt*32 + 8j + 4(lane/32) + c in acc[..][4j + c], j, c = 0..3
-      const int col_l = n0 + wn * CF::WN + 4 * (lane >> 5);
+      const int col_l = n0 + wn * CF::WN + 8 * (lane >> 5);
 #pragma unroll
       for (int mt = 0; mt < CF::MT; ++mt) {
         const int r = mt * 128 + wm * 32 + (lane & 31);
-        if (r < rows_valid) {
-          const size_t ro = (size_t)(row0 + r) * N + col_l;
+        const bool ok = r < rows_valid;
+        const size_t ro = (size_t)(row0 + (ok ? r : 0)) * N + col_l;
 #pragma unroll
-          for (int nt = 0; nt < CF::NT; ++nt)
+        for (int nt = 0; nt < CF::NT; ++nt)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const size_t o = ro + nt * 32 + 8 * j;
-              const f32x16_t& a0 = acc[0][mt][nt];
-              if constexpr (GATED) {
-                const f32x16_t& a1 = acc[1][mt][nt];
-                store_bf16x4(C + o, silu_f32(a0[4 * j]) * a1[4 * j], silu_f32(a0[4 * j + 1]) * a1[4 * j + 1],
-                             silu_f32(a0[4 * j + 2]) * a1[4 * j + 2], silu_f32(a0[4 * j + 3]) * a1[4 * j + 3]);
-                if (maps.save_g) {
-                  store_bf16x4(maps.save_g + o, a0[4 * j], a0[4 * j + 1], a0[4 * j + 2], a0[4 * j + 3]);
-                  store_bf16x4(maps.save_u + o, a1[4 * j], a1[4 * j + 1], a1[4 * j + 2], a1[4 * j + 3]);
+          for (int p = 0; p < 2; ++p) {
+            const size_t o = ro + nt * 32 + 16 * p;
+            const f32x16_t& a0 = acc[0][mt][nt];
+            const int i0 = 8 * p;
+            uint4 v;  // this lane's 16 bytes of C
+            if constexpr (GATED) {
+              const f32x16_t& a1 = acc[1][mt][nt];
+              float h[8];
+#pragma unroll
+              for (int c = 0; c < 8; ++c) h[c] = silu_f32(a0[i0 + c]) * a1[i0 + c];
+              v = pack_row16(h[0], h[1], h[2], h[3], h[4], h[5], h[6], h[7]);
+              if (maps.save_g) {
+                const uint4 g = pack_row16(a0, i0), u = pack_row16(a1, i0);
+                if (ok) {
+                  *reinterpret_cast<uint4*>(maps.save_g + o) = g;
+                  *reinterpret_cast<uint4*>(maps.save_u + o) = u;
                 }
-              } else {
-                store_bf16x4(C + o, a0[4 * j], a0[4 * j + 1], a0[4 * j + 2], a0[4 * j + 3]);
               }
+            } else {
+              v = pack_row16(a0, i0);
             }
-        }
+            if (ok) *reinterpret_cast<uint4*>(C + o) = v;
+          }
       }
     }
   }
