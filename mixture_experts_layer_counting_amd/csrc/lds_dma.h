@@ -62,8 +62,6 @@ __device__ __forceinline__ void wait_barrier_dyn(int n) {
   }
 }
 
-// MAPPED selects the row maps at compile time: gate/up gathers its A rows, down scatters
-// into the accumulator; the plain instantiations carry neither.
 // Wait until at most N of this wave's vector-memory operations are outstanding (no barrier).
 template <int N>
 __device__ __forceinline__ void wait_vm() {
