@@ -307,28 +307,6 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
 // kt-1, has then been read by both groups) and waits for them before the last barrier of
 // stage kt, so loads have four slots to land. Every barrier is preceded by lgkmcnt(0), so no
 // LDS read of a buffer is in flight when a later slot refills it.
-// Sixteen columns of one row of a row-lane 32x32 block, as bf16 (rounded to nearest even).
-// Lane l holds row l % 32: v0..v3 are columns 4(l / 32) + 0..3 and v4..v7 columns
-// 8 + 4(l / 32) + 0..3. v_permlane32_swap trades the second group of the lower half for the
-// first group of the upper half, after which lane l < 32 holds columns 0..7 and lane l + 32
-// columns 8..15: the 16 bytes this lane writes at its column 8(l / 32). All 64 lanes must be
-// active.
-__device__ __forceinline__ uint4 pack_row16(float v0, float v1, float v2, float v3, float v4, float v5,
-                                            float v6, float v7) {
-  const uint32_t a0 = pack_bf16x2(v0, v1), a1 = pack_bf16x2(v2, v3);
-  const uint32_t b0 = pack_bf16x2(v4, v5), b1 = pack_bf16x2(v6, v7);
-  // swap(x, y) returns (x of lanes 0..31 | y of lanes 0..31, x of lanes 32..63 | y of lanes
-  // 32..63): the lower half keeps x and receives the upper half's x as the second result; the
-  // upper half receives the lower half's y as the first result and keeps y
-  const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
-  const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
-  return make_uint4(s0[0], s1[0], s0[1], s1[1]);
-}
-
-__device__ __forceinline__ uint4 pack_row16(const f32x16_t& a, int i0) {
-  return pack_row16(a[i0], a[i0 + 1], a[i0 + 2], a[i0 + 3], a[i0 + 4], a[i0 + 5], a[i0 + 6], a[i0 + 7]);
-}
-
 __device__ __forceinline__ void pp_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
@@ -424,10 +402,15 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
     d.n0 = ntile * BN;
     if constexpr (GATED && MAPPED) {
       d.rA = make_rsrc(A, (uint32_t)maps.a_rows * (uint32_t)Kd * 2u);
+      // Branch-free so that the loads go out together: each reads a row of this tile (also
+      // for rows past it), and the offset is chosen after the arithmetic. -1: padding row.
+      int src[A_LDP];
+#pragma unroll
+      for (int i = 0; i < A_LDP; ++i) src[i] = maps.a_src[d.row0 + min(a_row[i], d.rows_valid - 1)];
 #pragma unroll
       for (int i = 0; i < A_LDP; ++i) {
-        const int src = a_row[i] < d.rows_valid ? maps.a_src[d.row0 + a_row[i]] : -1;  // -1: padding row
-        d.a_off[i] = src >= 0 ? (src / maps.a_k - a_row[i]) * Kd * 2 + a_voff[i] : (int)0x80000000u;
+        const int off = (src[i] / maps.a_k - a_row[i]) * Kd * 2 + a_voff[i];
+        d.a_off[i] = (a_row[i] < d.rows_valid && src[i] >= 0) ? off : (int)0x80000000u;
       }
     } else {
       d.rA = make_rsrc(A + (size_t)d.row0 * Kd, (uint32_t)d.rows_valid * (uint32_t)Kd * 2u);

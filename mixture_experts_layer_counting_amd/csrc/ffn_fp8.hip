@@ -61,7 +61,9 @@ struct F8Cfg {
   static constexpr int SF_B = SF_A + F8_BM * 4;
   static constexpr int STAGE = SF_B + NB * 4 * BN;
   static constexpr int VM_PER_STAGE = A_LD + B_LD + 1;  // + one scale load per wave
-  static constexpr int SCHED_BYTES = (F8_MAX_E + 1 + 16) * 4;
+  // tile prefix per expert, per-wave scan sums, and the gate/up epilogue's per-row amax of
+  // the two column waves ([2][256] fp32)
+  static constexpr int SCHED_BYTES = (F8_MAX_E + 1 + 16 + 2 * F8_BM) * 4;
   static constexpr int LDS_BYTES = F8_NS * STAGE + SCHED_BYTES;
   static_assert(A_LD >= 1 && B_LD >= 1, "tile too small");
   // the scale loads: waves 0-3 take 64 activation rows each (4 B per lane), waves 4-7 take
@@ -176,76 +178,108 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     for (int kk = 0; kk < CF::KK; ++kk) b_off[nt][kk] = c * CF::B_ROW + (((2 * kk + g2) ^ ((c >> 2) & 3)) << 4);
   }
 
-  for (int t = slot; t < total; t += G) {
-    const int e = find_expert(tstart, E, t);
-    const int lt = t - tstart[e];
-    const int gbeg = cu[e];
-    const int rows_e = cu[e + 1] - gbeg;
+  // Operand order of the MFMA: with the weight fragment first the accumulator comes out
+  // transposed, lane l holding one output row (l % 32 of its 32-row block) and runs of four
+  // consecutive columns, which the epilogues write as 8- and 16-byte row runs. The scatter
+  // epilogue keeps the other order (32 lanes of a row add into 32 consecutive floats).
+  constexpr bool ROW_LANES = !(!GATED && MAPPED);
+  float* xpart = reinterpret_cast<float*>(wsum + 16);  // [2][F8_BM] row amax of the column waves
+
+  // one output tile: rows, columns, the stage buffer its stage 0 uses, load descriptors
+  struct Tile {
+    int e, row0, rows_valid, n0, nmt, base, sc_voff;
+    i32x4_t rA, rB0, rB1;
+    int a_ld_off[CF::A_LD];
+  };
+  const int sc_row = (wave & 3) * 64 + lane;  // activation-scale row of waves 0-3
+  auto decode = [&](int t, int base) __attribute__((always_inline)) {
+    Tile d;
+    d.e = find_expert(tstart, E, t);
+    const int lt = t - tstart[d.e];
+    const int gbeg = cu[d.e];
+    const int rows_e = cu[d.e + 1] - gbeg;
     const int mte = (rows_e + F8_BM - 1) / F8_BM;
     const int ntile = lt / mte;
     const int mtile = lt - ntile * mte;
     const int chunk = even_chunk(rows_e, mte);
-    const int row0 = gbeg + mtile * chunk;
-    const int rows_valid = min(chunk, rows_e - mtile * chunk);
-    const int n0 = ntile * BN;
-
+    d.row0 = gbeg + mtile * chunk;
+    d.rows_valid = min(chunk, rows_e - mtile * chunk);
+    d.n0 = ntile * BN;
+    d.base = base;
     // A rows of this tile (see the bf16 kernels): rows past rows_valid load past the range.
-    // The activation-scale load of waves 0-3 covers tile rows 64 wave + lane.
-    i32x4_t rA;
-    int a_ld_off[CF::A_LD];
-    int sc_voff = 0;
-    const int sc_row = (wave & 3) * 64 + lane;
     if constexpr (GATED && MAPPED) {
-      rA = f8_rsrc(A, (uint32_t)maps.a_rows * (uint32_t)Kd);
+      d.rA = f8_rsrc(A, (uint32_t)maps.a_rows * (uint32_t)Kd);
+      // Branch-free so that the loads go out together: each reads a row of this tile (also
+      // for rows past it), and the offset is chosen after the arithmetic. -1: padding row.
+      int src[CF::A_LD];
+#pragma unroll
+      for (int i = 0; i < CF::A_LD; ++i) src[i] = maps.a_src[d.row0 + min(a_row[i], d.rows_valid - 1)];
+      const int ssrc0 = maps.a_src[d.row0 + min(sc_row, d.rows_valid - 1)];
 #pragma unroll
       for (int i = 0; i < CF::A_LD; ++i) {
-        const int src = a_row[i] < rows_valid ? maps.a_src[row0 + a_row[i]] : -1;  // -1: padding row
-        a_ld_off[i] = src >= 0 ? (src / maps.a_k - a_row[i]) * Kd + a_voff[i] : (int)0x80000000u;
+        const int off = (src[i] / maps.a_k - a_row[i]) * Kd + a_voff[i];
+        d.a_ld_off[i] = (a_row[i] < d.rows_valid && src[i] >= 0) ? off : (int)0x80000000u;
       }
-      const int ssrc = sc_row < rows_valid ? maps.a_src[row0 + sc_row] : -1;
-      sc_voff = ssrc >= 0 ? (ssrc / maps.a_k) * nsf * 4 : (int)0x80000000u;
+      const int ssrc = sc_row < d.rows_valid ? ssrc0 : -1;
+      d.sc_voff = ssrc >= 0 ? (ssrc / maps.a_k) * nsf * 4 : (int)0x80000000u;
     } else {
-      rA = f8_rsrc(A + (size_t)row0 * Kd, (uint32_t)rows_valid * (uint32_t)Kd);
+      d.rA = f8_rsrc(A + (size_t)d.row0 * Kd, (uint32_t)d.rows_valid * (uint32_t)Kd);
 #pragma unroll
-      for (int i = 0; i < CF::A_LD; ++i) a_ld_off[i] = a_voff[i];
-      sc_voff = (row0 + sc_row) * 4;
+      for (int i = 0; i < CF::A_LD; ++i) d.a_ld_off[i] = a_voff[i];
+      d.sc_voff = (d.row0 + sc_row) * 4;
     }
-    const int nmt = __builtin_amdgcn_readfirstlane((wm * 32 < rows_valid) + (128 + wm * 32 < rows_valid));
-    const size_t wbase = ((size_t)e * N + n0) * kbytes;
-    const uint32_t b_rem = (uint32_t)((size_t)(N - n0) * kbytes);
-    const i32x4_t rB0 = f8_rsrc(B0 + wbase, b_rem);
-    const i32x4_t rB1 = GATED ? f8_rsrc(B1 + wbase, b_rem) : rB0;
-    auto issue = [&](int kt) {
-      const uint32_t so = smem_lds + (uint32_t)((kt % F8_NS) * CF::STAGE);
+    d.nmt = __builtin_amdgcn_readfirstlane((wm * 32 < d.rows_valid) + (128 + wm * 32 < d.rows_valid));
+    const size_t wbase = ((size_t)d.e * N + d.n0) * kbytes;
+    const uint32_t b_rem = (uint32_t)((size_t)(N - d.n0) * kbytes);
+    d.rB0 = f8_rsrc(B0 + wbase, b_rem);
+    d.rB1 = GATED ? f8_rsrc(B1 + wbase, b_rem) : d.rB0;
+    return d;
+  };
+  // this wave's share of stage kt of tile d, into buffer (d.base + kt) mod F8_NS
+  auto issue = [&](const Tile& d, int kt) __attribute__((always_inline)) {
+    const uint32_t so = smem_lds + (uint32_t)(((unsigned)(d.base + kt) % F8_NS) * CF::STAGE);
 #pragma unroll
-      for (int i = 0; i < CF::A_LD; ++i) f8_dma16(rA, so + (wave + 8 * i) * 1024, a_ld_off[i], kt * F8_BK);
+    for (int i = 0; i < CF::A_LD; ++i) f8_dma16(d.rA, so + (wave + 8 * i) * 1024, d.a_ld_off[i], kt * F8_BK);
 #pragma unroll
-      for (int i = 0; i < CF::B_LD; ++i) {
-        const int j = wave + 8 * i;
-        const bool second = GATED && (j / (CF::B_BYTES / 1024)) != 0;
-        f8_dma16(second ? rB1 : rB0, so + CF::A_BYTES + j * 1024, b_voff[i], kt * (F8_BK / 2));
-      }
-      if (wave < 4) {
-        // activation scales of block kt for tile rows 64 wave + lane. Plain: block-major
-        // [Kd/128][M], rows >= M read as zero. Gathered: x_sf [a_rows][Kd/128] of the row's token.
-        if constexpr (GATED && MAPPED)
-          f8_dma4(f8_rsrc(A_sf, (uint32_t)maps.a_rows * (uint32_t)nsf * 4u), so + CF::SF_A + wave * 256,
-                  sc_voff, kt * 4);
-        else
-          f8_dma4(f8_rsrc(A_sf + (size_t)kt * M, (uint32_t)M * 4u), so + CF::SF_A + wave * 256, sc_voff, 0);
-      } else {
-        // weight scales of k-blocks 4kt..4kt+3, LDS [nb][kb][BN]: load j covers bytes
-        // 256 j .. 256 j + 255 of that block, i.e. matrix nb = j*256 / (4 BN), k-block rows of BN
-        const int j = wave - 4;
-        const int byte = j * 256 + lane * 4;
-        const int nb = byte / (4 * BN);
-        const int kb = (byte % (4 * BN)) / BN;
-        const int col = byte % BN;
-        const uint8_t* sfb = (GATED && nb) ? B1_sf : B0_sf;
-        f8_dma4(f8_rsrc(sfb + ((size_t)e * ksf_b + 4 * (size_t)kt) * N, (uint32_t)N * 4u),
-                so + CF::SF_B + j * 256, kb * N + n0 + col, 0);
-      }
-    };
+    for (int i = 0; i < CF::B_LD; ++i) {
+      const int j = wave + 8 * i;
+      const bool second = GATED && (j / (CF::B_BYTES / 1024)) != 0;
+      f8_dma16(second ? d.rB1 : d.rB0, so + CF::A_BYTES + j * 1024, b_voff[i], kt * (F8_BK / 2));
+    }
+    if (wave < 4) {
+      // activation scales of block kt for tile rows 64 wave + lane. Plain: block-major
+      // [Kd/128][M], rows >= M read as zero. Gathered: x_sf [a_rows][Kd/128] of the row's token.
+      if constexpr (GATED && MAPPED)
+        f8_dma4(f8_rsrc(A_sf, (uint32_t)maps.a_rows * (uint32_t)nsf * 4u), so + CF::SF_A + wave * 256,
+                d.sc_voff, kt * 4);
+      else
+        f8_dma4(f8_rsrc(A_sf + (size_t)kt * M, (uint32_t)M * 4u), so + CF::SF_A + wave * 256, d.sc_voff, 0);
+    } else {
+      // weight scales of k-blocks 4kt..4kt+3, LDS [nb][kb][BN]: load j covers bytes
+      // 256 j .. 256 j + 255 of that block, i.e. matrix nb = j*256 / (4 BN), k-block rows of BN
+      const int j = wave - 4;
+      const int byte = j * 256 + lane * 4;
+      const int nb = byte / (4 * BN);
+      const int kb = (byte % (4 * BN)) / BN;
+      const int col = byte % BN;
+      const uint8_t* sfb = (GATED && nb) ? B1_sf : B0_sf;
+      f8_dma4(f8_rsrc(sfb + ((size_t)d.e * ksf_b + 4 * (size_t)kt) * N, (uint32_t)N * 4u),
+              so + CF::SF_B + j * 256, kb * N + d.n0 + col, 0);
+    }
+  };
+
+  // The first two stages of a tile go out as soon as their buffers are free: for the first
+  // tile here, for the others right after the previous tile's K loop (its last barrier
+  // follows every read of the buffers they use), so that they land during that tile's
+  // epilogue. Each tile's stages continue the buffer rotation of the previous one.
+  Tile cur;
+  if (slot < total) {
+    cur = decode(slot, 0);
+    issue(cur, 0);
+    if (nk > 1) issue(cur, 1);
+  }
+  for (int t = slot; t < total; t += G) {
+    const int row0 = cur.row0, rows_valid = cur.rows_valid, n0 = cur.n0, nmt = cur.nmt, base = cur.base;
     f32x16_t acc[CF::NB][CF::MT][CF::NT];
 #pragma unroll
     for (int nb = 0; nb < CF::NB; ++nb)
@@ -256,21 +290,19 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[nb][mt][nt][i] = 0.f;
 
-    __syncthreads();
-    issue(0);
-    if (nk > 1) issue(1);
     // the K loop over the first MTV row blocks of this wave (MTV fixed at compile time; a
     // wave with none still issues its loads and meets every barrier)
     auto k_loop = [&](auto mtv) {
       constexpr int MTV = decltype(mtv)::value;
       for (int kt = 0; kt < nk; ++kt) {
-        // stage kt complete for every wave; stage kt+1 (if any) may still be in flight. The
+        // stage kt complete for every wave; stage kt+1 (if any) may still be in flight (and
+        // the previous tile's output stores, issued after both, only add to the count). The
         // barrier also means every wave is done with stage kt-1, whose buffer stage kt+2 reuses.
         if (kt + 1 < nk) f8_wait_barrier<CF::VM_PER_STAGE>();
         else f8_wait_barrier<0>();
-        if (kt + 2 < nk) issue(kt + 2);
+        if (kt + 2 < nk) issue(cur, kt + 2);
         if constexpr (MTV > 0) {
-          const unsigned char* sa_l = smem + (kt % F8_NS) * CF::STAGE;
+          const unsigned char* sa_l = smem + ((unsigned)(base + kt) % F8_NS) * CF::STAGE;
           const unsigned char* sb_l = sa_l + CF::A_BYTES;
           // this stage's scales as e8m0 bytes: one per row block (the row's 1x128 block), and
           // per fragment and MFMA step the byte of k-block 2kk + G of the lane's column
@@ -297,9 +329,14 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
                 const i32x8_t bfr = __builtin_shufflevector(bq, z, 0, 1, 2, 3, 4, 5, 6, 7);
                 const int sbw = sfb[(nb * 4 + 2 * kk + g2) * BN + wn * CF::WN + nt * 32 + (lane & 31)];
 #pragma unroll
-                for (int mt = 0; mt < MTV; ++mt)
-                  acc[nb][mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                      af[mt], bfr, acc[nb][mt][nt], 0, 4, 0, sa[mt], 0, sbw);
+                for (int mt = 0; mt < MTV; ++mt) {
+                  if constexpr (ROW_LANES)  // weights (fp4, format 4) as the first operand
+                    acc[nb][mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        bfr, af[mt], acc[nb][mt][nt], 4, 0, 0, sbw, 0, sa[mt]);
+                  else
+                    acc[nb][mt][nt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        af[mt], bfr, acc[nb][mt][nt], 0, 4, 0, sa[mt], 0, sbw);
+                }
               }
             }
           }
@@ -310,54 +347,56 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     else if (nmt == 1) k_loop(std::integral_constant<int, 1>{});
     else k_loop(std::integral_constant<int, 0>{});
 
+    if (t + G < total) {
+      cur = decode(t + G, (unsigned)(base + nk) % F8_NS);
+      issue(cur, 0);
+      if (nk > 1) issue(cur, 1);
+    }
+
     if constexpr (GATED) {
-      // SwiGLU, then per-row amax over this wave's 64 columns of the 128-column block; the two
-      // column halves (wn = 0, 1) meet in LDS.
-      float* part = reinterpret_cast<float*>(smem);  // [2][256]
-      float hv[CF::MT][CF::NT][16];
-      float rmax[CF::MT][16];
+      // Row-lane layout: lane l holds row mt*128 + wm*32 + l%32, and block nt's acc[..][4j+c]
+      // is column nt*32 + 8j + 4(l/32) + c of this wave's WN columns. h = silu(g) * u replaces
+      // g in place; the row's amax over the wave's columns combines the lane's values with
+      // lane l^32's, then over the tile's 128-column scale block with the other column wave's
+      // through LDS.
+      float rmax[CF::MT];
 #pragma unroll
-      for (int mt = 0; mt < CF::MT; ++mt)
+      for (int mt = 0; mt < CF::MT; ++mt) {
+        float mx = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float m = 0.f;
+        for (int nt = 0; nt < CF::NT; ++nt)
 #pragma unroll
-          for (int nt = 0; nt < CF::NT; ++nt) {
+          for (int i = 0; i < 16; ++i) {
             const float v = silu_f32(acc[0][mt][nt][i]) * acc[1][mt][nt][i];
-            hv[mt][nt][i] = v;
-            m = fmaxf(m, __builtin_fabsf(v));
+            acc[0][mt][nt][i] = v;
+            mx = fmaxf(mx, __builtin_fabsf(v));
           }
-#pragma unroll
-          for (int off = 1; off < 32; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-          rmax[mt][i] = m;
-        }
-      __syncthreads();  // every wave is done with the stage buffers
-      if ((lane & 31) == 0) {
-#pragma unroll
-        for (int mt = 0; mt < CF::MT; ++mt)
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            part[wn * 256 + mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3)] = rmax[mt][i];
+        rmax[mt] = fmaxf(mx, __shfl_xor(mx, 32, 64));
       }
-      __syncthreads();
+      if (lane < 32) {
 #pragma unroll
-      for (int mt = 0; mt < CF::MT; ++mt)
+        for (int mt = 0; mt < CF::MT; ++mt) xpart[wn * F8_BM + mt * 128 + wm * 32 + lane] = rmax[mt];
+      }
+      __syncthreads();  // xpart is written again only after the next tile's K loop barriers
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3);
-          const float amax = fmaxf(part[r], part[256 + r]);
-          const float s = fp8_pow2_scale(amax);
-          const float inv = 1.0f / s;
-          if (r < rows_valid) {
-            const size_t ro = (size_t)(row0 + r);
+      for (int mt = 0; mt < CF::MT; ++mt) {
+        const int r = mt * 128 + wm * 32 + (lane & 31);
+        const bool ok = r < rows_valid;
+        const float s = fp8_pow2_scale(fmaxf(xpart[r], xpart[F8_BM + r]));
+        const float inv = 1.0f / s;  // exact: s is a power of two
+        uint8_t* rowp = C8 + (size_t)(row0 + (ok ? r : 0)) * N + n0 + wn * CF::WN + 8 * (lane >> 5);
 #pragma unroll
-            for (int nt = 0; nt < CF::NT; ++nt) {
-              const int col = n0 + wn * CF::WN + nt * 32 + (lane & 31);
-              C8[ro * N + col] = (uint8_t)f32_to_e4m3(hv[mt][nt][i] * inv);
-            }
-            if (wn == 0 && (lane & 31) == 0) C8_sf[(size_t)(n0 / 128) * M + ro] = s;  // [N/128][M]
+        for (int nt = 0; nt < CF::NT; ++nt)
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            const f32x16_t& h = acc[0][mt][nt];
+            const int i0 = 8 * p;
+            const uint2 q = pack_row8_e4m3(h[i0] * inv, h[i0 + 1] * inv, h[i0 + 2] * inv, h[i0 + 3] * inv,
+                                           h[i0 + 4] * inv, h[i0 + 5] * inv, h[i0 + 6] * inv, h[i0 + 7] * inv);
+            if (ok) *reinterpret_cast<uint2*>(rowp + nt * 32 + 16 * p) = q;
           }
-        }
+        if (ok && wn == 0 && lane < 32) C8_sf[(size_t)(n0 / 128) * M + row0 + r] = s;  // [N/128][M]
+      }
     } else if constexpr (MAPPED) {
 #pragma unroll
       for (int mt = 0; mt < CF::MT; ++mt)
@@ -374,17 +413,21 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
           }
         }
     } else {
+      // row-lane layout as above; 16-byte bf16 row runs
+      const int col_l = n0 + wn * CF::WN + 8 * (lane >> 5);
 #pragma unroll
-      for (int mt = 0; mt < CF::MT; ++mt)
+      for (int mt = 0; mt < CF::MT; ++mt) {
+        const int r = mt * 128 + wm * 32 + (lane & 31);
+        const bool ok = r < rows_valid;
+        const size_t ro = (size_t)(row0 + (ok ? r : 0)) * N + col_l;
 #pragma unroll
-        for (int nt = 0; nt < CF::NT; ++nt) {
-          const int col = n0 + wn * CF::WN + nt * 32 + (lane & 31);
+        for (int nt = 0; nt < CF::NT; ++nt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * g2 + (i & 3);
-            if (r < rows_valid) C16[(size_t)(row0 + r) * N + col] = f32_to_bf16_bits(acc[0][mt][nt][i]);
+          for (int p = 0; p < 2; ++p) {
+            const uint4 v = pack_row16(acc[0][mt][nt], 8 * p);
+            if (ok) *reinterpret_cast<uint4*>(C16 + ro + nt * 32 + 16 * p) = v;
           }
-        }
+      }
     }
   }
 }

@@ -77,6 +77,46 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
 // instructions per element in the epilogues.
 __device__ __forceinline__ float silu_f32(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
+// Sixteen columns of one row of a row-lane 32x32 block, as bf16 (rounded to nearest even).
+// Lane l holds row l % 32: v0..v3 are columns 4(l / 32) + 0..3 and v4..v7 columns
+// 8 + 4(l / 32) + 0..3. v_permlane32_swap trades the second group of the lower half for the
+// first group of the upper half, after which lane l < 32 holds columns 0..7 and lane l + 32
+// columns 8..15: the 16 bytes this lane writes at its column 8(l / 32). All 64 lanes must be
+// active.
+__device__ __forceinline__ uint4 pack_row16(float v0, float v1, float v2, float v3, float v4, float v5,
+                                            float v6, float v7) {
+  const uint32_t a0 = pack_bf16x2(v0, v1), a1 = pack_bf16x2(v2, v3);
+  const uint32_t b0 = pack_bf16x2(v4, v5), b1 = pack_bf16x2(v6, v7);
+  // swap(x, y) returns (x of lanes 0..31 | y of lanes 0..31, x of lanes 32..63 | y of lanes
+  // 32..63): the lower half keeps x and receives the upper half's x as the second result; the
+  // upper half receives the lower half's y as the first result and keeps y
+  const auto s0 = __builtin_amdgcn_permlane32_swap(a0, b0, false, false);
+  const auto s1 = __builtin_amdgcn_permlane32_swap(a1, b1, false, false);
+  return make_uint4(s0[0], s1[0], s0[1], s1[1]);
+}
+
+__device__ __forceinline__ uint4 pack_row16(const f32x16_t& a, int i0) {
+  return pack_row16(a[i0], a[i0 + 1], a[i0 + 2], a[i0 + 3], a[i0 + 4], a[i0 + 5], a[i0 + 6], a[i0 + 7]);
+}
+
+// fp32 -> OCP e4m3fn codes of four values (gfx950's v_cvt_pk_fp8_f32: round to nearest even;
+// identical to f32_to_e4m3 below on every |v| <= 448, which was checked on the device for all
+// such fp32 values), packed low byte first. Adding +0 turns -0 into +0, so an exact zero
+// encodes as 0x00 as f32_to_e4m3 does; callers keep |v| <= 448.
+__device__ __forceinline__ uint32_t pack_e4m3x4(float v0, float v1, float v2, float v3) {
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(v0 + 0.0f, v1 + 0.0f, 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(v2 + 0.0f, v3 + 0.0f, lo, true);
+}
+
+// Sixteen columns of one row of a row-lane 32x32 block as e4m3 codes, laid out as in
+// pack_row16: lane l < 32 gets columns 0..7 and lane l + 32 columns 8..15 (8 bytes).
+__device__ __forceinline__ uint2 pack_row8_e4m3(float v0, float v1, float v2, float v3, float v4, float v5,
+                                               float v6, float v7) {
+  const uint32_t a = pack_e4m3x4(v0, v1, v2, v3), b = pack_e4m3x4(v4, v5, v6, v7);
+  const auto sw = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+  return make_uint2(sw[0], sw[1]);
+}
+
 // ---- OCP 8-bit formats -----------------------------------------------------------------
 
 // e8m0 byte of an fp32 power of two
