@@ -307,6 +307,44 @@ def test_small_fp8_mxfp4_layer(spec):
     assert same >= 0.99 * n
 
 
+# Expert sizes on both sides of the 32-row MFMA block and the 256-row tile: an expert's rows
+# are spread evenly over its tiles in 32-row blocks (257 -> 160 + 97, 513 -> 192 + 192 + 129,
+# 769 -> 4 tiles), blocks past a tile's rows are skipped, and the gathered-row loads of a
+# tile read only rows of that tile.
+EDGE_COUNTS = [0, 1, 31, 32, 33, 255, 256, 257, 300, 511, 512, 513, 769, 2]
+
+
+def edge_routing(counts, K, seed):
+    """topk_idx with exactly counts[e] copies of expert e, no token twice on one expert (the
+    copies laid out expert by expert, column-major over [T, K]: an expert's copies in column 1
+    start after its copies in column 0 end, since no count exceeds T), Dirichlet(1) weights."""
+    T = sum(counts) // K
+    assert sum(counts) == T * K and max(counts) <= T
+    ids = np.repeat(np.arange(len(counts)), counts)
+    idx = ids.reshape(K, T).T.copy()
+    assert all(len(set(row)) == K for row in idx.tolist())
+    wts = np.random.default_rng(seed).dirichlet(np.ones(K), size=T).astype(np.float32)
+    return idx.astype(np.int32), wts
+
+
+@pytest.mark.parametrize("act,wgt", [("bf16", "bf16"), ("fp8", "mxfp4")])
+def test_expert_sizes_around_tile_boundaries(act, wgt):
+    K = 2
+    T, E = sum(EDGE_COUNTS) // K, len(EDGE_COUNTS)
+    say(f"{act} x {wgt}: expert sizes {EDGE_COUNTS}")
+    w = gen.make(T=T, H=512, Hp=256, E=E, K=K, act=act, wgt=wgt, out="bf16", routing="balanced", cid=61,
+                 device=DEV)
+    idx, wts = edge_routing(EDGE_COUNTS, K, 61)
+    w.topk_idx = torch.from_numpy(idx).to(DEV)
+    w.topk_w = torch.from_numpy(wts).to(DEV)
+    r, ref = full_check(w)
+    assert np.array_equal(ref["counts"], np.asarray(EDGE_COUNTS))
+    # the layer (rows gathered from x, no x_perm) gives the same bits as the steps
+    out, _, _ = run_layer(w)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), r["out"].view(torch.int16))
+
+
 @pytest.mark.slow
 def test_c5_full_size_sampled():
     say("c5 fp8 x mxfp4 E=384 maxvio=1, full size")
