@@ -140,37 +140,66 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dgrad_kernel(
         for (int nt = 0; nt < 4; ++nt)
           bfr[nt] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const i32x4_t*>(
                                                      sw_ + (wn * 128 + nt * 32) * BW_ROWB + fk[kk]));
+        // weight fragment first: the accumulator comes out transposed (one output row per lane)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nt], af[mt], acc[mt][nt], 0, 0, 0);
       }
     }
 
-    // epilogue: lane holds column lane%32 of rows 8*(i/4) + 4*(lane/32) + i%4
+    // epilogue: lane holds row mt*128 + wm*32 + lane%32 and, for j = 0..3, the columns
+    // nt*32 + 8j + 4(lane/32) + 0..3 in acc[..][4j .. 4j+3]; outputs leave as 16-byte row runs
+    // (pack_row16: lane l < 32 writes columns 16p + 0..7, lane l + 32 columns 16p + 8..15)
+    const int h4 = 4 * (lane >> 5);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) {
+      const int r = mt * 128 + wm * 32 + (lane & 31);
+      const bool ok = r < rows_valid;
+      const size_t ro = (size_t)(row0 + (ok ? r : 0)) * N + n0 + wn * 128;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int col = n0 + wn * 128 + nt * 32 + (lane & 31);
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          if (r < rows_valid) {
-            const size_t o = (size_t)(row0 + r) * N + col;
-            const float v = acc[mt][nt][i];
-            if constexpr (EPI == BW_EPI_STORE) {
-              C[o] = f32_to_bf16_bits(v);
-            } else {
-              const float g = bf16f(G[o]), u = bf16f(U[o]);
-              const float sg = 1.0f / (1.0f + __expf(-g));
-              DG[o] = f32_to_bf16_bits(v * u * sg * (1.0f + g * (1.0f - sg)));
-              DU[o] = f32_to_bf16_bits(v * g * sg);
+        for (int p = 0; p < 2; ++p) {
+          const f32x16_t& a = acc[mt][nt];
+          const size_t o = ro + nt * 32 + 16 * p;  // this 16-column run
+          float v[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) v[c] = a[8 * p + c];
+          if constexpr (EPI == BW_EPI_STORE) {
+            const uint4 q = pack_row16(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
+            if (ok) *reinterpret_cast<uint4*>(C + o + 8 * (lane >> 5)) = q;
+          } else {
+            // g, u of the lane's eight columns 16p + h4 + 0..3 and 16p + 8 + h4 + 0..3
+            uint2 gq[2] = {make_uint2(0, 0), make_uint2(0, 0)}, uq[2] = {make_uint2(0, 0), make_uint2(0, 0)};
+            if (ok) {
+#pragma unroll
+              for (int hh = 0; hh < 2; ++hh) {
+                gq[hh] = *reinterpret_cast<const uint2*>(G + o + 8 * hh + h4);
+                uq[hh] = *reinterpret_cast<const uint2*>(U + o + 8 * hh + h4);
+              }
+            }
+            float dg[8], du[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+              const uint2 gw = gq[c >> 2], uw = uq[c >> 2];
+              const uint32_t gb = ((c & 2) ? gw.y : gw.x) >> (16 * (c & 1));
+              const uint32_t ub = ((c & 2) ? uw.y : uw.x) >> (16 * (c & 1));
+              const float g = bf16f((uint16_t)gb), u = bf16f((uint16_t)ub);
+              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));  // sigmoid(g)
+              dg[c] = v[c] * u * sg * (1.0f + g * (1.0f - sg));
+              du[c] = v[c] * g * sg;
+            }
+            const uint4 qg = pack_row16(dg[0], dg[1], dg[2], dg[3], dg[4], dg[5], dg[6], dg[7]);
+            const uint4 qu = pack_row16(du[0], du[1], du[2], du[3], du[4], du[5], du[6], du[7]);
+            if (ok) {
+              *reinterpret_cast<uint4*>(DG + o + 8 * (lane >> 5)) = qg;
+              *reinterpret_cast<uint4*>(DU + o + 8 * (lane >> 5)) = qu;
             }
           }
         }
-      }
+    }
   }
 }
 
@@ -268,27 +297,30 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_wgrad_kernel(
           const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(p + 4 * ROW));
           bfr[nt] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
+        // B fragment first: the accumulator comes out transposed, lane l holding row m of dW
+        // (l % 32 of the block) and runs of four consecutive n
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mt], bfr[nt], acc[mt][nt], 0, 0, 0);
+            acc[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[nt], af[mt], acc[mt][nt], 0, 0, 0);
       }
     }
 
-    // dW[e][m][n]: lane holds column n = lane%32 of rows m = 8*(i/4) + 4*(lane/32) + i%4
+    // dW[e][m][n]: lane holds row m = wm*64 + mt*32 + lane%32 and, for j = 0..3, the columns
+    // n = nt*32 + 8j + 4(lane/32) + 0..3 in acc[..][4j .. 4j+3]: 16-byte row stores
     float* We = W + (size_t)e * Md * Nd;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 2; ++mt) {
+      float* row = We + (size_t)(m0 + wm * 64 + mt * 32 + (lane & 31)) * Nd + n0 + wn * 128 + 4 * (lane >> 5);
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int n = n0 + wn * 128 + nt * 32 + (lane & 31);
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int m = m0 + wm * 64 + mt * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-          We[(size_t)m * Nd + n] = acc[mt][nt][i];
+        for (int j = 0; j < 4; ++j) {
+          const f32x16_t& a = acc[mt][nt];
+          *reinterpret_cast<float4*>(row + nt * 32 + 8 * j) = make_float4(a[4 * j], a[4 * j + 1], a[4 * j + 2], a[4 * j + 3]);
         }
-      }
+    }
   }
 }
 
