@@ -46,6 +46,66 @@ enum { BW_EPI_STORE = 0, BW_EPI_SWIGLU = 1 };
 
 __device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
+// Epilogue of the data-gradient kernels. Row-lane accumulators (the weight fragment is the
+// first MFMA operand): lane l holds row mt*128 + wm*32 + l%32 and, for j = 0..3, the
+// columns nt*32 + 8j + 4(l/32) + 0..3 in acc[..][4j .. 4j+3]; outputs leave as 16-byte row
+// runs (pack_row16: lane l < 32 writes columns 16p + 0..7, lane l + 32 columns 16p + 8..15).
+// EPI_STORE writes C = acc in bf16; EPI_SWIGLU takes acc as dh and writes dg, du from g, u.
+template <int EPI>
+__device__ __forceinline__ void dgrad_epilogue(const f32x16_t (&acc)[2][4], int row0, int rows_valid, int n0,
+                                               int N, int wm, int wn, int lane, uint16_t* __restrict__ C,
+                                               const uint16_t* __restrict__ G, const uint16_t* __restrict__ U,
+                                               uint16_t* __restrict__ DG, uint16_t* __restrict__ DU) {
+  const int h4 = 4 * (lane >> 5);
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    const int r = mt * 128 + wm * 32 + (lane & 31);
+    const bool ok = r < rows_valid;
+    const size_t ro = (size_t)(row0 + (ok ? r : 0)) * N + n0 + wn * 128;
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        const f32x16_t& a = acc[mt][nt];
+        const size_t o = ro + nt * 32 + 16 * p;  // this 16-column run
+        float v[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[c] = a[8 * p + c];
+        if constexpr (EPI == BW_EPI_STORE) {
+          const uint4 q = pack_row16(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
+          if (ok) *reinterpret_cast<uint4*>(C + o + 8 * (lane >> 5)) = q;
+        } else {
+          // g, u of the lane's eight columns 16p + h4 + 0..3 and 16p + 8 + h4 + 0..3
+          uint2 gq[2] = {make_uint2(0, 0), make_uint2(0, 0)}, uq[2] = {make_uint2(0, 0), make_uint2(0, 0)};
+          if (ok) {
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              gq[hh] = *reinterpret_cast<const uint2*>(G + o + 8 * hh + h4);
+              uq[hh] = *reinterpret_cast<const uint2*>(U + o + 8 * hh + h4);
+            }
+          }
+          float dg[8], du[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const uint2 gw = gq[c >> 2], uw = uq[c >> 2];
+            const uint32_t gb = ((c & 2) ? gw.y : gw.x) >> (16 * (c & 1));
+            const uint32_t ub = ((c & 2) ? uw.y : uw.x) >> (16 * (c & 1));
+            const float g = bf16f((uint16_t)gb), u = bf16f((uint16_t)ub);
+            const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));  // sigmoid(g)
+            dg[c] = v[c] * u * sg * (1.0f + g * (1.0f - sg));
+            du[c] = v[c] * g * sg;
+          }
+          const uint4 qg = pack_row16(dg[0], dg[1], dg[2], dg[3], dg[4], dg[5], dg[6], dg[7]);
+          const uint4 qu = pack_row16(du[0], du[1], du[2], du[3], du[4], du[5], du[6], du[7]);
+          if (ok) {
+            *reinterpret_cast<uint4*>(DG + o + 8 * (lane >> 5)) = qg;
+            *reinterpret_cast<uint4*>(DU + o + 8 * (lane >> 5)) = qu;
+          }
+        }
+      }
+  }
+}
+
 template <int EPI, bool DUAL>
 __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dgrad_kernel(
     const uint16_t* __restrict__ A0, const uint16_t* __restrict__ A1, const int* __restrict__ cu,
@@ -149,57 +209,7 @@ __global__ __launch_bounds__(BW_THREADS, 1) void bwd_dgrad_kernel(
       }
     }
 
-    // epilogue: lane holds row mt*128 + wm*32 + lane%32 and, for j = 0..3, the columns
-    // nt*32 + 8j + 4(lane/32) + 0..3 in acc[..][4j .. 4j+3]; outputs leave as 16-byte row runs
-    // (pack_row16: lane l < 32 writes columns 16p + 0..7, lane l + 32 columns 16p + 8..15)
-    const int h4 = 4 * (lane >> 5);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int r = mt * 128 + wm * 32 + (lane & 31);
-      const bool ok = r < rows_valid;
-      const size_t ro = (size_t)(row0 + (ok ? r : 0)) * N + n0 + wn * 128;
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          const f32x16_t& a = acc[mt][nt];
-          const size_t o = ro + nt * 32 + 16 * p;  // this 16-column run
-          float v[8];
-#pragma unroll
-          for (int c = 0; c < 8; ++c) v[c] = a[8 * p + c];
-          if constexpr (EPI == BW_EPI_STORE) {
-            const uint4 q = pack_row16(v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]);
-            if (ok) *reinterpret_cast<uint4*>(C + o + 8 * (lane >> 5)) = q;
-          } else {
-            // g, u of the lane's eight columns 16p + h4 + 0..3 and 16p + 8 + h4 + 0..3
-            uint2 gq[2] = {make_uint2(0, 0), make_uint2(0, 0)}, uq[2] = {make_uint2(0, 0), make_uint2(0, 0)};
-            if (ok) {
-#pragma unroll
-              for (int hh = 0; hh < 2; ++hh) {
-                gq[hh] = *reinterpret_cast<const uint2*>(G + o + 8 * hh + h4);
-                uq[hh] = *reinterpret_cast<const uint2*>(U + o + 8 * hh + h4);
-              }
-            }
-            float dg[8], du[8];
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-              const uint2 gw = gq[c >> 2], uw = uq[c >> 2];
-              const uint32_t gb = ((c & 2) ? gw.y : gw.x) >> (16 * (c & 1));
-              const uint32_t ub = ((c & 2) ? uw.y : uw.x) >> (16 * (c & 1));
-              const float g = bf16f((uint16_t)gb), u = bf16f((uint16_t)ub);
-              const float sg = __builtin_amdgcn_rcpf(1.0f + __expf(-g));  // sigmoid(g)
-              dg[c] = v[c] * u * sg * (1.0f + g * (1.0f - sg));
-              du[c] = v[c] * g * sg;
-            }
-            const uint4 qg = pack_row16(dg[0], dg[1], dg[2], dg[3], dg[4], dg[5], dg[6], dg[7]);
-            const uint4 qu = pack_row16(du[0], du[1], du[2], du[3], du[4], du[5], du[6], du[7]);
-            if (ok) {
-              *reinterpret_cast<uint4*>(DG + o + 8 * (lane >> 5)) = qg;
-              *reinterpret_cast<uint4*>(DU + o + 8 * (lane >> 5)) = qu;
-            }
-          }
-        }
-    }
+    dgrad_epilogue<EPI>(acc, row0, rows_valid, n0, N, wm, wn, lane, C, G, U, DG, DU);
   }
 }
 
