@@ -313,7 +313,14 @@ __device__ __forceinline__ void pp_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-template <bool GATED, int BN, int BK, int NS, bool MAPPED>
+// With PF (cross-tile prefetch) the next tile of the block is decoded inside the K loop of
+// the current one, from LDS copies of the tile prefix and cu_seqlens; when gathering, group 0
+// loads its 256 row sources straight into LDS NS steps before they are needed, counting that
+// load in its stage waits. The next tile's stages 0..NS-2 then go out in the last NS-1 K steps
+// (the slots that load nothing for the current tile) into the buffers they use in the next
+// tile (stage s -> buffer s % NS needs nk % NS == 0), and only stage NS-1 is issued after
+// the last barrier. Needs nk >= 2 NS: the decode happens at K step kd = nk - 2 NS + 1 >= 1.
+template <bool GATED, int BN, int BK, int NS, bool MAPPED, bool PF>
 __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
     const uint16_t* __restrict__ A, const int* __restrict__ cu, int M, int E, int Kd, int N,
     const uint16_t* __restrict__ B0, const uint16_t* __restrict__ B1, uint16_t* __restrict__ C,
@@ -333,9 +340,14 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
   constexpr bool ROW_LANES = !(!GATED && MAPPED);
   static_assert(CF::KK % KH == 0 && PER_MAT % 4 == 0 && A_LDP >= 1, "ping-pong tiling");
   static_assert(VMG * (NS - 1) < 64, "vmcnt range");
+  static_assert(!PF || NS >= 3, "prefetch needs at least three stages");
+  // a row-source load rides in group 0's stage waits when prefetching a gathered tile
+  constexpr bool XA = PF && GATED && MAPPED;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int* tstart = reinterpret_cast<int*>(smem + NS * CF::STAGE);
   int* wsum = tstart + FB_MAX_E + 1;
+  int* cu_l = wsum + 16;              // PF: copy of cu_seqlens[0..E]
+  int* src_l = cu_l + FB_MAX_E + 1;   // PF, gathering: the next tile's FB_BM row sources
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -345,8 +357,11 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
   const bool g0 = wave < 4;
   const int gw = wave & 3;
   const int ntn = N / BN;
+  if constexpr (PF)
+    for (int i = tid; i <= E; i += FB_THREADS) cu_l[i] = cu[i];  // ordered by the prefix's barriers
   const int total = build_tile_prefix<FB_BM, FB_THREADS>(cu, E, ntn, tstart, wsum);
   const int nk = Kd / BK;
+  const int kd = nk - 2 * NS + 1;     // PF: K step at which the next tile is decoded
   const int G = gridDim.x;
   const int slot = xcd_slot(blockIdx.x, G);
 
@@ -380,19 +395,28 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
   const int bP = (wn * CF::WN) / 16 + (g & 1);
   const int b_fbase = (8 * (g >> 1) + (jj >> 2)) * CF::B_ROW + 8 * (jj & 3) + ((bP ^ ((jj >> 2) << 1)) << 5);
   const uint32_t smem_lds = lds_addr(smem);
+  constexpr int SRC_OFF = NS * CF::STAGE + CF::SCHED_BYTES + (FB_MAX_E + 1) * 4;  // src_l in smem
 
   // one output tile: its expert, rows, columns and load descriptors
   struct Tile {
-    int row0, rows_valid, n0, nmt;
+    int e, row0, rows_valid, n0, nmt;
     i32x4_t rA, rB0, rB1;
     int a_off[A_LDP];
   };
-  auto decode = [&](int t) __attribute__((always_inline)) {
+  // A offsets of a gathered tile from the sources of this wave's A rows. The rows past the
+  // tile read a clamped source and are then pointed out of range. -1: padding row.
+  auto gather_offsets = [&](Tile& d, const int (&src)[A_LDP]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < A_LDP; ++i) {
+      const int off = (src[i] / maps.a_k - a_row[i]) * Kd * 2 + a_voff[i];
+      d.a_off[i] = (a_row[i] < d.rows_valid && src[i] >= 0) ? off : (int)0x80000000u;
+    }
+  };
+  // tile t of expert e, whose rows start at gbeg: everything but a gathered tile's A offsets
+  auto decode_tile = [&](int t, int e, int gbeg, int rows_e) __attribute__((always_inline)) {
     Tile d;
-    const int e = find_expert(tstart, E, t);
+    d.e = e;
     const int lt = t - tstart[e];
-    const int gbeg = cu[e];
-    const int rows_e = cu[e + 1] - gbeg;
     const int mte = (rows_e + FB_BM - 1) / FB_BM;
     const int ntile = n_fastest ? lt % ntn : lt / mte;
     const int mtile = n_fastest ? lt / ntn : lt - ntile * mte;
@@ -402,16 +426,6 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
     d.n0 = ntile * BN;
     if constexpr (GATED && MAPPED) {
       d.rA = make_rsrc(A, (uint32_t)maps.a_rows * (uint32_t)Kd * 2u);
-      // Branch-free so that the loads go out together: each reads a row of this tile (also
-      // for rows past it), and the offset is chosen after the arithmetic. -1: padding row.
-      int src[A_LDP];
-#pragma unroll
-      for (int i = 0; i < A_LDP; ++i) src[i] = maps.a_src[d.row0 + min(a_row[i], d.rows_valid - 1)];
-#pragma unroll
-      for (int i = 0; i < A_LDP; ++i) {
-        const int off = (src[i] / maps.a_k - a_row[i]) * Kd * 2 + a_voff[i];
-        d.a_off[i] = (a_row[i] < d.rows_valid && src[i] >= 0) ? off : (int)0x80000000u;
-      }
     } else {
       d.rA = make_rsrc(A + (size_t)d.row0 * Kd, (uint32_t)d.rows_valid * (uint32_t)Kd * 2u);
 #pragma unroll
@@ -423,6 +437,34 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
     d.rB1 = GATED ? make_rsrc(B1 + woff, b_rem) : d.rB0;
     d.nmt = __builtin_amdgcn_readfirstlane((wm * 32 < d.rows_valid) + (128 + wm * 32 < d.rows_valid));
     return d;
+  };
+  auto decode = [&](int t) __attribute__((always_inline)) {
+    const int e = find_expert(tstart, E, t);
+    const int gbeg = cu[e];
+    Tile d = decode_tile(t, e, gbeg, cu[e + 1] - gbeg);
+    if constexpr (GATED && MAPPED) {
+      // Branch-free so that the loads go out together: each reads a row of this tile (also
+      // for rows past it), and the offset is chosen after the arithmetic.
+      int src[A_LDP];
+#pragma unroll
+      for (int i = 0; i < A_LDP; ++i) src[i] = maps.a_src[d.row0 + min(a_row[i], d.rows_valid - 1)];
+      gather_offsets(d, src);
+    }
+    return d;
+  };
+  // PF: tile t, a later tile than one of expert e_prev, from LDS only. The tile prefix is
+  // nondecreasing and tstart[E] = total > t, so the owner is e_prev plus the number of
+  // experts after it that start at or before t, counted 64 at a time with a ballot.
+  auto decode_next = [&](int t, int e_prev) __attribute__((always_inline)) {
+    int e = e_prev;
+    for (;;) {
+      const int i = e + 1 + lane;
+      const int c = __popcll(__ballot(i < E && tstart[min(i, E)] <= t));
+      e += c;
+      if (c < 64) break;
+    }
+    const int gbeg = __builtin_amdgcn_readfirstlane(cu_l[e]);
+    return decode_tile(t, e, gbeg, __builtin_amdgcn_readfirstlane(cu_l[e + 1]) - gbeg);
   };
   // group 0 only: this wave's share of stage kt of tile d
   auto issue = [&](const Tile& d, int kt) __attribute__((always_inline)) {
@@ -449,6 +491,8 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
   }
   for (int t = slot; t < total; t += G) {
     const int row0 = cur.row0, rows_valid = cur.rows_valid, n0 = cur.n0, nmt = cur.nmt;
+    const bool has_next = t + G < total;
+    Tile nxt;
 
     f32x16_t acc[CF::NB][CF::MT][CF::NT];
 #pragma unroll
@@ -517,10 +561,39 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
       if (g0) wait_vm_dyn<VMG * (NS - 1)>(min(NS - 1, nk - 1) * VMG);
       pp_barrier();                 // stage 0 has landed for everyone
       if (!g0) pp_barrier();        // group 1: one slot behind
-      for (int kt = 0; kt < nk; ++kt) {
+      // One K step. The steps before kd (all of them without prefetch, or without a next
+      // tile) run the plain body; the last 2 NS - 1 steps of a tile with a successor also
+      // decode it, load its row sources and issue its first stages.
+      auto step = [&](int kt, auto tailc) __attribute__((always_inline)) {
+        constexpr bool TAIL = decltype(tailc)::value;
         mread(kt, H0);
         // buffer (kt+NS-1) % NS held stage kt-1, whose last reader (group 1) is done
-        if (g0 && kt >= 1 && kt + NS - 1 < nk) issue(cur, kt + NS - 1);
+        if constexpr (TAIL) {
+          if constexpr (XA) {
+            // the row sources landed before the last barrier of step kd + NS - 1; step kd + NS
+            // is also the first to issue a stage of the next tile
+            if (g0 && kt == kd + NS) {
+              int src[A_LDP];
+#pragma unroll
+              for (int i = 0; i < A_LDP; ++i) src[i] = src_l[min(a_row[i], nxt.rows_valid - 1)];
+              gather_offsets(nxt, src);
+            }
+          }
+          if (g0) {
+            if (kt + NS - 1 < nk) issue(cur, kt + NS - 1);
+            else issue(nxt, kt + NS - 1 - nk);
+          }
+          if (kt == kd) {
+            nxt = decode_next(t + G, cur.e);
+            // group-0 wave gw loads row sources [64 gw, 64 gw + 64) of the next tile, after
+            // stage kd + NS - 1; the entries past its rows read as zeros and are never used
+            if (XA && g0)
+              lds_dma4(make_rsrc(maps.a_src + nxt.row0, (uint32_t)nxt.rows_valid * 4u),
+                       smem_lds + (uint32_t)(SRC_OFF + 256 * gw), (64 * gw + lane) * 4, 0);
+          }
+        } else {
+          if (g0 && kt >= 1 && kt + NS - 1 < nk) issue(cur, kt + NS - 1);
+        }
         pp_barrier();
         compute();
         if constexpr (UPS == 2) {
@@ -530,9 +603,20 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
           compute();
         }
         // stage kt+1 landed before it is read (younger stages may stay in flight)
-        if (g0 && kt + 1 < nk) wait_vm_dyn<VMG * (NS - 2)>(min(NS - 2, nk - 2 - kt) * VMG);
+        if constexpr (TAIL) {
+          // NS-2 younger stages are always in flight (some of them the next tile's), and the
+          // row-source load issued at step kd after stage kd+NS-1 is younger than stage kt+1
+          // for kt <= kd+NS-2
+          if (g0 && kt + 1 < nk) wait_vm_dyn<VMG * (NS - 2) + XA>((NS - 2) * VMG + (XA && kt <= kd + NS - 2));
+        } else {
+          if (g0 && kt + 1 < nk) wait_vm_dyn<VMG * (NS - 2)>(min(NS - 2, nk - 2 - kt) * VMG);
+        }
         pp_barrier();
-      }
+      };
+      const int kmain = (PF && has_next) ? kd : nk;
+      for (int kt = 0; kt < kmain; ++kt) step(kt, std::false_type{});
+      if constexpr (PF)
+        for (int kt = kmain; kt < nk; ++kt) step(kt, std::true_type{});
       if (g0) pp_barrier();         // same number of barriers in both groups
     };
     if (nmt == 2) run(std::integral_constant<int, 2>{});
@@ -540,10 +624,17 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
     else run(std::integral_constant<int, 0>{});
     // The last barrier of run() follows every LDS read of this tile in both groups, so every
     // buffer is free: the next tile's first stages go out before this tile's stores.
-    if (t + G < total) {
-      cur = decode(t + G);
-      if (g0)
-        for (int st = 0; st < NS && st < nk; ++st) issue(cur, st);
+    if constexpr (PF) {
+      if (has_next) {
+        cur = nxt;
+        if (g0) issue(cur, NS - 1);   // into the buffer of this tile's last stage
+      }
+    } else {
+      if (t + G < total) {
+        cur = decode(t + G);
+        if (g0)
+          for (int st = 0; st < NS && st < nk; ++st) issue(cur, st);
+      }
     }
 
     // epilogue
@@ -651,19 +742,33 @@ static int pipe_variant() {
   return v;
 }
 
-template <bool GATED, int BN, int BK, int NS, bool MAPPED>
+// Cross-tile prefetch in the ping-pong kernel: on wherever the K loop is long enough and a
+// whole number of stage rounds (MOE_FFN_PF = "0" turns it off).
+static bool prefetch_enabled() {
+  static int v = -1;
+  if (v < 0) {
+    const char* p = std::getenv("MOE_FFN_PF");
+    v = !(p && p[0] == '0');
+  }
+  return v != 0;
+}
+
+template <bool GATED, int BN, int BK, int NS, bool MAPPED, bool PF>
 static moe_status_t launch_pp_k(const uint16_t* A, const int* cu, int M, int E, int Kd, int N,
                                 const uint16_t* B0, const uint16_t* B1, uint16_t* C,
                                 const RowMaps& maps, hipStream_t s) {
   using CF = FbCfg<GATED, BN, BK, NS>;
+  // PF adds the cu_seqlens copy and the row sources of the next tile
+  constexpr int LDS = CF::LDS_BYTES + (PF ? (FB_MAX_E + 1 + FB_BM) * 4 : 0);
+  static_assert(LDS <= 160 * 1024, "LDS budget");
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_pp_kernel<GATED, BN, BK, NS, MAPPED>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS_BYTES) != hipSuccess)
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_pp_kernel<GATED, BN, BK, NS, MAPPED, PF>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, LDS) != hipSuccess)
       return MOE_EHIP;
     attr_set = true;
   }
-  ffn_bf16_pp_kernel<GATED, BN, BK, NS, MAPPED><<<device_cu_count(), FB_THREADS, CF::LDS_BYTES, s>>>(
+  ffn_bf16_pp_kernel<GATED, BN, BK, NS, MAPPED, PF><<<device_cu_count(), FB_THREADS, LDS, s>>>(
       A, cu, M, E, Kd, N, B0, B1, C, tile_order_n_fastest(M, E), maps);
   return launch_status();
 }
@@ -676,11 +781,18 @@ static moe_status_t launch_fb_any(const uint16_t* A, const int* cu, int M, int E
   if (pipe_variant() >= 2) {
     const bool mapped = GATED ? maps.a_src != nullptr : maps.s_acc != nullptr;
     if (pipe_variant() == 3) {
-      if (mapped) return launch_pp_k<GATED, BN, 32, 4, true>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
-      return launch_pp_k<GATED, BN, 32, 4, false>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
+      // (not with the scatter epilogue, whose registers leave no room for the next tile)
+      const int nk = Kd / 32;
+      if (prefetch_enabled() && nk % 4 == 0 && nk >= 8) {
+        if constexpr (GATED)
+          if (mapped) return launch_pp_k<GATED, BN, 32, 4, true, true>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
+        if (!mapped) return launch_pp_k<GATED, BN, 32, 4, false, true>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
+      }
+      if (mapped) return launch_pp_k<GATED, BN, 32, 4, true, false>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
+      return launch_pp_k<GATED, BN, 32, 4, false, false>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
     }
-    if (mapped) return launch_pp_k<GATED, BN, 64, 2, true>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
-    return launch_pp_k<GATED, BN, 64, 2, false>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
+    if (mapped) return launch_pp_k<GATED, BN, 64, 2, true, false>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
+    return launch_pp_k<GATED, BN, 64, 2, false, false>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
   }
   return launch_fb<GATED, BN, 64, 2>(A, cu, M, E, Kd, N, B0, B1, C, maps, s);
 }

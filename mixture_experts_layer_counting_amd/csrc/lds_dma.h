@@ -37,6 +37,20 @@ __device__ __forceinline__ void lds_dma16(i32x4_t rsrc_in, uint32_t lds_base, in
                : "memory", "m0");
 }
 
+// Direct global->LDS load of 4 bytes per lane (buffer_load_dword ... lds): lane l's dword lands
+// at lds_base + 4*l; offsets past the descriptor's range write zeros. Counted in vmcnt like
+// lds_dma16.
+__device__ __forceinline__ void lds_dma4(i32x4_t rsrc_in, uint32_t lds_base, int voff, int soff) {
+  i32x4_t rsrc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc_in[i]);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane((int)lds_base)), "v"(voff), "s"(rsrc),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory", "m0");
+}
+
 // Wait until at most N of this wave's vector-memory operations are outstanding, then
 // barrier the workgroup. The memory clobber keeps LDS reads on their side of the barrier.
 template <int N>

@@ -345,6 +345,28 @@ def test_expert_sizes_around_tile_boundaries(act, wgt):
     assert torch.equal(out.view(torch.int16), r["out"].view(torch.int16))
 
 
+# Blocks that run several tiles each, so that the bf16 kernels decode the next tile, load its
+# row sources and issue its first stages inside the current tile's K loop: 1024 experts, a
+# third of them empty and the rest from 1 to over 1300 rows (one grid stride passes well over
+# 64 experts), with K loops of 8 steps, and 16 large experts with K loops of 24 steps. The
+# gathered layer must give the same bits as the steps on permuted rows.
+SEVERAL_TILES = [
+    dict(T=2048, H=256, Hp=256, E=1024, K=8, routing="skew", beta=0.6),
+    dict(T=4096, H=768, Hp=768, E=16, K=6, routing="normal"),
+]
+
+
+@pytest.mark.parametrize("spec", SEVERAL_TILES, ids=lambda s: "T{T}_H{H}_Hp{Hp}_E{E}_K{K}".format(**s))
+def test_bf16_several_tiles_per_block(spec):
+    say(f"bf16 several tiles per block {spec}")
+    w = gen.make(**spec, act="bf16", wgt="bf16", out="bf16", cid=72, device=DEV)
+    r, ref = full_check(w)
+    assert int((np.diff(ref["cu_seqlens"]) > 0).sum()) > 1
+    out, _, _ = run_layer(w)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), r["out"].view(torch.int16))
+
+
 @pytest.mark.slow
 def test_c5_full_size_sampled():
     say("c5 fp8 x mxfp4 E=384 maxvio=1, full size")
