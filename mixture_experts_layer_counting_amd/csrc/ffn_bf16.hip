@@ -332,7 +332,15 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
   constexpr int B_LDP = CF::NB * CF::B_BYTES / (1024 * 4);
   constexpr int VMG = A_LDP + B_LDP;
   constexpr int PER_MAT = CF::B_BYTES / 1024;             // 1 KiB weight loads per matrix
-  constexpr int NF = CF::NB * CF::NT;                     // B fragments per k-step
+  // Wave layout: the block's columns form four strips of WS = BN/4 (PNT 32-column MFMA
+  // blocks, per weight matrix); waves w and w+4 share a SIMD and strip w % 4, and split its
+  // 32-row blocks between them, wave w the even ones (0, 2, 4, 6) and wave w+4 the odd ones.
+  // A tile of b row blocks gives the two waves of a SIMD ceil(b/2) and floor(b/2) blocks, so
+  // their slots stay even on the 192-row tiles an expert of 384 rows splits into.
+  constexpr int PMT = 4;                                  // row blocks per wave (at most)
+  constexpr int WS = BN / 4;
+  constexpr int PNT = WS / 32;
+  constexpr int NF = CF::NB * PNT;                        // B fragments per k-step
   // Operand order of the MFMA. With the weight fragment first the accumulator comes out
   // transposed: lane l holds one output row (l % 32 of the 32-row block) and four runs of four
   // consecutive columns, which the epilogue writes as 8-byte stores. The scatter epilogue keeps
@@ -352,8 +360,8 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int sc = wave & 3;            // column strip
+  const int hf = wave >> 2;           // 0: even row blocks, 1: odd ones
   const bool g0 = wave < 4;
   const int gw = wave & 3;
   const int ntn = N / BN;
@@ -386,13 +394,14 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
   }
 
   // LDS -> fragment offsets (as in ffn_bf16_kernel)
-  const int a_fbase = (wm * 32 + (lane & 31)) * CF::A_ROW;
+  // (row block 2 mt + hf starts 64 mt rows after block hf; the A swizzle repeats every 16 rows)
+  const int a_fbase = (hf * 32 + (lane & 31)) * CF::A_ROW;
   const int a_sw = ((lane & 31) / CF::A_SWZ_DIV) % CF::CPR;
   int a_fk[CF::KK];
 #pragma unroll
   for (int kk = 0; kk < CF::KK; ++kk) a_fk[kk] = a_fbase + ((((kk << 1) | (lane >> 5)) ^ a_sw) << 4);
   const int g = lane >> 4, jj = lane & 15;
-  const int bP = (wn * CF::WN) / 16 + (g & 1);
+  const int bP = (sc * WS) / 16 + (g & 1);
   const int b_fbase = (8 * (g >> 1) + (jj >> 2)) * CF::B_ROW + 8 * (jj & 3) + ((bP ^ ((jj >> 2) << 1)) << 5);
   const uint32_t smem_lds = lds_addr(smem);
   constexpr int SRC_OFF = NS * CF::STAGE + CF::SCHED_BYTES + (FB_MAX_E + 1) * 4;  // src_l in smem
@@ -435,7 +444,8 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
     const uint32_t b_rem = (uint32_t)(((size_t)Kd * N - d.n0) * 2);
     d.rB0 = make_rsrc(B0 + woff, b_rem);
     d.rB1 = GATED ? make_rsrc(B1 + woff, b_rem) : d.rB0;
-    d.nmt = __builtin_amdgcn_readfirstlane((wm * 32 < d.rows_valid) + (128 + wm * 32 < d.rows_valid));
+    // row blocks hf, hf + 2, ... below the tile's ceil(rows_valid / 32) blocks
+    d.nmt = __builtin_amdgcn_readfirstlane(min(PMT, ((d.rows_valid + 31) / 32 - hf + 1) / 2));
     return d;
   };
   auto decode = [&](int t) __attribute__((always_inline)) {
@@ -494,19 +504,19 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
     const bool has_next = t + G < total;
     Tile nxt;
 
-    f32x16_t acc[CF::NB][CF::MT][CF::NT];
+    f32x16_t acc[CF::NB][PMT][PNT];
 #pragma unroll
     for (int nb = 0; nb < CF::NB; ++nb)
 #pragma unroll
-      for (int mt = 0; mt < CF::MT; ++mt)
+      for (int mt = 0; mt < PMT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < CF::NT; ++nt)
+        for (int nt = 0; nt < PNT; ++nt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) acc[nb][mt][nt][i] = 0.f;
 
     auto run = [&](auto mtv) __attribute__((always_inline)) {
       constexpr int MTV = decltype(mtv)::value;
-      bf16x8_t fa[CF::MT > 0 ? CF::MT : 1][KH];
+      bf16x8_t fa[MTV > 0 ? MTV : 1][KH];
       bf16x8_t fb[NF][KH];
       // read the fragments of half HF of stage kt
       auto mread = [&](int kt, auto hfc) __attribute__((always_inline)) {
@@ -519,15 +529,15 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
             const int kk = HF * KH + q;
 #pragma unroll
             for (int mt = 0; mt < MTV; ++mt)
-              fa[mt][q] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const i32x4_t*>(sa + a_fk[kk] + mt * 128 * CF::A_ROW));
+              fa[mt][q] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const i32x4_t*>(sa + a_fk[kk] + mt * 64 * CF::A_ROW));
 #pragma unroll
             for (int nb = 0; nb < CF::NB; ++nb)
 #pragma unroll
-              for (int nt = 0; nt < CF::NT; ++nt) {
+              for (int nt = 0; nt < PNT; ++nt) {
                 const unsigned char* p = sb + nb * CF::B_BYTES + (b_fbase ^ (nt << 6)) + kk * 16 * CF::B_ROW;
                 const i16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(p));
                 const i16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((MOE_LDS i16x4_t*)(p + 4 * CF::B_ROW));
-                fb[nb * CF::NT + nt][q] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+                fb[nb * PNT + nt][q] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
               }
           }
         }
@@ -539,14 +549,14 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
 #pragma unroll
             for (int nb = 0; nb < CF::NB; ++nb)
 #pragma unroll
-              for (int nt = 0; nt < CF::NT; ++nt)
+              for (int nt = 0; nt < PNT; ++nt)
 #pragma unroll
                 for (int mt = 0; mt < MTV; ++mt) {
                   if constexpr (ROW_LANES)
-                    acc[nb][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb * CF::NT + nt][q], fa[mt][q],
+                    acc[nb][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[nb * PNT + nt][q], fa[mt][q],
                                                                               acc[nb][mt][nt], 0, 0, 0);
                   else
-                    acc[nb][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt][q], fb[nb * CF::NT + nt][q],
+                    acc[nb][mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt][q], fb[nb * PNT + nt][q],
                                                                               acc[nb][mt][nt], 0, 0, 0);
                 }
         }
@@ -619,7 +629,9 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
         for (int kt = kmain; kt < nk; ++kt) step(kt, std::true_type{});
       if (g0) pp_barrier();         // same number of barriers in both groups
     };
-    if (nmt == 2) run(std::integral_constant<int, 2>{});
+    if (nmt == 4) run(std::integral_constant<int, 4>{});
+    else if (nmt == 3) run(std::integral_constant<int, 3>{});
+    else if (nmt == 2) run(std::integral_constant<int, 2>{});
     else if (nmt == 1) run(std::integral_constant<int, 1>{});
     else run(std::integral_constant<int, 0>{});
     // The last barrier of run() follows every LDS read of this tile in both groups, so every
@@ -640,29 +652,29 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_pp_kernel(
     // epilogue
     if constexpr (!GATED && MAPPED) {
 #pragma unroll
-      for (int mt = 0; mt < CF::MT; ++mt)
+      for (int mt = 0; mt < PMT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int r = mt * 128 + wm * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          const int r = (2 * mt + hf) * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
           const int src = r < rows_valid ? maps.s_src[row0 + r] : -1;
           if (src >= 0) {
-            float* dst = maps.s_acc + (size_t)(src / maps.s_k) * N + n0 + wn * CF::WN + (lane & 31);
+            float* dst = maps.s_acc + (size_t)(src / maps.s_k) * N + n0 + sc * WS + (lane & 31);
             const float w = maps.s_w[row0 + r];
 #pragma unroll
-            for (int nt = 0; nt < CF::NT; ++nt) unsafeAtomicAdd(dst + nt * 32, w * acc[0][mt][nt][i]);
+            for (int nt = 0; nt < PNT; ++nt) unsafeAtomicAdd(dst + nt * 32, w * acc[0][mt][nt][i]);
           }
         }
     } else {
-      // row-lane layout: block (mt, nt) holds row mt*128 + wm*32 + lane%32 in this lane, and
+      // row-lane layout: block (mt, nt) holds row (2 mt + hf)*32 + lane%32 in this lane, and
       // columns nt*32 + 8j + 4(lane/32) + c in acc[..][4j + c], j, c = 0..3
-      const int col_l = n0 + wn * CF::WN + 8 * (lane >> 5);
+      const int col_l = n0 + sc * WS + 8 * (lane >> 5);
 #pragma unroll
-      for (int mt = 0; mt < CF::MT; ++mt) {
-        const int r = mt * 128 + wm * 32 + (lane & 31);
+      for (int mt = 0; mt < PMT; ++mt) {
+        const int r = (2 * mt + hf) * 32 + (lane & 31);
         const bool ok = r < rows_valid;
         const size_t ro = (size_t)(row0 + (ok ? r : 0)) * N + col_l;
 #pragma unroll
-        for (int nt = 0; nt < CF::NT; ++nt)
+        for (int nt = 0; nt < PNT; ++nt)
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
             const size_t o = ro + nt * 32 + 16 * p;
