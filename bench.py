@@ -193,11 +193,14 @@ def main():
                 fn()
         if quant:
             mark("quantize", lambda: moe.moe_quantize_fp8(x_in, moe.MOE_BF16, T, H, xq, xq_sf, None))
-        if w.logits is not None:
-            mark("route", lambda: moe.moe_route_topk(w.logits, T, E, K, topk_idx, topk_w, None))
-        mark("permute", lambda: moe.moe_permute_padded(w.x, w.x_sf, DT[w.act], topk_idx, topk_w, T, H, E, K,
-                                                       pad, counts, cu, pos, row_src, row_w, x_perm,
-                                                       x_perm_sf, ws, nws, None))
+        if w.logits is not None:   # routing and permutation in one call (stage "permute")
+            mark("permute", lambda: moe.moe_route_permute(w.logits, w.x, w.x_sf, DT[w.act], T, H, E, K, pad,
+                                                          topk_idx, topk_w, counts, cu, pos, row_src, row_w,
+                                                          x_perm, x_perm_sf, ws, nws, None))
+        else:
+            mark("permute", lambda: moe.moe_permute_padded(w.x, w.x_sf, DT[w.act], topk_idx, topk_w, T, H, E,
+                                                           K, pad, counts, cu, pos, row_src, row_w, x_perm,
+                                                           x_perm_sf, ws, nws, None))
         if args.xperm:
             mark("gate_up", lambda: moe.moe_ffn_gate_up(x_perm, x_perm_sf, DT[w.act], cu, MR, E, H, Hp,
                                                         w.w_gate, w.w_up, w.sf_gate, w.sf_up,
@@ -280,8 +283,11 @@ def main():
     dn_flops = 2.0 * M * H * Hp
     gu_bytes = M * H * ab + xsf_b + 2 * active * wmat + M * Hp * hb + hsf_b
     dn_bytes = M * Hp * hb + hsf_b + active * wmat + M * H * yb
-    # permute: topk_idx read; pos, row_src (and row_w from topk_w) written; + the row copy
+    # permute: topk_idx read; pos, row_src (and row_w from topk_w) written; + the row copy;
+    # with routing in the same call, the logits read and topk_idx / topk_w written instead
     perm_bytes = M * 4 + 2 * M * 4 + (2 * M * 4 if scatter else 0)
+    if w.logits is not None:
+        perm_bytes += T * E * 4 + M * 4
     if args.xperm:
         perm_bytes += T * H * ab + M * H * ab + (T * (H // 128) * 4 + xsf_b if w.act == "fp8" else 0)
     if scatter:   # zero the fp32 accumulator, then round it once into out (bf16)

@@ -144,12 +144,29 @@ MOE_API moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t a
  * row_src = -1 as a padding row). Other arguments and limits as moe_permute; pad >= 1
  * (pad = 1 is moe_permute). */
 MOE_API int64_t moe_padded_capacity(int32_t T, int32_t E, int32_t K, int32_t pad);
+
 MOE_API moe_status_t moe_permute_padded(const void* x, const float* x_sf, moe_dtype_t act,
                                 const int32_t* topk_idx, const float* topk_w, int32_t T, int32_t H,
                                 int32_t E, int32_t K, int32_t pad, int32_t* counts,
                                 int32_t* cu_seqlens, int32_t* pos, int32_t* row_src, float* row_w,
                                 void* x_perm, float* x_perm_sf, void* ws, size_t ws_bytes,
                                 hipStream_t stream);
+
+/* Routing and the permutation in one call: moe_route_topk on `logits` followed by
+ * moe_permute_padded on its result, with the same outputs bit for bit ("Distributed expert
+ * parallelism", lifecycle items 1-3). The first kernel ranks the tokens of each 128-token
+ * chunk and counts the chunk's picks per expert, which saves the permutation's separate
+ * histogram pass and one launch.
+ *  logits [T, E] fp32 in; topk_idx [T, K] int32 and topk_w [T, K] fp32 out (both required);
+ *  every other argument, the workspace (moe_permute_workspace_bytes) and the limits as
+ *  moe_permute_padded, with K <= E. The ids are produced here, so MOE_VALIDATE has nothing
+ *  to check. */
+MOE_API moe_status_t moe_route_permute(const float* logits, const void* x, const float* x_sf,
+                               moe_dtype_t act, int32_t T, int32_t H, int32_t E, int32_t K,
+                               int32_t pad, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                               int32_t* cu_seqlens, int32_t* pos, int32_t* row_src, float* row_w,
+                               void* x_perm, float* x_perm_sf, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
 
 /* Activation quantisation to FP8_E4M3 with 1x128 power-of-two scales ("Mixture of
  * Kittens", Step 8: activations are quantised for the fp8 GEMMs, fused into dispatch):

@@ -28,7 +28,7 @@ WS_FIELDS = ("topk_idx", "topk_w", "counts", "cu_seqlens", "pos", "row_src", "ro
              "x_perm_sf", "h", "h_sf", "y_rows", "permute_scratch", "acc_f32", "x_q", "x_q_sf")
 
 EXPORTS = ("moe_route_topk", "moe_permute_workspace_bytes", "moe_permute", "moe_padded_capacity",
-           "moe_permute_padded", "moe_quantize_fp8", "moe_ffn_gate_up",
+           "moe_permute_padded", "moe_route_permute", "moe_quantize_fp8", "moe_ffn_gate_up",
            "moe_ffn_gate_up_gather", "moe_ffn_down", "moe_ffn_down_scatter",
            "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn", "moe_combine",
            "moe_combine_shared", "moe_layer_workspace_bytes", "moe_layer_forward",
@@ -65,6 +65,8 @@ _SIGS = {
     "moe_padded_capacity": (ctypes.c_int64, [_I, _I, _I, _I]),
     "moe_permute_padded": (_I, [_P, _P, _E, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
                                 _P, _S, _P]),
+    "moe_route_permute": (_I, [_P, _P, _P, _E, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
+                               _P, _P, _S, _P]),
     "moe_quantize_fp8": (_I, [_P, _E, _I, _I, _P, _P, _P]),
     "moe_ffn_gate_up_gather": (_I, [_P, _P, _E, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _E,
                                     _P, _P, _P]),
@@ -162,6 +164,15 @@ def moe_permute_padded(x, x_sf, act, topk_idx, topk_w, T, H, E, K, pad, counts, 
                                     K, pad, _ptr(counts), _ptr(cu_seqlens), _ptr(pos), _ptr(row_src),
                                     _ptr(row_w), _ptr(x_perm), _ptr(x_perm_sf), _ptr(ws), ws_bytes,
                                     _stream(stream)), "moe_permute_padded")
+
+
+def moe_route_permute(logits, x, x_sf, act, T, H, E, K, pad, topk_idx, topk_w, counts, cu_seqlens,
+                      pos, row_src, row_w, x_perm, x_perm_sf, ws, ws_bytes, stream=None):
+    _check(lib().moe_route_permute(_ptr(logits), _ptr(x), _ptr(x_sf), act, T, H, E, K, pad,
+                                   _ptr(topk_idx), _ptr(topk_w), _ptr(counts), _ptr(cu_seqlens),
+                                   _ptr(pos), _ptr(row_src), _ptr(row_w), _ptr(x_perm),
+                                   _ptr(x_perm_sf), _ptr(ws), ws_bytes, _stream(stream)),
+           "moe_route_permute")
 
 
 def moe_quantize_fp8(x, x_dtype, R, C, q, sf, stream=None):

@@ -17,7 +17,9 @@ moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes, co
                             const float* topk_w, int T, int H, int E, int K, int* counts,
                             int* cu_seqlens, int* pos, int* row_src, float* row_w, void* x_perm,
                             float* x_perm_sf, void* ws, bool validate, int pad, int cap,
-                            int** err_out, hipStream_t s);
+                            int** err_out, hipStream_t s, bool hist_done);
+moe_status_t launch_route_hist(const float* logits, int T, int E, int K, int* topk_idx,
+                               float* topk_w, void* ws, hipStream_t s);
 moe_status_t launch_quantize_fp8(const void* x, moe_dtype_t xt, int R, int C, void* q, float* sf,
                                  hipStream_t s);
 moe_status_t launch_combine(const void*, moe_dtype_t, const int*, const float*, int, int, int,
@@ -151,7 +153,9 @@ size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t K) {
   return permute_ws_bytes(T, E, K);
 }
 
-static moe_status_t permute_impl(const void* x, const float* x_sf, moe_dtype_t act,
+// With logits, topk_idx and topk_w are outputs: the routing is computed together with the
+// permutation's histogram (moe_route_permute).
+static moe_status_t permute_impl(const float* logits, const void* x, const float* x_sf, moe_dtype_t act,
                                  const int32_t* topk_idx, const float* topk_w, int32_t T, int32_t H,
                                  int32_t E, int32_t K, int32_t pad, int32_t* counts,
                                  int32_t* cu_seqlens, int32_t* pos, int32_t* row_src, float* row_w,
@@ -163,6 +167,7 @@ static moe_status_t permute_impl(const void* x, const float* x_sf, moe_dtype_t a
   if (eb == 0) return MOE_EUNSUPPORTED;
   if (!counts || !cu_seqlens) return MOE_EINVAL;
   if (T > 0 && (!topk_idx || !pos || !row_src)) return MOE_EINVAL;
+  if (logits && (K > E || (T > 0 && !topk_w))) return MOE_EINVAL;
   if (T > 0 && x_perm && !x) return MOE_EINVAL;
   if (row_w && T > 0 && !topk_w) return MOE_EINVAL;
   if (act == MOE_FP8_E4M3) {
@@ -174,12 +179,18 @@ static moe_status_t permute_impl(const void* x, const float* x_sf, moe_dtype_t a
   const size_t need = permute_ws_bytes(T, E, K);
   if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
   poison(ws, ws_bytes, stream);
-  const bool validate = env_flag("MOE_VALIDATE");
+  // routed here, the ids are valid and distinct: nothing to validate
+  const bool validate = !logits && env_flag("MOE_VALIDATE");
   int* err = nullptr;
   const bool sf = act == MOE_FP8_E4M3 && x_perm;
+  if (logits && T > 0) {
+    const moe_status_t st = launch_route_hist(logits, T, E, K, const_cast<int32_t*>(topk_idx),
+                                              const_cast<float*>(topk_w), ws, stream);
+    if (st != MOE_OK) return st;
+  }
   moe_status_t st = launch_permute(x, sf ? x_sf : nullptr, eb, topk_idx, topk_w, T, H, E, K, counts,
                                    cu_seqlens, pos, row_src, row_w, x_perm, sf ? x_perm_sf : nullptr,
-                                   ws, validate, pad, (int)cap, &err, stream);
+                                   ws, validate, pad, (int)cap, &err, stream, logits != nullptr);
   if (st != MOE_OK || !validate) return st;
   int h_err = 0;
   if (hipMemcpyAsync(&h_err, err, sizeof(int), hipMemcpyDeviceToHost, stream) != hipSuccess ||
@@ -193,8 +204,8 @@ moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t act,
                          int32_t E, int32_t K, int32_t* counts, int32_t* cu_seqlens,
                          int32_t* pos, int32_t* row_src, float* row_w, void* x_perm,
                          float* x_perm_sf, void* ws, size_t ws_bytes, hipStream_t stream) {
-  return permute_impl(x, x_sf, act, topk_idx, topk_w, T, H, E, K, 1, counts, cu_seqlens, pos, row_src,
-                      row_w, x_perm, x_perm_sf, ws, ws_bytes, stream);
+  return permute_impl(nullptr, x, x_sf, act, topk_idx, topk_w, T, H, E, K, 1, counts, cu_seqlens, pos,
+                      row_src, row_w, x_perm, x_perm_sf, ws, ws_bytes, stream);
 }
 
 int64_t moe_padded_capacity(int32_t T, int32_t E, int32_t K, int32_t pad) {
@@ -208,8 +219,19 @@ moe_status_t moe_permute_padded(const void* x, const float* x_sf, moe_dtype_t ac
                                 int32_t* cu_seqlens, int32_t* pos, int32_t* row_src, float* row_w,
                                 void* x_perm, float* x_perm_sf, void* ws, size_t ws_bytes,
                                 hipStream_t stream) {
-  return permute_impl(x, x_sf, act, topk_idx, topk_w, T, H, E, K, pad, counts, cu_seqlens, pos, row_src,
-                      row_w, x_perm, x_perm_sf, ws, ws_bytes, stream);
+  return permute_impl(nullptr, x, x_sf, act, topk_idx, topk_w, T, H, E, K, pad, counts, cu_seqlens, pos,
+                      row_src, row_w, x_perm, x_perm_sf, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_route_permute(const float* logits, const void* x, const float* x_sf,
+                               moe_dtype_t act, int32_t T, int32_t H, int32_t E, int32_t K,
+                               int32_t pad, int32_t* topk_idx, float* topk_w, int32_t* counts,
+                               int32_t* cu_seqlens, int32_t* pos, int32_t* row_src, float* row_w,
+                               void* x_perm, float* x_perm_sf, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+  if (T > 0 && !logits) return MOE_EINVAL;
+  return permute_impl(T > 0 ? logits : nullptr, x, x_sf, act, topk_idx, topk_w, T, H, E, K, pad,
+                      counts, cu_seqlens, pos, row_src, row_w, x_perm, x_perm_sf, ws, ws_bytes, stream);
 }
 
 moe_status_t moe_quantize_fp8(const void* x, moe_dtype_t x_dtype, int32_t R, int32_t C, uint8_t* q,
@@ -579,10 +601,7 @@ static moe_status_t layer_forward_impl(const moe_layer_desc_t* d, const void* x,
 
   int32_t* topk_idx = static_cast<int32_t*>(at(WS_TOPK_IDX));
   float* topk_w = static_cast<float*>(at(WS_TOPK_W));
-  if (logits) {
-    st = moe_route_topk(logits, T, E, K, topk_idx, topk_w, stream);
-    if (st != MOE_OK) return st;
-  } else {
+  if (!logits) {
     topk_idx = const_cast<int32_t*>(topk_idx_in);
     topk_w = const_cast<float*>(topk_w_in);
   }
@@ -594,9 +613,13 @@ static moe_status_t layer_forward_impl(const moe_layer_desc_t* d, const void* x,
   float* h_sf = static_cast<float*>(at(WS_H_SF));
   const bool mat = layer_materializes(d), scatter = d->combine == MOE_COMBINE_SCATTER_ATOMIC;
   const size_t perm_ws = permute_ws_bytes(T, E, K);
-  st = moe_permute(x, x_sf, act, topk_idx, topk_w, T, H, E, K, counts, cu, pos, row_src, row_w,
-                   at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)), at(WS_PERM_SCRATCH), perm_ws,
-                   stream);
+  // routing from logits: top-k and the permutation's histogram come out of one kernel
+  st = logits ? moe_route_permute(logits, x, x_sf, act, T, H, E, K, 1, topk_idx, topk_w, counts, cu, pos,
+                                  row_src, row_w, at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)),
+                                  at(WS_PERM_SCRATCH), perm_ws, stream)
+              : moe_permute(x, x_sf, act, topk_idx, topk_w, T, H, E, K, counts, cu, pos, row_src, row_w,
+                            at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)), at(WS_PERM_SCRATCH),
+                            perm_ws, stream);
   if (st != MOE_OK) return st;
   if (mat)
     st = moe_ffn_gate_up(at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)), act, cu, M, E, H, Hp,
@@ -721,10 +744,7 @@ moe_status_t moe_layer_backward(const moe_layer_desc_t* d, const void* x, const 
   const int T = d->T, E = d->E, K = d->K, H = d->H, Hp = d->Hp, M = T * K;
   int32_t* topk_idx = static_cast<int32_t*>(at(BW_TOPK_IDX));
   float* topk_w = static_cast<float*>(at(BW_TOPK_W));
-  if (logits) {
-    st = moe_route_topk(logits, T, E, K, topk_idx, topk_w, stream);
-    if (st != MOE_OK) return st;
-  } else {
+  if (!logits) {
     topk_idx = const_cast<int32_t*>(topk_idx_in);
     topk_w = const_cast<float*>(topk_w_in);
   }
@@ -732,9 +752,13 @@ moe_status_t moe_layer_backward(const moe_layer_desc_t* d, const void* x, const 
   int32_t* pos = static_cast<int32_t*>(at(BW_POS));
   int32_t* row_src = static_cast<int32_t*>(at(BW_ROW_SRC));
   float* row_w = static_cast<float*>(at(BW_ROW_W));
-  st = moe_permute(x, nullptr, MOE_BF16, topk_idx, topk_w, T, H, E, K, static_cast<int32_t*>(at(BW_COUNTS)),
-                   cu, pos, row_src, row_w, at(BW_X_PERM), nullptr, at(BW_PERM_SCRATCH),
-                   permute_ws_bytes(T, E, K), stream);
+  int32_t* counts = static_cast<int32_t*>(at(BW_COUNTS));
+  st = logits ? moe_route_permute(logits, x, nullptr, MOE_BF16, T, H, E, K, 1, topk_idx, topk_w, counts, cu,
+                                  pos, row_src, row_w, at(BW_X_PERM), nullptr, at(BW_PERM_SCRATCH),
+                                  permute_ws_bytes(T, E, K), stream)
+              : moe_permute(x, nullptr, MOE_BF16, topk_idx, topk_w, T, H, E, K, counts, cu, pos, row_src,
+                            row_w, at(BW_X_PERM), nullptr, at(BW_PERM_SCRATCH), permute_ws_bytes(T, E, K),
+                            stream);
   if (st != MOE_OK) return st;
   // forward recomputed, keeping g and u
   RowMaps save;

@@ -25,12 +25,13 @@
 // T*K + E*(pad-1) rows. counts stay the real ones; cu_seqlens is padded; padding rows have
 // row_src = -1, row_w = 0, zero activations and scale 1.
 #include "moe_common.h"
+#include "route_common.h"
 
 #include <algorithm>
 
 namespace moe {
 
-constexpr int PERM_CHUNK = 128;  // tokens per histogram chunk
+constexpr int PERM_CHUNK = 16;   // tokens per histogram chunk
 constexpr int PERM_TB = 16;      // tokens per scatter block (divides PERM_CHUNK)
 constexpr int PERM_THREADS = 256;
 constexpr int PERM_WAVES = PERM_THREADS / MOE_WAVE;
@@ -58,6 +59,49 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_hist_kernel(
   if (bad) atomicOr(err, 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += PERM_THREADS) hist[(size_t)e * nch + c] = h[e];
+}
+
+// Routing and step 1 in one kernel, for moe_route_permute: the block of chunk c routes the
+// chunk's PERM_CHUNK tokens, one per wave, exactly as route_topk_kernel does, writes topk_idx / topk_w, and
+// counts the picks in LDS into hist[e][c]. The ids it produces are valid and distinct, so
+// there is nothing to check.
+constexpr int RH_THREADS = 1024;
+
+template <int ITEMS>
+__global__ __launch_bounds__(RH_THREADS) void route_hist_kernel(
+    const float* __restrict__ logits, int T, int E, int K, int nch, int* __restrict__ topk_idx,
+    float* __restrict__ topk_w, int* __restrict__ hist) {
+  constexpr int TPW = PERM_CHUNK / (RH_THREADS / MOE_WAVE);  // tokens per wave
+  constexpr int BATCH = (ITEMS <= 8 || TPW < 4) ? TPW : TPW / 4;  // logits held at once
+  __shared__ int h[PERM_MAX_E];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  for (int e = tid; e < E; e += RH_THREADS) h[e] = 0;
+  __syncthreads();
+  const int c = blockIdx.x;
+  const int tw = c * PERM_CHUNK + wave * TPW;
+  for (int b = 0; b < TPW; b += BATCH) {
+    float v[BATCH][ITEMS];
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j)  // tokens past T load row T-1 and are not ranked
+      route_load<ITEMS>(logits + (size_t)min(tw + b + j, T - 1) * E, E, lane, v[j]);
+#pragma unroll
+    for (int j = 0; j < BATCH; ++j) {
+      const int t = tw + b + j;
+      if (t >= T) break;
+      int my_e;
+      float my_w;
+      route_pick<ITEMS>(v[j], E, K, lane, my_e, my_w);
+      if (lane < K) {
+        topk_idx[(size_t)t * K + lane] = my_e;
+        topk_w[(size_t)t * K + lane] = my_w;
+        atomicAdd(&h[my_e], 1);
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += RH_THREADS) hist[(size_t)e * nch + c] = h[e];
 }
 
 // Wave-inclusive scan of v across the 64 lanes.
@@ -301,7 +345,7 @@ moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes,
                             const int* topk_idx, const float* topk_w, int T, int H, int E, int K,
                             int* counts, int* cu_seqlens, int* pos, int* row_src, float* row_w,
                             void* x_perm, float* x_perm_sf, void* ws, bool validate, int pad,
-                            int cap, int** err_out, hipStream_t s) {
+                            int cap, int** err_out, hipStream_t s, bool hist_done) {
   const int nch = (T + PERM_CHUNK - 1) / PERM_CHUNK;
   int* hist = static_cast<int*>(ws);
   int* err = reinterpret_cast<int*>(static_cast<char*>(ws) +
@@ -310,7 +354,7 @@ moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes,
   if (validate) {
     if (hipMemsetAsync(err, 0, sizeof(int), s) != hipSuccess) return MOE_EHIP;
   }
-  if (nch > 0) {
+  if (nch > 0 && !hist_done) {
     permute_hist_kernel<<<nch, PERM_THREADS, 0, s>>>(topk_idx, T, E, K, nch, hist, err);
     if (validate && K > 1)
       permute_dup_check_kernel<<<(T + 255) / 256, 256, 0, s>>>(topk_idx, T, K, err);
@@ -345,6 +389,24 @@ moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes,
     const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
     permute_sf_kernel<<<blocks, 256, 0, s>>>(x_sf, row_src, cu_seqlens, E, K, cap, sf_per_row, x_perm_sf);
   }
+  return launch_status();
+}
+
+moe_status_t launch_route_hist(const float* logits, int T, int E, int K, int* topk_idx,
+                               float* topk_w, void* ws, hipStream_t s) {
+  const int nch = (T + PERM_CHUNK - 1) / PERM_CHUNK;
+  if (nch == 0) return MOE_OK;
+  int* hist = static_cast<int*>(ws);
+  if (E <= 64)
+    route_hist_kernel<1><<<nch, RH_THREADS, 0, s>>>(logits, T, E, K, nch, topk_idx, topk_w, hist);
+  else if (E <= 128)
+    route_hist_kernel<2><<<nch, RH_THREADS, 0, s>>>(logits, T, E, K, nch, topk_idx, topk_w, hist);
+  else if (E <= 256)
+    route_hist_kernel<4><<<nch, RH_THREADS, 0, s>>>(logits, T, E, K, nch, topk_idx, topk_w, hist);
+  else if (E <= 512)
+    route_hist_kernel<8><<<nch, RH_THREADS, 0, s>>>(logits, T, E, K, nch, topk_idx, topk_w, hist);
+  else
+    route_hist_kernel<16><<<nch, RH_THREADS, 0, s>>>(logits, T, E, K, nch, topk_idx, topk_w, hist);
   return launch_status();
 }
 

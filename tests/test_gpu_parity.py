@@ -151,6 +151,66 @@ def test_permute_max_experts(act):
         assert np.array_equal(host(xsf), host(x_sf)[rs_ref // K].T)
 
 
+ROUTE_PERMUTE = [
+    # (T, H, E, K, act, pad, with x_perm)
+    (300, 256, 12, 3, "fp8", 1, True),
+    (1000, 256, 40, 4, "bf16", 1, False),
+    (257, 128, 1024, 8, "bf16", 4, True),     # 16 logits per lane, two batches per wave
+    (4096, 256, 64, 6, "bf16", 1, False),     # the c2 routing shape
+    (130, 128, 384, 8, "f32", 16, True),
+    (1, 128, 2, 2, "bf16", 1, True),
+    (0, 128, 8, 2, "bf16", 1, True),
+]
+
+
+@pytest.mark.parametrize("T,H,E,K,act,pad,xp", ROUTE_PERMUTE,
+                         ids=lambda v: str(v))
+def test_route_permute_is_route_then_permute(T, H, E, K, act, pad, xp):
+    """moe_route_permute gives bit for bit what moe_route_topk followed by moe_permute_padded
+    gives (both are pinned to the oracle elsewhere)."""
+    say(f"route_permute T={T} H={H} E={E} K={K} act={act} pad={pad} x_perm={xp}")
+    w = gen.make(T=T, H=H, Hp=128, E=E, K=K, act=act, wgt="bf16", routing="skew", beta=1.0, cid=73,
+                 device=DEV)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    f32 = dict(dtype=torch.float32, device=DEV)
+    cap = moe.moe_padded_capacity(T, E, K, pad)
+    dt = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "fp8": moe.MOE_FP8_E4M3}[act]
+    nws = moe.moe_permute_workspace_bytes(T, E, K)
+    res = []
+    for fused in (False, True):
+        o = dict(topk_idx=torch.full((T, K), -7, **i32), topk_w=torch.full((T, K), -7.0, **f32),
+                 counts=torch.full((E,), -7, **i32), cu=torch.full((E + 1,), -7, **i32),
+                 pos=torch.full((T, K), -7, **i32), row_src=torch.full((cap,), -7, **i32),
+                 row_w=torch.full((cap,), -7.0, **f32),
+                 x_perm=torch.full((cap, H), 7, dtype=w.x.dtype, device=DEV) if xp else None,
+                 x_perm_sf=torch.full((H // 128, cap), -7.0, **f32) if xp and act == "fp8" else None)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=DEV)
+        if fused:
+            moe.moe_route_permute(w.logits, w.x, w.x_sf, dt, T, H, E, K, pad, o["topk_idx"], o["topk_w"],
+                                  o["counts"], o["cu"], o["pos"], o["row_src"], o["row_w"], o["x_perm"],
+                                  o["x_perm_sf"], ws, nws)
+        else:
+            moe.moe_route_topk(w.logits, T, E, K, o["topk_idx"], o["topk_w"])
+            moe.moe_permute_padded(w.x, w.x_sf, dt, o["topk_idx"], o["topk_w"], T, H, E, K, pad, o["counts"],
+                                   o["cu"], o["pos"], o["row_src"], o["row_w"], o["x_perm"], o["x_perm_sf"],
+                                   ws, nws)
+        torch.cuda.synchronize()
+        res.append(o)
+    a, b = res
+    for k in a:
+        if a[k] is None:
+            continue
+        assert torch.equal(a[k].view(torch.int32) if a[k].dtype == torch.float32 else a[k],
+                           b[k].view(torch.int32) if b[k].dtype == torch.float32 else b[k]), k
+    if T > 0:
+        ref = oracle_routing(w)
+        assert np.array_equal(host(b["topk_idx"]), ref["topk_idx"])
+        assert np.array_equal(host(b["counts"]), ref["counts"])
+        if pad == 1:
+            assert np.array_equal(host(b["pos"]), ref["pos"])
+            assert np.array_equal(host(b["row_src"]), ref["row_src"])
+
+
 def test_empty_batch():
     say("T=0")
     E, K, H = 16, 2, 256
