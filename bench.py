@@ -20,6 +20,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import os
 import statistics
@@ -97,10 +98,15 @@ def copy_calibration(steps):
 
 
 def source_hash(*names):
+    """Hash of the kernel sources' code: comments and whitespace are dropped first, so that
+    only a change to the code itself invalidates the stored traffic counters."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "mixture_experts_layer_counting_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "mixture_experts_layer_counting_amd", "csrc", n)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -7,6 +7,9 @@
 // MoonEP "Integration": the stacked [E, ., .] weight tensors are addressed purely by expert
 // index and cu_seqlens selects each expert's rows.
 //
+// Two schedules share the tiling, the LDS layouts and the row maps described here: the plain
+// kernel ffn_bf16_kernel (this header) and the ping-pong kernel ffn_bf16_pp_kernel further
+// down, the default, which differs in its schedule, wave layout and cross-tile prefetch.
 // Design (one kernel body, GATED selects gate/up + SwiGLU or the plain down projection):
 //  * Persistent grid of one 512-thread block per CU. Each block derives the tile list from
 //    cu_seqlens in LDS (tiles per expert = ceil(rows / BM) * N / BN, exclusive prefix) and
@@ -14,7 +17,8 @@
 //    32 CUs of one XCD work on neighbouring tiles: the same expert's weight panel (tiles
 //    of one n-panel are consecutive over its m-tiles) and the same rows stay in that XCD's
 //    L2.
-//  * Block tile BM=256 rows x BN columns (per weight matrix), K step 64, two LDS stages.
+//  * Block tile BM=256 rows x BN columns (per weight matrix), K step 64, two LDS stages
+//    (the plain kernel's default; K step 32 with four stages is its other variant).
 //    8 waves as 4 (rows) x 2 (columns), each wave 64 x BN/2 with MFMA 32x32x16 bf16 and
 //    fp32 accumulators (128 per lane). A wave's two 32-row blocks are rows wm*32 + [0,32)
 //    and 128 + wm*32 + [0,32): with this interleave the padded rows of an expert's last tile
@@ -290,23 +294,26 @@ __global__ __launch_bounds__(FB_THREADS, 1) void ffn_bf16_kernel(
 }
 
 // ---- ping-pong schedule ---------------------------------------------------------------
-// Same tiles, LDS layout, fragments and epilogue as ffn_bf16_kernel with BK = 64 and two
-// stages. The eight waves form two groups of four, waves 0-3 and 4-7, so each SIMD holds
-// one wave of each. Time is cut into slots, one per half K step and group, separated by
-// workgroup barriers; in every slot one wave of a SIMD runs the 16 MFMAs of a half step from
-// fragments already in its registers while its partner reads the fragments of its next half
-// step from LDS (and, in group 0, issues the direct global->LDS loads of the next stage).
-// With the plain schedule both waves of a SIMD waited for the same stage and
-// then computed together, so load time and compute time added up.
+// The default kernel. Same tiles (256 rows x BN columns), A/B LDS layouts and swizzles as
+// ffn_bf16_kernel; by default K step BK = 32 with four stages (BK = 64 with two stages is
+// the older variant). The eight waves form two groups of four, waves 0-3 and 4-7, so each
+// SIMD holds one wave of each. Time is cut into slots, one per MFMA half-stage (two 16-deep
+// k-steps) and group, separated by workgroup barriers. In every slot one wave of a SIMD runs
+// its MFMAs from fragments already in its registers while its partner reads the fragments of
+// its next slot from LDS (and, in group 0, issues the direct global->LDS loads of a later
+// stage). With the plain schedule both waves of a SIMD waited for the same stage and then
+// computed together, so load time and compute time added up.
 //
-//   group 0: read h0(kt) | compute h0(kt) | read h1(kt) | compute h1(kt) | read h0(kt+1) ...
-//   group 1:   (wait)    | read h0(kt)    | compute h0  | read h1(kt)    | compute h1 ...
+//   group 0: read kt   | compute kt | read kt+1 | compute kt+1 | ...
+//   group 1:  (wait)   | read kt    | compute kt | read kt+1   | ...
 // Both groups execute the same instruction sequence; group 1 passes one extra barrier at the
 // start (and group 0 one at the end), which is all that offsets them. Group 0 issues the
-// direct loads of stage kt+1 while reading half 0 of stage kt (the buffer's previous stage,
-// kt-1, has then been read by both groups) and waits for them before the last barrier of
-// stage kt, so loads have four slots to land. Every barrier is preceded by lgkmcnt(0), so no
-// LDS read of a buffer is in flight when a later slot refills it.
+// direct loads of stage kt+NS-1 while reading stage kt (into the buffer of stage kt-1, which
+// group 1 finished reading one slot earlier) and, before the last barrier of stage kt, waits
+// until stage kt+1 has landed, so a stage has NS-1 steps to land. Every barrier is preceded
+// by lgkmcnt(0), so no LDS read of a buffer is in flight when a later slot refills it. The
+// wave layout (column strips, even/odd row blocks) and the cross-tile prefetch are described
+// at the kernel.
 __device__ __forceinline__ void pp_barrier() {
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" : : : "memory");
