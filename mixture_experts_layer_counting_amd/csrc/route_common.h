@@ -11,10 +11,67 @@
 
 #include "moe_common.h"
 
+#include <type_traits>
+
 namespace moe {
 
 __device__ __forceinline__ bool route_better(float av, int ae, float bv, int be) {
   return av > bv || (av == bv && ae < be);
+}
+
+// Wave-wide reductions without the LDS crossbar: within each 16-lane row, DPP moves pair lane
+// l with l^1, l^2 (quad permutes), then with the mirror lane of its 8 and of its 16; across
+// rows, v_permlane16_swap and v_permlane32_swap applied to a value and itself hand every lane
+// the values of both rows of its row pair, then of both halves. After each stage every lane
+// of a group holds the group's result, so the next stage only has to pair groups.
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov(int x) {
+  return __builtin_amdgcn_update_dpp(x, x, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_XOR1 = 0xB1;         // quad_perm [1, 0, 3, 2]
+constexpr int DPP_XOR2 = 0x4E;         // quad_perm [2, 3, 0, 1]
+constexpr int DPP_HALF_MIRROR = 0x141; // lane i <-> 7 - i within each 8
+constexpr int DPP_MIRROR = 0x140;      // lane i <-> 15 - i within each 16
+
+// The better of (bv, be) over the 64 lanes, in every lane ("better": larger value, then lower
+// id; the order is total, so the result does not depend on the pairing).
+__device__ __forceinline__ void wave_best(float& bv, int& be) {
+  auto take = [&](float ov, int oe) {
+    if (route_better(ov, oe, bv, be)) {
+      bv = ov;
+      be = oe;
+    }
+  };
+  auto dpp = [&](auto ctrl) {
+    constexpr int C = decltype(ctrl)::value;
+    take(__int_as_float(dpp_mov<C>(__float_as_int(bv))), dpp_mov<C>(be));
+  };
+  dpp(std::integral_constant<int, DPP_XOR1>{});
+  dpp(std::integral_constant<int, DPP_XOR2>{});
+  dpp(std::integral_constant<int, DPP_HALF_MIRROR>{});
+  dpp(std::integral_constant<int, DPP_MIRROR>{});
+  const auto v16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+  const auto e16 = __builtin_amdgcn_permlane16_swap((uint32_t)be, (uint32_t)be, false, false);
+  bv = __uint_as_float(v16[0]);
+  be = (int)e16[0];
+  take(__uint_as_float(v16[1]), (int)e16[1]);
+  const auto v32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bv), __float_as_uint(bv), false, false);
+  const auto e32 = __builtin_amdgcn_permlane32_swap((uint32_t)be, (uint32_t)be, false, false);
+  bv = __uint_as_float(v32[0]);
+  be = (int)e32[0];
+  take(__uint_as_float(v32[1]), (int)e32[1]);
+}
+
+// The sum of s over the 64 lanes, in every lane (in the pairing order above).
+__device__ __forceinline__ float wave_sum(float s) {
+  s += __int_as_float(dpp_mov<DPP_XOR1>(__float_as_int(s)));
+  s += __int_as_float(dpp_mov<DPP_XOR2>(__float_as_int(s)));
+  s += __int_as_float(dpp_mov<DPP_HALF_MIRROR>(__float_as_int(s)));
+  s += __int_as_float(dpp_mov<DPP_MIRROR>(__float_as_int(s)));
+  const auto p16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  s = __uint_as_float(p16[0]) + __uint_as_float(p16[1]);
+  const auto p32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+  return __uint_as_float(p32[0]) + __uint_as_float(p32[1]);
 }
 
 // This lane's ITEMS logits of the token at `row` (-inf past E; NaN never wins).
@@ -49,15 +106,7 @@ __device__ __forceinline__ void route_pick(const float (&v)[ITEMS], int E, int K
         be = e;
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      if (route_better(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
+    wave_best(bv, be);
     if ((be & 63) == lane) taken |= (1ull << (be >> 6));
     if (k == 0) top_v = bv;
     if (lane == k) {
@@ -66,10 +115,7 @@ __device__ __forceinline__ void route_pick(const float (&v)[ITEMS], int E, int K
     }
   }
   const float z = lane < K ? expf(my_v - top_v) : 0.f;
-  float s = z;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off, 64);
-  my_w = z / s;
+  my_w = z / wave_sum(z);
 }
 
 }  // namespace moe
