@@ -129,8 +129,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: this build runs the MoE hot path on exactly one GPU; multi-GPU "
-              "expert parallelism is designed but not built (see the sharding notes).",
+        print("bench.py: the library runs the MoE layer on exactly one GPU; expert parallelism "
+              "over several GPUs is designed but not implemented (see the sharding notes).",
               file=sys.stderr)
         sys.exit(2)
     if args.copy_calibration:
