@@ -24,7 +24,7 @@
  *    All shapes are static (M = T*K rows), cu_seqlens stays on the device.
  *  - Errors are returned as moe_status_t; nothing is thrown. Argument checks happen on the
  *    host before anything is enqueued: MOE_EINVAL (bad sizes, NULL where a buffer is needed,
- *    K > E), MOE_EUNSUPPORTED (a dtype combination or a dimension multiple this build does not
+ *    K > E), MOE_EUNSUPPORTED (a dtype combination or a dimension multiple the library does not
  *    implement), MOE_EWORKSPACE (workspace too small). A failed launch gives MOE_EHIP.
  *  - T = 0 and experts that receive no rows are legal and produce valid (empty) groups.
  *  - Expert ids outside [0, E) in a caller-given top-k are memory-safe: that copy is dropped
