@@ -9,7 +9,10 @@ its rows gathered from x -> down -> combine (c3 passes its given routing and ski
 ``--combine scatter`` fuses the weighted combine into the down projection (fp32 atomics into
 a zeroed accumulator, rounded once at the end); ``--xperm`` writes the permuted copy x_perm in
 the permute and reads it in gate/up instead of gathering. Inputs and weights are resident in
-HBM before the timed region starts.
+HBM before the timed region starts. Each timed region is preceded by the W warmup steps and
+then by untimed steps for at least ``--settle-ms`` (default 100 ms): the GPU raises its clock
+over the first tens of ms of work after an idle period, and the K timed steps measure the
+rate it holds under continuous work (``--settle-ms 0`` times the ramp instead).
 Prints ONE JSON line. ``value`` is tokens/s of the whole layer. ``roofline`` describes the
 dominant kernel (the gate/up grouped GEMM): its algorithmic flops or bytes per launch over
 its average duration measured with HIP events on the launch stream during the timed steps.
@@ -51,6 +54,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="untimed repetitions for at least this long before each timed region")
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--maxvio", type=float, default=1.0, help="skew target for c4")
     ap.add_argument("--cpu-sample-experts", type=int, default=0,
@@ -108,6 +113,24 @@ def source_hash(*names):
         src = re.sub(r"//[^\n]*", " ", src)
         h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
+
+
+def settle(fn, ms, torch):
+    """Untimed repetitions of fn for at least `ms` of wall time. After an idle period the GPU
+    raises its clock over the first tens of ms of work (c2: 0.45 ms per step in the first 25
+    steps, a steady 0.375 ms from about 30 ms on); the timed steps that follow then run at the
+    rate the GPU holds under continuous work."""
+    if ms <= 0:
+        return 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            fn()
+        n += 4
+        torch.cuda.synchronize()
+    return n
 
 
 def load_traffic(kernel, workload, khash):
@@ -229,6 +252,7 @@ def main():
 
     for _ in range(args.warmup):
         step(False)
+    settle(lambda: step(False), args.settle_ms, torch)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -253,6 +277,7 @@ def main():
             step(False)
         for _ in range(args.warmup):
             graph.replay()
+        settle(graph.replay, args.settle_ms, torch)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(args.steps):
@@ -325,6 +350,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": args.settle_ms,
         "ms_per_step": ms_step,
         "ms_per_step_eager": ms_step_eager,
         "timing": "HIP graph replay of the whole step" if not args.no_graph else "eager launches",
@@ -388,6 +414,7 @@ def time_fused(w, args, moe, torch):
     def timed(fn):
         for _ in range(args.warmup):
             fn()
+        settle(fn, args.settle_ms, torch)
         torch.cuda.synchronize()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
