@@ -194,7 +194,8 @@ def main():
     row_src = torch.empty(MR, **i32)
     scatter = args.combine == "scatter"
     x_perm = torch.empty((MR, H), dtype=TD[w.act], device=dev) if args.xperm else None
-    x_perm_sf = torch.empty((H // 128, MR), **f32) if args.xperm and w.act == "fp8" else None
+    # fp8: the permutation writes the block-major scales also when the rows are gathered
+    x_perm_sf = torch.empty((H // 128, MR), **f32) if w.act == "fp8" else None
     row_w = torch.empty(MR, **f32) if scatter else None
     h = torch.empty((MR, Hp), dtype=TD[hf], device=dev)
     h_sf = torch.empty((Hp // 128, MR), **f32) if w.act == "fp8" else None
@@ -235,9 +236,9 @@ def main():
                                                         w.w_gate, w.w_up, w.sf_gate, w.sf_up,
                                                         DT[w.wgt], h, h_sf, None))
         else:
-            mark("gate_up", lambda: moe.moe_ffn_gate_up_gather(w.x, w.x_sf, DT[w.act], row_src, T, K, cu,
-                                                               MR, E, H, Hp, w.w_gate, w.w_up, w.sf_gate,
-                                                               w.sf_up, DT[w.wgt], h, h_sf, None))
+            mark("gate_up", lambda: moe.moe_ffn_gate_up_gather(w.x, None, x_perm_sf, DT[w.act], row_src, T,
+                                                               K, cu, MR, E, H, Hp, w.w_gate, w.w_up,
+                                                               w.sf_gate, w.sf_up, DT[w.wgt], h, h_sf, None))
         if not scatter:
             mark("down", lambda: moe.moe_ffn_down(h, h_sf, DT[hf], cu, MR, E, H, Hp, w.w_down, w.sf_down,
                                                   DT[w.wgt], y, DT[yf], None))
@@ -319,8 +320,10 @@ def main():
     perm_bytes = M * 4 + 2 * M * 4 + (2 * M * 4 if scatter else 0)
     if w.logits is not None:
         perm_bytes += T * E * 4 + M * 4
+    if w.act == "fp8":   # x_sf read, the block-major permuted scales written
+        perm_bytes += T * (H // 128) * 4 + xsf_b
     if args.xperm:
-        perm_bytes += T * H * ab + M * H * ab + (T * (H // 128) * 4 + xsf_b if w.act == "fp8" else 0)
+        perm_bytes += T * H * ab + M * H * ab
     if scatter:   # zero the fp32 accumulator, then round it once into out (bf16)
         comb_bytes = T * H * 4 + ((T * H * 4 + T * H * ob) if w.out != "f32" else 0)
         dn_bytes = M * Hp * hb + hsf_b + active * wmat + M * 4 * 2   # + the fp32 adds, M*H*4

@@ -114,12 +114,13 @@ MOE_API size_t moe_permute_workspace_bytes(int32_t T, int32_t E, int32_t K);
  *  row_src    [T*K] int32 out: flat index t*K + k of the copy stored in each row.
  *  row_w      [T*K] fp32 out (or NULL): topk_w of the copy stored in each row.
  *  x_perm     [T*K, H] out, format `act`: x_perm[pos[t,k]] = x[t], bit for bit. May be NULL:
- *             then only the routing metadata is produced (x, x_sf and x_perm_sf are not
- *             touched), for consumers that gather rows through row_src, such as
+ *             then x is not read, for consumers that gather rows through row_src, such as
  *             moe_ffn_gate_up_gather.
- *  x_perm_sf  [H/128, T*K] fp32 out when act = FP8_E4M3 and x_perm is given, block-major:
- *             x_perm_sf[b][r] is the scale of block b of row r (the transpose of x_sf's
- *             layout).
+ *  x_perm_sf  [H/128, T*K] fp32 out or NULL, block-major: x_perm_sf[b][r] is the scale of
+ *             block b of row r (the transpose of x_sf's layout). act = FP8_E4M3 only, where
+ *             it is required with x_perm and may also be given without it (then x_sf is
+ *             required and only the scales are permuted: T*K*H/32 bytes, against T*K*H for
+ *             the rows). Rows past cu_seqlens[E] (dropped copies) are not written.
  * Row order is a stable counting sort: the rows of expert e hold its copies in ascending
  * t*K + k. The result is deterministic. Limits: E <= 1024, K <= 32. */
 MOE_API moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t act,
@@ -154,7 +155,7 @@ MOE_API moe_status_t moe_permute_padded(const void* x, const float* x_sf, moe_dt
 
 /* Routing and the permutation in one call: moe_route_topk on `logits` followed by
  * moe_permute_padded on its result, with the same outputs bit for bit ("Distributed expert
- * parallelism", lifecycle items 1-3). The first kernel ranks the tokens of each 128-token
+ * parallelism", lifecycle items 1-3). The first kernel ranks the tokens of each 16-token
  * chunk and counts the chunk's picks per expert, which saves the permutation's separate
  * histogram pass and one launch.
  *  logits [T, E] fp32 in; topk_idx [T, K] int32 and topk_w [T, K] fp32 out (both required);
@@ -205,11 +206,17 @@ MOE_API moe_status_t moe_ffn_gate_up(const void* x_perm, const float* x_perm_sf,
  * is x[row_src[r] / K], so
  *     h[r] = silu(x[row_src[r]/K] . Wg[e]) * (x[row_src[r]/K] . Wu[e]),
  * bitwise the same h as moe_ffn_gate_up on the x_perm that moe_permute would write.
- *  x [T, H] of format `act`; x_sf [T, H/128] fp32 (FP8_E4M3, the token layout of
- *  moe_permute's x_sf); row_src [M] from moe_permute or moe_permute_padded (a row with
+ *  x [T, H] of format `act`; row_src [M] from moe_permute or moe_permute_padded (a row with
  *  row_src = -1 is a padding row and reads zeros); other arguments as moe_ffn_gate_up.
+ *  FP8_E4M3 only, one of the two scale layouts (ignored otherwise, may be NULL):
+ *  x_perm_sf  [H/128, M] fp32, the permuted block-major scales that moe_permute writes when
+ *             given x_perm_sf without x_perm. Preferred: each stage reads them as contiguous
+ *             runs, once per row instead of once per row and output tile.
+ *  x_sf       [T, H/128] fp32, the token layout of moe_permute's x_sf, read when x_perm_sf
+ *             is NULL: each row's scales are gathered through row_src.
  * Needs T*H*bytes(act) < 2^31 (MOE_EUNSUPPORTED otherwise). */
-MOE_API moe_status_t moe_ffn_gate_up_gather(const void* x, const float* x_sf, moe_dtype_t act,
+MOE_API moe_status_t moe_ffn_gate_up_gather(const void* x, const float* x_sf,
+                                    const float* x_perm_sf, moe_dtype_t act,
                                     const int32_t* row_src, int32_t T, int32_t K,
                                     const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
                                     int32_t Hp, const void* w_gate, const void* w_up,
@@ -357,7 +364,8 @@ MOE_API moe_status_t moe_layer_backward(const moe_layer_desc_t* d, const void* x
 
 /* Byte offsets of the intermediates inside the moe_layer_forward workspace, for inspection.
  * offsets[i] (i in order): 0 topk_idx, 1 topk_w, 2 counts, 3 cu_seqlens, 4 pos, 5 row_src,
- * 6 row_w (scatter combine), 7 x_perm and 8 x_perm_sf (only when x_perm is written),
+ * 6 row_w (scatter combine), 7 x_perm (only when it is written), 8 x_perm_sf (FP8: the
+ * gathered gate/up reads the permuted block-major scales),
  * 9 h, 10 h_sf, 11 y_rows (gather combine), 12 permute scratch, 13 fp32 accumulator (scatter
  * combine with a BF16 output), 14 x_q and 15 x_q_sf (the quantised activations of a
  * (BF16, MXFP4) layer). Unused entries are set to SIZE_MAX. Writes n <= 16 entries;

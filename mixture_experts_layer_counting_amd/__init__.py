@@ -68,7 +68,7 @@ _SIGS = {
     "moe_route_permute": (_I, [_P, _P, _P, _E, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                                _P, _P, _S, _P]),
     "moe_quantize_fp8": (_I, [_P, _E, _I, _I, _P, _P, _P]),
-    "moe_ffn_gate_up_gather": (_I, [_P, _P, _E, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _E,
+    "moe_ffn_gate_up_gather": (_I, [_P, _P, _P, _E, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _E,
                                     _P, _P, _P]),
     "moe_ffn_down_scatter": (_I, [_P, _P, _E, _P, _I, _I, _I, _I, _P, _P, _E, _P, _P, _I, _I, _P,
                                   _P]),
@@ -187,9 +187,9 @@ def moe_ffn_gate_up(x_perm, x_perm_sf, act, cu_seqlens, M, E, H, Hp, w_gate, w_u
                                  _ptr(h_sf), _stream(stream)), "moe_ffn_gate_up")
 
 
-def moe_ffn_gate_up_gather(x, x_sf, act, row_src, T, K, cu_seqlens, M, E, H, Hp, w_gate, w_up,
-                           sf_gate, sf_up, wgt, h, h_sf, stream=None):
-    _check(lib().moe_ffn_gate_up_gather(_ptr(x), _ptr(x_sf), act, _ptr(row_src), T, K,
+def moe_ffn_gate_up_gather(x, x_sf, x_perm_sf, act, row_src, T, K, cu_seqlens, M, E, H, Hp, w_gate,
+                           w_up, sf_gate, sf_up, wgt, h, h_sf, stream=None):
+    _check(lib().moe_ffn_gate_up_gather(_ptr(x), _ptr(x_sf), _ptr(x_perm_sf), act, _ptr(row_src), T, K,
                                         _ptr(cu_seqlens), M, E, H, Hp, _ptr(w_gate), _ptr(w_up),
                                         _ptr(sf_gate), _ptr(sf_up), wgt, _ptr(h), _ptr(h_sf),
                                         _stream(stream)), "moe_ffn_gate_up_gather")

@@ -192,6 +192,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     int a_ld_off[CF::A_LD];
   };
   const int sc_row = (wave & 3) * 64 + lane;  // activation-scale row of waves 0-3
+  const bool sf_perm = GATED && MAPPED && maps.a_sf_perm != nullptr;
   auto decode = [&](int t, int base) __attribute__((always_inline)) {
     Tile d;
     d.e = find_expert(tstart, E, t);
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
         d.a_ld_off[i] = (a_row[i] < d.rows_valid && src[i] >= 0) ? off : (int)0x80000000u;
       }
       const int ssrc = sc_row < d.rows_valid ? ssrc0 : -1;
-      d.sc_voff = ssrc >= 0 ? (ssrc / maps.a_k) * nsf * 4 : (int)0x80000000u;
+      d.sc_voff = sf_perm ? (d.row0 + sc_row) * 4 : ssrc >= 0 ? (ssrc / maps.a_k) * nsf * 4 : (int)0x80000000u;
     } else {
       d.rA = f8_rsrc(A + (size_t)d.row0 * Kd, (uint32_t)d.rows_valid * (uint32_t)Kd);
 #pragma unroll
@@ -247,11 +248,15 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
       f8_dma16(second ? d.rB1 : d.rB0, so + CF::A_BYTES + j * 1024, b_voff[i], kt * (F8_BK / 2));
     }
     if (wave < 4) {
-      // activation scales of block kt for tile rows 64 wave + lane. Plain: block-major
-      // [Kd/128][M], rows >= M read as zero. Gathered: x_sf [a_rows][Kd/128] of the row's token.
-      if constexpr (GATED && MAPPED)
+      // activation scales of block kt for tile rows 64 wave + lane. Plain (or gathered rows
+      // with permuted scales): block-major [Kd/128][M], rows >= M read as zero, one 256-byte
+      // run per wave. Gathered: x_sf [a_rows][Kd/128] of the row's token, a line per lane.
+      if (GATED && MAPPED && !sf_perm)
         f8_dma4(f8_rsrc(A_sf, (uint32_t)maps.a_rows * (uint32_t)nsf * 4u), so + CF::SF_A + wave * 256,
                 d.sc_voff, kt * 4);
+      else if (GATED && MAPPED)
+        f8_dma4(f8_rsrc(maps.a_sf_perm + (size_t)kt * M, (uint32_t)M * 4u), so + CF::SF_A + wave * 256,
+                d.sc_voff, 0);
       else
         f8_dma4(f8_rsrc(A_sf + (size_t)kt * M, (uint32_t)M * 4u), so + CF::SF_A + wave * 256, d.sc_voff, 0);
     } else {

@@ -172,7 +172,8 @@ static moe_status_t permute_impl(const float* logits, const void* x, const float
   if (row_w && T > 0 && !topk_w) return MOE_EINVAL;
   if (act == MOE_FP8_E4M3) {
     if (H % 128) return MOE_EUNSUPPORTED;
-    if (T > 0 && x_perm && (!x_sf || !x_perm_sf)) return MOE_EINVAL;
+    if (T > 0 && x_perm && !x_perm_sf) return MOE_EINVAL;
+    if (T > 0 && x_perm_sf && !x_sf) return MOE_EINVAL;
   }
   const int64_t cap = (int64_t)T * K + (int64_t)E * (pad - 1);
   if (cap > std::numeric_limits<int32_t>::max() / 2) return MOE_EUNSUPPORTED;
@@ -182,7 +183,8 @@ static moe_status_t permute_impl(const float* logits, const void* x, const float
   // routed here, the ids are valid and distinct: nothing to validate
   const bool validate = !logits && env_flag("MOE_VALIDATE");
   int* err = nullptr;
-  const bool sf = act == MOE_FP8_E4M3 && x_perm;
+  // fp8: the block-major scales are written whenever x_perm_sf is given, also without x_perm
+  const bool sf = act == MOE_FP8_E4M3 && x_perm_sf;
   if (logits && T > 0) {
     const moe_status_t st = launch_route_hist(logits, T, E, K, const_cast<int32_t*>(topk_idx),
                                               const_cast<float*>(topk_w), ws, stream);
@@ -264,12 +266,15 @@ moe_status_t moe_ffn_gate_up(const void* x_perm, const float* x_perm_sf, moe_dty
   return launch_ffn_gate_up_bf16(x_perm, cu_seqlens, M, E, H, Hp, w_gate, w_up, h, RowMaps{}, stream);
 }
 
-moe_status_t moe_ffn_gate_up_gather(const void* x, const float* x_sf, moe_dtype_t act,
-                                    const int32_t* row_src, int32_t T, int32_t K,
-                                    const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
-                                    int32_t Hp, const void* w_gate, const void* w_up,
-                                    const uint8_t* sf_gate, const uint8_t* sf_up, moe_dtype_t wgt,
-                                    void* h, float* h_sf, hipStream_t stream) {
+// Gate/up with rows gathered from x through row_src. fp8: the activation scales come from
+// x_perm_sf ([H/128, M] block-major, as the permutation writes them) when it is given, else
+// they are gathered from x_sf row by row.
+static moe_status_t gate_up_gather(const void* x, const float* x_sf, const float* x_perm_sf,
+                                   moe_dtype_t act, const int32_t* row_src, int32_t T, int32_t K,
+                                   const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
+                                   int32_t Hp, const void* w_gate, const void* w_up,
+                                   const uint8_t* sf_gate, const uint8_t* sf_up, moe_dtype_t wgt,
+                                   void* h, float* h_sf, hipStream_t stream) {
   const Path p = ffn_path(act, wgt);
   if (p == PATH_NONE) return MOE_EUNSUPPORTED;
   if (T < 0 || K < 1) return MOE_EINVAL;
@@ -284,12 +289,23 @@ moe_status_t moe_ffn_gate_up_gather(const void* x, const float* x_sf, moe_dtype_
   maps.a_k = K;
   maps.a_rows = T;
   if (p == PATH_FP8_MXFP4) {
-    if (M > 0 && (!x_sf || !sf_gate || !sf_up || !h_sf)) return MOE_EINVAL;
+    if (M > 0 && ((!x_sf && !x_perm_sf) || !sf_gate || !sf_up || !h_sf)) return MOE_EINVAL;
+    maps.a_sf_perm = x_perm_sf;
     return launch_ffn_gate_up_fp8(x, x_sf, cu_seqlens, M, E, H, Hp, w_gate, sf_gate, w_up, sf_up, h,
                                   h_sf, maps, stream);
   }
   if (p == PATH_F32) return launch_ffn_gate_up_f32(x, cu_seqlens, M, E, H, Hp, w_gate, w_up, h, maps, stream);
   return launch_ffn_gate_up_bf16(x, cu_seqlens, M, E, H, Hp, w_gate, w_up, h, maps, stream);
+}
+
+moe_status_t moe_ffn_gate_up_gather(const void* x, const float* x_sf, const float* x_perm_sf,
+                                    moe_dtype_t act, const int32_t* row_src, int32_t T, int32_t K,
+                                    const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
+                                    int32_t Hp, const void* w_gate, const void* w_up,
+                                    const uint8_t* sf_gate, const uint8_t* sf_up, moe_dtype_t wgt,
+                                    void* h, float* h_sf, hipStream_t stream) {
+  return gate_up_gather(x, x_sf, x_perm_sf, act, row_src, T, K, cu_seqlens, M, E, H, Hp, w_gate, w_up,
+                        sf_gate, sf_up, wgt, h, h_sf, stream);
 }
 
 moe_status_t moe_ffn_down(const void* h, const float* h_sf, moe_dtype_t h_dtype,
@@ -438,7 +454,7 @@ static moe_status_t layer_layout(const moe_layer_desc_t* d, size_t* off, size_t*
   want(WS_ROW_SRC, M * 4);
   if (scatter) want(WS_ROW_W, M * 4);
   if (mat) want(WS_X_PERM, M * H * ab);
-  if (mat && fp8) want(WS_X_PERM_SF, M * (H / 128) * 4);
+  if (fp8) want(WS_X_PERM_SF, M * (H / 128) * 4);
   want(WS_H, M * Hp * hb);
   if (fp8) want(WS_H_SF, M * (Hp / 128) * 4);
   if (!scatter) want(WS_Y, M * H * yb);
@@ -625,8 +641,8 @@ static moe_status_t layer_forward_impl(const moe_layer_desc_t* d, const void* x,
     st = moe_ffn_gate_up(at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)), act, cu, M, E, H, Hp,
                          w_gate, w_up, sf_gate, sf_up, d->wgt, at(WS_H), h_sf, stream);
   else
-    st = moe_ffn_gate_up_gather(x, x_sf, act, row_src, T, K, cu, M, E, H, Hp, w_gate, w_up, sf_gate,
-                                sf_up, d->wgt, at(WS_H), h_sf, stream);
+    st = gate_up_gather(x, x_sf, static_cast<float*>(at(WS_X_PERM_SF)), act, row_src, T, K, cu, M, E,
+                        H, Hp, w_gate, w_up, sf_gate, sf_up, d->wgt, at(WS_H), h_sf, stream);
   if (st != MOE_OK) return st;
   if (!scatter) {
     st = moe_ffn_down(at(WS_H), h_sf, h_dtype_of(p), cu, M, E, H, Hp, w_down, sf_down, d->wgt, at(WS_Y),

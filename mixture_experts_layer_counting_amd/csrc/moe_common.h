@@ -36,12 +36,16 @@ bool env_flag(const char* name);
 
 // Optional row maps of a grouped-FFN launch; null pointers select the plain layout.
 //  gather  (gate/up): A row of group row r is row a_src[r] / a_k of A, which has a_rows rows.
+//                     fp8 only: with a_sf_perm set, the activation scales are read from the
+//                     permuted block-major copy a_sf_perm [Kd/128][M] (row r's scales at
+//                     column r) instead of being gathered from A's scales row by row.
 //  scatter (down):    instead of storing y[r], add s_w[r] * y[r] to row s_src[r] / s_k of the
 //                     fp32 accumulator s_acc (fp32 atomics).
 struct RowMaps {
   const int* a_src = nullptr;
   int a_k = 1;
   int a_rows = 0;
+  const float* a_sf_perm = nullptr;
   const int* s_src = nullptr;
   const float* s_w = nullptr;
   int s_k = 1;

@@ -290,22 +290,42 @@ __global__ __launch_bounds__(256) void permute_copy_kernel(const unsigned char* 
   }
 }
 
-// Block scales of the permuted rows, block-major [H/128][M]: consecutive threads write
-// consecutive rows (coalesced); the gathered reads of x_sf [T][H/128] stay in L2.
+// Block scales of the permuted rows, block-major [H/128][M], transposed through LDS: a block
+// takes 64 rows and up to 64 scale columns; it reads each row's source scales as one
+// contiguous run of x_sf [T][H/128] and writes each column's 64 rows as one 256-byte run.
+// Rows past cu_seqlens[E] (dropped copies) are left as they are; padding rows get scale 1.
+constexpr int PSF_ROWS = 64;
+constexpr int PSF_PER_THREAD = PSF_ROWS * PSF_ROWS / 256;
 __global__ __launch_bounds__(256) void permute_sf_kernel(const float* __restrict__ x_sf,
                                                          const int* __restrict__ row_src,
                                                          const int* __restrict__ cu_seqlens, int E,
                                                          int K, int M, int nsf,
                                                          float* __restrict__ x_perm_sf) {
+  __shared__ float tile[PSF_ROWS][PSF_ROWS + 1];
+  const int p0 = blockIdx.x * PSF_ROWS;
+  const int c0 = blockIdx.y * PSF_ROWS;
   const int rows = cu_seqlens[E];  // rows actually holding a copy
-  const size_t n = (size_t)nsf * M;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-    const int c = (int)(i / M);
-    const int p = (int)(i - (size_t)c * M);
-    if (p < rows) {
-      const int src = row_src[p];
-      x_perm_sf[i] = src >= 0 ? x_sf[(size_t)(src / K) * nsf + c] : 1.0f;  // padding: scale 1
-    }
+  const int nr = min(PSF_ROWS, rows - p0);
+  if (nr <= 0) return;
+  const int nc = min(PSF_ROWS, nsf - c0);
+  // thread -> column lane % 64 of rows wave + 4 i: each wave reads whole row runs; all loads
+  // of a thread are issued before the first LDS store
+  const int lane = threadIdx.x % PSF_ROWS, rq = threadIdx.x / PSF_ROWS;
+  float v[PSF_PER_THREAD];
+#pragma unroll
+  for (int i = 0; i < PSF_PER_THREAD; ++i) {
+    const int r = rq + 4 * i;
+    const int sr = r < nr ? row_src[p0 + r] : -1;
+    v[i] = (sr >= 0 && lane < nc) ? x_sf[(size_t)(sr / K) * nsf + c0 + lane] : 1.0f;  // padding: 1
+  }
+#pragma unroll
+  for (int i = 0; i < PSF_PER_THREAD; ++i) tile[rq + 4 * i][lane] = v[i];
+  __syncthreads();
+  // thread -> row lane % 64 of columns wave + 4 i: 256-byte runs of one column
+#pragma unroll
+  for (int i = 0; i < PSF_PER_THREAD; ++i) {
+    const int c = rq + 4 * i;
+    if (lane < nr && c < nc) x_perm_sf[(size_t)(c0 + c) * M + p0 + lane] = tile[lane][c];
   }
 }
 
@@ -385,9 +405,8 @@ moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes,
   if (T > 0 && x_perm && pad > 1)
     permute_zero_pad_kernel<<<cap, 256, 0, s>>>(row_src, cu_seqlens, E, xp, row_bytes);
   if (x_sf && x_perm_sf && T > 0) {
-    const size_t n = (size_t)sf_per_row * cap;
-    const int blocks = (int)std::min<size_t>((n + 255) / 256, 4096);
-    permute_sf_kernel<<<blocks, 256, 0, s>>>(x_sf, row_src, cu_seqlens, E, K, cap, sf_per_row, x_perm_sf);
+    const dim3 grid((cap + PSF_ROWS - 1) / PSF_ROWS, (sf_per_row + PSF_ROWS - 1) / PSF_ROWS);
+    permute_sf_kernel<<<grid, 256, 0, s>>>(x_sf, row_src, cu_seqlens, E, K, cap, sf_per_row, x_perm_sf);
   }
   return launch_status();
 }

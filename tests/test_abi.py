@@ -129,18 +129,21 @@ def test_layer_workspace_sizes_and_layout():
     assert moe.moe_layer_workspace_bytes(mixed) == 0
     fp8 = moe.LayerDesc(64, 256, 128, 4, 2, moe.MOE_FP8_E4M3, moe.MOE_MXFP4, moe.MOE_BF16, 0)
     lay8 = moe.moe_layer_workspace_layout(fp8)
-    assert lay8["x_perm_sf"] is None and lay8["h_sf"] is not None
+    # the gathered fp8 gate/up reads the permuted block-major scales, not x_perm
+    assert lay8["x_perm"] is None and lay8["x_perm_sf"] is not None and lay8["h_sf"] is not None
 
 
 def test_gather_and_scatter_argument_checks():
     g = moe.moe_ffn_gate_up_gather
-    # (x, x_sf, act, row_src, T, K, cu, M, E, H, Hp, wg, wu, sfg, sfu, wgt, h, h_sf)
-    _expect(moe.MOE_EINVAL, g, 16, None, moe.MOE_BF16, 16, -4, 2, 16, 8, 4, 128, 128, 16, 16, None,
-            None, moe.MOE_BF16, 16, None, 0)                              # T < 0
-    _expect(moe.MOE_EINVAL, g, 16, None, moe.MOE_BF16, None, 4, 2, 16, 8, 4, 128, 128, 16, 16, None,
-            None, moe.MOE_BF16, 16, None, 0)                              # NULL row_src
-    _expect(moe.MOE_EUNSUPPORTED, g, 16, None, moe.MOE_BF16, 16, 2 ** 20, 2, 16, 8, 4, 1024, 128, 16,
-            16, None, None, moe.MOE_BF16, 16, None, 0)                    # x past 2 GiB
+    # (x, x_sf, x_perm_sf, act, row_src, T, K, cu, M, E, H, Hp, wg, wu, sfg, sfu, wgt, h, h_sf)
+    _expect(moe.MOE_EINVAL, g, 16, None, None, moe.MOE_BF16, 16, -4, 2, 16, 8, 4, 128, 128, 16, 16,
+            None, None, moe.MOE_BF16, 16, None, 0)                        # T < 0
+    _expect(moe.MOE_EINVAL, g, 16, None, None, moe.MOE_BF16, None, 4, 2, 16, 8, 4, 128, 128, 16, 16,
+            None, None, moe.MOE_BF16, 16, None, 0)                        # NULL row_src
+    _expect(moe.MOE_EUNSUPPORTED, g, 16, None, None, moe.MOE_BF16, 16, 2 ** 20, 2, 16, 8, 4, 1024, 128,
+            16, 16, None, None, moe.MOE_BF16, 16, None, 0)                # x past 2 GiB
+    _expect(moe.MOE_EINVAL, g, 16, None, None, moe.MOE_FP8_E4M3, 16, 4, 2, 16, 8, 4, 128, 128, 16,
+            16, 16, 16, moe.MOE_MXFP4, 16, 16, 0)                         # fp8 without scales
     d = moe.moe_ffn_down_scatter
     # (h, h_sf, h_dtype, cu, M, E, H, Hp, wd, sfd, wgt, row_src, row_w, T, K, acc)
     _expect(moe.MOE_EINVAL, d, 16, None, moe.MOE_BF16, 16, 8, 4, 256, 128, 16, None, moe.MOE_BF16,

@@ -211,6 +211,50 @@ def test_route_permute_is_route_then_permute(T, H, E, K, act, pad, xp):
             assert np.array_equal(host(b["row_src"]), ref["row_src"])
 
 
+@pytest.mark.parametrize("T,H,E,K,pad", [(300, 512, 12, 3, 1), (1000, 8960, 16, 4, 1), (257, 256, 1024, 8, 16),
+                                         (65, 128, 8, 2, 64), (1, 128, 2, 2, 1)])
+def test_permute_writes_scales_without_x_perm(T, H, E, K, pad):
+    """fp8 metadata-only permutation with x_perm_sf given: the block-major scales of every row
+    holding a copy are x_sf of its token (scale 1 for padding rows), bit for bit what the
+    permutation with x_perm writes, and rows past cu_seqlens[E] are left untouched."""
+    say(f"scales without x_perm T={T} H={H} E={E} K={K} pad={pad}")
+    w = gen.make(T=T, H=H, Hp=128, E=E, K=K, act="fp8", wgt="bf16", routing="skew", beta=1.0, cid=74,
+                 device=DEV)
+    i32 = dict(dtype=torch.int32, device=DEV)
+    f32 = dict(dtype=torch.float32, device=DEV)
+    idx = torch.empty((T, K), **i32)
+    tw = torch.empty((T, K), **f32)
+    moe.moe_route_topk(w.logits, T, E, K, idx, tw)
+    if T > 2:
+        idx[T // 2, 0] = -1                    # a dropped copy: one row past cu_seqlens[E]
+    cap = moe.moe_padded_capacity(T, E, K, pad)
+    nws = moe.moe_permute_workspace_bytes(T, E, K)
+    res = []
+    for xp in (True, False):
+        o = dict(counts=torch.full((E,), -7, **i32), cu=torch.full((E + 1,), -7, **i32),
+                 pos=torch.full((T, K), -7, **i32), row_src=torch.full((cap,), -7, **i32),
+                 x_perm=torch.full((cap, H), 7, dtype=w.x.dtype, device=DEV) if xp else None,
+                 x_perm_sf=torch.full((H // 128, cap), -7.0, **f32))
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device=DEV)
+        moe.moe_permute_padded(w.x, w.x_sf, moe.MOE_FP8_E4M3, idx, tw, T, H, E, K, pad, o["counts"],
+                               o["cu"], o["pos"], o["row_src"], None, o["x_perm"], o["x_perm_sf"], ws, nws)
+        torch.cuda.synchronize()
+        res.append(o)
+    a, b = res
+    for k in ("counts", "cu", "pos", "row_src", "x_perm_sf"):
+        assert torch.equal(a[k].view(torch.int32), b[k].view(torch.int32)), k
+    rows = int(host(b["cu"])[-1])
+    rs = host(b["row_src"])[:rows]
+    xsf = host(w.x_sf)
+    want = np.where(rs[None, :] >= 0, xsf[np.maximum(rs, 0) // K].T, np.float32(1.0))
+    got = host(b["x_perm_sf"])
+    assert np.array_equal(got[:, :rows].view(np.int32), want.astype(np.float32).view(np.int32))
+    assert np.all(got[:, rows:] == -7.0)
+    if pad == 1:
+        dropped = {(T // 2) * K} if T > 2 else set()
+        assert sorted(rs.tolist()) == sorted(set(range(T * K)) - dropped)
+
+
 def test_empty_batch():
     say("T=0")
     E, K, H = 16, 2, 256
@@ -455,15 +499,19 @@ def test_gate_up_gather_is_bitwise_the_permuted_path(act, spec):
     r = run_steps(w)
     M = w.T * w.K
     from _gpu_run import DT, TORCH_DT, h_fmt
-    h2 = torch.empty_like(r["h"])
-    h2_sf = torch.empty_like(r["h_sf"]) if r["h_sf"] is not None else None
-    moe.moe_ffn_gate_up_gather(w.x, w.x_sf, DT[w.act], r["row_src"], w.T, w.K, r["cu_seqlens"], M, w.E,
-                               w.H, w.Hp, w.w_gate, w.w_up, w.sf_gate, w.sf_up, DT[w.wgt], h2, h2_sf)
-    torch.cuda.synchronize()
     rows = int(host(r["cu_seqlens"])[-1])
-    assert np.array_equal(host(h2)[:rows], host(r["h"])[:rows])
-    if h2_sf is not None:
-        assert np.array_equal(host(h2_sf)[:, :rows], host(r["h_sf"])[:, :rows])
+    # fp8: the activation scales gathered from x_sf (token layout) and read from the permuted
+    # block-major copy x_perm_sf give the same h
+    for x_sf, x_perm_sf in ((w.x_sf, None),) + (((None, r["x_perm_sf"]),) if act == "fp8" else ()):
+        h2 = torch.empty_like(r["h"])
+        h2_sf = torch.empty_like(r["h_sf"]) if r["h_sf"] is not None else None
+        moe.moe_ffn_gate_up_gather(w.x, x_sf, x_perm_sf, DT[w.act], r["row_src"], w.T, w.K, r["cu_seqlens"],
+                                   M, w.E, w.H, w.Hp, w.w_gate, w.w_up, w.sf_gate, w.sf_up, DT[w.wgt], h2,
+                                   h2_sf)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(h2)[:rows], host(r["h"])[:rows])
+        if h2_sf is not None:
+            assert np.array_equal(host(h2_sf)[:, :rows], host(r["h_sf"])[:, :rows])
 
 
 @pytest.mark.parametrize("act,spec", GATHER_CASES, ids=[c[0] for c in GATHER_CASES])
@@ -636,7 +684,7 @@ def padded_steps(w, pad, gather):
     r = dict(counts=torch.empty(E, **i32), cu_seqlens=torch.empty(E + 1, **i32),
              pos=torch.empty((T, K), **i32), row_src=torch.empty(cap, **i32), row_w=torch.empty(cap, **f32))
     r["x_perm"] = None if gather else torch.empty((cap, H), dtype=TORCH_DT[w.act], device=DEV)
-    r["x_perm_sf"] = None if gather or w.act != "fp8" else torch.empty((H // 128, cap), **f32)
+    r["x_perm_sf"] = None if w.act != "fp8" else torch.empty((H // 128, cap), **f32)
     nws = moe.moe_permute_workspace_bytes(T, E, K)
     ws = torch.empty(nws, dtype=torch.uint8, device=DEV)
     moe.moe_permute_padded(w.x, w.x_sf, DT[w.act], w.topk_idx, w.topk_w, T, H, E, K, pad, r["counts"],
@@ -645,8 +693,18 @@ def padded_steps(w, pad, gather):
     r["h"] = torch.empty((cap, Hp), dtype=TORCH_DT[h_fmt(w)], device=DEV)
     r["h_sf"] = torch.empty((Hp // 128, cap), **f32) if w.act == "fp8" else None
     if gather:
-        moe.moe_ffn_gate_up_gather(w.x, w.x_sf, DT[w.act], r["row_src"], T, K, r["cu_seqlens"], cap, E, H,
-                                   Hp, w.w_gate, w.w_up, w.sf_gate, w.sf_up, DT[w.wgt], r["h"], r["h_sf"])
+        # fp8: scales from the permuted copy; the token-layout gather must give the same h
+        moe.moe_ffn_gate_up_gather(w.x, None if r["x_perm_sf"] is not None else w.x_sf, r["x_perm_sf"],
+                                   DT[w.act], r["row_src"], T, K, r["cu_seqlens"], cap, E, H, Hp, w.w_gate,
+                                   w.w_up, w.sf_gate, w.sf_up, DT[w.wgt], r["h"], r["h_sf"])
+        if r["x_perm_sf"] is not None:
+            h_t, h_t_sf = torch.empty_like(r["h"]), torch.empty_like(r["h_sf"])
+            moe.moe_ffn_gate_up_gather(w.x, w.x_sf, None, DT[w.act], r["row_src"], T, K, r["cu_seqlens"], cap,
+                                       E, H, Hp, w.w_gate, w.w_up, w.sf_gate, w.sf_up, DT[w.wgt], h_t, h_t_sf)
+            torch.cuda.synchronize()
+            rows = int(host(r["cu_seqlens"])[-1])
+            assert np.array_equal(host(h_t)[:rows], host(r["h"])[:rows])
+            assert np.array_equal(host(h_t_sf)[:, :rows], host(r["h_sf"])[:, :rows])
     else:
         moe.moe_ffn_gate_up(r["x_perm"], r["x_perm_sf"], DT[w.act], r["cu_seqlens"], cap, E, H, Hp,
                             w.w_gate, w.w_up, w.sf_gate, w.sf_up, DT[w.wgt], r["h"], r["h_sf"])
@@ -689,15 +747,15 @@ def test_padded_layout_and_results(act, pad, gather):
     assert np.array_equal(host(r["row_src"]), prs)
     tw = host(w.topk_w).ravel()
     assert np.array_equal(host(r["row_w"]), np.where(prs >= 0, tw[np.maximum(prs, 0)], 0).astype(np.float32))
+    real = prs[:pcu[-1]] >= 0
     if not gather:
         xp = host(r["x_perm"])[:pcu[-1]]
-        real = prs[:pcu[-1]] >= 0
         assert np.array_equal(xp[real], host(w.x)[prs[:pcu[-1]][real] // w.K])
         assert not xp[~real].any()
-        if w.act == "fp8":
-            sfp = host(r["x_perm_sf"])[:, :pcu[-1]].T
-            assert np.array_equal(sfp[real], host(w.x_sf)[prs[:pcu[-1]][real] // w.K])
-            assert np.all(sfp[~real] == 1.0)
+    if w.act == "fp8":   # written with and without x_perm
+        sfp = host(r["x_perm_sf"])[:, :pcu[-1]].T
+        assert np.array_equal(sfp[real], host(w.x_sf)[prs[:pcu[-1]][real] // w.K])
+        assert np.all(sfp[~real] == 1.0)
     # per-row results do not depend on where a group starts: same output, bit for bit
     assert np.array_equal(host(r["out"]), host(base["out"]))
     ref = oracle_layer(w)
