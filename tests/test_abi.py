@@ -38,6 +38,33 @@ def test_library_exports_every_declared_symbol():
     assert exported == set(declared())          # nothing else leaks out of the library
 
 
+def prototypes():
+    """name -> list of parameter declarations, from the MOE_API prototypes of the header."""
+    text = re.sub(r"/\*.*?\*/", " ", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = [q.strip() for q in m.group(2).split(",") if q.strip()]
+        out[m.group(1)] = [] if params == ["void"] else params
+    return out
+
+
+def test_binding_signatures_match_the_header():
+    # ctypes does not check arity or types: a binding out of step with a prototype would pass
+    # the wrong pointer for an argument without any error
+    protos = prototypes()
+    assert set(protos) == set(moe.EXPORTS)
+    for name, params in protos.items():
+        restype, argtypes = moe._SIGS[name]
+        assert len(argtypes) == len(params), (name, len(argtypes), len(params))
+        for decl, ct in zip(params, argtypes):
+            if "*" in decl or decl.startswith("hipStream_t"):
+                assert ct is ctypes.c_void_p or (isinstance(ct, type) and issubclass(ct, ctypes._Pointer)), (name, decl)
+            elif decl.startswith("size_t"):
+                assert ct is ctypes.c_size_t, (name, decl)
+            else:
+                assert ct in (ctypes.c_int32, ctypes.c_int), (name, decl)
+
+
 def test_status_strings():
     assert moe.status_str(moe.MOE_OK) == "MOE_OK"
     assert "workspace" in moe.status_str(moe.MOE_EWORKSPACE)
