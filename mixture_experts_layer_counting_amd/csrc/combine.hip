@@ -42,7 +42,9 @@ __device__ __forceinline__ void store8(float* p, const float* f) {
   reinterpret_cast<float4*>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
 }
 
-template <typename YT, typename OT, int KMAX>
+// NU: chunks per thread and pass. Two measured best at H = 7168 (c3-c5 layers: three and four
+// were no faster, and at H = 2048 a thread has only two chunks).
+template <typename YT, typename OT, int KMAX, int NU = 2>
 __global__ __launch_bounds__(128) void combine_kernel(const YT* __restrict__ y_rows,
                                                       const int* __restrict__ pos,
                                                       const float* __restrict__ topk_w, int T,
@@ -57,7 +59,40 @@ __global__ __launch_bounds__(128) void combine_kernel(const YT* __restrict__ y_r
     w[k] = k < K ? (topk_w ? topk_w[(size_t)t * K + k] : 1.0f) : 0.f;  // NULL: unit weights
   }
   const int nchunk = H / 8;
-  for (int c = threadIdx.x; c < nchunk; c += blockDim.x) {
+  const int B = blockDim.x;
+  // NU chunks per thread and pass (NU * K row loads in flight), then one chunk at a time
+  int c = threadIdx.x;
+  for (; c + (NU - 1) * B < nchunk; c += NU * B) {
+    float acc[NU][8];
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      if (p[k] >= 0) {
+        float v[NU][8];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) load8(y_rows + (size_t)p[k] * H + (c + u * B) * 8, v[u]);
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[u][i] = fmaf(w[k], v[u][i], acc[u][i]);
+      }
+    }
+    if (add) {
+      float v[NU][8];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) load8(add + (size_t)t * H + (c + u * B) * 8, v[u]);
+#pragma unroll
+      for (int u = 0; u < NU; ++u)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[u][i] += v[u][i];
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) store8(out + (size_t)t * H + (c + u * B) * 8, acc[u]);
+  }
+  for (; c < nchunk; c += B) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
