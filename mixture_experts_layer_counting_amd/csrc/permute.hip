@@ -16,9 +16,12 @@
 //              counts the copies of earlier tokens of its chunk, ranks its own copies
 //              with wave ballots (match by key bits + mbcnt) in flat order, and writes pos /
 //              row_src / row_w.
-//  4. copy:    one block per token copies its row once from x to its K rows of x_perm
-//              with 16-byte loads and stores (the HBM-bound part).
-//  (fp8 only) sf: gathers the 1x128 block scales into the block-major x_perm_sf.
+//  4. copy:    (only when x_perm is wanted) one block per token copies its row once from x
+//              to its K rows of x_perm with 16-byte loads and stores (the HBM-bound part).
+//  (fp8 only) sf: transposes the 1x128 block scales of the rows into the block-major
+//              x_perm_sf through LDS, with or without the row copy.
+// With routing in the same call (moe_route_permute), step 1 is route_hist_kernel: top-k of
+// each token of a chunk and the chunk's histogram in one kernel.
 // Padded variant (MoonEP "API walkthrough": token_padding and padded cu_seqlens;
 // "Distributed expert parallelism", "Static-capacity versus dropless dispatch"): every
 // group is rounded up to a multiple of `pad` rows inside a static buffer of
