@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--settle-ms", type=float, default=100.0,
                     help="untimed repetitions for at least this long before each timed region")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="steps timed one at a time after evicting the caches (0: skip)")
     ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--maxvio", type=float, default=1.0, help="skew target for c4")
     ap.add_argument("--cpu-sample-experts", type=int, default=0,
@@ -288,6 +290,25 @@ def main():
         graph_check = bool(torch.equal(out, eager_out)) if not scatter else \
             float((out.float() - eager_out.float()).abs().max() / eager_out.float().abs().max().clamp_min(1e-30))
     ms_step = elapsed * 1e3 / args.steps
+    # Cold-cache step time, reported beside the headline: each step replayed alone right after
+    # a 1 GiB read, which evicts the 256 MB memory-side cache (MALL) and the L2s, so nothing the
+    # previous step touched is served from them. Median over the steps; one replay per event
+    # pair, so the graph's launch is inside each sample.
+    cold_ms = None
+    if not args.no_graph and args.cold_steps > 0:
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        samples = []
+        for _ in range(args.cold_steps):
+            flush.sum()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            graph.replay()
+            b.record()
+            torch.cuda.synchronize()
+            samples.append(a.elapsed_time(b))
+        cold_ms = float(statistics.median(samples))
+        del flush
     # per stage: total event time of the stage in a step (the scatter combine has two parts),
     # median over the timed steps
     def per_step(name):
@@ -356,6 +377,7 @@ def main():
         "settle_ms": args.settle_ms,
         "ms_per_step": ms_step,
         "ms_per_step_eager": ms_step_eager,
+        "ms_per_step_cold_cache": cold_ms,
         "timing": "HIP graph replay of the whole step" if not args.no_graph else "eager launches",
         "graph_replay_matches_eager": graph_check,
         "higher_is_better": True,
