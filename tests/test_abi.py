@@ -101,6 +101,8 @@ def test_permute_argument_checks():
     _expect(moe.MOE_EUNSUPPORTED, f, *a)
     a = list(args); a[2] = moe.MOE_FP8_E4M3; a[6] = 128                  # fp8 needs scales
     _expect(moe.MOE_EINVAL, f, *a)
+    a = list(args); a[2] = moe.MOE_FP8_E4M3; a[6] = 128; a[14] = None; a[15] = 16
+    _expect(moe.MOE_EINVAL, f, *a)                                       # permuted scales need x_sf
     a = list(args); a[0] = None
     _expect(moe.MOE_EINVAL, f, *a)
 
