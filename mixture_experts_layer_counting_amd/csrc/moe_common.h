@@ -145,14 +145,17 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
   return sgn | code;
 }
 
-// Scale of a 1x128 block: the smallest power of two s with 448 s >= amax (amax = 0 -> 1).
+// Scale of a 1x128 block: the smallest power of two s with 448 s >= amax, at least 2^-127
+// (the smallest e8m0 value, so pow2_to_e8m0 gives byte 0 for it and 1 / s = 2^127 stays
+// finite); amax = 0 -> 1. With amax = m 2^ea, m in [0.5, 1) (frexp is exact, subnormals
+// included) and 448 = 0.875 2^9: s = 2^(ea - 9) when m <= 0.875, else 2^(ea - 8). No division,
+// so nothing underflows for tiny blocks; the exponent is clamped before ldexp, so s is exact.
 __device__ __forceinline__ float fp8_pow2_scale(float amax) {
   if (!(amax > 0.f)) return 1.0f;
-  int ex;
-  const float mant = __builtin_frexpf(amax / 448.0f, &ex);  // amax/448 = mant * 2^ex
-  float s = __builtin_ldexpf(1.0f, mant == 0.5f ? ex - 1 : ex);
-  if (448.0f * s < amax) s *= 2.0f;
-  return s;
+  int ea;
+  const float m = __builtin_frexpf(amax, &ea);
+  const int e = ea - 9 + (m > 0.875f ? 1 : 0);
+  return __builtin_ldexpf(1.0f, e < -127 ? -127 : e);
 }
 
 // Wave-uniform broadcast from lane `src`.

@@ -85,10 +85,10 @@ def decode_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """
     packed = np.asarray(packed, dtype=np.uint8)
     N, half = packed.shape
-    codes = np.empty((N, 2 * half), dtype=np.uint8)
-    codes[:, 0::2] = packed & 0xF
-    codes[:, 1::2] = packed >> 4
-    vals = decode_e2m1(codes) * np.repeat(decode_e8m0(np.asarray(scales).T), 32, axis=1)
+    # the two elements of every possible byte: (low nibble, high nibble)
+    byte_vals = np.stack([decode_e2m1(np.arange(256) & 0xF), decode_e2m1(np.arange(256) >> 4)], axis=1)
+    vals = byte_vals[packed].reshape(N, 2 * half)          # [n, k]: k = 2j low, 2j+1 high
+    vals *= np.repeat(decode_e8m0(np.asarray(scales).T), 32, axis=1)
     return vals.T
 
 
@@ -118,14 +118,16 @@ def round_e4m3fn(v: np.ndarray) -> np.ndarray:
 
 
 def fp8_block_scale(amax: np.ndarray) -> np.ndarray:
-    """Smallest power of two s with 448*s >= amax (s = 1 when amax = 0)."""
+    """Smallest power of two s with 448*s >= amax, but never below 2^-127, the smallest
+    value an e8m0 scale byte can hold (OCP Microscaling v1.0, scale format E8M0), so that
+    every scale is one the block-scaled matrix instructions can take (s = 1 when amax = 0)."""
     amax = np.asarray(amax, dtype=np.float64)
     out = np.ones_like(amax)
     nz = amax > 0
     e = np.ceil(np.log2(amax[nz] / 448.0))
     e = np.where(448.0 * np.exp2(e) < amax[nz], e + 1, e)
     e = np.where(448.0 * np.exp2(e - 1) >= amax[nz], e - 1, e)
-    out[nz] = np.exp2(e)
+    out[nz] = np.exp2(np.maximum(e, -127.0))
     return out
 
 

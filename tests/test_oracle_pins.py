@@ -39,7 +39,8 @@ def test_four_rank_example_routing_counts_permutation():
 
 
 def test_four_rank_example_combine_adds_scaled_outputs():
-    """Token A's expert-1 and expert-5 outputs are scaled by A's weights and added."""
+    """Combine of the worked example: token A ends up as w_A0 * E1(A) + w_A1 * E5(A), with
+    w_A its two routing weights (accumulated, not overwritten)."""
     g = _golden("four_rank_example.json")
     rng = np.random.default_rng(1)
     H = 4
@@ -387,6 +388,22 @@ def test_bf16_decode_matches_torch():
 def test_fp8_block_scale_and_requant_identity_on_grid():
     s = O.fp8_block_scale(np.array([448.0, 449.0, 224.0, 0.0, 1.0, 448.0 * 2 ** -20]))
     assert s.tolist() == [1.0, 2.0, 0.5, 1.0, 2.0 ** -8, 2.0 ** -20]
+    # the e8m0 floor: no scale below 2^-127 (byte 0), however small the block
+    s = O.fp8_block_scale(np.array([448.0 * 2 ** -127, 448.0 * 2 ** -127 * 1.5, 2.0 ** -130, 2.0 ** -149]))
+    assert s.tolist() == [2.0 ** -127, 2.0 ** -126, 2.0 ** -127, 2.0 ** -127]
+
+
+def test_quantize_fp8_tiny_block_codes():
+    """A block far below the e8m0 range keeps the 2^-127 scale; its codes are then the
+    values times 2^127, rounded on the e4m3 grid: 2^-130 -> 2^-3 (code 0x20), 2^-137 ->
+    2^-10, which rounds to the smallest subnormal 2^-9 only from above half of it (so 0),
+    3 * 2^-138 -> 1.5 * 2^-10 (rounds to 2^-9, code 0x01), and -2^-128 -> -0.5 (0xB0)."""
+    x = np.zeros((1, 128))
+    x[0, :5] = [2.0 ** -130, 2.0 ** -137, 3 * 2.0 ** -138, -2.0 ** -128, 0.0]
+    codes, s = O.quantize_fp8_1x128(x)
+    assert s.tolist() == [[2.0 ** -127]]
+    assert codes[0, :5].tolist() == [0x20, 0x00, 0x01, 0xB0, 0x00]
+    assert np.all(codes[0, 5:] == 0)
     rng = np.random.default_rng(4)
     codes = rng.integers(0, 0x7F, size=(3, 256), dtype=np.uint8)
     codes[:, ::128] = 0x7E                          # make each block's amax exactly 448
