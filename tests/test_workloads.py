@@ -87,3 +87,46 @@ def test_numpy_bits_roundtrip():
     bits = to_numpy_bits(t)
     assert bits.dtype == np.uint16
     assert np.array_equal(O.decode_bf16(bits), t.to(torch.float64).numpy())
+
+
+def test_oracle_rows_matches_whole_layer():
+    """The row-sampling helper of the full-size GPU checks (one weight decode per expert,
+    several routings, MXFP4 experts decoded in spawned worker processes) gives the oracle
+    layer's own y_rows, h and h scales at the rows it is asked for."""
+    import os
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from _oracle_run import oracle_layer, oracle_routing, oracle_rows, rel_err, x_f64, weight_fn
+    for act, wgt in (("bf16", "bf16"), ("fp8", "mxfp4")):
+        w = gen.make(T=200, H=256, Hp=128, E=10, K=3, routing="skew", beta=0.7, act=act, wgt=wgt, cid=5)
+        ref = oracle_routing(w)
+        full = oracle_layer(w)
+        rows = [0, 5, 17, 599]
+        res = oracle_rows(w, [(ref, rows), (ref, [3, 5])], workers=2)
+        assert sorted(res[0]) == rows and sorted(res[1]) == [3, 5]
+        for r in rows:
+            assert rel_err(res[0][r][1], full["y_rows"][r]) <= 1e-12
+        assert np.array_equal(res[1][5][1], res[0][5][1])
+        if act == "fp8":
+            # h and its scales: the oracle's requantisation of the row's SwiGLU output
+            e = int(np.searchsorted(ref["cu_seqlens"], 17, side="right") - 1)
+            wg, wu, _ = weight_fn(w)(e)
+            xr = x_f64(w)[ref["row_src"][17] // w.K][None, :]
+            g, u = xr @ wg, xr @ wu
+            hq, s = O.requant_fp8_1x128(O.silu(g) * u)
+            assert rel_err(res[0][17][0], hq[0]) <= 1e-12 and np.array_equal(res[0][17][2], s[0])
+        else:
+            assert res[0][17][2] is None
+
+
+def test_with_maxvio_keeps_inputs_and_swaps_routing():
+    """A c4-shaped layer (small T and H, the calibrated skew of the full shape does not
+    apply) rebuilt for another maxvio target keeps x and the weights and takes that
+    target's logits."""
+    w = gen.make(T=64, H=128, Hp=128, E=384, K=8, routing="skew", beta=0.0, maxvio=0.2, cid=3)
+    w.T = 8192   # the calibration table is keyed by the full shape
+    w2 = gen.with_maxvio(w, 10.0)
+    assert w2.x is w.x and w2.w_gate is w.w_gate and w2.w_down is w.w_down
+    assert w2.meta["maxvio_target"] == 10.0 and w2.meta["beta"] == gen.skew_beta(8192, 384, 8, 10.0)
+    ref = gen.skew_logits(8192, 384, w2.meta["beta"], 0, 3)
+    assert np.array_equal(w2.logits.numpy(), ref)

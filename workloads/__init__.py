@@ -12,4 +12,5 @@ from .gen import (  # noqa: F401
     config,
     make,
     to_numpy_bits,
+    with_maxvio,
 )

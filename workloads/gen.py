@@ -6,10 +6,10 @@ Recipe (all draws seeded; every tensor is reproducible on its own):
   Dirichlet combine weights) use numpy PCG64 seeded by
   ``SeedSequence([seed, config_id, tensor_id, expert_id])``, so they are identical on
   every machine.
-* Stacked expert weights use a torch generator on the target device, one stream per
-  (tensor, expert), so a 34 GB weight set is drawn in HBM in well under a second.
-  The host never needs the whole set: a check that wants expert ``e`` copies back
-  exactly the bits the GPU holds.
+* Stacked expert weights use one torch generator per tensor on the target device and are
+  drawn in chunks of experts (at most 2^28 values per draw), so a 34 GB weight set takes a
+  few dozen launches and well under a second in HBM. The host never needs the whole set: a
+  check that wants expert ``e`` copies back exactly the bits the GPU holds.
 * Values are rounded once, here, to the storage format the library consumes
   (fp32, bf16 round-to-nearest-even, OCP e4m3fn with power-of-two 1x128 block scales,
   OCP MXFP4 = e2m1 codes with an e8m0 scale per 32 reduction elements). Both the HIP
@@ -126,44 +126,48 @@ def _torch_gen(device, seed, cid, tid, eid=0) -> torch.Generator:
 def _to_e4m3_blocked(x32: torch.Tensor):
     """fp32 [R, C] -> (e4m3fn codes uint8 [R, C], fp32 power-of-two scales [R, C/128]).
 
-    Scale s = 2^ceil(log2(amax/448)) per 1x128 block (amax = 0 -> s = 1), codes are
-    x/s rounded to nearest even by torch's e4m3fn cast (|x/s| <= 448 by construction).
+    Scale s = 2^ceil(log2(amax/448)) per 1x128 block, at least 2^-127 (the smallest e8m0
+    value; amax = 0 -> s = 1), codes are x/s rounded to nearest even by torch's e4m3fn cast
+    (|x/s| <= 448 by construction).
     """
     R, C = x32.shape
     blocks = x32.reshape(R, C // 128, 128)
     amax = blocks.abs().amax(dim=2)
-    ratio = amax / 448.0
-    mant, expo = torch.frexp(ratio)
-    # ceil(log2(r)): r = mant * 2^expo with mant in [0.5, 1); exact power of two -> expo-1
-    ce = torch.where(mant == 0.5, expo - 1, expo)
-    scale = torch.where(amax > 0, torch.ldexp(torch.ones_like(ratio), ce), torch.ones_like(ratio))
+    # amax = mant * 2^expo, mant in [0.5, 1), and 448 = 0.875 * 2^9: the smallest power of two
+    # s with 448 s >= amax is 2^(expo - 9) when mant <= 0.875, else 2^(expo - 8)
+    mant, expo = torch.frexp(amax)
+    ce = (expo - 9 + (mant > 0.875).to(expo.dtype)).clamp_min(-127)
+    scale = torch.where(amax > 0, torch.ldexp(torch.ones_like(amax), ce), torch.ones_like(amax))
     q = (blocks / scale.unsqueeze(2)).to(torch.float8_e4m3fn)
     return q.view(torch.uint8).reshape(R, C), scale.to(torch.float32)
 
 
 def _to_mxfp4(w_kn: torch.Tensor):
-    """Logical fp32 W [Kred, N] -> (packed bytes [N, Kred/2], e8m0 scales [Kred/32, N]).
+    """Logical fp32 W [..., Kred, N] -> (packed bytes [..., N, Kred/2], e8m0 scales
+    [..., Kred/32, N]); leading dimensions (a chunk of experts) are carried through.
 
     OCP MX: per 32 reduction elements X = 2^(floor(log2 amax) - 2); element codes are
     e2m1 round-to-nearest-even of w/X, saturating at 6; amax = 0 -> scale byte 0.
     """
-    Kred, N = w_kn.shape
-    w = w_kn.t().reshape(N, Kred // 32, 32)
-    amax = w.abs().amax(dim=2)
+    *lead, Kred, N = w_kn.shape
+    w = w_kn.transpose(-1, -2).reshape(*lead, N, Kred // 32, 32)
+    amax = w.abs().amax(dim=-1)
     _, expo = torch.frexp(amax)                 # amax = m * 2^expo, m in [0.5, 1)
     shared = expo.to(torch.int32) - 1 - 2       # floor(log2 amax) - emax(e2m1)
     sbyte = torch.where(amax > 0, shared + 127, torch.zeros_like(shared)).clamp(0, 254)
     X = torch.ldexp(torch.ones_like(amax), sbyte.to(torch.int32) - 127)
-    v = w / X.unsqueeze(2)
+    v = w / X.unsqueeze(-1)
+    del w
     a = v.abs()
     # e2m1 magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6; ">=" where a tie rounds up to the even code
-    mag = ((a > 0.25).to(torch.uint8) + (a >= 0.75).to(torch.uint8) + (a > 1.25).to(torch.uint8)
-           + (a >= 1.75).to(torch.uint8) + (a > 2.5).to(torch.uint8) + (a >= 3.5).to(torch.uint8)
-           + (a > 5.0).to(torch.uint8))
+    mag = (a > 0.25).to(torch.uint8)
+    for bound, ge in ((0.75, True), (1.25, False), (1.75, True), (2.5, False), (3.5, True), (5.0, False)):
+        mag += (a >= bound) if ge else (a > bound)
+    del a
     code = mag | ((v < 0).to(torch.uint8) << 3)
-    code = code.reshape(N, Kred // 2, 2)
-    packed = code[:, :, 0] | (code[:, :, 1] << 4)
-    return packed.contiguous(), sbyte.to(torch.uint8).t().contiguous()
+    code = code.reshape(*lead, N, Kred // 2, 2)
+    packed = code[..., 0] | (code[..., 1] << 4)
+    return packed.contiguous(), sbyte.to(torch.uint8).transpose(-1, -2).contiguous()
 
 
 # ----------------------------------------------------------------------------- routing inputs
@@ -186,36 +190,48 @@ def skew_logits(T: int, E: int, beta: float, seed: int = 0, cid: int = 3) -> np.
 
 
 # ----------------------------------------------------------------------------- weights
+_CHUNK_VALUES = 1 << 28   # fp32 values drawn per launch (1 GiB)
+
+
+def _weight_chunks(device, seed, cid, E, H, Hp):
+    """(tensor index, first expert, fp32 chunk [n, rows, cols]) for gate, up and down, drawn
+    N(0, 1/fan_in) from one generator per tensor, experts in order, a chunk of experts per
+    draw (fan_in = H for gate/up, Hp for down)."""
+    per = max(1, _CHUNK_VALUES // (H * Hp))
+    for i, (tid, shp, std) in enumerate(((2, (H, Hp), 1.0 / math.sqrt(H)),
+                                         (3, (H, Hp), 1.0 / math.sqrt(H)),
+                                         (4, (Hp, H), 1.0 / math.sqrt(Hp)))):
+        g = _torch_gen(device, seed, cid, tid)
+        for e0 in range(0, E, per):
+            n = min(per, E - e0)
+            yield i, e0, torch.randn((n, *shp), generator=g, device=device).mul_(std)
+
+
 def _draw_weights(device, seed, cid, E, H, Hp, wgt):
     """Stacked gate/up [E,H,Hp] and down [E,Hp,H] weights, N(0, 1/fan_in)."""
-    std_gu = 1.0 / math.sqrt(H)
-    std_d = 1.0 / math.sqrt(Hp)
     if wgt in ("f32", "bf16"):
         dt = torch.float32 if wgt == "f32" else torch.bfloat16
-        wg = torch.empty((E, H, Hp), dtype=dt, device=device)
-        wu = torch.empty((E, H, Hp), dtype=dt, device=device)
-        wd = torch.empty((E, Hp, H), dtype=dt, device=device)
-        for e in range(E):
-            for tid, dst, shp, std in ((2, wg, (H, Hp), std_gu), (3, wu, (H, Hp), std_gu),
-                                       (4, wd, (Hp, H), std_d)):
-                g = _torch_gen(device, seed, cid, tid, e)
-                dst[e].copy_(torch.randn(shp, generator=g, device=device) * std)
-        return wg, wu, wd, None, None, None
+        out = (torch.empty((E, H, Hp), dtype=dt, device=device),
+               torch.empty((E, H, Hp), dtype=dt, device=device),
+               torch.empty((E, Hp, H), dtype=dt, device=device))
+        for i, e0, chunk in _weight_chunks(device, seed, cid, E, H, Hp):
+            out[i][e0:e0 + chunk.shape[0]].copy_(chunk)      # bf16: round to nearest even
+            del chunk
+        return (*out, None, None, None)
     if wgt == "mxfp4":
-        wg = torch.empty((E, Hp, H // 2), dtype=torch.uint8, device=device)
-        wu = torch.empty((E, Hp, H // 2), dtype=torch.uint8, device=device)
-        wd = torch.empty((E, H, Hp // 2), dtype=torch.uint8, device=device)
-        sg = torch.empty((E, H // 32, Hp), dtype=torch.uint8, device=device)
-        su = torch.empty((E, H // 32, Hp), dtype=torch.uint8, device=device)
-        sd = torch.empty((E, Hp // 32, H), dtype=torch.uint8, device=device)
-        for e in range(E):
-            for tid, dw, ds, shp, std in ((2, wg, sg, (H, Hp), std_gu), (3, wu, su, (H, Hp), std_gu),
-                                          (4, wd, sd, (Hp, H), std_d)):
-                g = _torch_gen(device, seed, cid, tid, e)
-                p, s = _to_mxfp4(torch.randn(shp, generator=g, device=device) * std)
-                dw[e].copy_(p)
-                ds[e].copy_(s)
-        return wg, wu, wd, sg, su, sd
+        packed = (torch.empty((E, Hp, H // 2), dtype=torch.uint8, device=device),
+                  torch.empty((E, Hp, H // 2), dtype=torch.uint8, device=device),
+                  torch.empty((E, H, Hp // 2), dtype=torch.uint8, device=device))
+        scales = (torch.empty((E, H // 32, Hp), dtype=torch.uint8, device=device),
+                  torch.empty((E, H // 32, Hp), dtype=torch.uint8, device=device),
+                  torch.empty((E, Hp // 32, H), dtype=torch.uint8, device=device))
+        for i, e0, chunk in _weight_chunks(device, seed, cid, E, H, Hp):
+            p, sc = _to_mxfp4(chunk)
+            del chunk
+            packed[i][e0:e0 + p.shape[0]].copy_(p)
+            scales[i][e0:e0 + p.shape[0]].copy_(sc)
+            del p, sc
+        return (*packed, *scales)
     raise ValueError(wgt)
 
 
@@ -305,6 +321,19 @@ def config(name: str, device="cpu", maxvio: Optional[float] = None, seed: int = 
     label = name if maxvio is None or name == "c5" else f"{name}_maxvio{maxvio:g}"
     return make(**s, routing=routing, beta=beta, maxvio=maxvio, seed=seed,
                 cid=_CONFIG_ID[name], device=device, name=label, shared_hs=shared_hs)
+
+
+def with_maxvio(w: Workload, maxvio: float) -> Workload:
+    """The skewed workload ``w`` (c4 shape) with the routing logits of another maxvio target:
+    same activations and weights, logits N(0,1) + the bias calibrated for ``maxvio``."""
+    if w.meta.get("routing") != "skew":
+        raise ValueError("with_maxvio needs a skew-routed workload")
+    beta = skew_beta(w.T, w.E, w.K, maxvio, lowp=(w.act == "fp8"))
+    seed, cid = w.meta["seed"], w.meta["cid"]
+    logits = torch.from_numpy(skew_logits(w.T, w.E, beta, seed, cid)).to(w.x.device)
+    meta = dict(w.meta, beta=beta, maxvio_target=maxvio)
+    return dataclasses.replace(w, logits=logits, meta=meta,
+                               name=w.name.split("_maxvio")[0] + f"_maxvio{maxvio:g}")
 
 
 def to_numpy_bits(t: Optional[torch.Tensor]) -> Optional[np.ndarray]:
