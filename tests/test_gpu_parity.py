@@ -14,7 +14,7 @@ from workloads import gen, to_numpy_bits
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 from _gpu_run import run_layer, run_steps  # noqa: E402
-from _oracle_run import oracle_layer, oracle_routing, oracle_tokens, rel_err  # noqa: E402
+from _oracle_run import oracle_layer, oracle_routing, oracle_rows, rel_err  # noqa: E402
 
 import mixture_experts_layer_counting_amd as moe  # noqa: E402
 
@@ -335,42 +335,6 @@ def test_debug_poison_leaves_no_nan():
     assert rel_err(O.decode_bf16(host(out)), ref["out"]) <= 2e-2
 
 
-# ----------------------------------------------------------------------------- full size, sampled
-
-def sampled_check(w, n_tokens=4):
-    """Full-size run: integers and x_perm in full, out[t] for a few tokens (one of them on
-    the busiest expert) from the oracle's direct expert loop."""
-    r = run_steps(w, with_row_w=False)
-    torch.cuda.synchronize()
-    ref = oracle_routing(w)
-    check_integers(r, ref, w.K)
-    check_x_perm(w, r, ref)
-    counts = ref["counts"]
-    hot = int(np.argmax(counts))
-    hot_rows = ref["row_src"][ref["cu_seqlens"][hot]:ref["cu_seqlens"][hot + 1]] // w.K
-    tokens = sorted({0, w.T - 1, int(hot_rows[0]), int(hot_rows[-1])})[:n_tokens]
-    want = oracle_tokens(w, tokens, ref)
-    out = O.decode_bf16(host(r["out"]))
-    errs = [rel_err(out[t], want[t]) for t in tokens]
-    mv = O.maxvio(counts, w.T, w.K, w.E)
-    print(f"  tokens {tokens} rel errs {[f'{e:.2e}' for e in errs]} maxvio {mv:.3f} "
-          f"rows/expert min {counts.min()} max {counts.max()}", flush=True)
-    assert max(errs) <= TOL[w.act]
-
-
-@pytest.mark.slow
-def test_c3_full_size_sampled():
-    say("c3 bf16 52 slots, full size")
-    sampled_check(gen.config("c3", device=DEV))
-
-
-@pytest.mark.slow
-@pytest.mark.parametrize("maxvio", [1.0, 20.0])
-def test_c4_full_size_sampled(maxvio):
-    say(f"c4 bf16 E=384 maxvio={maxvio}, full size")
-    sampled_check(gen.config("c4", device=DEV, maxvio=maxvio))
-
-
 # ----------------------------------------------------------------------------- fp8 x MXFP4
 
 FP8_SMALL = [
@@ -469,12 +433,6 @@ def test_bf16_several_tiles_per_block(spec):
     out, _, _ = run_layer(w)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), r["out"].view(torch.int16))
-
-
-@pytest.mark.slow
-def test_c5_full_size_sampled():
-    say("c5 fp8 x mxfp4 E=384 maxvio=1, full size")
-    sampled_check(gen.config("c5", device=DEV))
 
 
 # ----------------------------------------------------------------------------- row maps
@@ -580,28 +538,6 @@ def test_layer_scatter_combine_empty_experts_and_t0():
     assert out0.shape == (0, 256)
 
 
-def sampled_layer_check(w, combine, n_tokens=4):
-    """Full size through moe_layer_forward: out[t] for a few tokens from the oracle."""
-    out, ws, lay = run_layer(w, combine=combine)
-    torch.cuda.synchronize()
-    ref = oracle_routing(w)
-    tokens = sorted({0, 1, w.T // 2, w.T - 1})[:n_tokens]
-    want = oracle_tokens(w, tokens, ref)
-    o = decode_out(w, out)
-    errs = [rel_err(o[t], want[t]) for t in tokens]
-    print(f"  tokens {tokens} rel errs {[f'{e:.2e}' for e in errs]}", flush=True)
-    assert max(errs) <= TOL[w.act]
-
-
-@pytest.mark.slow
-@pytest.mark.parametrize("cfg", ["c3", "c5"])
-def test_full_size_layer_gather_and_scatter(cfg):
-    say(f"{cfg} full size through moe_layer_forward: gathered gate/up, both combines")
-    w = gen.config(cfg, device=DEV)
-    sampled_layer_check(w, moe.MOE_COMBINE_GATHER)
-    sampled_layer_check(w, moe.MOE_COMBINE_SCATTER_ATOMIC)
-
-
 # ----------------------------------------------------------------------------- shared expert
 
 SHARED_CASES = [
@@ -662,6 +598,13 @@ def test_quantize_fp8_bit_exact(dt):
     x[5, :128] = 0.0                     # all-zero block
     x[6, 128:256] = 1e-30                # tiny block (subnormal scale range)
     x[7, 0] = 448.0 * 2 ** 10            # block amax exactly on a power-of-two boundary
+    # blocks below the e8m0 floor (scale 2^-127): bf16 / fp32 subnormals, and one value of
+    # 2^-149 whose amax / 448 would underflow to zero
+    x[8, 256:384] = torch.randn(128, generator=g) * 2.0 ** -131
+    x[9, 384:512] = torch.randn(128, generator=g) * 2.0 ** -140
+    x[10, 128:256] = 0.0
+    x[10, 130] = 2.0 ** -149
+    x[11, 640:768] = torch.randn(128, generator=g) * 2.0 ** -120
     xt = x.to(torch.bfloat16 if dt == "bf16" else torch.float32)
     xd = xt.to(DEV)
     q = torch.empty((R, C), dtype=torch.uint8, device=DEV)
@@ -857,3 +800,115 @@ def test_layer_backward_t0():
     r = run_backward(w, dout)
     torch.cuda.synchronize()
     assert not r["dWg"].any() and not r["dWu"].any() and not r["dWd"].any()
+
+
+# ----------------------------------------------------------------------------- full size, every group
+#
+# The full-size workloads, with every step at its real shape (224-step K loops at H = 7168,
+# several tiles per block, the cross-tile prefetch tail): routing, counts, cu_seqlens, the
+# permutation and the permuted rows compared in full; y_rows compared with the oracle at the
+# first and last row of every non-empty expert group and at all K rows of 16 tokens (whose
+# out is then the oracle's combine of those rows); moe_layer_forward, the path bench.py
+# times (rows gathered from x), bitwise equal to the step-by-step path; the layer with the
+# scatter-add combine within tolerance at the same tokens. Every expert's weights are
+# decoded once per test, for all its routings.
+
+def probe_rows(ref, K, n_tokens=16, seed=0):
+    """(rows, tokens): the first and last row of every non-empty group, and all K rows of
+    the first and last token, of the tokens at both ends of the busiest and of the least busy
+    group, and of seeded random tokens up to ``n_tokens``."""
+    cu, counts, row_src = ref["cu_seqlens"], ref["counts"], ref["row_src"]
+    T = ref["pos"].shape[0]
+    rows = set()
+    for e in np.nonzero(counts)[0]:
+        rows.update((int(cu[e]), int(cu[e + 1]) - 1))
+    hot = int(np.argmax(counts))
+    cold = int(np.argmin(np.where(counts > 0, counts, np.iinfo(np.int64).max)))
+    toks = {0, T - 1}
+    for e in (hot, cold):
+        toks.update(int(row_src[r]) // K for r in (int(cu[e]), int(cu[e + 1]) - 1))
+    rng = np.random.default_rng(seed)
+    while len(toks) < min(n_tokens, T):
+        toks.add(int(rng.integers(T)))
+    toks = sorted(toks)
+    for t in toks:
+        rows.update(int(p) for p in ref["pos"][t])
+    return sorted(rows), toks
+
+
+def full_size_check(variants):
+    """``variants``: [(label, workload)], all with the same x and weights (c4's routings)."""
+    cases = []
+    for label, w in variants:
+        say(f"  {label}: steps, moe_layer_forward (gather combine and scatter-add combine)")
+        r = run_steps(w, with_row_w=False)
+        torch.cuda.synchronize()
+        ref = oracle_routing(w)
+        check_integers(r, ref, w.K)
+        check_x_perm(w, r, ref)
+        del r["x_perm"]
+        out_l, ws, _ = run_layer(w)
+        torch.cuda.synchronize()
+        assert torch.equal(out_l, r["out"]), f"{label}: moe_layer_forward differs from the steps"
+        del out_l, ws
+        out_sc, ws, _ = run_layer(w, combine=moe.MOE_COMBINE_SCATTER_ATOMIC)
+        torch.cuda.synchronize()
+        del ws
+        rows, toks = probe_rows(ref, w.K)
+        ri = torch.tensor(rows, dtype=torch.int64, device=DEV)
+        ti = torch.tensor(toks, dtype=torch.int64, device=DEV)
+        c = dict(label=label, ref=ref, rows=rows, toks=toks, y=host(r["y_rows"].index_select(0, ri)),
+                 out=host(r["out"].index_select(0, ti)), out_sc=host(out_sc.index_select(0, ti)),
+                 maxvio=O.maxvio(ref["counts"], w.T, w.K, w.E))
+        if w.act == "fp8":
+            c["h"] = host(r["h"].index_select(0, ri))
+            c["h_sf"] = host(r["h_sf"].index_select(1, ri)).T
+        cases.append(c)
+        del r, out_sc
+        torch.cuda.empty_cache()
+    w0 = variants[0][1]
+    tol = TOL[w0.act]
+    say(f"  oracle: {sum(len(c['rows']) for c in cases)} rows over {w0.E} experts")
+    want = oracle_rows(w0, [(c["ref"], c["rows"]) for c in cases])
+    for c, wr in zip(cases, want):
+        ref = c["ref"]
+        y_ref = np.stack([wr[r][1] for r in c["rows"]])
+        e_y = max(rel_err(g, f) for g, f in zip(O.decode_bf16(c["y"]), y_ref))
+        # out at the sampled tokens: the oracle's combine of the oracle's rows
+        at = {r: i for i, r in enumerate(c["rows"])}
+        pos_sub = np.array([[at[int(p)] for p in ref["pos"][t]] for t in c["toks"]])
+        out_ref = O.combine(y_ref, pos_sub, ref["topk_w"][c["toks"]])
+        e_out = max(rel_err(g, f) for g, f in zip(O.decode_bf16(c["out"]), out_ref))
+        e_sc = max(rel_err(g, f) for g, f in zip(O.decode_bf16(c["out_sc"]), out_ref))
+        msg = (f"  {c['label']}: maxvio {c['maxvio']:.3f}, rows/group {ref['counts'].min()}-"
+               f"{ref['counts'].max()}; {len(c['rows'])} rows: y rel err {e_y:.2e}; {len(c['toks'])} "
+               f"tokens: out {e_out:.2e}, scatter-add out {e_sc:.2e}")
+        if w0.act == "fp8":
+            h_ref = np.stack([wr[r][0] for r in c["rows"]])
+            s_ref = np.stack([wr[r][2] for r in c["rows"]])
+            h_got = O.decode_fp8_rows(c["h"], c["h_sf"])
+            e_h = max(rel_err(g, f) for g, f in zip(h_got, h_ref))
+            same = float((c["h_sf"].astype(np.float64) == s_ref).mean())
+            msg += f"; h rel err {e_h:.2e}, identical h scales {same:.4f}"
+            assert e_h <= tol and same >= 0.99, msg
+        print(msg, flush=True)
+        assert e_y <= tol and e_out <= tol and e_sc <= tol, msg
+
+
+@pytest.mark.slow
+def test_c3_full_size_every_group():
+    say("c3 bf16 rank share (52 slots, 65536 rows, H=7168, Hp=2048), full size")
+    full_size_check([("c3", gen.config("c3", device=DEV))])
+
+
+@pytest.mark.slow
+def test_c4_full_size_every_group_all_maxvio():
+    say("c4 bf16 T=8192 E=384 K=8, full size, maxvio 0.2 / 1 / 10 / 20 (same x and weights)")
+    base = gen.config("c4", device=DEV, maxvio=1.0)
+    full_size_check([(f"c4 maxvio {mv:g}", gen.with_maxvio(base, mv)) for mv in gen.SKEW_TARGETS])
+
+
+@pytest.mark.slow
+def test_c5_full_size_every_group():
+    say("c5 fp8 x MXFP4 T=8192 E=384 K=8 maxvio 1, full size (h checked too)")
+    full_size_check([("c5", gen.config("c5", device=DEV))])
