@@ -1,7 +1,11 @@
 """Benchmark of the MoE-layer hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c2|c3|c4|c5] [--maxvio V]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1|c2|c3|c4|c5] [--maxvio V]
                     [--combine gather|scatter] [--xperm]
+
+The default workload is the full single-GPU layer (T=8192 H=7168 H'=2048 E=384 K=8, bf16) at
+maxvio 1; the other maxvio targets (0.2, 10, 20) are timed in the same run on the same
+inputs (only the routing logits change) and reported under ``skew_sweep``.
 
 One step = one pass of the whole path over one batch of synthetic input, through the C ABI,
 in the order moe_layer_forward runs it: route -> permute metadata -> gate/up + SwiGLU with
@@ -58,8 +62,10 @@ def parse():
                     help="untimed repetitions for at least this long before each timed region")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="steps timed one at a time after evicting the caches (0: skip)")
-    ap.add_argument("--config", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
-    ap.add_argument("--maxvio", type=float, default=1.0, help="skew target for c4")
+    ap.add_argument("--config", default="c4", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--maxvio", type=float, default=1.0, help="skew target for c4 (the headline)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="c4: skip timing the other maxvio targets (0.2, 1, 10, 20) beside the headline")
     ap.add_argument("--cpu-sample-experts", type=int, default=0,
                     help="experts in the oracle timing sample (0: whole layer when it is small)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -211,9 +217,11 @@ def main():
 
     stages = ["quantize", "route", "permute", "gate_up", "down", "combine"]   # combine: acc zero + store (scatter)
     ev = {s: [] for s in stages}
+    stage_fns = {}
 
     def step(record):
         def mark(name, fn):
+            stage_fns[name] = fn
             if record:
                 a = torch.cuda.Event(enable_timing=True)
                 b = torch.cuda.Event(enable_timing=True)
@@ -309,6 +317,25 @@ def main():
             samples.append(a.elapsed_time(b))
         cold_ms = float(statistics.median(samples))
         del flush
+    # Cold-cache stage times of the HBM-bound stages: the permute (routing included when it
+    # comes from logits) and the combine, each run alone right after the same cache eviction,
+    # median over --cold-steps. The step has run before, so every input of the stage is in place.
+    stage_ms_cold = {}
+    if args.cold_steps > 0 and not scatter:
+        flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        for name in ("permute", "combine"):
+            samples = []
+            for _ in range(args.cold_steps):
+                flush.sum()
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                stage_fns[name]()
+                b.record(stream)
+                torch.cuda.synchronize()
+                samples.append(a.elapsed_time(b))
+            stage_ms_cold[name] = float(statistics.median(samples))
+        del flush
     # per stage: total event time of the stage in a step (the scatter combine has two parts),
     # median over the timed steps
     def per_step(name):
@@ -354,8 +381,10 @@ def main():
     gu_s = stage_ms["gate_up"] / 1e3
     t_mfma = gu_flops / (peak_flops * 1e12)
     t_hbm = gu_bytes / (PEAK_HBM_GBS * 1e9)
-    khash = source_hash("ffn_bf16.hip", "tile_sched.h", "moe_common.h", "lds_dma.h")
-    traffic = load_traffic("gate_up" if args.xperm else "gate_up_gather", args.config, khash)
+    kfiles = {"bf16": "ffn_bf16.hip", "fp8": "ffn_fp8.hip", "f32": "ffn_f32.hip"}[w.act]
+    khash = source_hash(kfiles, "tile_sched.h", "moe_common.h", "lds_dma.h")
+    wl_key = f"{args.config}_maxvio{args.maxvio:g}" if args.config == "c4" else args.config
+    traffic = load_traffic("gate_up" if args.xperm else "gate_up_gather", wl_key, khash)
     if t_mfma >= t_hbm:
         roof = {"bound": "mfma", "achieved": gu_flops / gu_s / 1e12, "peak": peak_flops, "unit": "TFLOP/s"}
     else:
@@ -363,7 +392,12 @@ def main():
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
     roof["kernel"] = "ffn_gate_up (grouped GEMM gate+up, SwiGLU epilogue)"
-    roof["per_launch"] = {"flops": gu_flops, "bytes": gu_bytes, "avg_ms": stage_ms["gate_up"]}
+    roof["per_launch"] = {"flops": gu_flops, "bytes": gu_bytes, "avg_ms": stage_ms["gate_up"],
+                          "mfma_time_at_peak_ms": t_mfma * 1e3, "hbm_time_at_peak_ms": t_hbm * 1e3}
+    # the other roofline beside the binding one: the kernel's rate against the MFMA peak of its
+    # input type (the metric's "% of MFMA peak") and against the HBM peak
+    roof["mfma_frac"] = gu_flops / gu_s / 1e12 / peak_flops
+    roof["hbm_frac"] = gu_bytes / gu_s / 1e9 / PEAK_HBM_GBS
 
     ffn_ms = stage_ms["gate_up"] + stage_ms["down"]
     ffn_tflops = (gu_flops + dn_flops) / (ffn_ms / 1e3) / 1e12
@@ -399,9 +433,16 @@ def main():
             "permute_gbs": perm_bytes / (stage_ms["permute"] / 1e3) / 1e9,
             "combine_gbs": comb_bytes / (stage_ms["combine"] / 1e3) / 1e9,
         },
+        "stage_ms_cold": stage_ms_cold,
+        "stage_rates_cold": {f"{k}_gbs": {"permute": perm_bytes, "combine": comb_bytes}[k] / (v / 1e3) / 1e9
+                             for k, v in stage_ms_cold.items()},
         "routing": {"maxvio": float(cnt.max() / (T * K / E) - 1.0), "active_experts": active,
                     "rows_min": int(cnt.min()), "rows_max": int(cnt.max()),
-                    "maxvio_target": w.meta.get("maxvio_target")},
+                    "maxvio_target": w.meta.get("maxvio_target"),
+                    # per-expert real rows and the rows of its group as laid out (padded when
+                    # --pad > 1): both, so padding never hides in the rates
+                    "counts": [int(v) for v in cnt],
+                    "group_rows": [int(v) for v in (cu[1:] - cu[:-1]).cpu().tolist()]},
         "roofline": roof,
     }
     if args.shared_hs:
@@ -409,8 +450,62 @@ def main():
     if args.backward and w.act == "bf16" and w.wgt == "bf16":
         line["backward"] = time_backward(w, args, moe, torch)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args, out)
+        line["cpu_baseline"] = cpu_baseline(w, args, out, y if pad == 1 else None)
+    if args.config == "c4" and not args.no_sweep:
+        line["skew_sweep"] = skew_sweep(w, args, step, graph if not args.no_graph else None, ev, counts,
+                                        stage_ms, ms_step, torch)
     print(json.dumps(line), flush=True)
+
+
+def skew_sweep(w, args, step, graph, ev, counts, stage_ms, ms_step, torch):
+    """The same layer at every maxvio target: only the routing logits change (copied into the
+    buffer the step and its graph read), x and the weights stay. Per target: the step time
+    (graph replays, as the headline), tokens/s and the per-stage times (eager pass, HIP events
+    on the launch stream). The headline target reuses the headline's figures."""
+    from workloads import gen
+    base = w.logits.clone()
+    res = {}
+    for mv in gen.SKEW_TARGETS:
+        if mv == args.maxvio:
+            cnt = counts.cpu().numpy()
+            res[f"{mv:g}"] = {"ms_per_step": ms_step, "tokens_per_s": w.T / (ms_step / 1e3),
+                              "stage_ms": {k: stage_ms[k] for k in ("permute", "gate_up", "down", "combine")},
+                              "maxvio": float(cnt.max() / (w.T * w.K / w.E) - 1.0),
+                              "rows_min": int(cnt.min()), "rows_max": int(cnt.max())}
+            continue
+        w.logits.copy_(gen.with_maxvio(w, mv).logits)
+        for _ in range(args.warmup):
+            step(False)
+        settle(lambda: step(False), args.settle_ms, torch)
+        for k in ev:
+            ev[k].clear()
+        torch.cuda.synchronize()
+        for _ in range(args.steps):
+            step(True)
+        torch.cuda.synchronize()
+        st = {}
+        for name in ("permute", "gate_up", "down", "combine"):
+            per = len(ev[name]) // args.steps
+            st[name] = float(statistics.median(
+                [sum(a.elapsed_time(b) for a, b in ev[name][i * per:(i + 1) * per]) for i in range(args.steps)]))
+        run = graph.replay if graph is not None else (lambda: step(False))
+        for _ in range(args.warmup):
+            run()
+        settle(run, args.settle_ms, torch)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            run()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        cnt = counts.cpu().numpy()
+        res[f"{mv:g}"] = {"ms_per_step": ms, "tokens_per_s": w.T / (ms / 1e3), "stage_ms": st,
+                          "maxvio": float(cnt.max() / (w.T * w.K / w.E) - 1.0),
+                          "rows_min": int(cnt.min()), "rows_max": int(cnt.max())}
+    w.logits.copy_(base)
+    ms = [v["ms_per_step"] for v in res.values()]
+    res["slowest_over_fastest"] = max(ms) / min(ms)
+    return res
 
 
 def time_fused(w, args, moe, torch):
@@ -508,9 +603,11 @@ def time_backward(w, args, moe, torch):
             "work": "forward recomputed + dgrad + wgrad (18 M H H' flops), bf16, HIP graph replay"}
 
 
-def cpu_baseline(w, args, gpu_out):
+def cpu_baseline(w, args, gpu_out, gpu_y=None):
     """The oracle, as it stands, on the host: whole layer when small, else routing + permute +
-    combine for all tokens and the FFN for a sample of experts, scaled to all experts."""
+    combine for all tokens and the FFN for a sample of experts, scaled to all experts. The
+    GPU's result is compared with the oracle's: the whole output when every expert is in the
+    sample, else the permuted rows y of the sampled experts."""
     import numpy as np
     import torch
 
@@ -537,6 +634,7 @@ def cpu_baseline(w, args, gpu_out):
     n_sample = args.cpu_sample_experts or (w.E if w.T * w.H <= 4096 * 2048 else 8)
     n_sample = min(n_sample, w.E)
     experts = None
+    sampled_rows, y_sampled = [], []
 
     def one_pass():
         """One oracle pass over the sample; returns (seconds it stands for, measured seconds, out)."""
@@ -566,6 +664,10 @@ def cpu_baseline(w, args, gpu_out):
         out = O.combine(y_rows, pos, wts)
         t3 = time.perf_counter()
         scale = w.E / len(experts)
+        sampled_rows.clear()
+        sampled_rows.extend((int(cu[e]), int(cu[e + 1])) for e in experts)
+        y_sampled.clear()
+        y_sampled.extend(y_rows[lo:hi] for lo, hi in sampled_rows)
         return (t1 - t0) + t_ffn * scale + (t3 - t2), (t1 - t0) + t_ffn + (t3 - t2), out
 
     # repeat the pass until about 10 s of host work has been measured (at most 20 passes)
@@ -587,6 +689,19 @@ def cpu_baseline(w, args, gpu_out):
         got = gpu_out.detach().cpu()
         got = got.double().numpy() if got.dtype == torch.float32 else got.to(torch.float64).numpy()
         res["gpu_vs_oracle_rel_err"] = float(np.abs(got - ref).max() / np.abs(ref).max())
+        res["gpu_vs_oracle_what"] = "out, every token"
+    elif gpu_y is not None:
+        errs, n = [], 0
+        for (lo, hi), yr in zip(sampled_rows, y_sampled):
+            if hi == lo:
+                continue
+            got = gpu_y[lo:hi].detach().cpu()
+            got = got.double().numpy() if got.dtype == torch.float32 else got.to(torch.float64).numpy()
+            errs.append(float(np.abs(got - yr).max() / np.abs(yr).max()))
+            n += hi - lo
+        res["gpu_vs_oracle_rel_err"] = max(errs) if errs else None
+        res["gpu_vs_oracle_what"] = (f"y_rows of the {len(errs)} sampled experts ({n} rows), "
+                                     "max over experts of max|err| / max|ref|")
     return res
 
 

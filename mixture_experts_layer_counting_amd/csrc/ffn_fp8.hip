@@ -30,6 +30,7 @@
 // the A descriptor's range. The optional row maps (gathering A rows and their scales from
 // the token matrix x [T, H] with x_sf [T, H/128]; scattering row_w * y into an fp32
 // accumulator) work as in the bf16 kernels.
+#include "lds_dma.h"
 #include "moe_common.h"
 #include "tile_sched.h"
 
@@ -72,47 +73,6 @@ struct F8Cfg {
   static_assert(STAGE % 16 == 0, "stage alignment");
   static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
-
-__device__ __forceinline__ i32x4_t f8_rsrc(const void* base, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(base);
-  i32x4_t r;
-  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
-  r[1] = __builtin_amdgcn_readfirstlane((int)(uint32_t)(a >> 32) & 0xffff);
-  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
-  r[3] = 0x00020000;
-  return r;
-}
-
-// Direct global->LDS 16-byte load (see ffn_bf16.hip): asm so the compiler does not wait for
-// it before unrelated LDS reads; completion is tracked with f8_wait_barrier.
-__device__ __forceinline__ void f8_dma16(i32x4_t rsrc_in, uint32_t lds_base, int voff, int soff) {
-  i32x4_t rsrc;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc_in[i]);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane((int)lds_base)), "v"(voff), "s"(rsrc),
-                 "s"(__builtin_amdgcn_readfirstlane(soff))
-               : "memory", "m0");
-}
-
-// 4-byte variant: lane l writes LDS base + 4 l.
-__device__ __forceinline__ void f8_dma4(i32x4_t rsrc_in, uint32_t lds_base, int voff, int soff) {
-  i32x4_t rsrc;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc_in[i]);
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
-               :
-               : "s"(__builtin_amdgcn_readfirstlane((int)lds_base)), "v"(voff), "s"(rsrc),
-                 "s"(__builtin_amdgcn_readfirstlane(soff))
-               : "memory", "m0");
-}
-
-// Wait until at most N of this wave's vector-memory loads are outstanding, then barrier.
-template <int N>
-__device__ __forceinline__ void f8_wait_barrier() {
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" : : "n"(N) : "memory");
-}
 
 template <bool GATED, int BN, bool MAPPED>
 __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
@@ -209,7 +169,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     d.base = base;
     // A rows of this tile (see the bf16 kernels): rows past rows_valid load past the range.
     if constexpr (GATED && MAPPED) {
-      d.rA = f8_rsrc(A, (uint32_t)maps.a_rows * (uint32_t)Kd);
+      d.rA = make_rsrc(A, (uint32_t)maps.a_rows * (uint32_t)Kd);
       // Branch-free so that the loads go out together: each reads a row of this tile (also
       // for rows past it), and the offset is chosen after the arithmetic. -1: padding row.
       int src[CF::A_LD];
@@ -224,7 +184,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
       const int ssrc = sc_row < d.rows_valid ? ssrc0 : -1;
       d.sc_voff = sf_perm ? (d.row0 + sc_row) * 4 : ssrc >= 0 ? (ssrc / maps.a_k) * nsf * 4 : (int)0x80000000u;
     } else {
-      d.rA = f8_rsrc(A + (size_t)d.row0 * Kd, (uint32_t)d.rows_valid * (uint32_t)Kd);
+      d.rA = make_rsrc(A + (size_t)d.row0 * Kd, (uint32_t)d.rows_valid * (uint32_t)Kd);
 #pragma unroll
       for (int i = 0; i < CF::A_LD; ++i) d.a_ld_off[i] = a_voff[i];
       d.sc_voff = (d.row0 + sc_row) * 4;
@@ -232,33 +192,33 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     d.nmt = __builtin_amdgcn_readfirstlane((wm * 32 < d.rows_valid) + (128 + wm * 32 < d.rows_valid));
     const size_t wbase = ((size_t)d.e * N + d.n0) * kbytes;
     const uint32_t b_rem = (uint32_t)((size_t)(N - d.n0) * kbytes);
-    d.rB0 = f8_rsrc(B0 + wbase, b_rem);
-    d.rB1 = GATED ? f8_rsrc(B1 + wbase, b_rem) : d.rB0;
+    d.rB0 = make_rsrc(B0 + wbase, b_rem);
+    d.rB1 = GATED ? make_rsrc(B1 + wbase, b_rem) : d.rB0;
     return d;
   };
   // this wave's share of stage kt of tile d, into buffer (d.base + kt) mod F8_NS
   auto issue = [&](const Tile& d, int kt) __attribute__((always_inline)) {
     const uint32_t so = smem_lds + (uint32_t)(((unsigned)(d.base + kt) % F8_NS) * CF::STAGE);
 #pragma unroll
-    for (int i = 0; i < CF::A_LD; ++i) f8_dma16(d.rA, so + (wave + 8 * i) * 1024, d.a_ld_off[i], kt * F8_BK);
+    for (int i = 0; i < CF::A_LD; ++i) lds_dma16(d.rA, so + (wave + 8 * i) * 1024, d.a_ld_off[i], kt * F8_BK);
 #pragma unroll
     for (int i = 0; i < CF::B_LD; ++i) {
       const int j = wave + 8 * i;
       const bool second = GATED && (j / (CF::B_BYTES / 1024)) != 0;
-      f8_dma16(second ? d.rB1 : d.rB0, so + CF::A_BYTES + j * 1024, b_voff[i], kt * (F8_BK / 2));
+      lds_dma16(second ? d.rB1 : d.rB0, so + CF::A_BYTES + j * 1024, b_voff[i], kt * (F8_BK / 2));
     }
     if (wave < 4) {
       // activation scales of block kt for tile rows 64 wave + lane. Plain (or gathered rows
       // with permuted scales): block-major [Kd/128][M], rows >= M read as zero, one 256-byte
       // run per wave. Gathered: x_sf [a_rows][Kd/128] of the row's token, a line per lane.
       if (GATED && MAPPED && !sf_perm)
-        f8_dma4(f8_rsrc(A_sf, (uint32_t)maps.a_rows * (uint32_t)nsf * 4u), so + CF::SF_A + wave * 256,
+        lds_dma4(make_rsrc(A_sf, (uint32_t)maps.a_rows * (uint32_t)nsf * 4u), so + CF::SF_A + wave * 256,
                 d.sc_voff, kt * 4);
       else if (GATED && MAPPED)
-        f8_dma4(f8_rsrc(maps.a_sf_perm + (size_t)kt * M, (uint32_t)M * 4u), so + CF::SF_A + wave * 256,
+        lds_dma4(make_rsrc(maps.a_sf_perm + (size_t)kt * M, (uint32_t)M * 4u), so + CF::SF_A + wave * 256,
                 d.sc_voff, 0);
       else
-        f8_dma4(f8_rsrc(A_sf + (size_t)kt * M, (uint32_t)M * 4u), so + CF::SF_A + wave * 256, d.sc_voff, 0);
+        lds_dma4(make_rsrc(A_sf + (size_t)kt * M, (uint32_t)M * 4u), so + CF::SF_A + wave * 256, d.sc_voff, 0);
     } else {
       // weight scales of k-blocks 4kt..4kt+3, LDS [nb][kb][BN]: load j covers bytes
       // 256 j .. 256 j + 255 of that block, i.e. matrix nb = j*256 / (4 BN), k-block rows of BN
@@ -268,7 +228,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
       const int kb = (byte % (4 * BN)) / BN;
       const int col = byte % BN;
       const uint8_t* sfb = (GATED && nb) ? B1_sf : B0_sf;
-      f8_dma4(f8_rsrc(sfb + ((size_t)d.e * ksf_b + 4 * (size_t)kt) * N, (uint32_t)N * 4u),
+      lds_dma4(make_rsrc(sfb + ((size_t)d.e * ksf_b + 4 * (size_t)kt) * N, (uint32_t)N * 4u),
               so + CF::SF_B + j * 256, kb * N + d.n0 + col, 0);
     }
   };
@@ -303,8 +263,8 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
         // stage kt complete for every wave; stage kt+1 (if any) may still be in flight (and
         // the previous tile's output stores, issued after both, only add to the count). The
         // barrier also means every wave is done with stage kt-1, whose buffer stage kt+2 reuses.
-        if (kt + 1 < nk) f8_wait_barrier<CF::VM_PER_STAGE>();
-        else f8_wait_barrier<0>();
+        if (kt + 1 < nk) wait_barrier<CF::VM_PER_STAGE>();
+        else wait_barrier<0>();
         if (kt + 2 < nk) issue(cur, kt + 2);
         if constexpr (MTV > 0) {
           const unsigned char* sa_l = smem + ((unsigned)(base + kt) % F8_NS) * CF::STAGE;
