@@ -129,6 +129,27 @@ MOE_API moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t a
                          int32_t* pos, int32_t* row_src, float* row_w, void* x_perm,
                          float* x_perm_sf, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_permute for callers that cannot allocate device memory or pass a workspace: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same arguments,
+ * outputs (bit for bit) and limits as moe_permute, without ws / ws_bytes: the sort's scratch
+ * (the per-chunk histograms, ceil(T/16)*E*4 bytes + 256) lives in a static 4 MiB device array
+ * of the library, one per device, held until the process ends. The call allocates nothing
+ * and enqueues kernels only.
+ *  - Returns MOE_EUNSUPPORTED, before touching the device, when ceil(T/16)*E*4 + 256 bytes
+ *    exceed 4 MiB (e.g. T = 8192 allows E <= 2047 within the E <= 1024 limit; E = 1024 allows
+ *    T <= 16368); MOE_EHIP if the scratch's device address cannot be obtained.
+ *  - Every call on one device uses that device's one array, which keeps the last call's
+ *    contents (every entry a call reads is written by that call first). Calls that can overlap
+ *    on one device (different streams without ordering, or several host threads) race on it:
+ *    order them on one stream.
+ *  - MOE_VALIDATE and MOE_DEBUG_POISON do not apply (both need host-side work). */
+MOE_API moe_status_t moe_permute_noalloc(const void* x, const float* x_sf, moe_dtype_t act,
+                                 const int32_t* topk_idx, const float* topk_w, int32_t T,
+                                 int32_t H, int32_t E, int32_t K, int32_t* counts,
+                                 int32_t* cu_seqlens, int32_t* pos, int32_t* row_src,
+                                 float* row_w, void* x_perm, float* x_perm_sf,
+                                 hipStream_t stream);
+
 /* The static-capacity (padded) variant of moe_permute (MoonEP "API walkthrough": buffer
  * token_padding and a padded cu_seqlens; "Distributed expert parallelism", "Static-capacity
  * versus dropless dispatch" and "Hidden padding in metrics"): every expert group is padded

@@ -27,7 +27,8 @@ MOE_COMBINE_GATHER, MOE_COMBINE_SCATTER_ATOMIC = range(2)
 WS_FIELDS = ("topk_idx", "topk_w", "counts", "cu_seqlens", "pos", "row_src", "row_w", "x_perm",
              "x_perm_sf", "h", "h_sf", "y_rows", "permute_scratch", "acc_f32", "x_q", "x_q_sf")
 
-EXPORTS = ("moe_route_topk", "moe_permute_workspace_bytes", "moe_permute", "moe_padded_capacity",
+EXPORTS = ("moe_route_topk", "moe_permute_workspace_bytes", "moe_permute", "moe_permute_noalloc",
+           "moe_padded_capacity",
            "moe_permute_padded", "moe_route_permute", "moe_quantize_fp8", "moe_ffn_gate_up",
            "moe_ffn_gate_up_gather", "moe_ffn_down", "moe_ffn_down_scatter",
            "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn", "moe_combine",
@@ -61,6 +62,7 @@ _SIGS = {
     "moe_route_topk": (_I, [_P, _I, _I, _I, _P, _P, _P]),
     "moe_permute_workspace_bytes": (_S, [_I, _I, _I]),
     "moe_permute": (_I, [_P, _P, _E, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
+    "moe_permute_noalloc": (_I, [_P, _P, _E, _P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P]),
     "moe_ffn_gate_up": (_I, [_P, _P, _E, _P, _I, _I, _I, _I, _P, _P, _P, _P, _E, _P, _P, _P]),
     "moe_padded_capacity": (ctypes.c_int64, [_I, _I, _I, _I]),
     "moe_permute_padded": (_I, [_P, _P, _E, _P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P,
@@ -152,6 +154,14 @@ def moe_permute(x, x_sf, act, topk_idx, topk_w, T, H, E, K, counts, cu_seqlens, 
                              _ptr(counts), _ptr(cu_seqlens), _ptr(pos), _ptr(row_src), _ptr(row_w),
                              _ptr(x_perm), _ptr(x_perm_sf), _ptr(ws), ws_bytes, _stream(stream)),
            "moe_permute")
+
+
+def moe_permute_noalloc(x, x_sf, act, topk_idx, topk_w, T, H, E, K, counts, cu_seqlens, pos, row_src,
+                        row_w, x_perm, x_perm_sf, stream=None):
+    _check(lib().moe_permute_noalloc(_ptr(x), _ptr(x_sf), act, _ptr(topk_idx), _ptr(topk_w), T, H, E, K,
+                                     _ptr(counts), _ptr(cu_seqlens), _ptr(pos), _ptr(row_src), _ptr(row_w),
+                                     _ptr(x_perm), _ptr(x_perm_sf), _stream(stream)),
+           "moe_permute_noalloc")
 
 
 def moe_padded_capacity(T, E, K, pad) -> int:

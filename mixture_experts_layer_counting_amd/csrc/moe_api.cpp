@@ -8,6 +8,7 @@
 #include <limits>
 
 #include "moe_common.h"
+#include "noalloc.h"
 
 namespace moe {
 
@@ -160,7 +161,7 @@ static moe_status_t permute_impl(const float* logits, const void* x, const float
                                  int32_t E, int32_t K, int32_t pad, int32_t* counts,
                                  int32_t* cu_seqlens, int32_t* pos, int32_t* row_src, float* row_w,
                                  void* x_perm, float* x_perm_sf, void* ws, size_t ws_bytes,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, bool noalloc = false) {
   if (T < 0 || H < 1 || E < 1 || K < 1 || pad < 1) return MOE_EINVAL;
   if (E > 1024 || K > 32) return MOE_EUNSUPPORTED;
   const int eb = act_bytes(act);
@@ -178,10 +179,19 @@ static moe_status_t permute_impl(const float* logits, const void* x, const float
   const int64_t cap = (int64_t)T * K + (int64_t)E * (pad - 1);
   if (cap > std::numeric_limits<int32_t>::max() / 2) return MOE_EUNSUPPORTED;
   const size_t need = permute_ws_bytes(T, E, K);
+  if (noalloc) {
+    // the static scratch: sizes beyond it are rejected before anything touches the device
+    if (need > kNoallocScratchBytes) return MOE_EUNSUPPORTED;
+    ws = permute_noalloc_scratch();
+    ws_bytes = kNoallocScratchBytes;
+    if (!ws) return MOE_EHIP;
+  }
   if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
-  poison(ws, ws_bytes, stream);
+  // the no-alloc variant enqueues kernels only: no poison fill, no validation (which needs
+  // a memset, a copy to the host and a stream synchronisation)
+  if (!noalloc) poison(ws, ws_bytes, stream);
   // routed here, the ids are valid and distinct: nothing to validate
-  const bool validate = !logits && env_flag("MOE_VALIDATE");
+  const bool validate = !logits && !noalloc && env_flag("MOE_VALIDATE");
   int* err = nullptr;
   // fp8: the block-major scales are written whenever x_perm_sf is given, also without x_perm
   const bool sf = act == MOE_FP8_E4M3 && x_perm_sf;
@@ -208,6 +218,15 @@ moe_status_t moe_permute(const void* x, const float* x_sf, moe_dtype_t act,
                          float* x_perm_sf, void* ws, size_t ws_bytes, hipStream_t stream) {
   return permute_impl(nullptr, x, x_sf, act, topk_idx, topk_w, T, H, E, K, 1, counts, cu_seqlens, pos,
                       row_src, row_w, x_perm, x_perm_sf, ws, ws_bytes, stream);
+}
+
+moe_status_t moe_permute_noalloc(const void* x, const float* x_sf, moe_dtype_t act,
+                                 const int32_t* topk_idx, const float* topk_w, int32_t T, int32_t H,
+                                 int32_t E, int32_t K, int32_t* counts, int32_t* cu_seqlens,
+                                 int32_t* pos, int32_t* row_src, float* row_w, void* x_perm,
+                                 float* x_perm_sf, hipStream_t stream) {
+  return permute_impl(nullptr, x, x_sf, act, topk_idx, topk_w, T, H, E, K, 1, counts, cu_seqlens, pos,
+                      row_src, row_w, x_perm, x_perm_sf, nullptr, 0, stream, /*noalloc=*/true);
 }
 
 int64_t moe_padded_capacity(int32_t T, int32_t E, int32_t K, int32_t pad) {

@@ -27,7 +27,10 @@
 // group is rounded up to a multiple of `pad` rows inside a static buffer of
 // T*K + E*(pad-1) rows. counts stay the real ones; cu_seqlens is padded; padding rows have
 // row_src = -1, row_w = 0, zero activations and scale 1.
+#include <mutex>
+
 #include "moe_common.h"
+#include "noalloc.h"
 #include "route_common.h"
 
 #include <algorithm>
@@ -356,6 +359,28 @@ __global__ __launch_bounds__(256) void permute_zero_pad_kernel(const int* __rest
   } else {
     for (int c = threadIdx.x; c < row_bytes; c += blockDim.x) dst[c] = 0;
   }
+}
+
+// Scratch for callers that cannot allocate (moe_permute_noalloc): the chunk histograms and
+// the error word live in this file-scope array instead of a caller workspace. Every device
+// the library runs on holds its own copy until the process ends. In host code the array's
+// name is a host-side stand-in, not a device address: its address on a device comes from
+// hipGetSymbolAddress, taken once per device with that device current, and only that
+// address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+void* permute_noalloc_scratch() {
+  static std::mutex mu;
+  static void* ptr[64] = {nullptr};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    ptr[dev] = p;
+  }
+  return ptr[dev];
 }
 
 size_t permute_ws_bytes(int T, int E, int K) {
