@@ -7,9 +7,11 @@
 // FMA) and is rounded once, so the output is bitwise reproducible.
 //
 // One block per token; each thread owns 16-byte column chunks and keeps the K row loads
-// of a chunk in flight together. HBM-bound: M*H*b read + T*H*b written. An optional addend
+// of two chunks in flight together; the routed rows are read with non-temporal loads. HBM-bound: M*H*b read + T*H*b written. An optional addend
 // row per token (the shared expert's output: "Mixture of Kittens", Step 1, MoE(x) =
 // SharedExpert(x) + the weighted routed sum) is added after the k sum, before the rounding.
+#include <algorithm>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -29,6 +31,36 @@ __device__ __forceinline__ void load8(const float* p, float* f) {
   f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
   f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
 }
+// The routed rows are read once: non-temporal loads, so they stream past the caches instead of
+// displacing lines that are still in use (combine 212 -> 187-192 us at T=8192, K=8, H=7168).
+// Raw 16-byte words (eight bf16 or four fp32) are held until their FMAs: the loads of several
+// rows then go out together without unpacked copies in registers.
+template <typename YT>
+struct Raw8 {
+  i32x4_t q[sizeof(YT) / 2];
+};
+template <typename YT>
+__device__ __forceinline__ Raw8<YT> load8_nt(const YT* p) {
+  Raw8<YT> r;
+#pragma unroll
+  for (int j = 0; j < (int)(sizeof(YT) / 2); ++j)
+    r.q[j] = __builtin_nontemporal_load(reinterpret_cast<const i32x4_t*>(p) + j);
+  return r;
+}
+__device__ __forceinline__ void unpack8(const Raw8<uint16_t>& r, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = __uint_as_float((uint32_t)r.q[0][i] << 16);
+    f[2 * i + 1] = __uint_as_float((uint32_t)r.q[0][i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void unpack8(const Raw8<float>& r, float* f) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = __int_as_float(r.q[0][i]);
+    f[4 + i] = __int_as_float(r.q[1][i]);
+  }
+}
 __device__ __forceinline__ void store8(uint16_t* p, const float* f) {
   int4 v;
   v.x = (int)pack_bf16x2(f[0], f[1]);
@@ -42,14 +74,16 @@ __device__ __forceinline__ void store8(float* p, const float* f) {
   reinterpret_cast<float4*>(p)[1] = make_float4(f[4], f[5], f[6], f[7]);
 }
 
-// NU: chunks per thread and pass. Two measured best at H = 7168 (c3-c5 layers: three and four
-// were no faster, and at H = 2048 a thread has only two chunks).
+// NU: chunks per thread and pass. Two measured best at H = 7168 (three and four were no
+// faster). The block has about H / 16 threads (a multiple of 64, at most 512), so one pass
+// covers a whole row at H = 7168 (448 threads).
 template <typename YT, typename OT, int KMAX, int NU = 2>
-__global__ __launch_bounds__(128) void combine_kernel(const YT* __restrict__ y_rows,
+__global__ __launch_bounds__(512) void combine_kernel(const YT* __restrict__ y_rows,
                                                       const int* __restrict__ pos,
                                                       const float* __restrict__ topk_w, int T,
                                                       int H, int K, const YT* __restrict__ add,
                                                       OT* __restrict__ out) {
+  constexpr int KG = KMAX < 8 ? KMAX : 8;   // rows whose loads go out together
   const int t = blockIdx.x;
   int p[KMAX];
   float w[KMAX];
@@ -60,7 +94,8 @@ __global__ __launch_bounds__(128) void combine_kernel(const YT* __restrict__ y_r
   }
   const int nchunk = H / 8;
   const int B = blockDim.x;
-  // NU chunks per thread and pass (NU * K row loads in flight), then one chunk at a time
+  // NU chunks per thread and pass; the loads of KG rows x NU chunks are issued before their
+  // FMAs, which then run in k order
   int c = threadIdx.x;
   for (; c + (NU - 1) * B < nchunk; c += NU * B) {
     float acc[NU][8];
@@ -69,16 +104,23 @@ __global__ __launch_bounds__(128) void combine_kernel(const YT* __restrict__ y_r
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-      if (p[k] >= 0) {
-        float v[NU][8];
+    for (int k0 = 0; k0 < KMAX; k0 += KG) {
+      Raw8<YT> v[KG][NU];
 #pragma unroll
-        for (int u = 0; u < NU; ++u) load8(y_rows + (size_t)p[k] * H + (c + u * B) * 8, v[u]);
+      for (int k = 0; k < KG; ++k)
+        if (p[k0 + k] >= 0)
 #pragma unroll
-        for (int u = 0; u < NU; ++u)
+          for (int u = 0; u < NU; ++u) v[k][u] = load8_nt(y_rows + (size_t)p[k0 + k] * H + (c + u * B) * 8);
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[u][i] = fmaf(w[k], v[u][i], acc[u][i]);
-      }
+      for (int k = 0; k < KG; ++k)
+        if (p[k0 + k] >= 0)
+#pragma unroll
+          for (int u = 0; u < NU; ++u) {
+            float f[8];
+            unpack8(v[k][u], f);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[u][i] = fmaf(w[k0 + k], f[i], acc[u][i]);
+          }
     }
     if (add) {
       float v[NU][8];
@@ -95,13 +137,19 @@ __global__ __launch_bounds__(128) void combine_kernel(const YT* __restrict__ y_r
   for (; c < nchunk; c += B) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-      if (p[k] >= 0) {
-        float v[8];
-        load8(y_rows + (size_t)p[k] * H + c * 8, v);
+    for (int k0 = 0; k0 < KMAX; k0 += KG) {
+      Raw8<YT> v[KG];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[k], v[i], acc[i]);
-      }
+      for (int k = 0; k < KG; ++k)
+        if (p[k0 + k] >= 0) v[k] = load8_nt(y_rows + (size_t)p[k0 + k] * H + c * 8);
+#pragma unroll
+      for (int k = 0; k < KG; ++k)
+        if (p[k0 + k] >= 0) {
+          float f[8];
+          unpack8(v[k], f);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[k0 + k], f[i], acc[i]);
+        }
     }
     if (add) {
       float v[8];
@@ -155,18 +203,21 @@ static moe_status_t dispatch_combine(const void* y, const int* pos, const float*
   OT* o = static_cast<OT*>(out);
   const bool vec = (H % 8 == 0) && ((uintptr_t)y % 16 == 0) && ((uintptr_t)out % 16 == 0) &&
                    ((uintptr_t)add % 16 == 0);
+  // threads: two 16-byte chunks each per pass, whole waves, 64 .. 512
+  const int nchunk = H / 8;
+  const int nb = std::min(512, std::max(64, ((nchunk + 1) / 2 + 63) / 64 * 64));
   if (!vec) {
     combine_scalar_kernel<YT, OT><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, ad, o);
   } else if (K <= 2) {
-    combine_kernel<YT, OT, 2><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, ad, o);
+    combine_kernel<YT, OT, 2><<<T, nb, 0, s>>>(yr, pos, w, T, H, K, ad, o);
   } else if (K <= 4) {
-    combine_kernel<YT, OT, 4><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, ad, o);
+    combine_kernel<YT, OT, 4><<<T, nb, 0, s>>>(yr, pos, w, T, H, K, ad, o);
   } else if (K <= 8) {
-    combine_kernel<YT, OT, 8><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, ad, o);
+    combine_kernel<YT, OT, 8><<<T, nb, 0, s>>>(yr, pos, w, T, H, K, ad, o);
   } else if (K <= 16) {
-    combine_kernel<YT, OT, 16><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, ad, o);
+    combine_kernel<YT, OT, 16><<<T, nb, 0, s>>>(yr, pos, w, T, H, K, ad, o);
   } else {
-    combine_kernel<YT, OT, 32><<<T, 128, 0, s>>>(yr, pos, w, T, H, K, ad, o);
+    combine_kernel<YT, OT, 32><<<T, nb, 0, s>>>(yr, pos, w, T, H, K, ad, o);
   }
   return launch_status();
 }
