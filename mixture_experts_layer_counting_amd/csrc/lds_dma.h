@@ -37,6 +37,19 @@ __device__ __forceinline__ void lds_dma16(i32x4_t rsrc_in, uint32_t lds_base, in
                : "memory", "m0");
 }
 
+// lds_dma16 with the non-temporal cache policy (nt): for data read once, such as an expert's
+// weight panel streamed from HBM, so that it does not displace lines that are still reused.
+__device__ __forceinline__ void lds_dma16_nt(i32x4_t rsrc_in, uint32_t lds_base, int voff, int soff) {
+  i32x4_t rsrc;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) rsrc[i] = __builtin_amdgcn_readfirstlane(rsrc_in[i]);
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen nt lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane((int)lds_base)), "v"(voff), "s"(rsrc),
+                 "s"(__builtin_amdgcn_readfirstlane(soff))
+               : "memory", "m0");
+}
+
 // Direct global->LDS load of 4 bytes per lane (buffer_load_dword ... lds): lane l's dword lands
 // at lds_base + 4*l; offsets past the descriptor's range write zeros. Counted in vmcnt like
 // lds_dma16.

@@ -276,9 +276,11 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
 }
 
 // Copy each token row once from x to its K rows of x_perm (16-byte, 4-byte or 1-byte
-// accesses). One block per token keeps every CU busy on this HBM-bound copy.
+// accesses). One block per token keeps every CU busy on this HBM-bound copy; the block has a
+// thread per vector of the row (up to 1024), so a row is one pass (T=8192 K=8, 14 KiB rows:
+// 194 -> 178 us, 5.95 TB/s, against 256 threads; non-temporal stores were slower).
 template <int VB>
-__global__ __launch_bounds__(256) void permute_copy_kernel(const unsigned char* __restrict__ x,
+__global__ __launch_bounds__(1024) void permute_copy_kernel(const unsigned char* __restrict__ x,
                                                            const int* __restrict__ pos, int K,
                                                            unsigned char* __restrict__ x_perm,
                                                            int row_bytes) {
@@ -423,12 +425,15 @@ moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes,
   if (T > 0 && x_perm) {
     const bool a16 = (row_bytes % 16 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)x_perm % 16 == 0);
     const bool a4 = (row_bytes % 4 == 0) && ((uintptr_t)x % 4 == 0) && ((uintptr_t)x_perm % 4 == 0);
+    const int vb = a16 ? 16 : a4 ? 4 : 1;
+    // a thread per vector, whole waves, at least K (the block stages pos[t, 0..K-1])
+    const int nt = std::min(1024, std::max(64, (row_bytes / vb + 63) / 64 * 64));
     if (a16)
-      permute_copy_kernel<16><<<T, 256, 0, s>>>(xb, pos, K, xp, row_bytes);
+      permute_copy_kernel<16><<<T, nt, 0, s>>>(xb, pos, K, xp, row_bytes);
     else if (a4)
-      permute_copy_kernel<4><<<T, 256, 0, s>>>(xb, pos, K, xp, row_bytes);
+      permute_copy_kernel<4><<<T, nt, 0, s>>>(xb, pos, K, xp, row_bytes);
     else
-      permute_copy_kernel<1><<<T, 256, 0, s>>>(xb, pos, K, xp, row_bytes);
+      permute_copy_kernel<1><<<T, nt, 0, s>>>(xb, pos, K, xp, row_bytes);
   }
   if (T > 0 && x_perm && pad > 1)
     permute_zero_pad_kernel<<<cap, 256, 0, s>>>(row_src, cu_seqlens, E, xp, row_bytes);
