@@ -464,10 +464,11 @@ def skew_sweep(w, args, step, graph, ev, counts, stage_ms, ms_step, torch):
     on the launch stream). The headline target reuses the headline's figures."""
     from workloads import gen
     base = w.logits.clone()
+    head_cnt = counts.cpu().numpy()          # the headline routing, before any target replaces it
     res = {}
     for mv in gen.SKEW_TARGETS:
         if mv == args.maxvio:
-            cnt = counts.cpu().numpy()
+            cnt = head_cnt
             res[f"{mv:g}"] = {"ms_per_step": ms_step, "tokens_per_s": w.T / (ms_step / 1e3),
                               "stage_ms": {k: stage_ms[k] for k in ("permute", "gate_up", "down", "combine")},
                               "maxvio": float(cnt.max() / (w.T * w.K / w.E) - 1.0),
