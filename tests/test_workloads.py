@@ -120,13 +120,14 @@ def test_oracle_rows_matches_whole_layer():
 
 
 def test_with_maxvio_keeps_inputs_and_swaps_routing():
-    """A c4-shaped layer (small T and H, the calibrated skew of the full shape does not
-    apply) rebuilt for another maxvio target keeps x and the weights and takes that
-    target's logits."""
-    w = gen.make(T=64, H=128, Hp=128, E=384, K=8, routing="skew", beta=0.0, maxvio=0.2, cid=3)
-    w.T = 8192   # the calibration table is keyed by the full shape
+    """A layer of the full-size routing shape (T=8192, E=384, K=8; small H and H') rebuilt
+    for another maxvio target keeps x and the weights and takes that target's logits."""
+    w = gen.make(T=8192, H=128, Hp=128, E=384, K=8, routing="skew", beta=0.0, maxvio=0.2, cid=3)
     w2 = gen.with_maxvio(w, 10.0)
     assert w2.x is w.x and w2.w_gate is w.w_gate and w2.w_down is w.w_down
     assert w2.meta["maxvio_target"] == 10.0 and w2.meta["beta"] == gen.skew_beta(8192, 384, 8, 10.0)
     ref = gen.skew_logits(8192, 384, w2.meta["beta"], 0, 3)
     assert np.array_equal(w2.logits.numpy(), ref)
+    idx, _ = O.route_topk(ref, 8)
+    counts, _ = O.count_offsets(idx, 384)
+    assert abs(O.maxvio(counts, 8192, 8, 384) - 10.0) <= 0.1
