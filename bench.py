@@ -83,6 +83,10 @@ def parse():
                     help="time eager launches instead of replays of the step captured as a HIP graph")
     ap.add_argument("--backward", action="store_true",
                     help="also time moe_layer_backward (bf16 layers), reported under 'backward'")
+    ap.add_argument("--ffn", default="auto", choices=["auto", "two", "fused"],
+                    help="bf16: gate/up and down as two persistent launches or as one "
+                         "(moe_grouped_ffn_fused, reported as stage 'ffn'); auto picks as "
+                         "moe_layer_forward does: one launch when T*K <= 256*E")
     ap.add_argument("--xperm", action="store_true",
                     help="materialise x_perm in the permute instead of gathering rows in gate/up")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -212,10 +216,21 @@ def main():
     acc = (out if w.out == "f32" else torch.empty((T, H), **f32)) if scatter else None
     nws = moe.moe_permute_workspace_bytes(T, E, K)
     ws = torch.empty(nws, dtype=torch.uint8, device=dev)
+    if args.ffn == "auto":
+        args.ffn = "fused" if (w.act == "bf16" and not scatter and not args.xperm and pad == 1
+                               and M <= 256 * E and H % 256 == 0 and Hp % 128 == 0
+                               and min(H, Hp) >= 256) else "two"
+    fused = args.ffn == "fused"
+    if fused:
+        if w.act != "bf16" or scatter or args.xperm or pad != 1:
+            sys.exit("bench.py: --ffn fused takes the bf16 layer with gathered rows and the gather combine")
+        nws_f = moe.moe_grouped_ffn_fused_workspace_bytes(M, E, Hp)
+        ws_f = torch.empty(nws_f, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
 
-    stages = ["quantize", "route", "permute", "gate_up", "down", "combine"]   # combine: acc zero + store (scatter)
+    # combine: acc zero + store (scatter); ffn: gate/up and down as one launch (--ffn fused)
+    stages = ["quantize", "route", "permute", "gate_up", "down", "ffn", "combine"]
     ev = {s: [] for s in stages}
     stage_fns = {}
 
@@ -241,6 +256,12 @@ def main():
             mark("permute", lambda: moe.moe_permute_padded(w.x, w.x_sf, DT[w.act], topk_idx, topk_w, T, H, E,
                                                            K, pad, counts, cu, pos, row_src, row_w, x_perm,
                                                            x_perm_sf, ws, nws, None))
+        if fused:
+            mark("ffn", lambda: moe.moe_grouped_ffn_fused(w.x, DT[w.act], row_src, T, K, cu, M, E, H, Hp,
+                                                          w.w_gate, w.w_up, w.w_down, DT[w.wgt], y, DT[yf],
+                                                          ws_f, nws_f, None))
+            mark("combine", lambda: moe.moe_combine(y, DT[yf], pos, topk_w, T, H, K, out, DT[w.out], None))
+            return
         if args.xperm:
             mark("gate_up", lambda: moe.moe_ffn_gate_up(x_perm, x_perm_sf, DT[w.act], cu, MR, E, H, Hp,
                                                         w.w_gate, w.w_up, w.sf_gate, w.sf_up,
@@ -378,29 +399,41 @@ def main():
     else:
         comb_bytes = M * H * yb + T * H * ob
     peak_flops = {"f32": PEAK_FP32_TFLOPS, "bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS}[w.act]
-    gu_s = stage_ms["gate_up"] / 1e3
-    t_mfma = gu_flops / (peak_flops * 1e12)
-    t_hbm = gu_bytes / (PEAK_HBM_GBS * 1e9)
-    kfiles = {"bf16": "ffn_bf16.hip", "fp8": "ffn_fp8.hip", "f32": "ffn_f32.hip"}[w.act]
-    khash = source_hash(kfiles, "tile_sched.h", "moe_common.h", "lds_dma.h")
-    wl_key = f"{args.config}_maxvio{args.maxvio:g}" if args.config == "c4" else args.config
-    traffic = load_traffic("gate_up" if args.xperm else "gate_up_gather", wl_key, khash)
-    if t_mfma >= t_hbm:
-        roof = {"bound": "mfma", "achieved": gu_flops / gu_s / 1e12, "peak": peak_flops, "unit": "TFLOP/s"}
+    # the dominant kernel: gate/up, or with --ffn fused the single launch that runs gate/up and down
+    if fused:
+        k_ms, k_flops, k_bytes = stage_ms["ffn"], gu_flops + dn_flops, gu_bytes + dn_bytes
+        kname = "ffn_fused (gate/up + SwiGLU and down in one persistent launch)"
+        kfiles, tkernel = ("ffn_fused.hip",), "ffn_fused"
     else:
-        roof = {"bound": "hbm", "achieved": gu_bytes / gu_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        k_ms, k_flops, k_bytes = stage_ms["gate_up"], gu_flops, gu_bytes
+        kname = "ffn_gate_up (grouped GEMM gate+up, SwiGLU epilogue)"
+        kfiles = ({"bf16": "ffn_bf16.hip", "fp8": "ffn_fp8.hip", "f32": "ffn_f32.hip"}[w.act],)
+        tkernel = "gate_up" if args.xperm else "gate_up_gather"
+    k_s = k_ms / 1e3
+    t_mfma = k_flops / (peak_flops * 1e12)
+    t_hbm = k_bytes / (PEAK_HBM_GBS * 1e9)
+    khash = source_hash(*kfiles, "tile_sched.h", "moe_common.h", "lds_dma.h")
+    wl_key = f"{args.config}_maxvio{args.maxvio:g}" if args.config == "c4" else args.config
+    traffic = load_traffic(tkernel, wl_key, khash)
+    if t_mfma >= t_hbm:
+        roof = {"bound": "mfma", "achieved": k_flops / k_s / 1e12, "peak": peak_flops, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": k_bytes / k_s / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic
-    roof["kernel"] = "ffn_gate_up (grouped GEMM gate+up, SwiGLU epilogue)"
-    roof["per_launch"] = {"flops": gu_flops, "bytes": gu_bytes, "avg_ms": stage_ms["gate_up"],
+    roof["kernel"] = kname
+    roof["per_launch"] = {"flops": k_flops, "bytes": k_bytes, "avg_ms": k_ms,
                           "mfma_time_at_peak_ms": t_mfma * 1e3, "hbm_time_at_peak_ms": t_hbm * 1e3}
     # the other roofline beside the binding one: the kernel's rate against the MFMA peak of its
     # input type (the metric's "% of MFMA peak") and against the HBM peak
-    roof["mfma_frac"] = gu_flops / gu_s / 1e12 / peak_flops
-    roof["hbm_frac"] = gu_bytes / gu_s / 1e9 / PEAK_HBM_GBS
+    roof["mfma_frac"] = k_flops / k_s / 1e12 / peak_flops
+    roof["hbm_frac"] = k_bytes / k_s / 1e9 / PEAK_HBM_GBS
 
-    ffn_ms = stage_ms["gate_up"] + stage_ms["down"]
+    ffn_ms = stage_ms["ffn"] if fused else stage_ms["gate_up"] + stage_ms["down"]
     ffn_tflops = (gu_flops + dn_flops) / (ffn_ms / 1e3) / 1e12
+    rates = {"ffn_tflops": ffn_tflops} if fused else {
+        "gate_up_tflops": gu_flops / (stage_ms["gate_up"] / 1e3) / 1e12,
+        "down_tflops": dn_flops / (stage_ms["down"] / 1e3) / 1e12}
     line = {
         "metric": METRIC,
         "value": T * args.steps / elapsed,
@@ -422,14 +455,14 @@ def main():
         "config": {"workload": f"{args.config}: {DESCR[args.config]}", "T": T, "H": H, "Hp": Hp,
                    "E": E, "K": K, "act": w.act, "wgt": w.wgt, "combine": args.combine,
                    "x_perm": "materialised" if args.xperm else "gathered in gate/up",
+                   "ffn": "one persistent launch" if fused else "two persistent launches",
                    "pad": pad, "input": "bf16, quantised in the step" if quant else w.act},
         "rows": {"real": int(cnt.sum()), "in_groups": int(cu[-1].item()), "buffer": int(MR)},
         "grouped_ffn_tflops": ffn_tflops,
         "grouped_ffn_frac_of_mfma_peak": ffn_tflops / peak_flops,
         "stage_ms": stage_ms,
         "stage_rates": {
-            "gate_up_tflops": gu_flops / gu_s / 1e12,
-            "down_tflops": dn_flops / (stage_ms["down"] / 1e3) / 1e12,
+            **rates,
             "permute_gbs": perm_bytes / (stage_ms["permute"] / 1e3) / 1e9,
             "combine_gbs": comb_bytes / (stage_ms["combine"] / 1e3) / 1e9,
         },
@@ -445,6 +478,12 @@ def main():
                     "group_rows": [int(v) for v in (cu[1:] - cu[:-1]).cpu().tolist()]},
         "roofline": roof,
     }
+    if fused:
+        # control words of the last single-launch call (layout in include/moe.h)
+        o = (M * Hp * 2 + 255) // 256 * 256
+        c = ws_f[o:o + 64].view(torch.int32).cpu().tolist()
+        line["ffn_fused_ctl"] = {"error": c[8], "tiles": c[9], "not_prefetched": c[10],
+                                 "from_other_queues": c[11]}
     if args.shared_hs:
         line["fused"] = time_fused(w, args, moe, torch)
     if args.backward and w.act == "bf16" and w.wgt == "bf16":
@@ -455,6 +494,10 @@ def main():
         line["skew_sweep"] = skew_sweep(w, args, step, graph if not args.no_graph else None, ev, counts,
                                         stage_ms, ms_step, torch)
     print(json.dumps(line), flush=True)
+
+
+def sweep_stages(args):
+    return ("permute", "ffn", "combine") if args.ffn == "fused" else ("permute", "gate_up", "down", "combine")
 
 
 def skew_sweep(w, args, step, graph, ev, counts, stage_ms, ms_step, torch):
@@ -470,7 +513,7 @@ def skew_sweep(w, args, step, graph, ev, counts, stage_ms, ms_step, torch):
         if mv == args.maxvio:
             cnt = head_cnt
             res[f"{mv:g}"] = {"ms_per_step": ms_step, "tokens_per_s": w.T / (ms_step / 1e3),
-                              "stage_ms": {k: stage_ms[k] for k in ("permute", "gate_up", "down", "combine")},
+                              "stage_ms": {k: stage_ms[k] for k in sweep_stages(args)},
                               "maxvio": float(cnt.max() / (w.T * w.K / w.E) - 1.0),
                               "rows_min": int(cnt.min()), "rows_max": int(cnt.max())}
             continue
@@ -485,7 +528,7 @@ def skew_sweep(w, args, step, graph, ev, counts, stage_ms, ms_step, torch):
             step(True)
         torch.cuda.synchronize()
         st = {}
-        for name in ("permute", "gate_up", "down", "combine"):
+        for name in sweep_stages(args):
             per = len(ev[name]) // args.steps
             st[name] = float(statistics.median(
                 [sum(a.elapsed_time(b) for a, b in ev[name][i * per:(i + 1) * per]) for i in range(args.steps)]))

@@ -281,6 +281,39 @@ MOE_API moe_status_t moe_grouped_ffn(const void* x_perm, const float* x_perm_sf,
                              const uint8_t* sf_down, moe_dtype_t wgt, void* y_rows,
                              moe_dtype_t out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Scratch bytes moe_grouped_ffn_fused needs for M rows, E experts and intermediate size Hp:
+ * h [M, Hp] bf16 at offset 0, then the control words at offset align_up(M*Hp*2, 256). The
+ * control words are int32: [0, 8) queue counters, 8 error flag (0 when the call succeeded;
+ * 1: a readiness wait exceeded its bound of about a second, 2: a queue entry matched no tile;
+ * the results are then invalid), 9 tiles run, 10 tiles started without
+ * prefetch because their rows were not ready, 11 tiles taken from another XCD's queue, then
+ * from 16 on one readiness counter per m-tile. 0 if the arguments are invalid. */
+MOE_API size_t moe_grouped_ffn_fused_workspace_bytes(int32_t M, int32_t E, int32_t Hp);
+
+/* The bf16 grouped expert FFN in one persistent launch ("Mixture of Kittens", Step 7, the
+ * megakernel whose blocks coordinate through counters in global memory; the DeepGEMM
+ * Mega-MoE how-to, dispatch and both expert GEMMs in one kernel): gate/up + SwiGLU with rows
+ * gathered from x through row_src (as moe_ffn_gate_up_gather), then the down projection, as
+ * tiles of device-side work queues. A down tile starts as soon as the 256-row block of h it
+ * reads is complete, so the two projections overlap instead of running as two launches.
+ *     h[r] = silu(x[row_src[r]/K] . Wg[e]) * (x[row_src[r]/K] . Wu[e]),  y_rows[r] = h[r] . Wd[e]
+ * for the rows r of expert e, bitwise the same y_rows (and h) as moe_ffn_gate_up_gather
+ * followed by moe_ffn_down.
+ *  x [T, H] bf16; row_src [M] from moe_permute (-1: padding row, reads zeros); cu_seqlens
+ *  [E+1]; w_gate, w_up [E, H, Hp], w_down [E, Hp, H] bf16; y_rows [M, H] bf16 out. act, wgt
+ *  and out must be MOE_BF16 (MOE_EUNSUPPORTED otherwise). ws: moe_grouped_ffn_fused_workspace_bytes
+ *  bytes, holding h and the control words (layout above); they are reset on every call, so
+ *  calls sharing a workspace must be ordered (same stream).
+ * Needs H % 256 == 0, Hp % 128 == 0, H >= 256, Hp >= 256, E <= 1024 and T*H*2 < 2^31
+ * (MOE_EUNSUPPORTED otherwise). Two kernel launches: a reset of the control words and the
+ * persistent kernel. */
+MOE_API moe_status_t moe_grouped_ffn_fused(const void* x, moe_dtype_t act, const int32_t* row_src,
+                                   int32_t T, int32_t K, const int32_t* cu_seqlens, int32_t M,
+                                   int32_t E, int32_t H, int32_t Hp, const void* w_gate,
+                                   const void* w_up, const void* w_down, moe_dtype_t wgt,
+                                   void* y_rows, moe_dtype_t out, void* ws, size_t ws_bytes,
+                                   hipStream_t stream);
+
 /* Combine ("Distributed expert parallelism", lifecycle item 8 and "A four-rank example";
  * MoonEP "combine fwd"): out[t] = sum_{k=0..K-1} topk_w[t,k] * y_rows[pos[t,k]], summed in
  * fp32 in increasing k and rounded once to `out_dtype`; rows with pos < 0 are skipped.
@@ -310,7 +343,11 @@ MOE_API size_t moe_layer_workspace_bytes(const moe_layer_desc_t* d);
  *   -> permute metadata (counts, cu_seqlens, pos, row_src)
  *   -> gate/up + SwiGLU, its rows gathered from x (moe_ffn_gate_up_gather; with the
  *      environment variable MOE_LAYER_XPERM=1, or when T*H*bytes(act) >= 2^31, x_perm is
- *      written by moe_permute and read instead: same result, bit for bit)
+ *      written by moe_permute and read instead: same result, bit for bit). A bf16 layer
+ *      with the gather combine, on the shapes moe_grouped_ffn_fused takes and with
+ *      T*K <= 256*E (about one 256-row tile per expert), runs gate/up and down as that one
+ *      persistent launch instead (same result, bit for bit); MOE_LAYER_FUSED=1 or 0 forces
+ *      the choice.
  *   -> d->combine == MOE_COMBINE_GATHER: down -> y_rows -> moe_combine (deterministic);
  *      d->combine == MOE_COMBINE_SCATTER_ATOMIC: down with the weighted scatter-add fused
  *      into its epilogue (moe_ffn_down_scatter) into an fp32 accumulator (the output itself
@@ -389,8 +426,10 @@ MOE_API moe_status_t moe_layer_backward(const moe_layer_desc_t* d, const void* x
  * gathered gate/up reads the permuted block-major scales),
  * 9 h, 10 h_sf, 11 y_rows (gather combine), 12 permute scratch, 13 fp32 accumulator (scatter
  * combine with a BF16 output), 14 x_q and 15 x_q_sf (the quantised activations of a
- * (BF16, MXFP4) layer). Unused entries are set to SIZE_MAX. Writes n <= 16 entries;
- * returns MOE_EINVAL for an invalid `d`. Host-only; the sizes depend on MOE_LAYER_XPERM. */
+ * (BF16, MXFP4) layer), 16 the control words of the single-launch FFN (BF16 layers; layout
+ * as in moe_grouped_ffn_fused_workspace_bytes). Unused entries are set to SIZE_MAX. Writes
+ * n <= 17 entries; returns MOE_EINVAL for an invalid `d`. Host-only; the sizes depend on
+ * MOE_LAYER_XPERM. */
 MOE_API moe_status_t moe_layer_workspace_layout(const moe_layer_desc_t* d, size_t* offsets, int32_t n);
 
 /* Static text for a status code. */

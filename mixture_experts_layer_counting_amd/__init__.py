@@ -25,13 +25,15 @@ MOE_COMBINE_GATHER, MOE_COMBINE_SCATTER_ATOMIC = range(2)
 
 # offsets reported by moe_layer_workspace_layout, in order
 WS_FIELDS = ("topk_idx", "topk_w", "counts", "cu_seqlens", "pos", "row_src", "row_w", "x_perm",
-             "x_perm_sf", "h", "h_sf", "y_rows", "permute_scratch", "acc_f32", "x_q", "x_q_sf")
+             "x_perm_sf", "h", "h_sf", "y_rows", "permute_scratch", "acc_f32", "x_q", "x_q_sf",
+             "fused_ctl")
 
 EXPORTS = ("moe_route_topk", "moe_permute_workspace_bytes", "moe_permute", "moe_permute_noalloc",
            "moe_padded_capacity",
            "moe_permute_padded", "moe_route_permute", "moe_quantize_fp8", "moe_ffn_gate_up",
            "moe_ffn_gate_up_gather", "moe_ffn_down", "moe_ffn_down_scatter",
-           "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn", "moe_combine",
+           "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn",
+           "moe_grouped_ffn_fused_workspace_bytes", "moe_grouped_ffn_fused", "moe_combine",
            "moe_combine_shared", "moe_layer_workspace_bytes", "moe_layer_forward",
            "moe_layer_shared_workspace_bytes", "moe_layer_forward_shared", "moe_layer_workspace_layout",
            "moe_layer_backward_workspace_bytes", "moe_layer_backward",
@@ -78,6 +80,9 @@ _SIGS = {
     "moe_grouped_ffn_workspace_bytes": (_S, [_I, _I, _E, _E]),
     "moe_grouped_ffn": (_I, [_P, _P, _E, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _E, _P, _E,
                              _P, _S, _P]),
+    "moe_grouped_ffn_fused_workspace_bytes": (_S, [_I, _I, _I]),
+    "moe_grouped_ffn_fused": (_I, [_P, _E, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _E, _P, _E, _P,
+                                   _S, _P]),
     "moe_combine": (_I, [_P, _E, _P, _P, _I, _I, _I, _P, _E, _P]),
     "moe_layer_workspace_bytes": (_S, [ctypes.POINTER(LayerDesc)]),
     "moe_layer_forward": (_I, [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -229,6 +234,17 @@ def moe_grouped_ffn(x_perm, x_perm_sf, act, cu_seqlens, M, E, H, Hp, w_gate, w_u
                                  _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(sf_gate), _ptr(sf_up),
                                  _ptr(sf_down), wgt, _ptr(y_rows), out, _ptr(ws), ws_bytes,
                                  _stream(stream)), "moe_grouped_ffn")
+
+
+def moe_grouped_ffn_fused_workspace_bytes(M, E, Hp) -> int:
+    return int(lib().moe_grouped_ffn_fused_workspace_bytes(M, E, Hp))
+
+
+def moe_grouped_ffn_fused(x, act, row_src, T, K, cu_seqlens, M, E, H, Hp, w_gate, w_up, w_down, wgt,
+                          y_rows, out, ws, ws_bytes, stream=None):
+    _check(lib().moe_grouped_ffn_fused(_ptr(x), act, _ptr(row_src), T, K, _ptr(cu_seqlens), M, E, H, Hp,
+                                       _ptr(w_gate), _ptr(w_up), _ptr(w_down), wgt, _ptr(y_rows), out,
+                                       _ptr(ws), ws_bytes, _stream(stream)), "moe_grouped_ffn_fused")
 
 
 def moe_combine(y_rows, y_dtype, pos, topk_w, T, H, K, out, out_dtype, stream=None):

@@ -38,6 +38,10 @@ moe_status_t launch_ffn_gate_up_f32(const void*, const int*, int, int, int, int,
                                     const void*, void*, const RowMaps&, hipStream_t);
 moe_status_t launch_ffn_down_f32(const void*, const int*, int, int, int, int, const void*, void*,
                                  const RowMaps&, hipStream_t);
+size_t fused_ctl_ints(int M, int E);
+moe_status_t launch_ffn_fused_bf16(const void* x, const int* row_src, int T, int K, const int* cu, int M,
+                                   int E, int H, int Hp, const void* wg, const void* wu, const void* wd,
+                                   void* h, void* y, int* ctl, hipStream_t s);
 moe_status_t launch_acc_zero(float* acc, size_t n, hipStream_t s);
 moe_status_t launch_acc_store(const float* acc, size_t n, const void* add, moe_dtype_t add_dtype,
                               void* out, moe_dtype_t out_dtype, hipStream_t s);
@@ -118,6 +122,18 @@ static moe_status_t check_ffn_dims(Path p, int64_t M, int E, int H, int Hp, bool
     default:
       return MOE_EUNSUPPORTED;
   }
+}
+
+// Shapes the single-launch bf16 FFN (moe_grouped_ffn_fused) takes: those of both bf16 kernels
+// with K loops of at least eight 32-deep steps, and rows gathered with 32-bit offsets into x.
+static moe_status_t check_fused_dims(int64_t M, int T, int K, int E, int H, int Hp) {
+  if (T < 0 || K < 1) return MOE_EINVAL;
+  moe_status_t st = check_ffn_dims(PATH_BF16, M, E, H, Hp, true);
+  if (st == MOE_OK) st = check_ffn_dims(PATH_BF16, M, E, H, Hp, false);
+  if (st != MOE_OK) return st;
+  if (H % 256 || Hp % 128 || H < 256 || Hp < 256) return MOE_EUNSUPPORTED;
+  if ((int64_t)T * H * 2 >= (1ll << 31)) return MOE_EUNSUPPORTED;
+  return MOE_OK;
 }
 
 static void poison(void* ws, size_t bytes, hipStream_t s) {
@@ -408,6 +424,31 @@ moe_status_t moe_grouped_ffn(const void* x_perm, const float* x_perm_sf, moe_dty
                       y_rows, out, stream);
 }
 
+size_t moe_grouped_ffn_fused_workspace_bytes(int32_t M, int32_t E, int32_t Hp) {
+  if (M < 0 || E < 1 || Hp < 1) return 0;
+  return align_up((size_t)M * Hp * 2, 256) + align_up(fused_ctl_ints(M, E) * 4, 256) + 256;
+}
+
+moe_status_t moe_grouped_ffn_fused(const void* x, moe_dtype_t act, const int32_t* row_src, int32_t T,
+                                   int32_t K, const int32_t* cu_seqlens, int32_t M, int32_t E,
+                                   int32_t H, int32_t Hp, const void* w_gate, const void* w_up,
+                                   const void* w_down, moe_dtype_t wgt, void* y_rows, moe_dtype_t out,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+  if (act != MOE_BF16 || wgt != MOE_BF16 || out != MOE_BF16) return MOE_EUNSUPPORTED;
+  moe_status_t st = check_fused_dims(M, T, K, E, H, Hp);
+  if (st != MOE_OK) return st;
+  const size_t need = moe_grouped_ffn_fused_workspace_bytes(M, E, Hp);
+  if (need == 0) return MOE_EINVAL;
+  if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+  if (!cu_seqlens) return MOE_EINVAL;
+  if (M > 0 && (!x || !row_src || !w_gate || !w_up || !w_down || !y_rows)) return MOE_EINVAL;
+  poison(ws, ws_bytes, stream);
+  char* base = static_cast<char*>(ws);
+  int* ctl = reinterpret_cast<int*>(base + align_up((size_t)M * Hp * 2, 256));
+  return launch_ffn_fused_bf16(x, row_src, T, K, cu_seqlens, M, E, H, Hp, w_gate, w_up, w_down, base,
+                               y_rows, ctl, stream);
+}
+
 moe_status_t moe_combine(const void* y_rows, moe_dtype_t y_dtype, const int32_t* pos,
                          const float* topk_w, int32_t T, int32_t H, int32_t K, void* out,
                          moe_dtype_t out_dtype, hipStream_t stream) {
@@ -433,7 +474,7 @@ moe_status_t moe_combine_shared(const void* y_rows, moe_dtype_t y_dtype, const i
 
 enum {
   WS_TOPK_IDX, WS_TOPK_W, WS_COUNTS, WS_CU, WS_POS, WS_ROW_SRC, WS_ROW_W, WS_X_PERM,
-  WS_X_PERM_SF, WS_H, WS_H_SF, WS_Y, WS_PERM_SCRATCH, WS_ACC, WS_XQ, WS_XQ_SF, WS_N
+  WS_X_PERM_SF, WS_H, WS_H_SF, WS_Y, WS_PERM_SCRATCH, WS_ACC, WS_XQ, WS_XQ_SF, WS_FUSED_CTL, WS_N
 };
 
 // A BF16 layer with MXFP4 experts quantises its activations to fp8 (1x128 scales) once on
@@ -450,6 +491,23 @@ static moe_dtype_t layer_act(const moe_layer_desc_t* d) {
 // the copy, and so does an x too large for 32-bit row offsets.
 static bool layer_materializes(const moe_layer_desc_t* d) {
   return env_flag("MOE_LAYER_XPERM") || (int64_t)d->T * d->H * act_bytes(layer_act(d)) >= (1ll << 31);
+}
+
+// Whether moe_layer_forward runs the expert FFN as the single persistent launch
+// (moe_grouped_ffn_fused): bf16 layers that gather their rows and combine deterministically,
+// on the shapes that launch takes, when the average expert group fits one 256-row m-tile
+// (T*K <= 256*E). With several m-tiles per expert the two-launch schedule is faster: its
+// rounds start all m-tiles of a weight panel together, so they share the panel through L2,
+// which a dynamic queue staggers (T=8192 K=8 E=384: single launch 7.75 vs 7.83 ms per layer,
+// 8.59 vs 9.01 ms at maxvio 20; 65536 rows over 52 experts: 5.29 vs 5.07 ms). The
+// environment variable MOE_LAYER_FUSED=1 or 0 forces either path.
+static bool layer_fused(const moe_layer_desc_t* d) {
+  if (d->act != MOE_BF16 || d->wgt != MOE_BF16 || d->combine != MOE_COMBINE_GATHER) return false;
+  if (layer_materializes(d)) return false;
+  if (check_fused_dims((int64_t)d->T * d->K, d->T, d->K, d->E, d->H, d->Hp) != MOE_OK) return false;
+  const char* v = std::getenv("MOE_LAYER_FUSED");
+  if (v && v[0]) return v[0] != '0';
+  return (int64_t)d->T * d->K <= 256ll * d->E;
 }
 
 static moe_status_t layer_layout(const moe_layer_desc_t* d, size_t* off, size_t* total) {
@@ -484,6 +542,7 @@ static moe_status_t layer_layout(const moe_layer_desc_t* d, size_t* off, size_t*
     want(WS_XQ, T * H);
     want(WS_XQ_SF, T * (H / 128) * 4);
   }
+  if (d->act == MOE_BF16 && d->wgt == MOE_BF16) want(WS_FUSED_CTL, fused_ctl_ints((int)M, d->E) * 4);
   size_t o = 0;
   for (int i = 0; i < WS_N; ++i) {
     if (!used[i]) {
@@ -656,6 +715,14 @@ static moe_status_t layer_forward_impl(const moe_layer_desc_t* d, const void* x,
                             at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)), at(WS_PERM_SCRATCH),
                             perm_ws, stream);
   if (st != MOE_OK) return st;
+  if (layer_fused(d)) {
+    // gate/up and down in one persistent launch, then the deterministic combine
+    st = launch_ffn_fused_bf16(x, row_src, T, K, cu, M, E, H, Hp, w_gate, w_up, w_down, at(WS_H), at(WS_Y),
+                               static_cast<int*>(at(WS_FUSED_CTL)), stream);
+    if (st == MOE_OK) st = join_side();
+    if (st != MOE_OK) return st;
+    return launch_combine(at(WS_Y), y_dtype_of(p), pos, topk_w, T, H, K, y_s, out, d->out, stream);
+  }
   if (mat)
     st = moe_ffn_gate_up(at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)), act, cu, M, E, H, Hp,
                          w_gate, w_up, sf_gate, sf_up, d->wgt, at(WS_H), h_sf, stream);

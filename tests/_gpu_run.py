@@ -79,3 +79,28 @@ def run_layer_shared(w, combine=moe.MOE_COMBINE_GATHER, side_stream=None):
                                  w.ws_gate, w.ws_up, w.ws_down, out, ws, nbytes,
                                  side_stream=side_stream)
     return out, ws
+
+
+def run_fused(w, row_src, cu_seqlens, ws=None):
+    """moe_grouped_ffn_fused (bf16) on the permutation of run_steps: returns (y_rows, h,
+    control words as a host int64 array, workspace). ``ws`` may be given to reuse one."""
+    dev = w.x.device
+    M = w.T * w.K
+    nbytes = moe.moe_grouped_ffn_fused_workspace_bytes(M, w.E, w.Hp)
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    y = torch.empty((M, w.H), dtype=torch.bfloat16, device=dev)
+    moe.moe_grouped_ffn_fused(w.x, DT[w.act], row_src, w.T, w.K, cu_seqlens, M, w.E, w.H, w.Hp, w.w_gate,
+                              w.w_up, w.w_down, DT[w.wgt], y, DT["bf16"], ws, nbytes)
+    h_bytes = M * w.Hp * 2
+    ctl_off = (h_bytes + 255) // 256 * 256
+    h = ws[:h_bytes].view(torch.bfloat16).view(M, w.Hp)
+    ctl = ws[ctl_off:ctl_off + 16 * 4].view(torch.int32)
+    return y, h, ctl, ws
+
+
+def fused_tile_count(counts, H, Hp):
+    """Tiles of the single-launch FFN: per expert ceil(rows / 256) m-tiles, each with Hp/128
+    gate/up and H/256 down tiles."""
+    mt = sum((int(c) + 255) // 256 for c in counts)
+    return mt * (Hp // 128 + H // 256)

@@ -847,10 +847,29 @@ def full_size_check(variants):
         check_integers(r, ref, w.K)
         check_x_perm(w, r, ref)
         del r["x_perm"]
-        out_l, ws, _ = run_layer(w)
-        torch.cuda.synchronize()
-        assert torch.equal(out_l, r["out"]), f"{label}: moe_layer_forward differs from the steps"
-        del out_l, ws
+        # bf16: the layer with the FFN as two persistent launches, then as one (gate/up and
+        # down tiles from device-side queues): the same out, bit for bit, and for the single
+        # launch the same y_rows, every tile run once and no wait past its bound
+        for fused in (("0", "1") if w.act == "bf16" else (None,)):
+            if fused is not None:
+                os.environ["MOE_LAYER_FUSED"] = fused
+            try:
+                out_l, ws, lay = run_layer(w)
+            finally:
+                os.environ.pop("MOE_LAYER_FUSED", None)
+            torch.cuda.synchronize()
+            assert torch.equal(out_l, r["out"]), f"{label}: moe_layer_forward ({fused}) differs from the steps"
+            if fused == "1":
+                M = w.T * w.K
+                y_f = ws[lay["y_rows"]:lay["y_rows"] + M * w.H * 2].view(torch.bfloat16).view(M, w.H)
+                ctl = host(ws[lay["fused_ctl"]:lay["fused_ctl"] + 64].view(torch.int32))
+                print(f"  single launch: tiles {ctl[9]}, not prefetched {ctl[10]}, from other queues "
+                      f"{ctl[11]}", flush=True)
+                assert ctl[8] == 0 and ctl[9] == sum((int(c) + 255) // 256 for c in ref["counts"]) * (
+                    w.Hp // 128 + w.H // 256)
+                assert torch.equal(y_f, r["y_rows"]), f"{label}: single-launch y_rows differ"
+                del y_f
+            del out_l, ws
         out_sc, ws, _ = run_layer(w, combine=moe.MOE_COMBINE_SCATTER_ATOMIC)
         torch.cuda.synchronize()
         del ws

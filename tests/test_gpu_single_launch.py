@@ -1,0 +1,181 @@
+"""The bf16 expert FFN as one persistent launch (moe_grouped_ffn_fused, and moe_layer_forward
+with MOE_LAYER_FUSED=1) against the oracle and against the two-launch path, which it must
+match bit for bit: it runs the same tiles with the same MFMA order, only scheduled from
+device-side queues with down tiles waiting for the h rows they read."""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from workloads import gen, to_numpy_bits
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+from _gpu_run import fused_tile_count, run_fused, run_layer, run_steps  # noqa: E402
+from _oracle_run import oracle_layer, rel_err  # noqa: E402
+
+import mixture_experts_layer_counting_amd as moe  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+TOL_BF16 = 2e-2
+
+
+def say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def host(t):
+    return to_numpy_bits(t)
+
+
+def check_ctl(ctl, counts, H, Hp):
+    c = host(ctl).astype(np.int64)
+    want = fused_tile_count(counts, H, Hp)
+    print(f"  tiles {c[9]} (want {want}), not prefetched {c[10]}, from other queues {c[11]}, "
+          f"error {c[8]}", flush=True)
+    assert c[8] == 0, "a readiness wait exceeded its bound"
+    assert c[9] == want
+
+
+def check_against_steps(w, r, y, h):
+    rows = int(host(r["cu_seqlens"])[-1])
+    assert torch.equal(y[:rows].view(torch.int16), r["y_rows"][:rows].view(torch.int16))
+    assert torch.equal(h[:rows].view(torch.int16), r["h"][:rows].view(torch.int16))
+
+
+EDGE_COUNTS = [0, 1, 31, 32, 33, 255, 256, 257, 300, 511, 512, 513, 769, 2]
+
+CASES = [
+    dict(T=600, H=512, Hp=256, E=32, K=6, routing="skew", beta=3.0),     # many empty experts
+    dict(T=1000, H=256, Hp=384, E=40, K=4, routing="skew", beta=0.8),
+    dict(T=1000, H=256, Hp=256, E=1, K=1, routing="normal"),             # one queue holds all
+    dict(T=2048, H=256, Hp=256, E=1024, K=8, routing="skew", beta=0.6),  # 1024 experts
+    dict(T=4096, H=768, Hp=768, E=16, K=6, routing="normal"),            # several m-tiles each
+]
+
+
+@pytest.fixture(params=["phases", "lag1"])
+def queue_order(request):
+    """Queue order of the single launch: the default (each queue's gate/up tiles, then its
+    down tiles) and down tiles interleaved one expert behind their gate/up tiles, where many
+    of them wait for their rows."""
+    if request.param == "lag1":
+        os.environ["MOE_FUSED_LAG"] = "1"
+    yield request.param
+    os.environ.pop("MOE_FUSED_LAG", None)
+
+
+@pytest.mark.parametrize("spec", CASES, ids=lambda s: "T{T}_H{H}_Hp{Hp}_E{E}_K{K}_{routing}".format(**s))
+def test_fused_matches_oracle_and_two_launches(spec, queue_order):
+    say(f"single-launch FFN {spec}, queue order {queue_order}")
+    w = gen.make(**spec, act="bf16", wgt="bf16", out="bf16", cid=90, device=DEV)
+    r = run_steps(w)
+    y, h, ctl, _ = run_fused(w, r["row_src"], r["cu_seqlens"])
+    torch.cuda.synchronize()
+    check_ctl(ctl, host(r["counts"]), w.H, w.Hp)
+    check_against_steps(w, r, y, h)
+    ref = oracle_layer(w)
+    rows = int(ref["cu_seqlens"][-1])
+    e_y = rel_err(O.decode_bf16(host(y)[:rows]), ref["y_rows"][:rows])
+    print(f"  y_rows rel err {e_y:.3e}", flush=True)
+    assert e_y <= TOL_BF16
+
+
+def test_fused_expert_sizes_around_tile_boundaries():
+    K = 2
+    T, E = sum(EDGE_COUNTS) // K, len(EDGE_COUNTS)
+    say(f"single-launch FFN, expert sizes {EDGE_COUNTS}")
+    w = gen.make(T=T, H=512, Hp=256, E=E, K=K, act="bf16", wgt="bf16", out="bf16", routing="balanced",
+                 cid=91, device=DEV)
+    ids = np.repeat(np.arange(E), EDGE_COUNTS).reshape(K, T).T.copy().astype(np.int32)
+    wts = np.random.default_rng(91).dirichlet(np.ones(K), size=T).astype(np.float32)
+    w.topk_idx = torch.from_numpy(ids).to(DEV)
+    w.topk_w = torch.from_numpy(wts).to(DEV)
+    r = run_steps(w)
+    y, h, ctl, _ = run_fused(w, r["row_src"], r["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert np.array_equal(host(r["counts"]), np.asarray(EDGE_COUNTS))
+    check_ctl(ctl, EDGE_COUNTS, w.H, w.Hp)
+    check_against_steps(w, r, y, h)
+    ref = oracle_layer(w)
+    rows = int(ref["cu_seqlens"][-1])
+    assert rel_err(O.decode_bf16(host(y)[:rows]), ref["y_rows"][:rows]) <= TOL_BF16
+
+
+def test_fused_back_to_back_calls_share_a_workspace(queue_order):
+    """Two routings of one shape through one workspace without a host synchronisation between
+    them (the control words are reset by the launch itself), the second with the workspace
+    poisoned first: an h row read before it was written would show up as NaN."""
+    spec = dict(T=3000, H=512, Hp=512, E=24, K=4)
+    say(f"single-launch FFN, two calls on one workspace {spec}")
+    wa = gen.make(**spec, routing="skew", beta=1.5, act="bf16", wgt="bf16", out="bf16", cid=92, device=DEV)
+    wb = gen.make(**spec, routing="normal", act="bf16", wgt="bf16", out="bf16", cid=92, device=DEV)
+    wb.x, wb.w_gate, wb.w_up, wb.w_down = wa.x, wa.w_gate, wa.w_up, wa.w_down
+    ra, rb = run_steps(wa), run_steps(wb)
+    torch.cuda.synchronize()
+    assert not np.array_equal(host(ra["counts"]), host(rb["counts"]))
+    ya, ha, ctla, ws = run_fused(wa, ra["row_src"], ra["cu_seqlens"])
+    ya, ha, ctla = ya.clone(), ha.clone(), ctla.clone()
+    os.environ["MOE_DEBUG_POISON"] = "1"
+    try:
+        yb, hb, ctlb, _ = run_fused(wb, rb["row_src"], rb["cu_seqlens"], ws=ws)
+    finally:
+        del os.environ["MOE_DEBUG_POISON"]
+    torch.cuda.synchronize()
+    check_ctl(ctla, host(ra["counts"]), wa.H, wa.Hp)
+    check_ctl(ctlb, host(rb["counts"]), wb.H, wb.Hp)
+    check_against_steps(wa, ra, ya, ha)
+    check_against_steps(wb, rb, yb, hb)
+
+
+def run_layer_env(w, value):
+    os.environ["MOE_LAYER_FUSED"] = value
+    try:
+        return run_layer(w)
+    finally:
+        del os.environ["MOE_LAYER_FUSED"]
+
+
+@pytest.mark.parametrize("spec", [CASES[0], CASES[4]], ids=["E32_one_tile_per_expert", "E16_several_tiles"])
+def test_layer_single_launch_is_bitwise_two_launches(spec):
+    """moe_layer_forward with the FFN as one launch (MOE_LAYER_FUSED=1) and as two (=0), and
+    the default, which picks one launch when T*K <= 256*E."""
+    say(f"moe_layer_forward, one launch vs two {spec}")
+    w = gen.make(**spec, act="bf16", wgt="bf16", out="bf16", cid=93, device=DEV)
+    out_2, _, lay_2 = run_layer_env(w, "0")
+    out_1, ws_1, lay_1 = run_layer_env(w, "1")
+    out_d, ws_d, _ = run_layer(w)
+    torch.cuda.synchronize()
+    assert lay_1["fused_ctl"] is not None
+    c = host(ws_1[lay_1["fused_ctl"]:lay_1["fused_ctl"] + 64].view(torch.int32))
+    assert c[8] == 0 and c[9] > 0
+    assert torch.equal(out_1.view(torch.int16), out_2.view(torch.int16))
+    assert torch.equal(out_d.view(torch.int16), out_2.view(torch.int16))
+    # the default took the single launch exactly when the groups average one tile
+    cd = host(ws_d[lay_1["fused_ctl"]:lay_1["fused_ctl"] + 64].view(torch.int32))
+    assert (cd[9] > 0) == (w.T * w.K <= 256 * w.E)
+
+
+def test_fused_rejects_what_it_does_not_take():
+    say("moe_grouped_ffn_fused argument checks")
+    w = gen.make(T=64, H=512, Hp=256, E=4, K=2, routing="normal", act="bf16", wgt="bf16", out="bf16",
+                 cid=94, device=DEV)
+    r = run_steps(w)
+    M = w.T * w.K
+    n = moe.moe_grouped_ffn_fused_workspace_bytes(M, w.E, w.Hp)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    y = torch.empty((M, w.H), dtype=torch.bfloat16, device=DEV)
+    args = lambda **kw: dict(dict(x=w.x, act=moe.MOE_BF16, row_src=r["row_src"], T=w.T, K=w.K,  # noqa: E731
+                                  cu_seqlens=r["cu_seqlens"], M=M, E=w.E, H=w.H, Hp=w.Hp, w_gate=w.w_gate,
+                                  w_up=w.w_up, w_down=w.w_down, wgt=moe.MOE_BF16, y_rows=y,
+                                  out=moe.MOE_BF16, ws=ws, ws_bytes=n), **kw)
+    for kw, status in ((dict(act=moe.MOE_F32), moe.MOE_EUNSUPPORTED), (dict(H=384), moe.MOE_EUNSUPPORTED),
+                       (dict(Hp=128), moe.MOE_EUNSUPPORTED), (dict(ws_bytes=n - 1), moe.MOE_EWORKSPACE),
+                       (dict(y_rows=None), moe.MOE_EINVAL)):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_grouped_ffn_fused(**args(**kw))
+        assert ei.value.status == status
