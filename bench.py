@@ -73,8 +73,9 @@ def parse():
                     help="deterministic gather-reduce (default) or the scatter-add fused into down")
     ap.add_argument("--shared-hs", type=int, default=0,
                     help="also time moe_layer_forward and moe_layer_forward_shared (a shared "
-                         "expert of this intermediate size on a side stream); reported under "
-                         "'fused', the headline value stays the routed layer")
+                         "expert of this intermediate size on the same or a side stream); "
+                         "reported under 'layer_with_shared_expert', the headline value stays "
+                         "the routed layer")
     ap.add_argument("--pad", type=int, default=1,
                     help="static-capacity layout: pad every expert group to a multiple of this many rows")
     ap.add_argument("--bf16-input", action="store_true",
@@ -485,7 +486,7 @@ def main():
         line["ffn_fused_ctl"] = {"error": c[8], "tiles": c[9], "not_prefetched": c[10],
                                  "from_other_queues": c[11]}
     if args.shared_hs:
-        line["fused"] = time_fused(w, args, moe, torch)
+        line["layer_with_shared_expert"] = time_fused(w, args, moe, torch)
     if args.backward and w.act == "bf16" and w.wgt == "bf16":
         line["backward"] = time_backward(w, args, moe, torch)
     if not args.no_cpu_baseline:

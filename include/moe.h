@@ -379,7 +379,11 @@ MOE_API size_t moe_layer_shared_workspace_bytes(const moe_layer_desc_t* d, int32
  * ws_up [H, Hs], ws_down [Hs, H] in that format; needs the moe_ffn_gate_up / moe_ffn_down
  * limits with Hp = Hs. Its output is added in the combine (gather: moe_combine_shared;
  * scatter: to the fp32 accumulator before the rounding).
- * side_stream: when non-NULL and different from `stream`, the shared expert runs there,
+ * With the environment variable MOE_SHARED_FOLD=1, when the routed FFN runs as the single
+ * persistent launch (see moe_layer_forward) and Hs = Hp, the shared expert's tiles join that
+ * launch's queues as one more expert, alongside the routed tiles ("Mixture of Kittens",
+ * Step 9); side_stream is then not used, and the result is bitwise the same.
+ * side_stream: otherwise, when non-NULL and different from `stream`, the shared expert runs there,
  * overlapping the routed path ("Mixture of Kittens", Step 9: the shared expert FFN overlaps
  * the first dispatch); the call orders it after the work already on `stream` and makes
  * `stream` wait for it before the combine, so completion on `stream` covers everything.

@@ -71,16 +71,18 @@ constexpr int F_SPIN_MAX = 1 << 20;            // bound of one readiness wait (p
 enum { C_QCTR = 0, C_ERR = F_NQ, C_TILES, C_COLD, C_STEAL, C_HDR = 16 };
 
 // LDS after the stages: schedule arrays, the row sources of the next gathered tile, misc
+// (schedule experts: up to F_MAX_E routed ones, or F_MAX_E - 1 and the folded shared expert)
 constexpr int L_CU = 0;                                  // cu_seqlens [E+1]
-constexpr int L_MPRE = L_CU + F_MAX_E + 1;               // m-tile prefix [E+1]
-constexpr int L_SG = L_MPRE + F_MAX_E + 1;               // start of G(e) in the queues [E]
-constexpr int L_SD = L_SG + F_MAX_E;                     // start of D(e) [E]
+constexpr int L_MPRE = L_CU + F_MAX_E + 1;               // m-tile prefix [EE+1]
+constexpr int L_SG = L_MPRE + F_MAX_E + 1;               // start of G(e) in the queues [EE]
+constexpr int L_SD = L_SG + F_MAX_E;                     // start of D(e) [EE]
 constexpr int L_SRC = L_SD + F_MAX_E;                    // next tile's row sources [256]
 constexpr int L_RS = L_SRC + F_BM;                       // range starts [9]
 constexpr int L_QB = L_RS + 12;                          // queue bases [9]
 constexpr int L_TQ = L_QB + 12;                          // published next tile [4]
 constexpr int L_WSUM = L_TQ + 4;                         // scan scratch [8]
-constexpr int L_INTS = L_WSUM + 8;
+constexpr int L_SF = L_WSUM + 8;                         // shared-expert pointers [6 x 2]
+constexpr int L_INTS = L_SF + 12;
 constexpr int F_LDS = F_NS * F_STAGE + L_INTS * 4;
 static_assert(F_LDS <= 160 * 1024, "LDS budget");
 
@@ -117,11 +119,13 @@ __global__ void fused_ctl_reset_kernel(int* ctl, int n) {
 
 // x [T, H] bf16 (gathered through row_src / K); w_gate, w_up [E, H, Hp]; w_down [E, Hp, H];
 // h [M, Hp] and y [M, H] bf16; ctl: control words + ready counters (zeroed before the launch).
+// SHARED: the shared expert is folded in as expert E (sf); otherwise sf is unused.
+template <bool SHARED>
 __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
     const uint16_t* __restrict__ x, const int* __restrict__ row_src, int T, int K,
     const int* __restrict__ cu, int E, int H, int Hp, const uint16_t* __restrict__ wg,
     const uint16_t* __restrict__ wu, const uint16_t* __restrict__ wd, uint16_t* __restrict__ h,
-    uint16_t* __restrict__ y, int* __restrict__ ctl, int lag) {
+    uint16_t* __restrict__ y, int* __restrict__ ctl, int lag, SharedFold sf) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int* li = reinterpret_cast<int*>(smem + F_NS * F_STAGE);
   int* cu_l = li + L_CU;
@@ -132,6 +136,7 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
   int* qb = li + L_QB;
   int* tq = li + L_TQ;
   int* wsum = li + L_WSUM;
+  int* sfp = li + L_SF;
   int* ready = ctl + C_HDR;
 
   const int tid = threadIdx.x;
@@ -143,14 +148,25 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
   const int gw = wave & 3;
   const int ntg = Hp / 128, ntd = H / 256;           // n-tiles of a gate/up / down m-tile
   const int tgt = 8 * ntg;                           // ready count of a finished m-tile
+  // schedule experts: the E routed ones, then the shared expert (index E) when folded in
+  const int EE = E + (SHARED ? 1 : 0);
+  auto rows_of = [&](int e) { return e < E ? cu[e + 1] - cu[e] : sf.T; };
 
   // ---- schedule in LDS: m-tile prefix, ranges, queue bases, block starts ----
   for (int i = tid; i <= E; i += F_THREADS) cu_l[i] = cu[i];
+  // The shared expert's pointers wait in LDS and are read where a tile is decoded or stored,
+  // so that they do not hold scalar registers through the K loops.
+  if (SHARED && tid < 6) {
+    const void* pv[6] = {sf.x, sf.wg, sf.wu, sf.wd, sf.h, sf.y};
+    const uint64_t a = reinterpret_cast<uint64_t>(pv[tid]);
+    sfp[2 * tid] = (int)(uint32_t)a;
+    sfp[2 * tid + 1] = (int)(uint32_t)(a >> 32);
+  }
   {
     const int e0 = 2 * tid, e1 = 2 * tid + 1;
     int c0 = 0, c1 = 0;
-    if (e0 < E) c0 = (cu[e0 + 1] - cu[e0] + F_BM - 1) / F_BM;
-    if (e1 < E) c1 = (cu[e1 + 1] - cu[e1] + F_BM - 1) / F_BM;
+    if (e0 < EE) c0 = (rows_of(e0) + F_BM - 1) / F_BM;
+    if (e1 < EE) c1 = (rows_of(e1) + F_BM - 1) / F_BM;
     const int s = c0 + c1;
     const int incl = sched_wave_incl_scan(s);
     if (lane == 63) wsum[wave] = incl;
@@ -161,24 +177,24 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
       tot += wsum[w];
     }
     const int ex = base + incl - s;
-    if (e0 < E) mpre[e0] = ex;
-    if (e1 < E) mpre[e1] = ex + c0;
-    if (tid == 0) mpre[E] = tot;
+    if (e0 < EE) mpre[e0] = ex;
+    if (e1 < EE) mpre[e1] = ex + c0;
+    if (tid == 0) mpre[EE] = tot;
   }
   __syncthreads();
-  const int mtot = mpre[E];
+  const int mtot = mpre[EE];
   if (mtot == 0) return;
   // expert e belongs to range v(e) = floor(8 * midpoint of its m-tiles / mtot), nondecreasing
   auto range_of = [&](int e) { return min(F_NQ - 1, (4 * (mpre[e] + mpre[e + 1])) / mtot); };
-  for (int e = tid; e < E; e += F_THREADS) {
+  for (int e = tid; e < EE; e += F_THREADS) {
     const int ve = range_of(e), vp = e > 0 ? range_of(e - 1) : -1;
     for (int v = vp + 1; v <= ve; ++v) rs[v] = e;
-    if (e == E - 1)
-      for (int v = ve + 1; v <= F_NQ; ++v) rs[v] = E;
+    if (e == EE - 1)
+      for (int v = ve + 1; v <= F_NQ; ++v) rs[v] = EE;
   }
   __syncthreads();
   for (int v = tid; v <= F_NQ; v += F_THREADS) qb[v] = mpre[rs[v]] * (ntg + ntd);
-  for (int e = tid; e < E; e += F_THREADS) {
+  for (int e = tid; e < EE; e += F_THREADS) {
     const int v = range_of(e), a = rs[v], n = rs[v + 1] - a;
     sG[e] = mpre[e] * ntg + mpre[a + max(0, e - a - lag)] * ntd;
     sD[e] = mpre[a + min(n, e - a + lag + 1)] * ntg + mpre[e] * ntd;
@@ -205,15 +221,23 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
     int kind;        // 0 gate/up, 1 down
     int e, mt, row0, rows_valid, n0, nmt, nk;
     bool stream_b;   // gate/up of a single-m-tile expert: its panels' only reader
+    bool gathered;   // gate/up rows gathered from x through row_src (routed experts)
     i32x4_t rA, rB0, rB1;
     int a_off[F_LDP];
+  };
+  // shared-expert pointer i (0 x, 1 wg, 2 wu, 3 wd, 4 h, 5 y) from LDS
+  auto sfptr = [&](int i) __attribute__((always_inline)) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane(sfp[2 * i]);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane(sfp[2 * i + 1]);
+    return reinterpret_cast<uint16_t*>(((uint64_t)hi << 32) | lo);
   };
   // tile `id` of kind `kind` of expert e (everything but a gathered tile's A offsets)
   auto decode = [&](int id, int kind, int e) __attribute__((always_inline)) {
     Tile d;
     d.kind = kind;
     d.e = e;
-    const int gbeg = cu_l[e], rows_e = cu_l[e + 1] - gbeg;
+    const bool shared = SHARED && e >= E;   // the shared expert: rows 0..T-1 of its own h and y
+    const int gbeg = shared ? 0 : cu_l[e], rows_e = shared ? sf.T : cu_l[e + 1] - gbeg;
     const int mte = mpre[e + 1] - mpre[e];
     const int lt = id - (kind == 0 ? sG[e] : sD[e]);
     const int ntile = lt / mte, mtile = lt - ntile * mte;
@@ -222,22 +246,30 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
     d.row0 = gbeg + mtile * chunk;
     d.rows_valid = min(chunk, rows_e - mtile * chunk);
     d.stream_b = kind == 0 && mte == 1;
+    d.gathered = kind == 0 && !shared;
     if (kind == 0) {
       d.n0 = ntile * 128;
       d.nk = H / F_BK;
-      d.rA = make_rsrc(x, (uint32_t)T * (uint32_t)H * 2u);
-      const size_t woff = (size_t)e * H * Hp + d.n0;
+      const size_t woff = (shared ? 0 : (size_t)e * H * Hp) + d.n0;
       const uint32_t rem = (uint32_t)(((size_t)H * Hp - d.n0) * 2);
-      d.rB0 = make_rsrc(wg + woff, rem);
-      d.rB1 = make_rsrc(wu + woff, rem);
+      d.rB0 = make_rsrc((shared ? sfptr(1) : wg) + woff, rem);
+      d.rB1 = make_rsrc((shared ? sfptr(2) : wu) + woff, rem);
+      if (shared) {
+        // the shared expert reads the token rows in order: x row t is its row t
+        d.rA = make_rsrc(sfptr(0) + (size_t)d.row0 * H, (uint32_t)d.rows_valid * (uint32_t)H * 2u);
+#pragma unroll
+        for (int i = 0; i < F_LDP; ++i) d.a_off[i] = a_voff(i, H);
+      } else {
+        d.rA = make_rsrc(x, (uint32_t)T * (uint32_t)H * 2u);
+      }
     } else {
       d.n0 = ntile * 256;
       d.nk = Hp / F_BK;
-      d.rA = make_rsrc(h + (size_t)d.row0 * Hp, (uint32_t)d.rows_valid * (uint32_t)Hp * 2u);
+      d.rA = make_rsrc((shared ? sfptr(4) : h) + (size_t)d.row0 * Hp, (uint32_t)d.rows_valid * (uint32_t)Hp * 2u);
 #pragma unroll
       for (int i = 0; i < F_LDP; ++i) d.a_off[i] = a_voff(i, Hp);
-      const size_t woff = (size_t)e * Hp * H + d.n0;
-      d.rB0 = make_rsrc(wd + woff, (uint32_t)(((size_t)Hp * H - d.n0) * 2));
+      const size_t woff = (shared ? 0 : (size_t)e * Hp * H) + d.n0;
+      d.rB0 = make_rsrc((shared ? sfptr(3) : wd) + woff, (uint32_t)(((size_t)Hp * H - d.n0) * 2));
       d.rB1 = d.rB0;
     }
     d.nmt = __builtin_amdgcn_readfirstlane(min(F_PMT, ((d.rows_valid + 31) / 32 - hf + 1) / 2));
@@ -323,13 +355,13 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
     e = 0;
     rix = 0;
     if (id < 0) return;
-    const int eg = wave_find_le(sG, E, id);
+    const int eg = wave_find_le(sG, EE, id);
     if (eg >= 0 && id < sG[eg] + (mpre[eg + 1] - mpre[eg]) * ntg) {
       kind = 0;
       e = eg;
       return;
     }
-    const int ed = wave_find_le(sD, E, id);
+    const int ed = wave_find_le(sD, EE, id);
     const int mte = ed >= 0 ? mpre[ed + 1] - mpre[ed] : 0;
     if (mte == 0 || id >= sD[ed] + mte * ntd) {   // not a tile of the schedule (never expected)
       if (lane == 0) __hip_atomic_store(ctl + C_ERR, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -404,7 +436,7 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
     const int e0 = __builtin_amdgcn_readfirstlane(tq[2]);
     if (k0 < 0) return;
     cur = decode(id0, k0, e0);
-    if (cur.kind == 0) gather_from_global(cur);
+    if (cur.gathered) gather_from_global(cur);
     if (g0)
       for (int st = 0; st < F_NS; ++st) issue(cur, st);
   }
@@ -517,7 +549,7 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
             pf = has_next && __builtin_amdgcn_readfirstlane(tq[3]) != 0;
             if (pf) {
               nxt = decode(nx_id, nx_kind, nx_e);
-              xa = nxt.kind == 0;
+              xa = nxt.gathered;
               // group-0 wave gw loads row sources [64 gw, 64 gw + 64) of the next gathered
               // tile after stage kd + NS - 1; entries past its rows read as zeros
               if (xa && g0)
@@ -564,7 +596,8 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
     if (cur.kind == 0) {
       // h = silu(g) * u, stored write-through (agent scope) for the down tiles of other XCDs
       const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
-          h + (size_t)cur.row0 * Hp, (short)0, cur.rows_valid * Hp * 2, 0x00020000);
+          (SHARED && cur.e >= E ? sfptr(4) : h) + (size_t)cur.row0 * Hp, (short)0, cur.rows_valid * Hp * 2,
+          0x00020000);
       const int col = cur.n0 + sc * 32 + 8 * (lane >> 5);
 #pragma unroll
       for (int mt = 0; mt < F_PMT; ++mt) {
@@ -593,12 +626,13 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
         const int r = (2 * mt + hf) * 32 + (lane & 31);
         const bool ok = r < cur.rows_valid;
         const size_t ro = (size_t)(cur.row0 + (ok ? r : 0)) * H + col;
+        uint16_t* yo = SHARED && cur.e >= E ? sfptr(5) : y;
 #pragma unroll
         for (int f = 0; f < 2; ++f)
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
             const uint4 v = pack_row16(acc[f][mt], 8 * p);
-            if (ok) *reinterpret_cast<uint4*>(y + ro + f * 32 + 16 * p) = v;
+            if (ok) *reinterpret_cast<uint4*>(yo + ro + f * 32 + 16 * p) = v;
           }
       }
     }
@@ -614,7 +648,7 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
         if (lane == 0) __hip_atomic_fetch_add(ctl + C_COLD, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (nxt.kind == 1) wait_ready(mpre[nxt.e] + nxt.mt);
       }
-      if (nxt.kind == 0 && g0) gather_from_global(nxt);
+      if (nxt.gathered && g0) gather_from_global(nxt);
       f_barrier();
       cur = nxt;
       if (g0)
@@ -625,36 +659,40 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
   }
 }
 
-// Control words the fused launch needs: header + one ready counter per m-tile
-// (sum over experts of ceil(rows / 256) <= M / 256 + E).
+// Control words the fused launch needs for M rows over E schedule experts (the shared
+// expert, when folded in, counts as one more expert with T more rows): header + one ready
+// counter per m-tile (sum over experts of ceil(rows / 256) <= M / 256 + E).
 size_t fused_ctl_ints(int M, int E) { return (size_t)C_HDR + (size_t)M / F_BM + (size_t)E + 1; }
 
 moe_status_t launch_ffn_fused_bf16(const void* x, const int* row_src, int T, int K, const int* cu, int M,
                                    int E, int H, int Hp, const void* wg, const void* wu, const void* wd,
-                                   void* h, void* y, int* ctl, hipStream_t s) {
-  if (M == 0) return MOE_OK;
-  if (E > F_MAX_E || H % 256 || Hp % 128 || H < 256 || Hp < 256) return MOE_EUNSUPPORTED;
+                                   void* h, void* y, int* ctl, hipStream_t s, const SharedFold& sf) {
+  if (M == 0 && sf.T == 0) return MOE_OK;
+  if (E + (sf.T > 0 ? 1 : 0) > F_MAX_E || H % 256 || Hp % 128 || H < 256 || Hp < 256) return MOE_EUNSUPPORTED;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_fused_kernel),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_fused_kernel<false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, F_LDS) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_fused_kernel<true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, F_LDS) != hipSuccess)
       return MOE_EHIP;
     attr_set = true;
   }
-  const int n = (int)fused_ctl_ints(M, E);
+  const int n = (int)fused_ctl_ints(M + sf.T, E + (sf.T > 0 ? 1 : 0));
   fused_ctl_reset_kernel<<<(n + 255) / 256, 256, 0, s>>>(ctl, n);
-  // lag E: every queue holds all its gate/up tiles before all its down tiles.
+  // lag E + 1: every queue holds all its gate/up tiles before all its down tiles.
   // MOE_FUSED_LAG=n (n >= 1) interleaves them instead, n experts apart; then many down tiles
   // wait for their rows (the readiness path the tests exercise).
-  int lag = E;
+  int lag = E + 1;
   if (const char* v = std::getenv("MOE_FUSED_LAG")) {
-    const int n = std::atoi(v);
-    if (n >= 1) lag = std::min(n, E);
+    const int l = std::atoi(v);
+    if (l >= 1) lag = std::min(l, E + 1);
   }
-  ffn_bf16_fused_kernel<<<device_cu_count(), F_THREADS, F_LDS, s>>>(
+  auto kern = sf.T > 0 ? &ffn_bf16_fused_kernel<true> : &ffn_bf16_fused_kernel<false>;
+  kern<<<device_cu_count(), F_THREADS, F_LDS, s>>>(
       static_cast<const uint16_t*>(x), row_src, T, K, cu, E, H, Hp, static_cast<const uint16_t*>(wg),
       static_cast<const uint16_t*>(wu), static_cast<const uint16_t*>(wd), static_cast<uint16_t*>(h),
-      static_cast<uint16_t*>(y), ctl, lag);
+      static_cast<uint16_t*>(y), ctl, lag, sf);
   return launch_status();
 }
 

@@ -41,7 +41,7 @@ moe_status_t launch_ffn_down_f32(const void*, const int*, int, int, int, int, co
 size_t fused_ctl_ints(int M, int E);
 moe_status_t launch_ffn_fused_bf16(const void* x, const int* row_src, int T, int K, const int* cu, int M,
                                    int E, int H, int Hp, const void* wg, const void* wu, const void* wd,
-                                   void* h, void* y, int* ctl, hipStream_t s);
+                                   void* h, void* y, int* ctl, hipStream_t s, const SharedFold& sf);
 moe_status_t launch_acc_zero(float* acc, size_t n, hipStream_t s);
 moe_status_t launch_acc_store(const float* acc, size_t n, const void* add, moe_dtype_t add_dtype,
                               void* out, moe_dtype_t out_dtype, hipStream_t s);
@@ -446,7 +446,7 @@ moe_status_t moe_grouped_ffn_fused(const void* x, moe_dtype_t act, const int32_t
   char* base = static_cast<char*>(ws);
   int* ctl = reinterpret_cast<int*>(base + align_up((size_t)M * Hp * 2, 256));
   return launch_ffn_fused_bf16(x, row_src, T, K, cu_seqlens, M, E, H, Hp, w_gate, w_up, w_down, base,
-                               y_rows, ctl, stream);
+                               y_rows, ctl, stream, SharedFold{});
 }
 
 moe_status_t moe_combine(const void* y_rows, moe_dtype_t y_dtype, const int32_t* pos,
@@ -542,7 +542,9 @@ static moe_status_t layer_layout(const moe_layer_desc_t* d, size_t* off, size_t*
     want(WS_XQ, T * H);
     want(WS_XQ_SF, T * (H / 128) * 4);
   }
-  if (d->act == MOE_BF16 && d->wgt == MOE_BF16) want(WS_FUSED_CTL, fused_ctl_ints((int)M, d->E) * 4);
+  // (sized to also hold the shared expert's rows and m-tiles when moe_layer_forward_shared
+  // folds it into the launch)
+  if (d->act == MOE_BF16 && d->wgt == MOE_BF16) want(WS_FUSED_CTL, fused_ctl_ints((int)(M + T), d->E + 1) * 4);
   size_t o = 0;
   for (int i = 0; i < WS_N; ++i) {
     if (!used[i]) {
@@ -663,11 +665,30 @@ static moe_status_t layer_forward_impl(const moe_layer_desc_t* d, const void* x,
     x_sf = static_cast<float*>(at(WS_XQ_SF));
   }
 
-  // shared expert (one group of all T rows), on the side stream when one is given
+  // The shared expert (one group of all T rows): its own two launches, on the side stream when
+  // one is given. With MOE_SHARED_FOLD=1, when the routed FFN runs as the single launch and the
+  // shared expert has the routed intermediate size, its tiles join that launch's queues as one
+  // more expert instead ("Mixture of Kittens", Step 9: the shared expert's work overlaps the
+  // routed experts'). That is bitwise the same and no faster: T=8192 E=384 K=8 with Hs=2048
+  // took 8.43 ms against 8.42 ms. In a dynamic queue the shared expert's 32 m-tiles per weight
+  // panel start staggered and lose the L2 sharing of the panel that the two-launch schedule's
+  // rounds give them.
   void* y_s = sh ? base + y_s_off : nullptr;
+  const bool fold = sh && T > 0 && layer_fused(d) && sp == PATH_BF16 && sh->Hs == Hp && E < 1024 &&
+                    env_flag("MOE_SHARED_FOLD");
+  SharedFold sfold;
+  if (fold) {
+    sfold.x = static_cast<const uint16_t*>(xs);
+    sfold.wg = static_cast<const uint16_t*>(sh->w_gate);
+    sfold.wu = static_cast<const uint16_t*>(sh->w_up);
+    sfold.wd = static_cast<const uint16_t*>(sh->w_down);
+    sfold.h = reinterpret_cast<uint16_t*>(base + h_s_off);
+    sfold.y = static_cast<uint16_t*>(y_s);
+    sfold.T = T;
+  }
   hipEvent_t* ev = nullptr;
-  const bool side = sh && sh->side && sh->side != stream && T > 0;
-  if (sh && T > 0) {
+  const bool side = sh && sh->side && sh->side != stream && T > 0 && !fold;
+  if (sh && T > 0 && !fold) {
     hipStream_t ss = stream;
     if (side) {
       st = side_events(&ev);
@@ -718,7 +739,7 @@ static moe_status_t layer_forward_impl(const moe_layer_desc_t* d, const void* x,
   if (layer_fused(d)) {
     // gate/up and down in one persistent launch, then the deterministic combine
     st = launch_ffn_fused_bf16(x, row_src, T, K, cu, M, E, H, Hp, w_gate, w_up, w_down, at(WS_H), at(WS_Y),
-                               static_cast<int*>(at(WS_FUSED_CTL)), stream);
+                               static_cast<int*>(at(WS_FUSED_CTL)), stream, sfold);
     if (st == MOE_OK) st = join_side();
     if (st != MOE_OK) return st;
     return launch_combine(at(WS_Y), y_dtype_of(p), pos, topk_w, T, H, K, y_s, out, d->out, stream);

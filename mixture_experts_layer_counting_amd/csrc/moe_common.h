@@ -55,6 +55,17 @@ struct RowMaps {
   uint16_t* save_u = nullptr;
 };
 
+// The shared expert folded into the single-launch bf16 FFN as one more expert (T = 0: none):
+// a dense SwiGLU FFN of intermediate size Hp (the routed experts' own) over the T token rows
+// of x in order, with its own weights wg, wu [H, Hp] and wd [Hp, H] and its own h [T, Hp] and
+// y [T, H] ("Mixture of Kittens", Step 1: MoE(x) = SharedExpert(x) + the routed sum).
+struct SharedFold {
+  const uint16_t* x = nullptr;
+  const uint16_t *wg = nullptr, *wu = nullptr, *wd = nullptr;
+  uint16_t *h = nullptr, *y = nullptr;
+  int T = 0;
+};
+
 // ---- device helpers -----------------------------------------------------------------
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {

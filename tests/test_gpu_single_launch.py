@@ -179,3 +179,42 @@ def test_fused_rejects_what_it_does_not_take():
         with pytest.raises(moe.MoeError) as ei:
             moe.moe_grouped_ffn_fused(**args(**kw))
         assert ei.value.status == status
+
+
+@pytest.mark.parametrize("spec", [dict(T=600, H=512, Hp=256, E=32, K=6, routing="skew", beta=3.0),
+                                  dict(T=1100, H=768, Hp=384, E=16, K=3, routing="normal")],
+                         ids=["T600_E32", "T1100_E16"])
+def test_shared_expert_folded_into_the_single_launch(spec, queue_order):
+    """moe_layer_forward_shared with the shared expert's tiles in the routed launch's queues
+    (MOE_SHARED_FOLD=1; bf16, T*K <= 256*E, Hs = Hp): the oracle's result, and bitwise the
+    result with the shared expert as its own two launches (the default), also given a side
+    stream."""
+    from _gpu_run import layer_desc, run_layer_shared
+    from _oracle_run import oracle_layer_shared
+    say(f"shared expert folded into the single launch {spec}, queue order {queue_order}")
+    w = gen.make(**spec, act="bf16", wgt="bf16", out="bf16", cid=95, device=DEV, shared_hs=spec["Hp"])
+    assert w.T * w.K <= 256 * w.E
+    os.environ["MOE_SHARED_FOLD"] = "1"
+    try:
+        out_f, ws_f = run_layer_shared(w)
+        out_fs, _ = run_layer_shared(w, side_stream=torch.cuda.Stream())
+    finally:
+        del os.environ["MOE_SHARED_FOLD"]
+    out_s, _ = run_layer_shared(w)
+    torch.cuda.synchronize()
+    lay = moe.moe_layer_workspace_layout(layer_desc(w))
+    c = host(ws_f[lay["fused_ctl"]:lay["fused_ctl"] + 64].view(torch.int32)).astype(np.int64)
+    r = run_steps(w)
+    torch.cuda.synchronize()
+    routed = fused_tile_count(host(r["counts"]), w.H, w.Hp)
+    shared = fused_tile_count([w.T], w.H, w.Hp)
+    print(f"  tiles {c[9]} (routed {routed} + shared {shared}), not prefetched {c[10]}, error {c[8]}",
+          flush=True)
+    assert c[8] == 0 and c[9] == routed + shared
+    assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16))
+    assert torch.equal(out_fs.view(torch.int16), out_s.view(torch.int16))
+    ref = oracle_layer_shared(w)
+    e = rel_err(O.decode_bf16(host(out_f)), ref["out"])
+    es = rel_err(O.decode_bf16(host(out_f)), ref["out"] - ref["y_shared"])
+    print(f"  out rel err {e:.3e}; without the shared term {es:.3e}", flush=True)
+    assert e <= TOL_BF16 and es > 10 * TOL_BF16
