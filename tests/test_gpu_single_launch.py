@@ -218,3 +218,30 @@ def test_shared_expert_folded_into_the_single_launch(spec, queue_order):
     es = rel_err(O.decode_bf16(host(out_f)), ref["out"] - ref["y_shared"])
     print(f"  out rel err {e:.3e}; without the shared term {es:.3e}", flush=True)
     assert e <= TOL_BF16 and es > 10 * TOL_BF16
+
+
+def test_layer_single_launch_empty_batch_and_dropped_copies():
+    """The layer on a shape that takes the single launch: T = 0 gives an empty output; copies
+    with invalid expert ids are dropped (cu_seqlens[E] < T*K), and the result is bitwise the
+    two-launch layer's."""
+    say("single launch: T=0, and invalid ids (dropped copies)")
+    w0 = gen.make(T=0, H=512, Hp=256, E=16, K=2, routing="normal", act="bf16", wgt="bf16", out="bf16",
+                  cid=96, device=DEV)
+    out0, _, _ = run_layer(w0)
+    torch.cuda.synchronize()
+    assert out0.shape == (0, 512)
+    w = gen.make(T=512, H=512, Hp=256, E=16, K=2, routing="balanced", act="bf16", wgt="bf16", out="bf16",
+                 cid=96, device=DEV)
+    bad = w.topk_idx.clone()
+    bad[5, 1] = 17
+    bad[9, 0] = -3
+    bad[300, 1] = 99
+    w.topk_idx = bad
+    out_1, ws_1, lay = run_layer_env(w, "1")
+    out_2, _, _ = run_layer_env(w, "0")
+    torch.cuda.synchronize()
+    c = host(ws_1[lay["fused_ctl"]:lay["fused_ctl"] + 64].view(torch.int32))
+    cu = host(ws_1[lay["cu_seqlens"]:lay["cu_seqlens"] + 4 * (w.E + 1)].view(torch.int32))
+    assert int(cu[-1]) == w.T * w.K - 3
+    assert c[8] == 0 and c[9] == fused_tile_count(np.diff(cu), w.H, w.Hp)
+    assert torch.equal(out_1.view(torch.int16), out_2.view(torch.int16))
