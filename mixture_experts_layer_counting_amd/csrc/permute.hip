@@ -128,12 +128,23 @@ __global__ __launch_bounds__(256) void permute_scan_kernel(int* __restrict__ his
   if (e >= E) return;
   int running = 0;
   int* row = hist + (size_t)e * nch;
-  for (int base = 0; base < nch; base += 64) {
-    const int i = base + lane;
-    const int v = i < nch ? row[i] : 0;
-    const int incl = wave_incl_scan(v);
-    if (i < nch) row[i] = running + incl - v;
-    running += __shfl(incl, 63, 64);
+  // SCAN_BATCH groups of 64 chunk counts are loaded before any is scanned, so a wave waits
+  // for one load round trip per 64 * SCAN_BATCH chunks rather than one per 64
+  constexpr int SCAN_BATCH = 8;
+  for (int base = 0; base < nch; base += 64 * SCAN_BATCH) {
+    int v[SCAN_BATCH];
+#pragma unroll
+    for (int u = 0; u < SCAN_BATCH; ++u) {
+      const int i = base + 64 * u + lane;
+      v[u] = i < nch ? row[i] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < SCAN_BATCH; ++u) {
+      const int i = base + 64 * u + lane;
+      const int incl = wave_incl_scan(v[u]);
+      if (i < nch) row[i] = running + incl - v[u];
+      running += __shfl(incl, 63, 64);
+    }
   }
   if (lane == 0) counts[e] = running;
 }
@@ -178,6 +189,19 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
+  const int tb0 = blockIdx.x * PERM_TB;
+  const int tb1 = min(T, tb0 + PERM_TB);
+  const int chunk = tb0 / PERM_CHUNK;
+  const int tc0 = chunk * PERM_CHUNK;
+  const int nb = (tb1 - tb0) * K;
+  const int* idx = topk_idx + (size_t)tb0 * K;
+  // the first group's expert ids, their chunk offsets and weights are loaded before the scan
+  // of counts below, so that their round trips overlap it instead of following it
+  const int e_first = tid < nb ? idx[tid] : -1;
+  const bool v_first = tid < nb && (unsigned)e_first < (unsigned)E;
+  const int co_first = v_first ? choff[(size_t)e_first * nch + chunk] : 0;
+  const float w_first = (v_first && row_w) ? topk_w[(size_t)tb0 * K + tid] : 0.f;
+
   // 1. cu_seqlens from counts (block-wide exclusive scan, E <= 1024: 4 per thread)
   {
     int loc[4];
@@ -206,17 +230,15 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
       cu[E] = total;
     }
   }
-  for (int e = tid; e < E; e += PERM_THREADS) pre[e] = 0;
-  for (int i = tid; i < PERM_WAVES * PERM_MAX_E; i += PERM_THREADS) (&wh[0][0])[i] = 0;
+  for (int e = tid; e < E; e += PERM_THREADS) {
+    pre[e] = 0;
+#pragma unroll
+    for (int w = 0; w < PERM_WAVES; ++w) wh[w][e] = 0;
+  }
   __syncthreads();
   if (blockIdx.x == 0)
     for (int e = tid; e <= E; e += PERM_THREADS) cu_seqlens[e] = cu[e];
   if (T == 0) return;
-
-  const int tb0 = blockIdx.x * PERM_TB;
-  const int tb1 = min(T, tb0 + PERM_TB);
-  const int chunk = tb0 / PERM_CHUNK;
-  const int tc0 = chunk * PERM_CHUNK;
 
   // 2. copies of earlier tokens in the same chunk
   {
@@ -230,12 +252,10 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
   __syncthreads();
 
   // 3. stable ranks of this block's copies, 256 at a time in flat order
-  const int nb = (tb1 - tb0) * K;
-  const int* idx = topk_idx + (size_t)tb0 * K;
   for (int g = 0; g < nb; g += PERM_THREADS) {
     const int i = g + tid;
     const bool in = i < nb;
-    const int e = in ? idx[i] : -1;
+    const int e = g == 0 ? e_first : in ? idx[i] : -1;
     const bool valid = in && (unsigned)e < (unsigned)E;
     const int key = valid ? e : (1 << key_bits) - 1;
     const uint64_t m = match_any(key, key_bits);
@@ -245,7 +265,7 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
     if (in) {
       int p = -1;
       if (valid) {
-        p = cu[e] + choff[(size_t)e * nch + chunk] + pre[e] + r;
+        p = cu[e] + (g == 0 ? co_first : choff[(size_t)e * nch + chunk]) + pre[e] + r;
         for (int w = 0; w < wave; ++w) p += wh[w][e];
         if (p < cu[e] || p >= cu[e + 1]) {  // cannot happen; keeps every store in bounds
           atomicOr(err, 4);
@@ -253,7 +273,7 @@ __global__ __launch_bounds__(PERM_THREADS) void permute_scatter_kernel(
         } else {
           const int flat = tb0 * K + i;
           row_src[p] = flat;
-          if (row_w) row_w[p] = topk_w[flat];
+          if (row_w) row_w[p] = g == 0 ? w_first : topk_w[flat];
         }
       }
       pos[(size_t)tb0 * K + i] = p;
