@@ -290,6 +290,28 @@ moe_status_t launch_acc_zero(float* acc, size_t n, hipStream_t s) {
   return launch_status();
 }
 
+// Byte fill: the debug poison of a workspace and the clearing of an error word. A kernel
+// rather than hipMemsetAsync, so that a stream captured into a HIP graph records no memset
+// node.
+__global__ __launch_bounds__(256) void fill_bytes_kernel(unsigned char* __restrict__ p, size_t n,
+                                                         unsigned char v) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t i0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t head = (16 - (uintptr_t)p % 16) % 16 < n ? (16 - (uintptr_t)p % 16) % 16 : n;
+  const size_t n16 = (n - head) / 16;
+  const uint32_t w = 0x01010101u * v;
+  uint4* q = reinterpret_cast<uint4*>(p + head);
+  for (size_t i = i0; i < n16; i += stride) q[i] = make_uint4(w, w, w, w);
+  for (size_t i = i0; i < head; i += stride) p[i] = v;
+  for (size_t i = head + n16 * 16 + i0; i < n; i += stride) p[i] = v;
+}
+
+moe_status_t launch_fill_bytes(void* p, size_t n, unsigned char v, hipStream_t s) {
+  if (n == 0) return MOE_OK;
+  fill_bytes_kernel<<<stream_grid(n / 16 + 1), 256, 0, s>>>(static_cast<unsigned char*>(p), n, v);
+  return launch_status();
+}
+
 moe_status_t launch_acc_store(const float* acc, size_t n, const void* add, moe_dtype_t add_dtype,
                               void* out, moe_dtype_t ot, hipStream_t s) {
   if (n == 0) return MOE_OK;

@@ -43,6 +43,7 @@ moe_status_t launch_ffn_fused_bf16(const void* x, const int* row_src, int T, int
                                    int E, int H, int Hp, const void* wg, const void* wu, const void* wd,
                                    void* h, void* y, int* ctl, hipStream_t s, const SharedFold& sf);
 moe_status_t launch_acc_zero(float* acc, size_t n, hipStream_t s);
+moe_status_t launch_fill_bytes(void* p, size_t n, unsigned char v, hipStream_t s);
 moe_status_t launch_acc_store(const float* acc, size_t n, const void* add, moe_dtype_t add_dtype,
                               void* out, moe_dtype_t out_dtype, hipStream_t s);
 moe_status_t launch_dense_cu(int* cu, int T, hipStream_t s);
@@ -137,7 +138,7 @@ static moe_status_t check_fused_dims(int64_t M, int T, int K, int E, int H, int 
 }
 
 static void poison(void* ws, size_t bytes, hipStream_t s) {
-  if (ws && bytes && env_flag("MOE_DEBUG_POISON")) (void)hipMemsetAsync(ws, 0xFF, bytes, s);
+  if (ws && bytes && env_flag("MOE_DEBUG_POISON")) (void)launch_fill_bytes(ws, bytes, 0xFF, s);
 }
 
 }  // namespace moe

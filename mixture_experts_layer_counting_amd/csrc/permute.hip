@@ -37,6 +37,8 @@
 
 namespace moe {
 
+moe_status_t launch_fill_bytes(void* p, size_t n, unsigned char v, hipStream_t s);
+
 constexpr int PERM_CHUNK = 16;   // tokens per histogram chunk
 constexpr int PERM_TB = 16;      // tokens per scatter block (divides PERM_CHUNK)
 constexpr int PERM_THREADS = 256;
@@ -422,7 +424,8 @@ moe_status_t launch_permute(const void* x, const float* x_sf, int elem_bytes,
                                     align_up(sizeof(int) * ((size_t)nch * E), 256));
   *err_out = err;
   if (validate) {
-    if (hipMemsetAsync(err, 0, sizeof(int), s) != hipSuccess) return MOE_EHIP;
+    const moe_status_t st = launch_fill_bytes(err, sizeof(int), 0, s);
+    if (st != MOE_OK) return st;
   }
   if (nch > 0 && !hist_done) {
     permute_hist_kernel<<<nch, PERM_THREADS, 0, s>>>(topk_idx, T, E, K, nch, hist, err);

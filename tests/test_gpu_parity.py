@@ -13,7 +13,7 @@ from oracle import moe_oracle as O
 from workloads import gen, to_numpy_bits
 
 sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
-from _gpu_run import run_layer, run_steps  # noqa: E402
+from _gpu_run import layer_desc, run_layer, run_steps  # noqa: E402
 from _oracle_run import oracle_layer, oracle_routing, oracle_rows, rel_err  # noqa: E402
 
 import mixture_experts_layer_counting_amd as moe  # noqa: E402
@@ -324,12 +324,20 @@ def test_layer_forward_matches_steps_and_is_deterministic():
 def test_debug_poison_leaves_no_nan():
     say("MOE_DEBUG_POISON")
     w = gen.make(T=200, H=256, Hp=128, E=8, K=2, routing="normal", cid=56, device=DEV)
+    d = layer_desc(w)
+    need = moe.moe_layer_workspace_bytes(d)
+    extra = 4099   # never written by the layer; an odd length for the fill's tail
+    ws = torch.zeros(need + extra, dtype=torch.uint8, device=DEV)
+    out = torch.empty((w.T, w.H), dtype=torch.bfloat16, device=DEV)
     os.environ["MOE_DEBUG_POISON"] = "1"
     try:
-        out, _, _ = run_layer(w)
+        moe.moe_layer_forward(d, w.x, w.x_sf, w.logits, w.topk_idx, w.topk_w, w.w_gate, w.w_up,
+                              w.w_down, w.sf_gate, w.sf_up, w.sf_down, out, ws, need + extra)
         torch.cuda.synchronize()
     finally:
         del os.environ["MOE_DEBUG_POISON"]
+    # the poison covered the whole workspace the caller passed
+    assert bool((ws[need:] == 0xFF).all())
     assert not torch.isnan(out.float()).any()
     ref = oracle_layer(w)
     assert rel_err(O.decode_bf16(host(out)), ref["out"]) <= 2e-2
