@@ -86,8 +86,9 @@ def parse():
                     help="also time moe_layer_backward (bf16 layers), reported under 'backward'")
     ap.add_argument("--ffn", default="auto", choices=["auto", "two", "fused"],
                     help="bf16: gate/up and down as two persistent launches or as one "
-                         "(moe_grouped_ffn_fused, reported as stage 'ffn'); auto picks as "
-                         "moe_layer_forward does: one launch when T*K <= 256*E")
+                         "(moe_grouped_ffn_fused, or moe_grouped_ffn_fused_scatter with --combine "
+                         "scatter, reported as stage 'ffn'); auto picks as moe_layer_forward does: "
+                         "one launch when T*K <= 256*E and the combine is the gather")
     ap.add_argument("--xperm", action="store_true",
                     help="materialise x_perm in the permute instead of gathering rows in gate/up")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -223,8 +224,8 @@ def main():
                                and min(H, Hp) >= 256) else "two"
     fused = args.ffn == "fused"
     if fused:
-        if w.act != "bf16" or scatter or args.xperm or pad != 1:
-            sys.exit("bench.py: --ffn fused takes the bf16 layer with gathered rows and the gather combine")
+        if w.act != "bf16" or args.xperm or pad != 1:
+            sys.exit("bench.py: --ffn fused takes the bf16 layer with gathered rows and no padding")
         nws_f = moe.moe_grouped_ffn_fused_workspace_bytes(M, E, Hp)
         ws_f = torch.empty(nws_f, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -257,6 +258,15 @@ def main():
             mark("permute", lambda: moe.moe_permute_padded(w.x, w.x_sf, DT[w.act], topk_idx, topk_w, T, H, E,
                                                            K, pad, counts, cu, pos, row_src, row_w, x_perm,
                                                            x_perm_sf, ws, nws, None))
+        if fused and scatter:
+            # the weighted combine in the single launch's down epilogue, into the fp32 accumulator
+            mark("combine", lambda: acc.zero_())
+            mark("ffn", lambda: moe.moe_grouped_ffn_fused_scatter(w.x, DT[w.act], row_src, T, K, cu, M, E, H,
+                                                                  Hp, w.w_gate, w.w_up, w.w_down, DT[w.wgt],
+                                                                  row_w, acc, ws_f, nws_f, None))
+            if acc is not out:
+                mark("combine", lambda: out.copy_(acc))
+            return
         if fused:
             mark("ffn", lambda: moe.moe_grouped_ffn_fused(w.x, DT[w.act], row_src, T, K, cu, M, E, H, Hp,
                                                           w.w_gate, w.w_up, w.w_down, DT[w.wgt], y, DT[yf],
@@ -404,7 +414,7 @@ def main():
     if fused:
         k_ms, k_flops, k_bytes = stage_ms["ffn"], gu_flops + dn_flops, gu_bytes + dn_bytes
         kname = "ffn_fused (gate/up + SwiGLU and down in one persistent launch)"
-        kfiles, tkernel = ("ffn_fused.hip",), "ffn_fused"
+        kfiles, tkernel = ("ffn_fused.hip",), "ffn_fused_scatter" if scatter else "ffn_fused"
     else:
         k_ms, k_flops, k_bytes = stage_ms["gate_up"], gu_flops, gu_bytes
         kname = "ffn_gate_up (grouped GEMM gate+up, SwiGLU epilogue)"

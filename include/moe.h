@@ -314,6 +314,22 @@ MOE_API moe_status_t moe_grouped_ffn_fused(const void* x, moe_dtype_t act, const
                                    void* y_rows, moe_dtype_t out, void* ws, size_t ws_bytes,
                                    hipStream_t stream);
 
+/* moe_grouped_ffn_fused with the weighted combine in the down tiles' epilogue instead of
+ * y_rows (DeepGEMM Mega-MoE how-to: dispatch, both expert GEMMs, SwiGLU and the combine in
+ * one kernel; MoonEP "combine fwd" weights the rows): for every row r of expert e's group,
+ *     acc[row_src[r] / K] += row_w[r] * (h[r] . Wd[e]),
+ * added with fp32 atomics, as moe_ffn_down_scatter does, so the order of a token's K
+ * additions (and its last bit) may vary between runs. acc [T, H] fp32 is accumulated into:
+ * the caller zeroes it first. row_w [M] from moe_permute; rows with row_src = -1 are skipped.
+ * Other arguments, the workspace (h and the control words), limits and launches as
+ * moe_grouped_ffn_fused; act and wgt must be MOE_BF16. */
+MOE_API moe_status_t moe_grouped_ffn_fused_scatter(const void* x, moe_dtype_t act, const int32_t* row_src,
+                                           int32_t T, int32_t K, const int32_t* cu_seqlens, int32_t M,
+                                           int32_t E, int32_t H, int32_t Hp, const void* w_gate,
+                                           const void* w_up, const void* w_down, moe_dtype_t wgt,
+                                           const float* row_w, float* acc, void* ws, size_t ws_bytes,
+                                           hipStream_t stream);
+
 /* Combine ("Distributed expert parallelism", lifecycle item 8 and "A four-rank example";
  * MoonEP "combine fwd"): out[t] = sum_{k=0..K-1} topk_w[t,k] * y_rows[pos[t,k]], summed in
  * fp32 in increasing k and rounded once to `out_dtype`; rows with pos < 0 are skipped.
@@ -351,7 +367,10 @@ MOE_API size_t moe_layer_workspace_bytes(const moe_layer_desc_t* d);
  *   -> d->combine == MOE_COMBINE_GATHER: down -> y_rows -> moe_combine (deterministic);
  *      d->combine == MOE_COMBINE_SCATTER_ATOMIC: down with the weighted scatter-add fused
  *      into its epilogue (moe_ffn_down_scatter) into an fp32 accumulator (the output itself
- *      when d->out is F32, else a workspace buffer rounded once into out at the end).
+ *      when d->out is F32, else a workspace buffer rounded once into out at the end). With
+ *      this combine the FFN runs as two launches unless MOE_LAYER_FUSED=1 asks for the
+ *      single launch, which then adds the rows in its down epilogue
+ *      (moe_grouped_ffn_fused_scatter; bf16 layers on the shapes it takes).
  *  x [T, H] (format d->act, with x_sf for FP8_E4M3); logits [T, E] fp32 or NULL;
  *  topk_idx_in / topk_w_in [T, K] when logits == NULL; weights as for moe_grouped_ffn;
  *  out [T, H] of d->out, 16-byte aligned. `ws` must hold moe_layer_workspace_bytes(d) bytes;

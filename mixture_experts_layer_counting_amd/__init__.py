@@ -33,7 +33,8 @@ EXPORTS = ("moe_route_topk", "moe_permute_workspace_bytes", "moe_permute", "moe_
            "moe_permute_padded", "moe_route_permute", "moe_quantize_fp8", "moe_ffn_gate_up",
            "moe_ffn_gate_up_gather", "moe_ffn_down", "moe_ffn_down_scatter",
            "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn",
-           "moe_grouped_ffn_fused_workspace_bytes", "moe_grouped_ffn_fused", "moe_combine",
+           "moe_grouped_ffn_fused_workspace_bytes", "moe_grouped_ffn_fused",
+           "moe_grouped_ffn_fused_scatter", "moe_combine",
            "moe_combine_shared", "moe_layer_workspace_bytes", "moe_layer_forward",
            "moe_layer_shared_workspace_bytes", "moe_layer_forward_shared", "moe_layer_workspace_layout",
            "moe_layer_backward_workspace_bytes", "moe_layer_backward",
@@ -83,6 +84,8 @@ _SIGS = {
     "moe_grouped_ffn_fused_workspace_bytes": (_S, [_I, _I, _I]),
     "moe_grouped_ffn_fused": (_I, [_P, _E, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _E, _P, _E, _P,
                                    _S, _P]),
+    "moe_grouped_ffn_fused_scatter": (_I, [_P, _E, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _E, _P,
+                                           _P, _P, _S, _P]),
     "moe_combine": (_I, [_P, _E, _P, _P, _I, _I, _I, _P, _E, _P]),
     "moe_layer_workspace_bytes": (_S, [ctypes.POINTER(LayerDesc)]),
     "moe_layer_forward": (_I, [ctypes.POINTER(LayerDesc), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
@@ -245,6 +248,14 @@ def moe_grouped_ffn_fused(x, act, row_src, T, K, cu_seqlens, M, E, H, Hp, w_gate
     _check(lib().moe_grouped_ffn_fused(_ptr(x), act, _ptr(row_src), T, K, _ptr(cu_seqlens), M, E, H, Hp,
                                        _ptr(w_gate), _ptr(w_up), _ptr(w_down), wgt, _ptr(y_rows), out,
                                        _ptr(ws), ws_bytes, _stream(stream)), "moe_grouped_ffn_fused")
+
+
+def moe_grouped_ffn_fused_scatter(x, act, row_src, T, K, cu_seqlens, M, E, H, Hp, w_gate, w_up, w_down,
+                                  wgt, row_w, acc, ws, ws_bytes, stream=None):
+    _check(lib().moe_grouped_ffn_fused_scatter(_ptr(x), act, _ptr(row_src), T, K, _ptr(cu_seqlens), M, E,
+                                               H, Hp, _ptr(w_gate), _ptr(w_up), _ptr(w_down), wgt,
+                                               _ptr(row_w), _ptr(acc), _ptr(ws), ws_bytes, _stream(stream)),
+           "moe_grouped_ffn_fused_scatter")
 
 
 def moe_combine(y_rows, y_dtype, pos, topk_w, T, H, K, out, out_dtype, stream=None):

@@ -6,7 +6,9 @@
 // through counters in global memory) and Step 3 (work of the next chunk overlaps the current
 // one); the DeepGEMM Mega-MoE how-to (dispatch, both expert GEMMs and SwiGLU in one kernel).
 // Gate/up rows are gathered from the token matrix through row_src ("no permute in"); the
-// down tiles write y_rows for the deterministic combine.
+// down tiles write y_rows for the deterministic combine, or, in the scattering instantiation,
+// add their weighted rows into the token accumulator with atomics (the combine in the down
+// epilogue).
 //
 // Work list. Expert e with rows_e rows has mte = ceil(rows_e / 256) m-tiles (the row split of
 // even_chunk, as in the two-launch kernels), giving mte * Hp/128 gate/up tiles (G) and
@@ -120,12 +122,16 @@ __global__ void fused_ctl_reset_kernel(int* ctl, int n) {
 // x [T, H] bf16 (gathered through row_src / K); w_gate, w_up [E, H, Hp]; w_down [E, Hp, H];
 // h [M, Hp] and y [M, H] bf16; ctl: control words + ready counters (zeroed before the launch).
 // SHARED: the shared expert is folded in as expert E (sf); otherwise sf is unused.
-template <bool SHARED>
+// SCATTER: the down tiles add row_w[r] * y[r] into s_acc [T, H] (fp32) at token row_src[r] / K
+// with atomics instead of storing y (the weighted combine in the down epilogue); y is unused.
+template <bool SHARED, bool SCATTER>
 __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
     const uint16_t* __restrict__ x, const int* __restrict__ row_src, int T, int K,
     const int* __restrict__ cu, int E, int H, int Hp, const uint16_t* __restrict__ wg,
     const uint16_t* __restrict__ wu, const uint16_t* __restrict__ wd, uint16_t* __restrict__ h,
-    uint16_t* __restrict__ y, int* __restrict__ ctl, int lag, SharedFold sf) {
+    uint16_t* __restrict__ y, int* __restrict__ ctl, int lag, SharedFold sf,
+    const float* __restrict__ row_w, float* __restrict__ s_acc) {
+  static_assert(!(SHARED && SCATTER), "the shared expert is folded in with the gather combine only");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int* li = reinterpret_cast<int*>(smem + F_NS * F_STAGE);
   int* cu_l = li + L_CU;
@@ -509,6 +515,8 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
           }
         }
       };
+      // weights as the first operand: each lane holds one output row (row-lane layout); the
+      // scattering down tiles take the other order, each lane then holding one column
       auto compute = [&]() __attribute__((always_inline)) {
         if constexpr (MTV > 0) {
 #pragma unroll
@@ -516,8 +524,12 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
 #pragma unroll
             for (int f = 0; f < 2; ++f)
 #pragma unroll
-              for (int mt = 0; mt < MTV; ++mt)
-                acc[f][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][q], fa[mt][q], acc[f][mt], 0, 0, 0);
+              for (int mt = 0; mt < MTV; ++mt) {
+                if constexpr (SCATTER && KIND == 1)
+                  acc[f][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mt][q], fb[f][q], acc[f][mt], 0, 0, 0);
+                else
+                  acc[f][mt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[f][q], fa[mt][q], acc[f][mt], 0, 0, 0);
+              }
         }
       };
       constexpr std::integral_constant<int, 0> H0{};
@@ -619,6 +631,24 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
       if (lane == 0)
         __hip_atomic_fetch_add(ready + mpre[cur.e] + cur.mt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (pf && g0) issue(nxt, F_NS - 1);
+    } else if constexpr (SCATTER) {
+      // column-lane layout: element i of block (mt, f) is row (2 mt + hf) * 32 + 8 (i / 4) +
+      // 4 (lane / 32) + i % 4 and column f * 32 + lane % 32 of this wave's 64-column strip, so
+      // the 32 lanes of a row add into 32 consecutive floats of its token's accumulator row
+      const int col = cur.n0 + sc * 64 + (lane & 31);
+#pragma unroll
+      for (int mt = 0; mt < F_PMT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int r = (2 * mt + hf) * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+          const int src = r < cur.rows_valid ? row_src[cur.row0 + r] : -1;   // -1: padding row
+          if (src >= 0) {
+            float* dst = s_acc + (size_t)(src / K) * H + col;
+            const float wr = row_w[cur.row0 + r];
+#pragma unroll
+            for (int f = 0; f < 2; ++f) unsafeAtomicAdd(dst + f * 32, wr * acc[f][mt][i]);
+          }
+        }
     } else {
       const int col = cur.n0 + sc * 64 + 8 * (lane >> 5);
 #pragma unroll
@@ -666,14 +696,18 @@ size_t fused_ctl_ints(int M, int E) { return (size_t)C_HDR + (size_t)M / F_BM + 
 
 moe_status_t launch_ffn_fused_bf16(const void* x, const int* row_src, int T, int K, const int* cu, int M,
                                    int E, int H, int Hp, const void* wg, const void* wu, const void* wd,
-                                   void* h, void* y, int* ctl, hipStream_t s, const SharedFold& sf) {
+                                   void* h, void* y, int* ctl, hipStream_t s, const SharedFold& sf,
+                                   const float* row_w, float* s_acc) {
   if (M == 0 && sf.T == 0) return MOE_OK;
   if (E + (sf.T > 0 ? 1 : 0) > F_MAX_E || H % 256 || Hp % 128 || H < 256 || Hp < 256) return MOE_EUNSUPPORTED;
+  if (s_acc && (sf.T > 0 || !row_w)) return MOE_EINVAL;
   static bool attr_set = false;
   if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_fused_kernel<false>),
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_fused_kernel<false, false>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, F_LDS) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_fused_kernel<true>),
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_fused_kernel<true, false>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, F_LDS) != hipSuccess ||
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_fused_kernel<false, true>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, F_LDS) != hipSuccess)
       return MOE_EHIP;
     attr_set = true;
@@ -688,11 +722,12 @@ moe_status_t launch_ffn_fused_bf16(const void* x, const int* row_src, int T, int
     const int l = std::atoi(v);
     if (l >= 1) lag = std::min(l, E + 1);
   }
-  auto kern = sf.T > 0 ? &ffn_bf16_fused_kernel<true> : &ffn_bf16_fused_kernel<false>;
+  auto kern = s_acc ? &ffn_bf16_fused_kernel<false, true>
+                    : sf.T > 0 ? &ffn_bf16_fused_kernel<true, false> : &ffn_bf16_fused_kernel<false, false>;
   kern<<<device_cu_count(), F_THREADS, F_LDS, s>>>(
       static_cast<const uint16_t*>(x), row_src, T, K, cu, E, H, Hp, static_cast<const uint16_t*>(wg),
       static_cast<const uint16_t*>(wu), static_cast<const uint16_t*>(wd), static_cast<uint16_t*>(h),
-      static_cast<uint16_t*>(y), ctl, lag, sf);
+      static_cast<uint16_t*>(y), ctl, lag, sf, row_w, s_acc);
   return launch_status();
 }
 

@@ -41,7 +41,8 @@ moe_status_t launch_ffn_down_f32(const void*, const int*, int, int, int, int, co
 size_t fused_ctl_ints(int M, int E);
 moe_status_t launch_ffn_fused_bf16(const void* x, const int* row_src, int T, int K, const int* cu, int M,
                                    int E, int H, int Hp, const void* wg, const void* wu, const void* wd,
-                                   void* h, void* y, int* ctl, hipStream_t s, const SharedFold& sf);
+                                   void* h, void* y, int* ctl, hipStream_t s, const SharedFold& sf,
+                                   const float* row_w, float* s_acc);
 moe_status_t launch_acc_zero(float* acc, size_t n, hipStream_t s);
 moe_status_t launch_fill_bytes(void* p, size_t n, unsigned char v, hipStream_t s);
 moe_status_t launch_acc_store(const float* acc, size_t n, const void* add, moe_dtype_t add_dtype,
@@ -447,7 +448,28 @@ moe_status_t moe_grouped_ffn_fused(const void* x, moe_dtype_t act, const int32_t
   char* base = static_cast<char*>(ws);
   int* ctl = reinterpret_cast<int*>(base + align_up((size_t)M * Hp * 2, 256));
   return launch_ffn_fused_bf16(x, row_src, T, K, cu_seqlens, M, E, H, Hp, w_gate, w_up, w_down, base,
-                               y_rows, ctl, stream, SharedFold{});
+                               y_rows, ctl, stream, SharedFold{}, nullptr, nullptr);
+}
+
+moe_status_t moe_grouped_ffn_fused_scatter(const void* x, moe_dtype_t act, const int32_t* row_src,
+                                           int32_t T, int32_t K, const int32_t* cu_seqlens, int32_t M,
+                                           int32_t E, int32_t H, int32_t Hp, const void* w_gate,
+                                           const void* w_up, const void* w_down, moe_dtype_t wgt,
+                                           const float* row_w, float* acc, void* ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+  if (act != MOE_BF16 || wgt != MOE_BF16) return MOE_EUNSUPPORTED;
+  moe_status_t st = check_fused_dims(M, T, K, E, H, Hp);
+  if (st != MOE_OK) return st;
+  const size_t need = moe_grouped_ffn_fused_workspace_bytes(M, E, Hp);
+  if (need == 0) return MOE_EINVAL;
+  if (!ws || ws_bytes < need) return MOE_EWORKSPACE;
+  if (!cu_seqlens) return MOE_EINVAL;
+  if (M > 0 && (!x || !row_src || !w_gate || !w_up || !w_down || !row_w || !acc)) return MOE_EINVAL;
+  poison(ws, ws_bytes, stream);
+  char* base = static_cast<char*>(ws);
+  int* ctl = reinterpret_cast<int*>(base + align_up((size_t)M * Hp * 2, 256));
+  return launch_ffn_fused_bf16(x, row_src, T, K, cu_seqlens, M, E, H, Hp, w_gate, w_up, w_down, base,
+                               nullptr, ctl, stream, SharedFold{}, row_w, acc);
 }
 
 moe_status_t moe_combine(const void* y_rows, moe_dtype_t y_dtype, const int32_t* pos,
@@ -495,20 +517,23 @@ static bool layer_materializes(const moe_layer_desc_t* d) {
 }
 
 // Whether moe_layer_forward runs the expert FFN as the single persistent launch
-// (moe_grouped_ffn_fused): bf16 layers that gather their rows and combine deterministically,
-// on the shapes that launch takes, when the average expert group fits one 256-row m-tile
+// (moe_grouped_ffn_fused, or moe_grouped_ffn_fused_scatter with the scatter-add combine): by
+// default, bf16 layers that gather their rows and combine deterministically, on the shapes
+// that launch takes, when the average expert group fits one 256-row m-tile
 // (T*K <= 256*E). With several m-tiles per expert the two-launch schedule is faster: its
 // rounds start all m-tiles of a weight panel together, so they share the panel through L2,
 // which a dynamic queue staggers (T=8192 K=8 E=384: single launch 7.75 vs 7.83 ms per layer,
-// 8.59 vs 9.01 ms at maxvio 20; 65536 rows over 52 experts: 5.29 vs 5.07 ms). The
-// environment variable MOE_LAYER_FUSED=1 or 0 forces either path.
+// 8.59 vs 9.01 ms at maxvio 20; 65536 rows over 52 experts: 5.29 vs 5.07 ms). With the
+// scatter-add combine the two launches stay the default: at T=8192 K=8 E=384 the layer took
+// 9.58 ms with them against 9.79 ms as one launch. The environment variable MOE_LAYER_FUSED=1
+// or 0 forces either path for both combines.
 static bool layer_fused(const moe_layer_desc_t* d) {
-  if (d->act != MOE_BF16 || d->wgt != MOE_BF16 || d->combine != MOE_COMBINE_GATHER) return false;
+  if (d->act != MOE_BF16 || d->wgt != MOE_BF16) return false;
   if (layer_materializes(d)) return false;
   if (check_fused_dims((int64_t)d->T * d->K, d->T, d->K, d->E, d->H, d->Hp) != MOE_OK) return false;
   const char* v = std::getenv("MOE_LAYER_FUSED");
   if (v && v[0]) return v[0] != '0';
-  return (int64_t)d->T * d->K <= 256ll * d->E;
+  return d->combine == MOE_COMBINE_GATHER && (int64_t)d->T * d->K <= 256ll * d->E;
 }
 
 static moe_status_t layer_layout(const moe_layer_desc_t* d, size_t* off, size_t* total) {
@@ -675,8 +700,8 @@ static moe_status_t layer_forward_impl(const moe_layer_desc_t* d, const void* x,
   // panel start staggered and lose the L2 sharing of the panel that the two-launch schedule's
   // rounds give them.
   void* y_s = sh ? base + y_s_off : nullptr;
-  const bool fold = sh && T > 0 && layer_fused(d) && sp == PATH_BF16 && sh->Hs == Hp && E < 1024 &&
-                    env_flag("MOE_SHARED_FOLD");
+  const bool fold = sh && T > 0 && layer_fused(d) && d->combine == MOE_COMBINE_GATHER && sp == PATH_BF16 &&
+                    sh->Hs == Hp && E < 1024 && env_flag("MOE_SHARED_FOLD");
   SharedFold sfold;
   if (fold) {
     sfold.x = static_cast<const uint16_t*>(xs);
@@ -737,13 +762,26 @@ static moe_status_t layer_forward_impl(const moe_layer_desc_t* d, const void* x,
                             at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)), at(WS_PERM_SCRATCH),
                             perm_ws, stream);
   if (st != MOE_OK) return st;
-  if (layer_fused(d)) {
+  if (layer_fused(d) && !scatter) {
     // gate/up and down in one persistent launch, then the deterministic combine
     st = launch_ffn_fused_bf16(x, row_src, T, K, cu, M, E, H, Hp, w_gate, w_up, w_down, at(WS_H), at(WS_Y),
-                               static_cast<int*>(at(WS_FUSED_CTL)), stream, sfold);
+                               static_cast<int*>(at(WS_FUSED_CTL)), stream, sfold, nullptr, nullptr);
     if (st == MOE_OK) st = join_side();
     if (st != MOE_OK) return st;
     return launch_combine(at(WS_Y), y_dtype_of(p), pos, topk_w, T, H, K, y_s, out, d->out, stream);
+  }
+  if (layer_fused(d)) {
+    // one persistent launch whose down tiles add the weighted rows into the fp32 accumulator
+    float* acc = d->out == MOE_F32 ? static_cast<float*>(out) : static_cast<float*>(at(WS_ACC));
+    const size_t n = (size_t)T * H;
+    if (n == 0) return join_side();
+    st = launch_acc_zero(acc, n, stream);
+    if (st == MOE_OK)
+      st = launch_ffn_fused_bf16(x, row_src, T, K, cu, M, E, H, Hp, w_gate, w_up, w_down, at(WS_H), nullptr,
+                                 static_cast<int*>(at(WS_FUSED_CTL)), stream, SharedFold{}, row_w, acc);
+    if (st == MOE_OK) st = join_side();
+    if (st != MOE_OK) return st;
+    return launch_acc_store(acc, n, y_s, y_dtype_of(p), out, d->out, stream);
   }
   if (mat)
     st = moe_ffn_gate_up(at(WS_X_PERM), static_cast<float*>(at(WS_X_PERM_SF)), act, cu, M, E, H, Hp,

@@ -27,7 +27,8 @@ CASES = [
     ("bf16_one_ffn_launch", SKEW, "bf16", "bf16", "gather", "1"),
     ("bf16_two_ffn_launches", SKEW, "bf16", "bf16", "gather", "0"),
     ("fp8_mxfp4", dict(T=300, H=512, Hp=256, E=12, K=3, routing="skew", beta=0.5), "fp8", "mxfp4", "gather", None),
-    ("bf16_scatter_combine", SKEW, "bf16", "bf16", "scatter", None),
+    ("bf16_scatter_combine_one_ffn_launch", SKEW, "bf16", "bf16", "scatter", "1"),
+    ("bf16_scatter_combine_two_ffn_launches", SKEW, "bf16", "bf16", "scatter", "0"),
     ("f32", dict(T=333, H=200, Hp=72, E=9, K=3, routing="skew", beta=0.5), "f32", "f32", "gather", None),
 ]
 

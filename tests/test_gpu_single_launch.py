@@ -132,12 +132,75 @@ def test_fused_back_to_back_calls_share_a_workspace(queue_order):
     check_against_steps(wb, rb, yb, hb)
 
 
-def run_layer_env(w, value):
+def run_layer_env(w, value, combine=moe.MOE_COMBINE_GATHER):
     os.environ["MOE_LAYER_FUSED"] = value
     try:
-        return run_layer(w)
+        return run_layer(w, combine)
     finally:
         del os.environ["MOE_LAYER_FUSED"]
+
+
+def run_fused_scatter(w, r, ws=None):
+    """moe_grouped_ffn_fused_scatter on the permutation of run_steps into a zeroed fp32
+    accumulator: returns (acc [T, H], control words, workspace)."""
+    M = w.T * w.K
+    n = moe.moe_grouped_ffn_fused_workspace_bytes(M, w.E, w.Hp)
+    if ws is None:
+        ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    acc = torch.zeros((w.T, w.H), dtype=torch.float32, device=DEV)
+    moe.moe_grouped_ffn_fused_scatter(w.x, moe.MOE_BF16, r["row_src"], w.T, w.K, r["cu_seqlens"], M, w.E,
+                                      w.H, w.Hp, w.w_gate, w.w_up, w.w_down, moe.MOE_BF16, r["row_w"], acc,
+                                      ws, n)
+    o = (M * w.Hp * 2 + 255) // 256 * 256
+    return acc, ws[o:o + 64].view(torch.int32), ws
+
+
+def rel_to_max(got, ref):
+    return float((got.float() - ref.float()).abs().max() / ref.float().abs().max().clamp_min(1e-30))
+
+
+@pytest.mark.parametrize("spec", [CASES[0], CASES[1], CASES[4]],
+                         ids=lambda s: "T{T}_H{H}_Hp{Hp}_E{E}_K{K}_{routing}".format(**s))
+def test_fused_scatter_matches_oracle_and_two_launch_scatter(spec, queue_order):
+    """The single launch with the weighted combine in its down epilogue: the same fp32
+    products as moe_ffn_down_scatter after the two-launch gate/up, added with atomics in
+    another order, and the oracle's layer output."""
+    say(f"single-launch FFN with the scatter-add combine {spec}, queue order {queue_order}")
+    w = gen.make(**spec, act="bf16", wgt="bf16", out="bf16", cid=97, device=DEV)
+    r = run_steps(w)
+    M = w.T * w.K
+    acc_f, ctl, _ = run_fused_scatter(w, r)
+    acc_2 = torch.zeros_like(acc_f)
+    moe.moe_ffn_down_scatter(r["h"], None, moe.MOE_BF16, r["cu_seqlens"], M, w.E, w.H, w.Hp, w.w_down, None,
+                             moe.MOE_BF16, r["row_src"], r["row_w"], w.T, w.K, acc_2)
+    torch.cuda.synchronize()
+    check_ctl(ctl, host(r["counts"]), w.H, w.Hp)
+    d = rel_to_max(acc_f, acc_2)
+    ref = oracle_layer(w)
+    e = rel_err(host(acc_f), ref["out"])
+    print(f"  against the two-launch scatter {d:.3e}, against the oracle {e:.3e}", flush=True)
+    assert d <= 1e-5
+    assert e <= TOL_BF16
+
+
+@pytest.mark.parametrize("spec", [CASES[0], CASES[4]], ids=["E32_one_tile_per_expert", "E16_several_tiles"])
+def test_layer_scatter_combine_in_the_single_launch(spec):
+    """moe_layer_forward with MOE_COMBINE_SCATTER_ATOMIC as one launch (MOE_LAYER_FUSED=1) and as
+    two (=0): within one bf16 rounding of each other, and the oracle's output."""
+    say(f"moe_layer_forward, scatter-add combine, one launch vs two {spec}")
+    w = gen.make(**spec, act="bf16", wgt="bf16", out="bf16", cid=98, device=DEV)
+    out_1, ws_1, lay = run_layer_env(w, "1", moe.MOE_COMBINE_SCATTER_ATOMIC)
+    out_2, _, _ = run_layer_env(w, "0", moe.MOE_COMBINE_SCATTER_ATOMIC)
+    torch.cuda.synchronize()
+    c = host(ws_1[lay["fused_ctl"]:lay["fused_ctl"] + 64].view(torch.int32))
+    cu = host(ws_1[lay["cu_seqlens"]:lay["cu_seqlens"] + 4 * (w.E + 1)].view(torch.int32))
+    assert c[8] == 0 and c[9] == fused_tile_count(np.diff(cu), w.H, w.Hp)
+    d = rel_to_max(out_1, out_2)
+    ref = oracle_layer(w)
+    e = rel_err(O.decode_bf16(host(out_1)), ref["out"])
+    print(f"  one launch vs two {d:.3e}, against the oracle {e:.3e}", flush=True)
+    assert d <= 2.0 ** -7
+    assert e <= TOL_BF16
 
 
 @pytest.mark.parametrize("spec", [CASES[0], CASES[4]], ids=["E32_one_tile_per_expert", "E16_several_tiles"])
@@ -178,6 +241,17 @@ def test_fused_rejects_what_it_does_not_take():
                        (dict(y_rows=None), moe.MOE_EINVAL)):
         with pytest.raises(moe.MoeError) as ei:
             moe.moe_grouped_ffn_fused(**args(**kw))
+        assert ei.value.status == status
+    acc = torch.zeros((w.T, w.H), dtype=torch.float32, device=DEV)
+    sargs = lambda **kw: dict(dict(x=w.x, act=moe.MOE_BF16, row_src=r["row_src"], T=w.T, K=w.K,  # noqa: E731
+                                   cu_seqlens=r["cu_seqlens"], M=M, E=w.E, H=w.H, Hp=w.Hp, w_gate=w.w_gate,
+                                   w_up=w.w_up, w_down=w.w_down, wgt=moe.MOE_BF16, row_w=r["row_w"], acc=acc,
+                                   ws=ws, ws_bytes=n), **kw)
+    for kw, status in ((dict(act=moe.MOE_F32), moe.MOE_EUNSUPPORTED), (dict(H=384), moe.MOE_EUNSUPPORTED),
+                       (dict(ws_bytes=n - 1), moe.MOE_EWORKSPACE), (dict(row_w=None), moe.MOE_EINVAL),
+                       (dict(acc=None), moe.MOE_EINVAL)):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.moe_grouped_ffn_fused_scatter(**sargs(**kw))
         assert ei.value.status == status
 
 
