@@ -306,7 +306,9 @@ MOE_API size_t moe_grouped_ffn_fused_workspace_bytes(int32_t M, int32_t E, int32
  *  calls sharing a workspace must be ordered (same stream).
  * Needs H % 256 == 0, Hp % 128 == 0, H >= 256, Hp >= 256, E <= 1024 and T*H*2 < 2^31
  * (MOE_EUNSUPPORTED otherwise). Two kernel launches: a reset of the control words and the
- * persistent kernel. */
+ * persistent kernel. Test hooks: MOE_FUSED_LAG=n queues each expert's down tiles n experts
+ * behind its gate/up tiles (default: all gate/up tiles of a queue first), and
+ * MOE_FUSED_SPIN_MAX=n lowers the bound of a readiness wait to n polls (error 1 when reached). */
 MOE_API moe_status_t moe_grouped_ffn_fused(const void* x, moe_dtype_t act, const int32_t* row_src,
                                    int32_t T, int32_t K, const int32_t* cu_seqlens, int32_t M,
                                    int32_t E, int32_t H, int32_t Hp, const void* w_gate,

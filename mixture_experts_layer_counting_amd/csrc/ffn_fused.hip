@@ -67,7 +67,7 @@ constexpr int F_LDP = 4;                       // A (and weight) loads per group
 constexpr int F_VMG = 2 * F_LDP;
 constexpr int F_KK = F_BK / 16;                // MFMA k-steps per stage
 constexpr int F_PMT = 4;                       // row blocks per wave (at most)
-constexpr int F_SPIN_MAX = 1 << 20;            // bound of one readiness wait (polls, about 1 s)
+constexpr int F_SPIN_MAX = 1 << 20;            // default bound of one readiness wait (polls, about 1 s)
 
 // control words (int32) at the start of the caller's control area; ready[] follows
 enum { C_QCTR = 0, C_ERR = F_NQ, C_TILES, C_COLD, C_STEAL, C_HDR = 16 };
@@ -129,7 +129,7 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
     const uint16_t* __restrict__ x, const int* __restrict__ row_src, int T, int K,
     const int* __restrict__ cu, int E, int H, int Hp, const uint16_t* __restrict__ wg,
     const uint16_t* __restrict__ wu, const uint16_t* __restrict__ wd, uint16_t* __restrict__ h,
-    uint16_t* __restrict__ y, int* __restrict__ ctl, int lag, SharedFold sf,
+    uint16_t* __restrict__ y, int* __restrict__ ctl, int lag, int spin_max, SharedFold sf,
     const float* __restrict__ row_w, float* __restrict__ s_acc) {
   static_assert(!(SHARED && SCATTER), "the shared expert is folded in with the gather combine only");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
     const int v = __hip_atomic_load(ready + rix, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return __builtin_amdgcn_readfirstlane(v) >= tgt;
   };
-  // Bounded: past F_SPIN_MAX polls, or as soon as any block has set the error word, give up
+  // Bounded: past spin_max polls, or as soon as any block has set the error word, give up
   // (the results are then invalid and the error word says so).
   auto wait_ready = [&](int rix) {
     for (int n = 0;; ++n) {
@@ -389,7 +389,7 @@ __global__ __launch_bounds__(F_THREADS, 1) void ffn_bf16_fused_kernel(
       if ((n & 255) == 255 &&
           __builtin_amdgcn_readfirstlane(__hip_atomic_load(ctl + C_ERR, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)))
         return;
-      if (n >= F_SPIN_MAX) {
+      if (n >= spin_max) {
         if (lane == 0) __hip_atomic_store(ctl + C_ERR, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
       }
@@ -722,12 +722,18 @@ moe_status_t launch_ffn_fused_bf16(const void* x, const int* row_src, int T, int
     const int l = std::atoi(v);
     if (l >= 1) lag = std::min(l, E + 1);
   }
+  // MOE_FUSED_SPIN_MAX=n (n >= 0) lowers the bound of a readiness wait, so that a test can
+  // make waits give up and check that the launch still ends and reports it in the error word.
+  int spin_max = F_SPIN_MAX;
+  if (const char* v = std::getenv("MOE_FUSED_SPIN_MAX")) {
+    if (v[0]) spin_max = std::max(0, std::min(std::atoi(v), F_SPIN_MAX));
+  }
   auto kern = s_acc ? &ffn_bf16_fused_kernel<false, true>
                     : sf.T > 0 ? &ffn_bf16_fused_kernel<true, false> : &ffn_bf16_fused_kernel<false, false>;
   kern<<<device_cu_count(), F_THREADS, F_LDS, s>>>(
       static_cast<const uint16_t*>(x), row_src, T, K, cu, E, H, Hp, static_cast<const uint16_t*>(wg),
       static_cast<const uint16_t*>(wu), static_cast<const uint16_t*>(wd), static_cast<uint16_t*>(h),
-      static_cast<uint16_t*>(y), ctl, lag, sf, row_w, s_acc);
+      static_cast<uint16_t*>(y), ctl, lag, spin_max, sf, row_w, s_acc);
   return launch_status();
 }
 

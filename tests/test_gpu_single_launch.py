@@ -132,6 +132,36 @@ def test_fused_back_to_back_calls_share_a_workspace(queue_order):
     check_against_steps(wb, rb, yb, hb)
 
 
+def test_wait_bound_ends_the_launch_and_sets_the_error_word():
+    """The readiness waits are bounded. With the bound lowered to zero polls
+    (MOE_FUSED_SPIN_MAX=0) and each expert's down tiles queued one expert behind its gate/up
+    tiles (MOE_FUSED_LAG=1), down tiles taken before their rows are ready give up waiting at
+    once. The launch still ends, runs every tile once and reports error 1 (its results are then
+    invalid). The next call on the same workspace, with the default bound, is correct again:
+    each launch resets its control words."""
+    spec = CASES[0]
+    say(f"single-launch FFN, readiness waits bounded at 0 polls {spec}")
+    w = gen.make(**spec, act="bf16", wgt="bf16", out="bf16", cid=99, device=DEV)
+    r = run_steps(w)
+    os.environ["MOE_FUSED_LAG"] = "1"
+    os.environ["MOE_FUSED_SPIN_MAX"] = "0"
+    try:
+        _, _, ctl, ws = run_fused(w, r["row_src"], r["cu_seqlens"])
+        torch.cuda.synchronize()
+        c = host(ctl).astype(np.int64)
+    finally:
+        del os.environ["MOE_FUSED_LAG"]
+        del os.environ["MOE_FUSED_SPIN_MAX"]
+    want = fused_tile_count(host(r["counts"]), w.H, w.Hp)
+    print(f"  error {c[8]}, tiles {c[9]} (want {want}), not prefetched {c[10]}", flush=True)
+    assert c[8] == 1
+    assert c[9] == want
+    y, h, ctl2, _ = run_fused(w, r["row_src"], r["cu_seqlens"], ws=ws)
+    torch.cuda.synchronize()
+    check_ctl(ctl2, host(r["counts"]), w.H, w.Hp)
+    check_against_steps(w, r, y, h)
+
+
 def run_layer_env(w, value, combine=moe.MOE_COMBINE_GATHER):
     os.environ["MOE_LAYER_FUSED"] = value
     try:
