@@ -503,7 +503,7 @@ def main():
         line["cpu_baseline"] = cpu_baseline(w, args, out, y if pad == 1 else None)
     if args.config == "c4" and not args.no_sweep:
         line["skew_sweep"] = skew_sweep(w, args, step, graph if not args.no_graph else None, ev, counts,
-                                        stage_ms, ms_step, torch)
+                                        stage_ms, ms_step, torch, out, y if pad == 1 else None)
     print(json.dumps(line), flush=True)
 
 
@@ -511,11 +511,13 @@ def sweep_stages(args):
     return ("permute", "ffn", "combine") if args.ffn == "fused" else ("permute", "gate_up", "down", "combine")
 
 
-def skew_sweep(w, args, step, graph, ev, counts, stage_ms, ms_step, torch):
+def skew_sweep(w, args, step, graph, ev, counts, stage_ms, ms_step, torch, out=None, y=None):
     """The same layer at every maxvio target: only the routing logits change (copied into the
     buffer the step and its graph read), x and the weights stay. Per target: the step time
     (graph replays, as the headline), tokens/s and the per-stage times (eager pass, HIP events
-    on the launch stream). The headline target reuses the headline's figures."""
+    on the launch stream), and unless --no-cpu-baseline the oracle timed on a shorter sample
+    (about 2.5 s of host work) with its comparison against the GPU's rows. The headline target
+    reuses the headline's figures (its oracle timing is the line's cpu_baseline)."""
     from workloads import gen
     base = w.logits.clone()
     head_cnt = counts.cpu().numpy()          # the headline routing, before any target replaces it
@@ -557,6 +559,8 @@ def skew_sweep(w, args, step, graph, ev, counts, stage_ms, ms_step, torch):
         res[f"{mv:g}"] = {"ms_per_step": ms, "tokens_per_s": w.T / (ms / 1e3), "stage_ms": st,
                           "maxvio": float(cnt.max() / (w.T * w.K / w.E) - 1.0),
                           "rows_min": int(cnt.min()), "rows_max": int(cnt.max())}
+        if not args.no_cpu_baseline and out is not None:
+            res[f"{mv:g}"]["cpu_baseline"] = cpu_baseline(w, args, out, y, budget_s=2.5)
     w.logits.copy_(base)
     ms = [v["ms_per_step"] for v in res.values()]
     res["slowest_over_fastest"] = max(ms) / min(ms)
@@ -658,7 +662,7 @@ def time_backward(w, args, moe, torch):
             "work": "forward recomputed + dgrad + wgrad (18 M H H' flops), bf16, HIP graph replay"}
 
 
-def cpu_baseline(w, args, gpu_out, gpu_y=None):
+def cpu_baseline(w, args, gpu_out, gpu_y=None, budget_s=10.0):
     """The oracle, as it stands, on the host: whole layer when small, else routing + permute +
     combine for all tokens and the FFN for a sample of experts, scaled to all experts. The
     GPU's result is compared with the oracle's: the whole output when every expert is in the
@@ -725,9 +729,9 @@ def cpu_baseline(w, args, gpu_out, gpu_y=None):
         y_sampled.extend(y_rows[lo:hi] for lo, hi in sampled_rows)
         return (t1 - t0) + t_ffn * scale + (t3 - t2), (t1 - t0) + t_ffn + (t3 - t2), out
 
-    # repeat the pass until about 10 s of host work has been measured (at most 20 passes)
+    # repeat the pass until about budget_s of host work has been measured (at most 20 passes)
     totals, measured, ref = [], 0.0, None
-    while not totals or (measured < 10.0 and len(totals) < 20):
+    while not totals or (measured < budget_s and len(totals) < 20):
         tot, meas, ref = one_pass()
         totals.append(tot)
         measured += meas
