@@ -181,6 +181,40 @@ def test_gather_and_scatter_argument_checks():
             moe.MOE_BF16, 16, 16, 4, 2, 16, 0)                            # H % 256
 
 
+def test_single_launch_argument_checks():
+    """moe_grouped_ffn_fused and moe_grouped_ffn_fused_scatter reject on the host, before any
+    launch: unsupported formats and shapes, a short workspace, missing buffers."""
+    M, E, H, Hp = 64, 4, 512, 256
+    n = moe.moe_grouped_ffn_fused_workspace_bytes(M, E, Hp)
+    assert n >= M * Hp * 2 + 16 * 4
+    assert moe.moe_grouped_ffn_fused_workspace_bytes(-1, E, Hp) == 0
+    f = moe.moe_grouped_ffn_fused
+    # (x, act, row_src, T, K, cu, M, E, H, Hp, wg, wu, wd, wgt, y_rows, out, ws, ws_bytes, stream)
+    base = dict(x=16, act=moe.MOE_BF16, row_src=16, T=32, K=2, cu_seqlens=16, M=M, E=E, H=H, Hp=Hp,
+                w_gate=16, w_up=16, w_down=16, wgt=moe.MOE_BF16, y_rows=16, out=moe.MOE_BF16, ws=16,
+                ws_bytes=n, stream=0)
+    for kw, status in ((dict(act=moe.MOE_F32), moe.MOE_EUNSUPPORTED),
+                       (dict(out=moe.MOE_F32), moe.MOE_EUNSUPPORTED),
+                       (dict(H=384), moe.MOE_EUNSUPPORTED),             # H % 256
+                       (dict(Hp=128), moe.MOE_EUNSUPPORTED),            # K loop of down too short
+                       (dict(E=1025), moe.MOE_EUNSUPPORTED),
+                       (dict(K=0), moe.MOE_EINVAL),
+                       (dict(ws_bytes=n - 1), moe.MOE_EWORKSPACE),
+                       (dict(cu_seqlens=None), moe.MOE_EINVAL),
+                       (dict(y_rows=None), moe.MOE_EINVAL)):
+        _expect(status, lambda: f(**dict(base, **kw)))
+    s = moe.moe_grouped_ffn_fused_scatter
+    # (x, act, row_src, T, K, cu, M, E, H, Hp, wg, wu, wd, wgt, row_w, acc, ws, ws_bytes, stream)
+    sbase = dict(base, row_w=16, acc=16)
+    del sbase["y_rows"], sbase["out"]
+    for kw, status in ((dict(act=moe.MOE_FP8_E4M3), moe.MOE_EUNSUPPORTED),
+                       (dict(H=384), moe.MOE_EUNSUPPORTED),
+                       (dict(ws_bytes=n - 1), moe.MOE_EWORKSPACE),
+                       (dict(row_w=None), moe.MOE_EINVAL),
+                       (dict(acc=None), moe.MOE_EINVAL)):
+        _expect(status, lambda: s(**dict(sbase, **kw)))
+
+
 def test_layer_forward_rejects_small_workspace():
     d = moe.LayerDesc(64, 128, 64, 8, 2, moe.MOE_F32, moe.MOE_F32, moe.MOE_F32, 0)
     n = moe.moe_layer_workspace_bytes(d)
