@@ -89,6 +89,10 @@ def parse():
                          "(moe_grouped_ffn_fused, or moe_grouped_ffn_fused_scatter with --combine "
                          "scatter, reported as stage 'ffn'); auto picks as moe_layer_forward does: "
                          "one launch when T*K <= 256*E and the combine is the gather")
+    ap.add_argument("--mxfp4-layout", default="paired", choices=["plain", "paired"],
+                    help="MXFP4 weights (c5): repacked once before timing into the paired layout "
+                         "(moe_pack_mxfp4_pairs, MOE_MXFP4_PAIRED; the default, about 1 %% faster "
+                         "at c5) or read in their stored layout")
     ap.add_argument("--xperm", action="store_true",
                     help="materialise x_perm in the permute instead of gathering rows in gate/up")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -197,6 +201,18 @@ def main():
     DT = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "fp8": moe.MOE_FP8_E4M3, "mxfp4": moe.MOE_MXFP4}
     TD = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
     hf = "fp8" if w.act == "fp8" else w.act
+    # The weights as the step reads them. With --mxfp4-layout paired the MXFP4 codes are
+    # repacked once, before any timing (like loading the weights), into the layout of
+    # MOE_MXFP4_PAIRED; the oracle keeps reading the stored layout of w.
+    wg_g, wu_g, wd_g, wgt_g = w.w_gate, w.w_up, w.w_down, DT[w.wgt]
+    if w.wgt == "mxfp4" and args.mxfp4_layout == "paired":
+        def pack(t, n_cols, k_red):
+            o = torch.empty_like(t)
+            moe.moe_pack_mxfp4_pairs(t, o, E, n_cols, k_red, None)
+            return o
+        wg_g, wu_g, wd_g = pack(w.w_gate, Hp, H), pack(w.w_up, Hp, H), pack(w.w_down, H, Hp)
+        wgt_g = moe.MOE_MXFP4_PAIRED
+        torch.cuda.synchronize()
     yf = "f32" if w.act == "f32" else "bf16"
     i32 = dict(dtype=torch.int32, device=dev)
     f32 = dict(dtype=torch.float32, device=dev)
@@ -262,33 +278,33 @@ def main():
             # the weighted combine in the single launch's down epilogue, into the fp32 accumulator
             mark("combine", lambda: acc.zero_())
             mark("ffn", lambda: moe.moe_grouped_ffn_fused_scatter(w.x, DT[w.act], row_src, T, K, cu, M, E, H,
-                                                                  Hp, w.w_gate, w.w_up, w.w_down, DT[w.wgt],
+                                                                  Hp, wg_g, wu_g, wd_g, wgt_g,
                                                                   row_w, acc, ws_f, nws_f, None))
             if acc is not out:
                 mark("combine", lambda: out.copy_(acc))
             return
         if fused:
             mark("ffn", lambda: moe.moe_grouped_ffn_fused(w.x, DT[w.act], row_src, T, K, cu, M, E, H, Hp,
-                                                          w.w_gate, w.w_up, w.w_down, DT[w.wgt], y, DT[yf],
+                                                          wg_g, wu_g, wd_g, wgt_g, y, DT[yf],
                                                           ws_f, nws_f, None))
             mark("combine", lambda: moe.moe_combine(y, DT[yf], pos, topk_w, T, H, K, out, DT[w.out], None))
             return
         if args.xperm:
             mark("gate_up", lambda: moe.moe_ffn_gate_up(x_perm, x_perm_sf, DT[w.act], cu, MR, E, H, Hp,
-                                                        w.w_gate, w.w_up, w.sf_gate, w.sf_up,
-                                                        DT[w.wgt], h, h_sf, None))
+                                                        wg_g, wu_g, w.sf_gate, w.sf_up,
+                                                        wgt_g, h, h_sf, None))
         else:
             mark("gate_up", lambda: moe.moe_ffn_gate_up_gather(w.x, None, x_perm_sf, DT[w.act], row_src, T,
-                                                               K, cu, MR, E, H, Hp, w.w_gate, w.w_up,
-                                                               w.sf_gate, w.sf_up, DT[w.wgt], h, h_sf, None))
+                                                               K, cu, MR, E, H, Hp, wg_g, wu_g,
+                                                               w.sf_gate, w.sf_up, wgt_g, h, h_sf, None))
         if not scatter:
-            mark("down", lambda: moe.moe_ffn_down(h, h_sf, DT[hf], cu, MR, E, H, Hp, w.w_down, w.sf_down,
-                                                  DT[w.wgt], y, DT[yf], None))
+            mark("down", lambda: moe.moe_ffn_down(h, h_sf, DT[hf], cu, MR, E, H, Hp, wd_g, w.sf_down,
+                                                  wgt_g, y, DT[yf], None))
             mark("combine", lambda: moe.moe_combine(y, DT[yf], pos, topk_w, T, H, K, out, DT[w.out], None))
         else:
             mark("combine", lambda: acc.zero_())
-            mark("down", lambda: moe.moe_ffn_down_scatter(h, h_sf, DT[hf], cu, MR, E, H, Hp, w.w_down,
-                                                          w.sf_down, DT[w.wgt], row_src, row_w, T, K,
+            mark("down", lambda: moe.moe_ffn_down_scatter(h, h_sf, DT[hf], cu, MR, E, H, Hp, wd_g,
+                                                          w.sf_down, wgt_g, row_src, row_w, T, K,
                                                           acc, None))
             if acc is not out:
                 mark("combine", lambda: out.copy_(acc))
@@ -467,7 +483,8 @@ def main():
                    "E": E, "K": K, "act": w.act, "wgt": w.wgt, "combine": args.combine,
                    "x_perm": "materialised" if args.xperm else "gathered in gate/up",
                    "ffn": "one persistent launch" if fused else "two persistent launches",
-                   "pad": pad, "input": "bf16, quantised in the step" if quant else w.act},
+                   "pad": pad, "input": "bf16, quantised in the step" if quant else w.act,
+                   "mxfp4_layout": args.mxfp4_layout if w.wgt == "mxfp4" else None},
         "rows": {"real": int(cnt.sum()), "in_groups": int(cu[-1].item()), "buffer": int(MR)},
         "grouped_ffn_tflops": ffn_tflops,
         "grouped_ffn_frac_of_mfma_peak": ffn_tflops / peak_flops,

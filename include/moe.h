@@ -69,8 +69,19 @@ typedef enum {
  *                Stored reduction-contiguous: byte j of output column n holds reduction
  *                index 2j in its low nibble and 2j+1 in its high nibble. Scale bytes are
  *                stored block-major, [K/32][N] per expert, so the scales one K step needs
- *                for consecutive columns are contiguous. */
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3 = 2, MOE_MXFP4 = 3 } moe_dtype_t;
+ *                for consecutive columns are contiguous.
+ *  MOE_MXFP4_PAIRED  the same codes and scales with the code bytes of each expert matrix in
+ *                the paired layout [N/2][K/128][2][64]: for columns 2p and 2p+1 and each step
+ *                of 128 reduction elements, column 2p's 64 bytes then column 2p+1's, so one
+ *                128-byte line holds both (written by moe_pack_mxfp4_pairs). Accepted wherever
+ *                MOE_MXFP4 weights are, with bitwise the same results. */
+typedef enum {
+  MOE_F32 = 0,
+  MOE_BF16 = 1,
+  MOE_FP8_E4M3 = 2,
+  MOE_MXFP4 = 3,
+  MOE_MXFP4_PAIRED = 4
+} moe_dtype_t;
 
 /* How the K expert results of a token are summed.
  *  MOE_COMBINE_GATHER  deterministic gather-reduce in fixed k order (bitwise reproducible),
@@ -82,7 +93,7 @@ typedef enum { MOE_COMBINE_GATHER = 0, MOE_COMBINE_SCATTER_ATOMIC = 1 } moe_comb
 /* Whole-layer description. Supported (act, wgt, out) combinations:
  *  (F32, F32, F32), (BF16, BF16, BF16), (FP8_E4M3, MXFP4, BF16), and (BF16, MXFP4, BF16):
  *  BF16 activations quantised on entry to FP8_E4M3 with 1x128 scales (moe_quantize_fp8),
- *  then the FP8_E4M3 x MXFP4 path. */
+ *  then the FP8_E4M3 x MXFP4 path. MXFP4_PAIRED may stand for MXFP4 in both. */
 typedef struct {
   int32_t T, H, Hp, E, K;
   moe_dtype_t act, wgt, out;
@@ -189,6 +200,18 @@ MOE_API moe_status_t moe_route_permute(const float* logits, const void* x, const
                                int32_t* cu_seqlens, int32_t* pos, int32_t* row_src, float* row_w,
                                void* x_perm, float* x_perm_sf, void* ws, size_t ws_bytes,
                                hipStream_t stream);
+
+/* MXFP4 weight codes to the paired layout of MOE_MXFP4_PAIRED (the MoonEP news article,
+ * "Design principles and technical details": the weights are laid out for the GEMM). The
+ * fp8 x MXFP4 kernels stage 64 bytes of each column per K step; in the stored layout that is
+ * half a 128-byte line, in the paired layout two columns share each line, which halves the
+ * lines a weight load touches. A one-time preparation of a weight tensor, like loading it:
+ *  w [E, N, K/2] code bytes (MOE_MXFP4 layout of one projection: N output columns, reduction
+ *  K); w_paired [E, N/2, K/128, 2, 64] out, same size, not overlapping w. Both 16-byte
+ *  aligned. Needs N % 2 == 0 and K % 128 == 0 (MOE_EUNSUPPORTED otherwise). The scale bytes
+ *  are not touched: they keep their layout. One kernel launch, HBM-bound. */
+MOE_API moe_status_t moe_pack_mxfp4_pairs(const uint8_t* w, uint8_t* w_paired, int32_t E, int32_t N,
+                                          int32_t K, hipStream_t stream);
 
 /* Activation quantisation to FP8_E4M3 with 1x128 power-of-two scales ("Mixture of
  * Kittens", Step 8: activations are quantised for the fp8 GEMMs, fused into dispatch):

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 # moe_status_t
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_EWORKSPACE, MOE_EHIP = range(5)
 # moe_dtype_t
-MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4 = range(4)
+MOE_F32, MOE_BF16, MOE_FP8_E4M3, MOE_MXFP4, MOE_MXFP4_PAIRED = range(5)
 # moe_combine_t
 MOE_COMBINE_GATHER, MOE_COMBINE_SCATTER_ATOMIC = range(2)
 
@@ -30,7 +30,7 @@ WS_FIELDS = ("topk_idx", "topk_w", "counts", "cu_seqlens", "pos", "row_src", "ro
 
 EXPORTS = ("moe_route_topk", "moe_permute_workspace_bytes", "moe_permute", "moe_permute_noalloc",
            "moe_padded_capacity",
-           "moe_permute_padded", "moe_route_permute", "moe_quantize_fp8", "moe_ffn_gate_up",
+           "moe_permute_padded", "moe_route_permute", "moe_quantize_fp8", "moe_pack_mxfp4_pairs", "moe_ffn_gate_up",
            "moe_ffn_gate_up_gather", "moe_ffn_down", "moe_ffn_down_scatter",
            "moe_grouped_ffn_workspace_bytes", "moe_grouped_ffn",
            "moe_grouped_ffn_fused_workspace_bytes", "moe_grouped_ffn_fused",
@@ -73,6 +73,7 @@ _SIGS = {
     "moe_route_permute": (_I, [_P, _P, _P, _E, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P,
                                _P, _P, _S, _P]),
     "moe_quantize_fp8": (_I, [_P, _E, _I, _I, _P, _P, _P]),
+    "moe_pack_mxfp4_pairs": (_I, [_P, _P, _I, _I, _I, _P]),
     "moe_ffn_gate_up_gather": (_I, [_P, _P, _P, _E, _P, _I, _I, _P, _I, _I, _I, _I, _P, _P, _P, _P, _E,
                                     _P, _P, _P]),
     "moe_ffn_down_scatter": (_I, [_P, _P, _E, _P, _I, _I, _I, _I, _P, _P, _E, _P, _P, _I, _I, _P,
@@ -196,6 +197,11 @@ def moe_route_permute(logits, x, x_sf, act, T, H, E, K, pad, topk_idx, topk_w, c
 def moe_quantize_fp8(x, x_dtype, R, C, q, sf, stream=None):
     _check(lib().moe_quantize_fp8(_ptr(x), x_dtype, R, C, _ptr(q), _ptr(sf), _stream(stream)),
            "moe_quantize_fp8")
+
+
+def moe_pack_mxfp4_pairs(w, w_paired, E, N, K, stream=None):
+    _check(lib().moe_pack_mxfp4_pairs(_ptr(w), _ptr(w_paired), E, N, K, _stream(stream)),
+           "moe_pack_mxfp4_pairs")
 
 
 def moe_ffn_gate_up(x_perm, x_perm_sf, act, cu_seqlens, M, E, H, Hp, w_gate, w_up, sf_gate, sf_up,

@@ -79,7 +79,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     const uint8_t* __restrict__ A, const float* __restrict__ A_sf, const int* __restrict__ cu,
     int M, int E, int Kd, int N, const uint8_t* __restrict__ B0, const uint8_t* __restrict__ B0_sf,
     const uint8_t* __restrict__ B1, const uint8_t* __restrict__ B1_sf, uint8_t* __restrict__ C8,
-    float* __restrict__ C8_sf, uint16_t* __restrict__ C16, RowMaps maps) {
+    float* __restrict__ C8_sf, uint16_t* __restrict__ C16, RowMaps maps, int paired) {
   using CF = F8Cfg<GATED, BN>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   int* tstart = reinterpret_cast<int*>(smem + F8_NS * CF::STAGE);
@@ -111,14 +111,19 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
   }
   const int nsf = Kd / 128;  // activation scale blocks per row
   // B wave load j covers columns 16j'..16j'+15 (64 B each) of matrix j / (B_BYTES/1024):
-  // lane -> column lane/4, slot lane%4 holds chunk slot ^ ((col/4) % 4).
+  // lane -> column lane/4, slot lane%4 holds chunk slot ^ ((col/4) % 4). The stored [N][K/2]
+  // layout gives each column's 64 bytes of a K step half a 128-byte line; the paired layout
+  // ([N/2][K/128][2][64 B]) puts the 64-byte runs of columns 2p and 2p+1 side by side in one
+  // line, so a load touches 8 lines instead of 16. The bytes staged in LDS are the same.
   int b_voff[CF::B_LD];
 #pragma unroll
   for (int i = 0; i < CF::B_LD; ++i) {
     const int j = wave + 8 * i;
     const int c = (j % (CF::B_BYTES / 1024)) * 16 + (lane >> 2);
-    b_voff[i] = c * kbytes + (((lane & 3) ^ ((c >> 2) & 3)) << 4);
+    const int chunk = ((lane & 3) ^ ((c >> 2) & 3)) << 4;
+    b_voff[i] = paired ? (c >> 1) * Kd + (c & 1) * (F8_BK / 2) + chunk : c * kbytes + chunk;
   }
+  const int b_kstep = paired ? F8_BK : F8_BK / 2;   // bytes between K steps of one column
 
   // fragment offsets. A (fp8, 32x64 per MFMA): row mt*128 + wm*32 + lane%32, chunks 4kk + G
   // and 4kk + 2 + G. B (fp4): column wn*WN + nt*32 + lane%32, chunk 2kk + G.
@@ -205,7 +210,7 @@ __global__ __launch_bounds__(F8_THREADS, 1) void ffn_fp8_kernel(
     for (int i = 0; i < CF::B_LD; ++i) {
       const int j = wave + 8 * i;
       const bool second = GATED && (j / (CF::B_BYTES / 1024)) != 0;
-      lds_dma16(second ? d.rB1 : d.rB0, so + CF::A_BYTES + j * 1024, b_voff[i], kt * (F8_BK / 2));
+      lds_dma16(second ? d.rB1 : d.rB0, so + CF::A_BYTES + j * 1024, b_voff[i], kt * b_kstep);
     }
     if (wave < 4) {
       // activation scales of block kt for tile rows 64 wave + lane. Plain (or gathered rows
@@ -401,7 +406,7 @@ template <bool GATED, int BN, bool MAPPED>
 static moe_status_t launch_f8_k(const uint8_t* A, const float* A_sf, const int* cu, int M, int E,
                               int Kd, int N, const uint8_t* B0, const uint8_t* B0_sf,
                               const uint8_t* B1, const uint8_t* B1_sf, uint8_t* C8, float* C8_sf,
-                              uint16_t* C16, const RowMaps& maps, hipStream_t s) {
+                              uint16_t* C16, const RowMaps& maps, bool paired, hipStream_t s) {
   using CF = F8Cfg<GATED, BN>;
   static bool attr_set = false;
   if (!attr_set) {
@@ -411,7 +416,7 @@ static moe_status_t launch_f8_k(const uint8_t* A, const float* A_sf, const int* 
     attr_set = true;
   }
   ffn_fp8_kernel<GATED, BN, MAPPED><<<device_cu_count(), F8_THREADS, CF::LDS_BYTES, s>>>(
-      A, A_sf, cu, M, E, Kd, N, B0, B0_sf, B1, B1_sf, C8, C8_sf, C16, maps);
+      A, A_sf, cu, M, E, Kd, N, B0, B0_sf, B1, B1_sf, C8, C8_sf, C16, maps, paired ? 1 : 0);
   return launch_status();
 }
 
@@ -419,30 +424,32 @@ template <bool GATED, int BN>
 static moe_status_t launch_f8(const uint8_t* A, const float* A_sf, const int* cu, int M, int E,
                               int Kd, int N, const uint8_t* B0, const uint8_t* B0_sf,
                               const uint8_t* B1, const uint8_t* B1_sf, uint8_t* C8, float* C8_sf,
-                              uint16_t* C16, const RowMaps& maps, hipStream_t s) {
+                              uint16_t* C16, const RowMaps& maps, bool paired, hipStream_t s) {
   const bool mapped = GATED ? maps.a_src != nullptr : maps.s_acc != nullptr;
   if (mapped)
-    return launch_f8_k<GATED, BN, true>(A, A_sf, cu, M, E, Kd, N, B0, B0_sf, B1, B1_sf, C8, C8_sf, C16, maps, s);
-  return launch_f8_k<GATED, BN, false>(A, A_sf, cu, M, E, Kd, N, B0, B0_sf, B1, B1_sf, C8, C8_sf, C16, maps, s);
+    return launch_f8_k<GATED, BN, true>(A, A_sf, cu, M, E, Kd, N, B0, B0_sf, B1, B1_sf, C8, C8_sf, C16, maps,
+                                        paired, s);
+  return launch_f8_k<GATED, BN, false>(A, A_sf, cu, M, E, Kd, N, B0, B0_sf, B1, B1_sf, C8, C8_sf, C16, maps,
+                                       paired, s);
 }
 
 moe_status_t launch_ffn_gate_up_fp8(const void* x_perm, const float* x_sf, const int* cu, int M,
                                     int E, int H, int Hp, const void* wg, const uint8_t* sg,
                                     const void* wu, const uint8_t* su, void* h, float* h_sf,
-                                    const RowMaps& maps, hipStream_t s) {
+                                    const RowMaps& maps, bool paired, hipStream_t s) {
   if (M == 0) return MOE_OK;
   return launch_f8<true, 128>(static_cast<const uint8_t*>(x_perm), x_sf, cu, M, E, H, Hp,
                               static_cast<const uint8_t*>(wg), sg, static_cast<const uint8_t*>(wu),
-                              su, static_cast<uint8_t*>(h), h_sf, nullptr, maps, s);
+                              su, static_cast<uint8_t*>(h), h_sf, nullptr, maps, paired, s);
 }
 
 moe_status_t launch_ffn_down_fp8(const void* h, const float* h_sf, const int* cu, int M, int E,
                                  int H, int Hp, const void* wd, const uint8_t* sd, void* y,
-                                 const RowMaps& maps, hipStream_t s) {
+                                 const RowMaps& maps, bool paired, hipStream_t s) {
   if (M == 0) return MOE_OK;
   return launch_f8<false, 256>(static_cast<const uint8_t*>(h), h_sf, cu, M, E, Hp, H,
                                static_cast<const uint8_t*>(wd), sd, nullptr, nullptr, nullptr,
-                               nullptr, static_cast<uint16_t*>(y), maps, s);
+                               nullptr, static_cast<uint16_t*>(y), maps, paired, s);
 }
 
 }  // namespace moe

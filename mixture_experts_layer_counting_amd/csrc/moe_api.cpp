@@ -31,9 +31,10 @@ moe_status_t launch_ffn_down_bf16(const void*, const int*, int, int, int, int, c
                                   const RowMaps&, hipStream_t);
 moe_status_t launch_ffn_gate_up_fp8(const void*, const float*, const int*, int, int, int, int,
                                     const void*, const uint8_t*, const void*, const uint8_t*, void*,
-                                    float*, const RowMaps&, hipStream_t);
+                                    float*, const RowMaps&, bool paired, hipStream_t);
 moe_status_t launch_ffn_down_fp8(const void*, const float*, const int*, int, int, int, int,
-                                 const void*, const uint8_t*, void*, const RowMaps&, hipStream_t);
+                                 const void*, const uint8_t*, void*, const RowMaps&, bool paired, hipStream_t);
+moe_status_t launch_pack_mxfp4_pairs(const void* w, void* out, int E, int N, int K, hipStream_t s);
 moe_status_t launch_ffn_gate_up_f32(const void*, const int*, int, int, int, int, const void*,
                                     const void*, void*, const RowMaps&, hipStream_t);
 moe_status_t launch_ffn_down_f32(const void*, const int*, int, int, int, int, const void*, void*,
@@ -92,7 +93,7 @@ enum Path { PATH_NONE, PATH_F32, PATH_BF16, PATH_FP8_MXFP4 };
 static Path ffn_path(moe_dtype_t act, moe_dtype_t wgt) {
   if (act == MOE_F32 && wgt == MOE_F32) return PATH_F32;
   if (act == MOE_BF16 && wgt == MOE_BF16) return PATH_BF16;
-  if (act == MOE_FP8_E4M3 && wgt == MOE_MXFP4) return PATH_FP8_MXFP4;
+  if (act == MOE_FP8_E4M3 && (wgt == MOE_MXFP4 || wgt == MOE_MXFP4_PAIRED)) return PATH_FP8_MXFP4;
   return PATH_NONE;
 }
 
@@ -282,6 +283,16 @@ moe_status_t moe_quantize_fp8(const void* x, moe_dtype_t x_dtype, int32_t R, int
   return launch_quantize_fp8(x, x_dtype, R, C, q, sf, stream);
 }
 
+moe_status_t moe_pack_mxfp4_pairs(const uint8_t* w, uint8_t* w_paired, int32_t E, int32_t N, int32_t K,
+                                  hipStream_t stream) {
+  if (E < 0 || N < 0 || K < 0) return MOE_EINVAL;
+  if (N % 2 || K % 128) return MOE_EUNSUPPORTED;
+  if ((size_t)E * N * K == 0) return MOE_OK;
+  if (!w || !w_paired || w == w_paired) return MOE_EINVAL;
+  if ((uintptr_t)w % 16 || (uintptr_t)w_paired % 16) return MOE_EINVAL;
+  return launch_pack_mxfp4_pairs(w, w_paired, E, N, K, stream);
+}
+
 moe_status_t moe_ffn_gate_up(const void* x_perm, const float* x_perm_sf, moe_dtype_t act,
                              const int32_t* cu_seqlens, int32_t M, int32_t E, int32_t H,
                              int32_t Hp, const void* w_gate, const void* w_up,
@@ -296,7 +307,7 @@ moe_status_t moe_ffn_gate_up(const void* x_perm, const float* x_perm_sf, moe_dty
   if (p == PATH_FP8_MXFP4) {
     if (M > 0 && (!x_perm_sf || !sf_gate || !sf_up || !h_sf)) return MOE_EINVAL;
     return launch_ffn_gate_up_fp8(x_perm, x_perm_sf, cu_seqlens, M, E, H, Hp, w_gate, sf_gate, w_up,
-                                  sf_up, h, h_sf, RowMaps{}, stream);
+                                  sf_up, h, h_sf, RowMaps{}, wgt == MOE_MXFP4_PAIRED, stream);
   }
   if (p == PATH_F32)
     return launch_ffn_gate_up_f32(x_perm, cu_seqlens, M, E, H, Hp, w_gate, w_up, h, RowMaps{}, stream);
@@ -329,7 +340,7 @@ static moe_status_t gate_up_gather(const void* x, const float* x_sf, const float
     if (M > 0 && ((!x_sf && !x_perm_sf) || !sf_gate || !sf_up || !h_sf)) return MOE_EINVAL;
     maps.a_sf_perm = x_perm_sf;
     return launch_ffn_gate_up_fp8(x, x_sf, cu_seqlens, M, E, H, Hp, w_gate, sf_gate, w_up, sf_up, h,
-                                  h_sf, maps, stream);
+                                  h_sf, maps, wgt == MOE_MXFP4_PAIRED, stream);
   }
   if (p == PATH_F32) return launch_ffn_gate_up_f32(x, cu_seqlens, M, E, H, Hp, w_gate, w_up, h, maps, stream);
   return launch_ffn_gate_up_bf16(x, cu_seqlens, M, E, H, Hp, w_gate, w_up, h, maps, stream);
@@ -358,7 +369,7 @@ moe_status_t moe_ffn_down(const void* h, const float* h_sf, moe_dtype_t h_dtype,
   if (p == PATH_FP8_MXFP4) {
     if (M > 0 && (!h_sf || !sf_down)) return MOE_EINVAL;
     return launch_ffn_down_fp8(h, h_sf, cu_seqlens, M, E, H, Hp, w_down, sf_down, y_rows, RowMaps{},
-                               stream);
+                               wgt == MOE_MXFP4_PAIRED, stream);
   }
   if (p == PATH_F32) return launch_ffn_down_f32(h, cu_seqlens, M, E, H, Hp, w_down, y_rows, RowMaps{}, stream);
   return launch_ffn_down_bf16(h, cu_seqlens, M, E, H, Hp, w_down, y_rows, RowMaps{}, stream);
@@ -383,7 +394,8 @@ moe_status_t moe_ffn_down_scatter(const void* h, const float* h_sf, moe_dtype_t 
   maps.s_acc = acc;
   if (p == PATH_FP8_MXFP4) {
     if (M > 0 && (!h_sf || !sf_down)) return MOE_EINVAL;
-    return launch_ffn_down_fp8(h, h_sf, cu_seqlens, M, E, H, Hp, w_down, sf_down, nullptr, maps, stream);
+    return launch_ffn_down_fp8(h, h_sf, cu_seqlens, M, E, H, Hp, w_down, sf_down, nullptr, maps,
+                               wgt == MOE_MXFP4_PAIRED, stream);
   }
   if (p == PATH_F32) return launch_ffn_down_f32(h, cu_seqlens, M, E, H, Hp, w_down, nullptr, maps, stream);
   return launch_ffn_down_bf16(h, cu_seqlens, M, E, H, Hp, w_down, nullptr, maps, stream);
@@ -503,7 +515,7 @@ enum {
 // A BF16 layer with MXFP4 experts quantises its activations to fp8 (1x128 scales) once on
 // entry and then runs the fp8 x MXFP4 path ("Mixture of Kittens", Step 8).
 static bool layer_quantizes(const moe_layer_desc_t* d) {
-  return d->act == MOE_BF16 && d->wgt == MOE_MXFP4;
+  return d->act == MOE_BF16 && (d->wgt == MOE_MXFP4 || d->wgt == MOE_MXFP4_PAIRED);
 }
 static moe_dtype_t layer_act(const moe_layer_desc_t* d) {
   return layer_quantizes(d) ? MOE_FP8_E4M3 : d->act;

@@ -72,4 +72,37 @@ moe_status_t launch_quantize_fp8(const void* x, moe_dtype_t xt, int R, int C, vo
   return launch_status();
 }
 
+// MXFP4 weight codes from the stored layout [E][N][K/2] (each column's K/2 bytes contiguous)
+// to the paired layout [E][N/2][K/128][2][64]: for every pair of columns (2p, 2p+1) and every
+// step of 128 reduction elements, the two columns' 64-byte runs side by side, so that one
+// 128-byte line holds what the fp8 x MXFP4 kernels stage for both columns in one K step (the
+// MoonEP news article, "Design principles and technical details": the weights are laid out
+// for the GEMM). The scale bytes keep their layout. A thread per 16 output bytes; a plain
+// HBM-bound copy, run once per weight tensor.
+__global__ __launch_bounds__(256) void pack_mxfp4_pairs_kernel(const uint8_t* __restrict__ w,
+                                                               uint8_t* __restrict__ out, size_t n16,
+                                                               size_t per_e, int K) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t q = (size_t)blockIdx.x * blockDim.x + threadIdx.x; q < n16; q += stride) {
+    const size_t o = q * 16;
+    const size_t e = o / per_e, r = o % per_e;
+    const size_t p = r / K, r2 = r % K;          // column pair, then [K/128][2][64] within it
+    const size_t st = r2 / 128, r3 = r2 % 128;   // K step, then [2][64]
+    const size_t hcol = r3 / 64, b = r3 % 64;     // which column of the pair, byte in its run
+    const size_t src = e * per_e + (2 * p + hcol) * (size_t)(K / 2) + st * 64 + b;
+    *reinterpret_cast<uint4*>(out + o) = *reinterpret_cast<const uint4*>(w + src);
+  }
+}
+
+moe_status_t launch_pack_mxfp4_pairs(const void* w, void* out, int E, int N, int K, hipStream_t s) {
+  const size_t per_e = (size_t)N * (K / 2);
+  const size_t n16 = (size_t)E * per_e / 16;
+  if (n16 == 0) return MOE_OK;
+  const size_t want = (n16 + 255) / 256;
+  const int grid = (int)(want < 8192 ? want : 8192);
+  pack_mxfp4_pairs_kernel<<<grid, 256, 0, s>>>(static_cast<const uint8_t*>(w), static_cast<uint8_t*>(out),
+                                               n16, per_e, K);
+  return launch_status();
+}
+
 }  // namespace moe

@@ -3,7 +3,8 @@ import torch
 
 import mixture_experts_layer_counting_amd as moe
 
-DT = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "fp8": moe.MOE_FP8_E4M3, "mxfp4": moe.MOE_MXFP4}
+DT = {"f32": moe.MOE_F32, "bf16": moe.MOE_BF16, "fp8": moe.MOE_FP8_E4M3, "mxfp4": moe.MOE_MXFP4,
+      "mxfp4_paired": moe.MOE_MXFP4_PAIRED}
 TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
 
 
@@ -51,6 +52,21 @@ def run_steps(w, with_row_w=True):
     r["out"] = torch.empty((T, H), dtype=TORCH_DT[w.out], device=dev)
     moe.moe_combine(r["y_rows"], DT[y_fmt(w)], r["pos"], r["topk_w"], T, H, K, r["out"], DT[w.out])
     return r
+
+
+def paired(w):
+    """The workload with its MXFP4 weight codes repacked by moe_pack_mxfp4_pairs into the
+    MOE_MXFP4_PAIRED layout (gate/up: N = Hp output columns over K = H; down: N = H over
+    K = Hp). The scale tensors are shared: they keep their layout."""
+    import dataclasses
+    assert w.wgt == "mxfp4"
+
+    def pack(t, N, K):
+        out = torch.empty_like(t)
+        moe.moe_pack_mxfp4_pairs(t, out, w.E, N, K)
+        return out
+    return dataclasses.replace(w, wgt="mxfp4_paired", w_gate=pack(w.w_gate, w.Hp, w.H),
+                               w_up=pack(w.w_up, w.Hp, w.H), w_down=pack(w.w_down, w.H, w.Hp))
 
 
 def layer_desc(w, combine=moe.MOE_COMBINE_GATHER):

@@ -215,6 +215,16 @@ def test_single_launch_argument_checks():
         _expect(status, lambda: s(**dict(sbase, **kw)))
 
 
+def test_pack_mxfp4_pairs_argument_checks():
+    f = moe.moe_pack_mxfp4_pairs
+    _expect(moe.MOE_EUNSUPPORTED, f, 16, 32, 2, 3, 256, 0)      # N odd
+    _expect(moe.MOE_EUNSUPPORTED, f, 16, 32, 2, 4, 192, 0)      # K % 128
+    _expect(moe.MOE_EINVAL, f, 16, 16, 2, 4, 256, 0)            # in place
+    _expect(moe.MOE_EINVAL, f, None, 32, 2, 4, 256, 0)
+    _expect(moe.MOE_EINVAL, f, 16, 40, 2, 4, 256, 0)            # output not 16-byte aligned
+    _expect(moe.MOE_EINVAL, f, 16, 32, -1, 4, 256, 0)
+
+
 def test_layer_forward_rejects_small_workspace():
     d = moe.LayerDesc(64, 128, 64, 8, 2, moe.MOE_F32, moe.MOE_F32, moe.MOE_F32, 0)
     n = moe.moe_layer_workspace_bytes(d)

@@ -736,6 +736,51 @@ def test_layer_bf16_activations_mxfp4_experts(spec):
     assert np.array_equal(host(ws[lay["x_q"]:lay["x_q"] + n]).reshape(w.T, w.H), codes)
 
 
+# ----------------------------------------------------------------------------- paired MXFP4 layout
+
+def test_pack_mxfp4_pairs_layout():
+    """moe_pack_mxfp4_pairs writes [E][N/2][K/128][2][64] from [E][N][K/2]: output byte
+    (e, p, s, h, b) is input byte (e, 2p + h, 64 s + b), checked with numpy index arithmetic."""
+    rng = np.random.default_rng(71)
+    for E, N, K in ((3, 6, 256), (2, 258, 384), (1, 2, 128), (4, 128, 7168)):
+        say(f"pack MXFP4 pairs E={E} N={N} K={K}")
+        w = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+        wt = torch.from_numpy(w).to(DEV)
+        out = torch.full_like(wt, 0xA5)
+        moe.moe_pack_mxfp4_pairs(wt, out, E, N, K)
+        torch.cuda.synchronize()
+        want = w.reshape(E, N // 2, 2, K // 128, 64).transpose(0, 1, 3, 2, 4).reshape(E, N, K // 2)
+        assert np.array_equal(host(out), want)
+
+
+@pytest.mark.parametrize("spec", FP8_SMALL, ids=lambda s: "T{T}_H{H}_Hp{Hp}_E{E}_K{K}_{routing}".format(**s))
+def test_paired_mxfp4_weights_give_bitwise_the_same_results(spec):
+    """The fp8 x MXFP4 steps and layer with the weights repacked to MOE_MXFP4_PAIRED: h, its
+    scales, y_rows and out are bit for bit those of the stored layout (the kernels stage the
+    same bytes); the same for the layer that quantises bf16 activations on entry. The
+    scatter-add combine agrees within its atomic order."""
+    from _gpu_run import paired
+    say(f"MXFP4 paired layout against the stored one {spec}")
+    w = gen.make(**spec, act="fp8", wgt="mxfp4", out="bf16", cid=72, device=DEV)
+    wp = paired(w)
+    r, rp = run_steps(w), run_steps(wp)
+    out_l, _, _ = run_layer(w)
+    out_p, _, _ = run_layer(wp)
+    sc_l, _, _ = run_layer(w, combine=moe.MOE_COMBINE_SCATTER_ATOMIC)
+    sc_p, _, _ = run_layer(wp, combine=moe.MOE_COMBINE_SCATTER_ATOMIC)
+    torch.cuda.synchronize()
+    for k in ("h", "h_sf", "y_rows", "out"):
+        assert torch.equal(r[k], rp[k]), k
+    assert torch.equal(out_p, out_l)
+    d = float((sc_p.float() - sc_l.float()).abs().max() / sc_l.float().abs().max())
+    assert d <= 2.0 ** -7
+    wb = gen.make(**spec, act="bf16", wgt="mxfp4", out="bf16", cid=73, device=DEV)
+    ob, _, _ = run_layer(wb)
+    obp, _, _ = run_layer(paired(wb))
+    torch.cuda.synchronize()
+    assert torch.equal(obp, ob)
+
+
 # ----------------------------------------------------------------------------- backward
 
 BWD_CASES = [
@@ -878,6 +923,14 @@ def full_size_check(variants):
                 assert torch.equal(y_f, r["y_rows"]), f"{label}: single-launch y_rows differ"
                 del y_f
             del out_l, ws
+        if w.wgt == "mxfp4":
+            # the weights repacked to the paired layout: the same out, bit for bit
+            from _gpu_run import paired
+            wp = paired(w)
+            out_p, ws, _ = run_layer(wp)
+            torch.cuda.synchronize()
+            assert torch.equal(out_p, r["out"]), f"{label}: paired MXFP4 weights give another out"
+            del wp, out_p, ws
         out_sc, ws, _ = run_layer(w, combine=moe.MOE_COMBINE_SCATTER_ATOMIC)
         torch.cuda.synchronize()
         del ws
