@@ -739,13 +739,10 @@ static moe_status_t launch_fb_k(const uint16_t* A, const int* cu, int M, int E, 
                                 const uint16_t* B0, const uint16_t* B1, uint16_t* C,
                                 const RowMaps& maps, hipStream_t s) {
   using CF = FbCfg<GATED, BN, BK, NS>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_kernel<GATED, BN, BK, NS, MAPPED>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS_BYTES) != hipSuccess)
-      return MOE_EHIP;
-    attr_set = true;
-  }
+  static std::atomic<unsigned char> lds_set[MOE_MAX_DEVICES];
+  if (ensure_lds_limit(reinterpret_cast<const void*>(&ffn_bf16_kernel<GATED, BN, BK, NS, MAPPED>),
+                       CF::LDS_BYTES, lds_set) != MOE_OK)
+    return MOE_EHIP;
   const int grid = device_cu_count();
   ffn_bf16_kernel<GATED, BN, BK, NS, MAPPED><<<grid, FB_THREADS, CF::LDS_BYTES, s>>>(
       A, cu, M, E, Kd, N, B0, B1, C, tile_order_n_fastest(M, E), maps);
@@ -793,13 +790,10 @@ static moe_status_t launch_pp_k(const uint16_t* A, const int* cu, int M, int E, 
   // PF adds the cu_seqlens copy and the row sources of the next tile
   constexpr int LDS = CF::LDS_BYTES + (PF ? (FB_MAX_E + 1 + FB_BM) * 4 : 0);
   static_assert(LDS <= 160 * 1024, "LDS budget");
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_pp_kernel<GATED, BN, BK, NS, MAPPED, PF, NTB>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, LDS) != hipSuccess)
-      return MOE_EHIP;
-    attr_set = true;
-  }
+  static std::atomic<unsigned char> lds_set[MOE_MAX_DEVICES];
+  if (ensure_lds_limit(reinterpret_cast<const void*>(&ffn_bf16_pp_kernel<GATED, BN, BK, NS, MAPPED, PF, NTB>),
+                       LDS, lds_set) != MOE_OK)
+    return MOE_EHIP;
   ffn_bf16_pp_kernel<GATED, BN, BK, NS, MAPPED, PF, NTB><<<device_cu_count(), FB_THREADS, LDS, s>>>(
       A, cu, M, E, Kd, N, B0, B1, C, tile_order_n_fastest(M, E), maps);
   return launch_status();

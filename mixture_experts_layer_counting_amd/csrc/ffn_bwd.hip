@@ -425,13 +425,9 @@ static moe_status_t launch_dgrad(const uint16_t* A0, const uint16_t* A1, const i
                                  int Kd, int N, const uint16_t* W0, const uint16_t* W1, uint16_t* C,
                                  const uint16_t* G, const uint16_t* U, uint16_t* DG, uint16_t* DU,
                                  hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dgrad_kernel<EPI, DUAL>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, BW_LDS) != hipSuccess)
-      return MOE_EHIP;
-    attr_set = true;
-  }
+  static std::atomic<unsigned char> lds_set[MOE_MAX_DEVICES];
+  if (ensure_lds_limit(reinterpret_cast<const void*>(&bwd_dgrad_kernel<EPI, DUAL>), BW_LDS, lds_set) != MOE_OK)
+    return MOE_EHIP;
   bwd_dgrad_kernel<EPI, DUAL><<<device_cu_count(), BW_THREADS, BW_LDS, s>>>(A0, A1, cu, M, E, Kd, N, W0,
                                                                            W1, C, G, U, DG, DU);
   return launch_status();
@@ -461,13 +457,9 @@ moe_status_t launch_bwd_gate_up(const void* dg, const void* du, const int* cu, i
 // dW[e] = A_e^T . B_e for every expert (zero for empty experts)  [E, Md, Nd] fp32
 moe_status_t launch_bwd_wgrad(const void* A, const void* B, const int* cu, int E, int Md, int Nd,
                               float* W, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_wgrad_kernel),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 2 * BW_STAGE) != hipSuccess)
-      return MOE_EHIP;
-    attr_set = true;
-  }
+  static std::atomic<unsigned char> lds_set[MOE_MAX_DEVICES];
+  if (ensure_lds_limit(reinterpret_cast<const void*>(&bwd_wgrad_kernel), 2 * BW_STAGE, lds_set) != MOE_OK)
+    return MOE_EHIP;
   bwd_wgrad_kernel<<<device_cu_count(), BW_THREADS, 2 * BW_STAGE, s>>>(
       static_cast<const uint16_t*>(A), static_cast<const uint16_t*>(B), cu, E, Md, Nd, W);
   return launch_status();

@@ -408,13 +408,10 @@ static moe_status_t launch_f8_k(const uint8_t* A, const float* A_sf, const int* 
                               const uint8_t* B1, const uint8_t* B1_sf, uint8_t* C8, float* C8_sf,
                               uint16_t* C16, const RowMaps& maps, bool paired, hipStream_t s) {
   using CF = F8Cfg<GATED, BN>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_fp8_kernel<GATED, BN, MAPPED>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, CF::LDS_BYTES) != hipSuccess)
-      return MOE_EHIP;
-    attr_set = true;
-  }
+  static std::atomic<unsigned char> lds_set[MOE_MAX_DEVICES];
+  if (ensure_lds_limit(reinterpret_cast<const void*>(&ffn_fp8_kernel<GATED, BN, MAPPED>), CF::LDS_BYTES,
+                       lds_set) != MOE_OK)
+    return MOE_EHIP;
   ffn_fp8_kernel<GATED, BN, MAPPED><<<device_cu_count(), F8_THREADS, CF::LDS_BYTES, s>>>(
       A, A_sf, cu, M, E, Kd, N, B0, B0_sf, B1, B1_sf, C8, C8_sf, C16, maps, paired ? 1 : 0);
   return launch_status();

@@ -701,17 +701,13 @@ moe_status_t launch_ffn_fused_bf16(const void* x, const int* row_src, int T, int
   if (M == 0 && sf.T == 0) return MOE_OK;
   if (E + (sf.T > 0 ? 1 : 0) > F_MAX_E || H % 256 || Hp % 128 || H < 256 || Hp < 256) return MOE_EUNSUPPORTED;
   if (s_acc && (sf.T > 0 || !row_w)) return MOE_EINVAL;
-  static bool attr_set = false;
-  if (!attr_set) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_fused_kernel<false, false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, F_LDS) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_fused_kernel<true, false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, F_LDS) != hipSuccess ||
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_fused_kernel<false, true>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, F_LDS) != hipSuccess)
-      return MOE_EHIP;
-    attr_set = true;
-  }
+  static std::atomic<unsigned char> lds_set[3][MOE_MAX_DEVICES];
+  if (ensure_lds_limit(reinterpret_cast<const void*>(&ffn_bf16_fused_kernel<false, false>), F_LDS, lds_set[0]) !=
+          MOE_OK ||
+      ensure_lds_limit(reinterpret_cast<const void*>(&ffn_bf16_fused_kernel<true, false>), F_LDS, lds_set[1]) !=
+          MOE_OK ||
+      ensure_lds_limit(reinterpret_cast<const void*>(&ffn_bf16_fused_kernel<false, true>), F_LDS, lds_set[2]) != MOE_OK)
+    return MOE_EHIP;
   const int n = (int)fused_ctl_ints(M + sf.T, E + (sf.T > 0 ? 1 : 0));
   fused_ctl_reset_kernel<<<(n + 255) / 256, 256, 0, s>>>(ctl, n);
   // lag E + 1: every queue holds all its gate/up tiles before all its down tiles.

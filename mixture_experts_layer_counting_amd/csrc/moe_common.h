@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <stddef.h>
 
+#include <atomic>
+
 #include "../../include/moe.h"
 
 #define MOE_WAVE 64
@@ -31,6 +33,21 @@ inline moe_status_t launch_status() {
 }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+constexpr int MOE_MAX_DEVICES = 64;
+
+// Raise a kernel's dynamic LDS limit to `bytes` on the current device, once per device:
+// `done` is the caller's per-kernel table of device flags (a zero-initialised static). Two
+// threads arriving together may both set it, which is harmless.
+inline moe_status_t ensure_lds_limit(const void* kernel, int bytes, std::atomic<unsigned char>* done) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MOE_MAX_DEVICES) return MOE_EHIP;
+  if (done[dev].load(std::memory_order_acquire)) return MOE_OK;
+  if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess)
+    return MOE_EHIP;
+  done[dev].store(1, std::memory_order_release);
+  return MOE_OK;
+}
 
 bool env_flag(const char* name);
 
